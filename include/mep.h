@@ -1,0 +1,235 @@
+/*
+ * mep.h -- C ABI of the MI355X (gfx950) MoE routing and dispatch-layout
+ * library (libmep.so).
+ *
+ * Three calls form the data-parallel hot path of MoE expert dispatch on one
+ * GPU's token batch:
+ *
+ *   mep_route_topk   router logits [N,E] -> top-K expert ids and weights
+ *   mep_build_layout ids -> per-expert histogram, padded offsets, stable
+ *                    expanded<->permuted maps
+ *   mep_plan         ids + layout -> expert-parallel plan over R virtual
+ *                    ranks (membership, counts, prefix matrices, rank-tagged
+ *                    destinations with duplicate encoding, dedup lists)
+ *
+ * Sources, cited by page title and section:
+ *   [TRT]  TensorRT-LLM RoutingKernel.cuh (blockScaleMoe routing helpers,
+ *          histogram / offsets / permutation kernels)
+ *   [MOON] MoonEP planning.py (PlanningKernel: histogram, stable scatter,
+ *          padded group scan, dst computation, duplicate canonicalisation;
+ *          caller-allocated outputs and host-side checks)
+ *   [DEEP] DeepEP intranode.cu (notify_dispatch: rank prefix matrix,
+ *          aligned receive counts, channel prefix matrix, host asserts)
+ *
+ * Conventions shared by every call
+ *   - Pointers named as device buffers are device memory owned by the
+ *     caller: inputs are read only, outputs are preallocated, all arrays are
+ *     dense row-major.  `logits` must be 16-byte aligned, every other buffer
+ *     4-byte aligned ([MOON] launch helper alignment rules).
+ *   - Calls enqueue asynchronously on `stream` (a hipStream_t; NULL = the
+ *     null stream) and never synchronise.  They allocate nothing.
+ *   - Scratch lives in a caller-provided workspace of at least the size the
+ *     matching *_workspace_size call reports.  A workspace must be zero-filled
+ *     once before its first use; every call leaves it ready for the next one.
+ *     Calls sharing a workspace must be ordered (same stream, or synchronised);
+ *     overlapping calls on one workspace race.
+ *   - All checks run on the host before anything is enqueued.  On error
+ *     nothing is written and nothing is launched.  Capacities are checked
+ *     against worst-case bounds, so kernels have no error path.
+ *   - Optional outputs are marked "nullable"; NULL skips them.
+ *   - No exceptions cross the ABI; mep_status_string names a return code.
+ */
+#ifndef MEP_H_
+#define MEP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define MEP_OK 0
+#define MEP_ERR_INVALID_ARG 1 /* NULL required pointer, bad enum, bad size, misalignment */
+#define MEP_ERR_UNSUPPORTED 2 /* outside the supported envelope (see each call) */
+#define MEP_ERR_CAPACITY 3    /* caller capacity or workspace below the bound */
+#define MEP_ERR_DEVICE 4      /* the HIP runtime reported an error on launch */
+
+/* Logit element types. */
+#define MEP_F32 0  /* IEEE binary32 */
+#define MEP_BF16 1 /* bfloat16 (upper half of a binary32) */
+
+/* Scoring functions. */
+#define MEP_SOFTMAX 0
+#define MEP_SIGMOID 1
+
+typedef struct mep_route_params {
+    int score_fn;    /* MEP_SOFTMAX or MEP_SIGMOID */
+    int renormalize; /* 1: weights renormalised over the K selected experts */
+    int n_group;     /* expert groups for group-limited selection; 1 = off */
+    int topk_group;  /* groups kept when n_group > 1 */
+    int group_topn;  /* keys summed into a group's score (1 or 2) */
+    float scale;     /* factor applied to every weight */
+} mep_route_params;
+
+/*
+ * mep_route_topk -- top-K expert selection and routing weights.
+ *
+ * Per token t (row of `logits`):
+ *   key_e = logit_e                                 (MEP_SOFTMAX)
+ *   s_e   = sigmoid(logit_e), correctly rounded to binary32,
+ *   key_e = fl32(s_e + bias_e)                      (MEP_SIGMOID)
+ *   The sigmoid is the real function of [TRT] sigmoid_accurate; the library
+ *   returns its correctly rounded value so ids are reproducible bit for bit.
+ *   With n_group > 1 the experts form n_group contiguous groups; a group's
+ *   score is the binary32 sum of its group_topn largest keys (largest
+ *   first); the topk_group best groups (score desc, group index asc) stay
+ *   eligible.  The K best eligible experts (key desc, expert index asc) are
+ *   written to topk_ids[t*K + k] in that order.
+ *   Weights (computed in double, rounded once to binary32, then times scale):
+ *     softmax, renormalize: softmax over the K selected logits
+ *                           ([TRT] calcSoftmax over the top lanes)
+ *     softmax, no renorm:   softmax probability over all E logits
+ *                           ([TRT] calcSoftmax over the score vector)
+ *     sigmoid, renormalize: s_k / sum of the K selected s (0 if that is 0)
+ *     sigmoid, no renorm:   s_k
+ *
+ * Arguments
+ *   logits       device, [N,E] of `dtype`, 16-byte aligned
+ *   dtype        MEP_F32 or MEP_BF16
+ *   N            tokens, >= 0
+ *   E            experts, 1..1024
+ *   K            experts per token, 1..min(E,32)
+ *   bias         device, float[E]; required for MEP_SIGMOID, ignored otherwise
+ *   p            host pointer to the parameters above
+ *   topk_ids     device, int32[N,K] (output)
+ *   topk_weights device, float[N,K] (output, nullable)
+ * Returns MEP_ERR_UNSUPPORTED for E > 1024, K > min(E, 32), group_topn not
+ * in {1,2}, E % n_group != 0, or topk_group*(E/n_group) < K.
+ * Non-finite logits give unspecified (but memory-safe) results.
+ */
+int mep_route_topk(const void* logits, int dtype, int64_t N, int E, int K,
+                   const float* bias, const mep_route_params* p,
+                   int32_t* topk_ids, float* topk_weights, void* stream);
+
+/*
+ * mep_build_layout -- padded per-expert layout of the N*K routed slots.
+ *
+ * Slot i = t*K + k holds expert e = topk_ids[i].
+ *   tokens_per_expert[e] = #slots with expert e
+ *                          ([TRT] routingIndicesHistogramKernel)
+ *   padded_e = ceil(count_e / alignment) * alignment, 0 for an empty expert
+ *   cu_seqlens[0] = 0, cu_seqlens[e+1] = cu_seqlens[e] + padded_e
+ *                          ([MOON] Phase B2 padded group scan; [DEEP] aligned
+ *                           per-expert receive counts)
+ *   expanded_to_permuted[i] = cu_seqlens[e] + #{earlier slots with expert e}
+ *                          (stable by slot index: [MOON] run_c1 passA)
+ *   permuted_to_expanded[expanded_to_permuted[i]] = i; the padding rows of
+ *     [0, cu_seqlens[E]) hold -1 ([MOON] empty-slot sentinel)
+ *   zero_fill[e] = (cu_seqlens[e] + count_e, padded_e - count_e) if count_e > 0
+ *     and padded_e > count_e, else (0, 0)  ([MOON] zero-fill ranges)
+ *
+ * Arguments
+ *   topk_ids             device int32[N,K]; every id in [0,E) and the K ids of
+ *                        a token distinct (true of mep_route_topk output);
+ *                        other inputs give unspecified results
+ *   alignment            >= 1
+ *   tokens_per_expert    device int32[E] (nullable)
+ *   cu_seqlens           device int32[E+1]
+ *   expanded_to_permuted device int32[N*K]
+ *   permuted_to_expanded device int32[permuted_cap] (nullable); only the
+ *                        first cu_seqlens[E] entries are written
+ *   permuted_cap         >= N*K + min(E, N*K)*(alignment-1) when
+ *                        permuted_to_expanded is given, else ignored
+ *   zero_fill            device int32[E,2] (nullable)
+ *   ws, ws_bytes         workspace (see mep_layout_workspace_size)
+ * Returns MEP_ERR_UNSUPPORTED for E > 1024 or N*K > INT32_MAX - E*alignment.
+ */
+int mep_build_layout(const int32_t* topk_ids, int64_t N, int E, int K, int alignment,
+                     int32_t* tokens_per_expert, int32_t* cu_seqlens,
+                     int32_t* expanded_to_permuted, int32_t* permuted_to_expanded,
+                     int64_t permuted_cap, int32_t* zero_fill,
+                     void* ws, size_t ws_bytes, void* stream);
+
+size_t mep_layout_workspace_size(int64_t N, int E, int K);
+
+/* Outputs of mep_plan; every pointer is a device buffer and nullable. */
+typedef struct mep_plan_outputs {
+    uint8_t* is_token_in_rank;      /* [N,R]   1 iff some slot of t lands on r */
+    int32_t* num_tokens_per_rank;   /* [S,R]   tokens of shard s sent to rank r */
+    int32_t* num_tokens_per_expert; /* [S,E]   tokens of shard s routed to e */
+    int32_t* rank_prefix_matrix;    /* [S,R]   sum over s' <= s of the above */
+    int32_t* channel_prefix_matrix; /* [S,R,C] prefix over channels of shard s */
+    int32_t* recv_tokens;           /* [R]     tokens rank r receives */
+    int32_t* recv_cu_seqlens;       /* [R,epn+1] rank-local padded offsets */
+    int32_t* recv_zero_fill;        /* [E,2]   rank-local zero-fill ranges */
+    int32_t* dst;                   /* [N*K]   rank-tagged slot, dups as -raw-1 */
+    int32_t* dup_counts;            /* [R,2]   (groups, dups) per rank */
+    int32_t* dup_offsets;           /* [R+1,2] exclusive prefix of dup_counts */
+    int32_t* dup_groups;            /* [cap_groups,3] (primary_loff, dup_begin, dup_count) */
+    int64_t cap_groups;
+    int32_t* dup_loffs;             /* [cap_dups] rank-local offsets of duplicates */
+    int64_t cap_dups;
+} mep_plan_outputs;
+
+/*
+ * mep_plan -- expert-parallel dispatch plan over R virtual ranks.
+ *
+ * Experts are split contiguously: owner(e) = e / epn, epn = E / R.  The
+ * batch is the concatenation of num_src equal shards (virtual source ranks),
+ * shard s = tokens [s*n, (s+1)*n), n = N / num_src.
+ *   is_token_in_rank[t][r]      = 1 iff some k has owner(ids[t][k]) == r
+ *   num_tokens_per_rank[s][r], num_tokens_per_expert[s][e]: per-shard counts
+ *   rank_prefix_matrix[s][r]    = sum_{s' <= s} num_tokens_per_rank[s'][r]
+ *                                 ([DEEP] notify_dispatch rank prefix)
+ *   recv_tokens[r]              = rank_prefix_matrix[num_src-1][r]
+ *   channel c of shard s covers tokens s*n + [min(c*q,n), min((c+1)*q,n)),
+ *     q = ceil(n / num_channels); channel_prefix_matrix[s][r][c] counts the
+ *     tokens of channels 0..c of shard s that go to r
+ *                                 ([DEEP] notify_dispatch channel part)
+ *   recv_cu_seqlens[r][j]       = cu_seqlens[r*epn+j] - cu_seqlens[r*epn]
+ *   recv_zero_fill[e]           = zero-fill range of e relative to its rank's
+ *                                 first row, (0,0) when e is empty or unpadded
+ *   dst[i], slot i = t*K+k, expert e, owner r:
+ *     raw = r*NvS + expanded_to_permuted[i] - cu_seqlens[r*epn]
+ *     the first k of token t on rank r stores raw, later ones -raw-1
+ *                                 ([MOON] dst computation without capacity
+ *                                  moves; duplicate canonicalisation)
+ *   dedup: for each rank r and each token t (ascending) with >= 2 slots on
+ *     r, one group (primary_loff, dup_begin, dup_count): the rank-local slot
+ *     of its first k, the index of its first duplicate within r's dup_loffs
+ *     segment, and (slots on r) - 1.  The duplicates' rank-local slots follow
+ *     in k order.  Groups of r start at dup_groups[dup_offsets[r][0]], its
+ *     duplicates at dup_loffs[dup_offsets[r][1]]; dup_offsets[R] holds totals.
+ *     (Shapes and counts from [MOON]'s plan record; the order is defined
+ *     here and is deterministic.)
+ *
+ * Arguments
+ *   topk_ids, cu_seqlens, expanded_to_permuted: device inputs as produced by
+ *     mep_route_topk / mep_build_layout with the same N, E, K, alignment
+ *   R          ranks, divides E, E/R <= 1024, R <= 128
+ *   num_src    shards, divides N (N = 0 allowed)
+ *   num_channels >= 1
+ *   NvS        per-rank slot stride, >= N*min(K,epn) + epn*(alignment-1),
+ *              R*NvS <= INT32_MAX
+ *   out        host pointer to the output table; cap_groups must be >=
+ *              N*min(K/2, R) and cap_dups >= N*(K - ceil(K/epn)) when their
+ *              arrays are given (both bounds are 0 when epn == 1)
+ *   ws, ws_bytes workspace (see mep_plan_workspace_size)
+ */
+int mep_plan(const int32_t* topk_ids, const int32_t* cu_seqlens,
+             const int32_t* expanded_to_permuted, int64_t N, int E, int K,
+             int alignment, int R, int num_src, int num_channels, int64_t NvS,
+             const mep_plan_outputs* out, void* ws, size_t ws_bytes, void* stream);
+
+size_t mep_plan_workspace_size(int64_t N, int E, int K, int R, int num_src);
+
+/* Static, NUL-terminated name of a return code. */
+const char* mep_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MEP_H_ */

@@ -1,0 +1,401 @@
+"""Pins for the CPU oracle: each check compares the oracle with something other than itself
+(exact arithmetic, brute-force enumeration, closed forms, a textbook stable sort, invariants that
+the definitions imply, a hand-worked example).  CPU only."""
+import itertools
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+
+import numpy as np
+import pytest
+
+import oracle
+from expert_dispatch_layout_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_example.json")
+
+
+# ---------------------------------------------------------------------------------------------
+# Sigmoid: correctly rounded binary32 of 1/(1+exp(-x)), checked with 60-digit decimal arithmetic
+# ---------------------------------------------------------------------------------------------
+
+def _exact_sigmoid_f32(x: np.float32) -> np.float32:
+    getcontext().prec = 60
+    xd = Decimal(float(x))
+    # Beyond |x| = 200 the value is within e^-200 of 1 (or of 0), far inside the rounding interval
+    # of 1.0 (of 0.0: e^-200 < 2^-150), and the decimal exponential would overflow.
+    if xd > 200:
+        return np.float32(1.0)
+    if xd < -200:
+        return np.float32(0.0)
+    d = Decimal(1) / (Decimal(1) + (-xd).exp())
+    f = np.float32(float(d))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+
+    def cost(c):
+        return (abs(Decimal(float(c)) - d), int(np.array(c, np.float32).view(np.uint32)) & 1)
+
+    return min(cands, key=cost)
+
+
+def _bits(a):
+    return np.asarray(a, np.float32).view(np.uint32)
+
+
+def test_sigmoid_every_bf16_value():
+    b = np.arange(1 << 16, dtype=np.uint32)
+    finite = ((b >> 7) & 0xFF) != 0xFF
+    x = (b[finite] << 16).view(np.float32)
+    got = oracle.sigmoid(x)
+    want = np.array([_exact_sigmoid_f32(v) for v in x], np.float32)
+    bad = np.nonzero(_bits(got) != _bits(want))[0]
+    assert bad.size == 0, (x[bad[:5]], got[bad[:5]], want[bad[:5]])
+
+
+def test_sigmoid_random_fp32_and_specials():
+    rng = np.random.default_rng(7)
+    x = rng.uniform(-110, 30, 4000).astype(np.float32)
+    x = np.concatenate([x, np.array([0.0, -0.0, 1e-45, -1e-45, 17.5, 16.6, -87.0, -103.9, -104.0,
+                                     -150.0, 3.0e38, -3.0e38, np.inf, -np.inf], np.float32)])
+    got = oracle.sigmoid(x)
+    want = np.array([_exact_sigmoid_f32(v) for v in x], np.float32)
+    assert np.array_equal(_bits(got), _bits(want))
+    assert got[4000] == np.float32(0.5) and got[4001] == np.float32(0.5)
+
+
+def test_sigmoid_quad_fallback_cases_are_exact():
+    # Inputs whose double-precision evaluation sits too close to a float midpoint take the
+    # binary128 path; find some in [1, 4) and check them against decimal arithmetic.
+    x = (np.uint32(0x3F800000) + np.arange(1 << 22, dtype=np.uint32)).view(np.float32)
+    s, path = oracle.sigmoid(x, with_path=True)
+    hard = x[path == 2]
+    assert hard.size > 0
+    want = np.array([_exact_sigmoid_f32(v) for v in hard], np.float32)
+    assert np.array_equal(_bits(s[path == 2]), _bits(want))
+
+
+# ---------------------------------------------------------------------------------------------
+# Top-K selection: brute force over subsets
+# ---------------------------------------------------------------------------------------------
+
+def _beats(ka, ia, kb, ib):
+    return ka > kb or (ka == kb and ia < ib)
+
+
+def _brute_topk(keys, K, eligible):
+    """The unique K-subset of eligible experts all of whose members beat every non-member."""
+    cand = [e for e in range(len(keys)) if eligible[e]]
+    winners = []
+    for sub in itertools.combinations(cand, K):
+        rest = [e for e in cand if e not in sub]
+        if all(_beats(keys[a], a, keys[b], b) for a in sub for b in rest):
+            winners.append(sub)
+    assert len(winners) == 1
+    return sorted(winners[0], key=lambda e: (-keys[e], e))
+
+
+def _brute_groups(keys, n_group, topk_group, group_topn):
+    gs = len(keys) // n_group
+    scores = []
+    for g in range(n_group):
+        top = sorted(keys[g * gs:(g + 1) * gs], reverse=True)[:group_topn]
+        acc = np.float32(top[0])
+        for v in top[1:]:
+            acc = np.float32(acc + np.float32(v))
+        scores.append(acc)
+    kept = _brute_topk(scores, topk_group, [True] * n_group)
+    return [(e // gs) in kept for e in range(len(keys))]
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("E,K", [(6, 1), (6, 2), (8, 3), (10, 3)])
+def test_softmax_topk_matches_brute_force(seed, E, K):
+    rng = np.random.default_rng(100 * seed + E)
+    # few distinct values -> many ties; ties must go to the lower expert index
+    x = rng.integers(-2, 3, size=(12, E)).astype(np.float32) * np.float32(0.5)
+    ids, _ = oracle.route(x, K)
+    for t in range(x.shape[0]):
+        assert list(ids[t]) == _brute_topk(list(x[t]), K, [True] * E)
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("E,G,TG,K,topn", [(8, 4, 2, 2, 2), (12, 4, 2, 3, 2), (16, 4, 2, 4, 2),
+                                           (12, 3, 1, 2, 1), (16, 8, 3, 3, 2)])
+def test_sigmoid_group_topk_matches_brute_force(seed, E, G, TG, K, topn):
+    rng = np.random.default_rng(1000 * seed + E + G)
+    x = rng.standard_normal((10, E)).astype(np.float32)
+    x[:, 1] = x[:, 0]                         # equal sigmoid values inside a row
+    bias = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    if seed % 2 == 0:
+        bias[:] = 0.0                          # zero bias keeps the equal keys equal
+    ids, _ = oracle.route(x, K, bias=bias, score_fn=oracle.SIGMOID, n_group=G, topk_group=TG,
+                          group_topn=topn, scale=2.5)
+    s = oracle.sigmoid(x)
+    keys = (s + bias[None, :]).astype(np.float32)   # one binary32 addition, as numpy does it
+    for t in range(x.shape[0]):
+        elig = _brute_groups(list(keys[t]), G, TG, topn)
+        assert list(ids[t]) == _brute_topk(list(keys[t]), K, elig)
+
+
+def test_sigmoid_without_groups_orders_like_logits():
+    # sigmoid is monotone: with zero bias and no group limit the selection is the logit top-K
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((64, 32)).astype(np.float32)
+    a, _ = oracle.route(x, 6, bias=np.zeros(32, np.float32), score_fn=oracle.SIGMOID)
+    b, _ = oracle.route(x, 6)
+    assert np.array_equal(a, b)
+
+
+def test_group_limit_with_all_groups_kept_is_plain_topk():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((64, 32)).astype(np.float32)
+    bias = rng.uniform(-0.1, 0.1, 32).astype(np.float32)
+    a, wa = oracle.route(x, 5, bias=bias, score_fn=oracle.SIGMOID, n_group=4, topk_group=4)
+    b, wb = oracle.route(x, 5, bias=bias, score_fn=oracle.SIGMOID)
+    assert np.array_equal(a, b) and np.array_equal(wa, wb)
+
+
+# ---------------------------------------------------------------------------------------------
+# Weights: closed forms
+# ---------------------------------------------------------------------------------------------
+
+def test_weights_k1_equal_scale():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((50, 16)).astype(np.float32)
+    _, w = oracle.route(x, 1, scale=1.0)
+    assert np.all(w == 1.0)
+    _, w = oracle.route(x, 1, bias=np.zeros(16, np.float32), score_fn=oracle.SIGMOID, scale=2.5)
+    assert np.all(w == np.float32(2.5))
+
+
+def test_weights_k2_softmax_is_logistic():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((200, 8)).astype(np.float32)
+    ids, w = oracle.route(x, 2)
+    for t in range(200):
+        d = float(x[t, ids[t, 1]]) - float(x[t, ids[t, 0]])
+        w0 = 1.0 / (1.0 + math.exp(d))
+        assert abs(float(w[t, 0]) - w0) <= 1e-7 * w0
+        assert abs(float(w[t, 1]) - (1.0 - w0)) <= 1e-7 * (1.0 - w0) + 1e-12
+
+
+def test_weights_full_softmax_and_sums():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((100, 12)).astype(np.float32)
+    ids, w = oracle.route(x, 3, renormalize=False)
+    p = np.exp(x.astype(np.float64) - x.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    ref = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    np.testing.assert_allclose(w, ref, rtol=1e-7)
+    ids, w = oracle.route(x, 3, renormalize=True, scale=2.5)
+    np.testing.assert_allclose(w.astype(np.float64).sum(axis=1), 2.5, rtol=1e-6)
+
+
+def test_weights_sigmoid_renorm_closed_form():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((100, 16)).astype(np.float32)
+    bias = rng.uniform(-0.1, 0.1, 16).astype(np.float32)
+    ids, w = oracle.route(x, 4, bias=bias, score_fn=oracle.SIGMOID, n_group=4, topk_group=2,
+                          scale=2.5)
+    s = oracle.sigmoid(x).astype(np.float64)
+    sel = np.take_along_axis(s, ids.astype(np.int64), axis=1)
+    np.testing.assert_allclose(w, sel / sel.sum(axis=1, keepdims=True) * 2.5, rtol=1e-7)
+    ids2, w2 = oracle.route(x, 4, bias=bias, score_fn=oracle.SIGMOID, renormalize=False, scale=2.5)
+    assert np.array_equal(w2, (np.take_along_axis(oracle.sigmoid(x), ids2.astype(np.int64), axis=1)
+                               * np.float32(2.5)).astype(np.float32))
+
+
+# ---------------------------------------------------------------------------------------------
+# Layout: equal to a textbook stable sort, with padding invariants
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,E,K,A", [(0, 4, 2, 3), (1, 8, 3, 1), (37, 8, 2, 128), (500, 16, 4, 3),
+                                     (1000, 64, 8, 64), (333, 128, 8, 1), (200, 256, 8, 128)])
+def test_layout_equals_stable_sort(N, E, K, A):
+    ids = synth.random_ids(N, E, K, seed=N + E, hot=2)
+    L = oracle.layout(ids, E, A)
+    flat = ids.reshape(-1)
+    cnt = np.bincount(flat, minlength=E)
+    assert np.array_equal(L.tokens_per_expert, cnt)
+    assert L.cu_seqlens[0] == 0 and np.all(L.cu_seqlens % A == 0)
+    pad = np.diff(L.cu_seqlens)
+    assert np.all((pad >= cnt) & (pad < cnt + A) & ((cnt > 0) | (pad == 0)))
+    order = np.argsort(flat, kind="stable")           # slots grouped by expert, stable
+    P = np.empty(N * K, np.int64)
+    pos = 0
+    for e in range(E):
+        members = order[pos:pos + cnt[e]]
+        P[members] = L.cu_seqlens[e] + np.arange(cnt[e])
+        pos += cnt[e]
+    assert np.array_equal(L.expanded_to_permuted, P)
+    T = int(L.cu_seqlens[E])
+    inv = np.full(T, -1, np.int64)
+    inv[P] = np.arange(N * K)
+    assert np.array_equal(L.permuted_to_expanded, inv)
+    for e in range(E):
+        extra = pad[e] - cnt[e]
+        want = (L.cu_seqlens[e] + cnt[e], extra) if (cnt[e] > 0 and extra > 0) else (0, 0)
+        assert tuple(L.zero_fill[e]) == tuple(want)
+
+
+# ---------------------------------------------------------------------------------------------
+# Plan: invariants implied by the definitions
+# ---------------------------------------------------------------------------------------------
+
+def _check_plan(ids, E, R, S, C, A):
+    N, K = ids.shape
+    epn = E // R
+    L = oracle.layout(ids, E, A)
+    NvS = N * min(K, epn) + epn * (A - 1)
+    Pl = oracle.plan(ids, L.cu_seqlens, L.expanded_to_permuted, E, R, S, C, NvS)
+    owner = ids // epn
+    itr = np.zeros((N, R), np.uint8)
+    for r in range(R):
+        itr[:, r] = (owner == r).any(axis=1)
+    assert np.array_equal(Pl.is_token_in_rank, itr)
+    n = N // S if S else 0
+    ntpr = itr.reshape(S, n, R).sum(axis=1) if N else np.zeros((S, R))
+    assert np.array_equal(Pl.num_tokens_per_rank, ntpr)
+    assert np.array_equal(Pl.rank_prefix_matrix, np.cumsum(ntpr, axis=0))
+    assert np.array_equal(Pl.recv_tokens, Pl.rank_prefix_matrix[-1])
+    ntpe = np.zeros((S, E), np.int64)
+    for t in range(N):
+        for k in range(K):
+            ntpe[t // n, ids[t, k]] += 1
+    assert np.array_equal(Pl.num_tokens_per_expert, ntpe)
+    assert np.array_equal(Pl.num_tokens_per_expert.sum(axis=0), L.tokens_per_expert)
+    cp = Pl.channel_prefix_matrix
+    assert np.all(np.diff(cp, axis=2) >= 0) and np.array_equal(cp[:, :, -1], ntpr)
+    q = -(-n // C) if n else 0
+    for s in range(S):
+        for c in range(C):
+            end = min((c + 1) * q, n)
+            assert np.array_equal(cp[s, :, c], itr[s * n:s * n + end].sum(axis=0))
+    rc = Pl.recv_cu_seqlens
+    cu = L.cu_seqlens
+    for r in range(R):
+        assert np.array_equal(rc[r], cu[r * epn:(r + 1) * epn + 1] - cu[r * epn])
+    # dst decodes through the layout's inverse back to its own slot
+    inv = L.permuted_to_expanded
+    d = Pl.dst.astype(np.int64)
+    raw = np.where(d >= 0, d, -d - 1)
+    r_of = raw // NvS
+    assert np.array_equal(r_of, owner.reshape(-1))
+    slot = cu[r_of * epn] + raw % NvS
+    assert np.array_equal(inv[slot], np.arange(N * K))
+    # exactly the first slot of each (token, rank) is non-negative
+    for t in range(N):
+        seen = set()
+        for k in range(K):
+            r = owner[t, k]
+            assert (d[t * K + k] >= 0) == (r not in seen)
+            seen.add(r)
+    # dedup counts: duplicates are the slots beyond one per (token, rank)
+    slots_per_rank = np.bincount(owner.reshape(-1), minlength=R)
+    assert np.array_equal(Pl.dup_counts[:, 1], slots_per_rank - Pl.recv_tokens)
+    assert np.all(Pl.dup_counts[:, 0] <= Pl.recv_tokens)
+    hits = np.stack([(owner == r).sum(axis=1) for r in range(R)], axis=1)   # [N,R]
+    assert np.array_equal(Pl.dup_counts[:, 0], (hits >= 2).sum(axis=0))
+    assert np.array_equal(Pl.dup_offsets[1:], np.cumsum(Pl.dup_counts, axis=0))
+    assert np.array_equal(Pl.dup_offsets[0], [0, 0])
+    if epn == 1:
+        assert Pl.dup_offsets[R].tolist() == [0, 0]
+    # every group decodes to (token, rank) in ascending token order and lists its duplicates
+    for r in range(R):
+        g0, g1 = Pl.dup_offsets[r, 0], Pl.dup_offsets[r + 1, 0]
+        seg = Pl.dup_loffs[Pl.dup_offsets[r, 1]:Pl.dup_offsets[r + 1, 1]]
+        prev_t = -1
+        nxt = 0
+        for g in range(g0, g1):
+            ploff, begin, cnt = Pl.dup_groups[g]
+            i = inv[cu[r * epn] + ploff]
+            t = i // K
+            assert t > prev_t and owner[t, i % K] == r
+            prev_t = t
+            ks = [k for k in range(K) if owner[t, k] == r]
+            assert ks[0] == i % K and cnt == len(ks) - 1 and begin == nxt
+            for j, k in enumerate(ks[1:]):
+                assert inv[cu[r * epn] + seg[begin + j]] == t * K + k
+            nxt += cnt
+        assert nxt == len(seg)
+    return Pl
+
+
+@pytest.mark.parametrize("N,E,K,R,S,C,A", [(0, 8, 2, 2, 2, 4, 1), (128, 8, 2, 2, 2, 24, 1),
+                                           (128, 8, 2, 2, 1, 24, 1), (96, 8, 2, 8, 8, 5, 128),
+                                           (256, 64, 8, 8, 4, 24, 16), (240, 32, 6, 4, 3, 7, 3),
+                                           (64, 16, 4, 16, 2, 3, 2), (200, 256, 8, 32, 8, 24, 128)])
+def test_plan_invariants(N, E, K, R, S, C, A):
+    ids = synth.random_ids(N, E, K, seed=7 * N + E, hot=3)
+    _check_plan(ids, E, R, S, C, A)
+
+
+def test_plan_shards_are_a_split_of_one_source():
+    ids = synth.random_ids(512, 64, 8, seed=11, hot=4)
+    L = oracle.layout(ids, 64, 16)
+    NvS = 512 * 8 + 8 * 15
+    many = oracle.plan(ids, L.cu_seqlens, L.expanded_to_permuted, 64, 8, 8, 24, NvS)
+    one = oracle.plan(ids, L.cu_seqlens, L.expanded_to_permuted, 64, 8, 1, 24, NvS)
+    assert np.array_equal(many.num_tokens_per_rank.sum(axis=0), one.num_tokens_per_rank[0])
+    assert np.array_equal(many.num_tokens_per_expert.sum(axis=0), one.num_tokens_per_expert[0])
+    for name in ("dst", "dup_counts", "dup_offsets", "dup_groups", "dup_loffs", "recv_tokens",
+                 "is_token_in_rank", "recv_cu_seqlens", "recv_zero_fill"):
+        assert np.array_equal(getattr(many, name), getattr(one, name)), name
+
+
+# ---------------------------------------------------------------------------------------------
+# Hand-worked example
+# ---------------------------------------------------------------------------------------------
+
+def test_hand_example():
+    g = json.load(open(GOLDEN))
+    rs = g["routing_softmax"]
+    ids, w = oracle.route(np.array(rs["logits"], np.float32), rs["K"])
+    assert ids.tolist() == rs["ids"]
+    np.testing.assert_allclose(w, np.array(rs["weights"]), rtol=1e-7)
+
+    rg = g["routing_sigmoid_group"]
+    x = np.array(rg["logits"], np.float32)
+    b = np.array(rg["bias"], np.float32)
+    ids, w = oracle.route(x, rg["K"], bias=b, score_fn=oracle.SIGMOID, n_group=rg["n_group"],
+                          topk_group=rg["topk_group"], group_topn=rg["group_topn"],
+                          scale=rg["scale"])
+    assert ids.tolist() == rg["ids"]
+    ids2, _ = oracle.route(x, rg["K"], bias=b, score_fn=oracle.SIGMOID)
+    assert ids2.tolist() == rg["ids_without_group_limit"]
+    s = 1.0 / (1.0 + np.exp(-x.astype(np.float64)[0]))
+    sel = s[[7, 4]]
+    np.testing.assert_allclose(w[0], sel / sel.sum() * 2.5, rtol=1e-6)
+
+    lp = g["layout_plan"]
+    ids = np.array(lp["ids"], np.int32)
+    L = oracle.layout(ids, lp["E"], lp["alignment"])
+    for k in ("tokens_per_expert", "cu_seqlens", "expanded_to_permuted", "permuted_to_expanded",
+              "zero_fill"):
+        assert getattr(L, k).tolist() == lp[k], k
+    Pl = oracle.plan(ids, L.cu_seqlens, L.expanded_to_permuted, lp["E"], lp["R"], lp["num_src"],
+                     lp["num_channels"], lp["NvS"])
+    for k in ("is_token_in_rank", "num_tokens_per_rank", "num_tokens_per_expert",
+              "rank_prefix_matrix", "recv_tokens", "channel_prefix_matrix", "recv_cu_seqlens",
+              "recv_zero_fill", "dst", "dup_counts", "dup_offsets", "dup_groups", "dup_loffs"):
+        assert getattr(Pl, k).tolist() == lp[k], k
+
+
+# ---------------------------------------------------------------------------------------------
+# Workload generators feed the oracle end to end (small prefix of each workload)
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_workload_prefix_end_to_end(name):
+    wl = synth.WORKLOADS[name]
+    n = min(wl.N, 64 * wl.R)
+    inp = synth.make_inputs(wl, N=n)
+    ids, w = oracle.route(inp.logits, wl.K, bias=inp.bias, score_fn=wl.score_fn,
+                          renormalize=wl.renormalize, n_group=wl.n_group,
+                          topk_group=wl.topk_group, group_topn=wl.group_topn, scale=wl.scale,
+                          dtype=wl.dtype)
+    assert np.all((ids >= 0) & (ids < wl.E))
+    assert all(len(set(r)) == wl.K for r in ids.tolist())
+    np.testing.assert_allclose(w.astype(np.float64).sum(axis=1), wl.scale, rtol=1e-6)
+    _check_plan(ids, wl.E, wl.R, wl.S, wl.num_channels, wl.alignment)

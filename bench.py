@@ -1,0 +1,215 @@
+"""Benchmark of the MoE routing + dispatch-layout hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of router logits already resident in HBM:
+mep_route_topk -> mep_build_layout -> mep_plan, back to back on one stream.  The default workload
+is N=65536 tokens, E=256 experts, K=8, fp32 logits, sigmoid scoring with a per-expert bias,
+8 groups keep 4 by top-2 sum, weights renormalised x2.5, alignment 128, R=8 virtual ranks with
+one source shard per rank and 24 channels.
+
+Input and output buffers rotate over several distinct sets (together larger than the 256 MB
+Infinity Cache) so every step reads logits from HBM, not from the last-level cache.
+
+Prints one JSON line.  `roofline` describes the dominant kernel (routing): algorithmic bytes per
+launch / its average duration, timed with HIP events on the launch stream inside the timed
+region.  `cpu_baseline` is the CPU oracle timed on this host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+LLC_BYTES = 256 * 1024 * 1024  # MI355X Infinity Cache
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time for the oracle baseline (0 disables it)")
+    return ap.parse_args()
+
+
+def route_bytes(wl) -> int:
+    """Compulsory HBM bytes of one routing launch: logits read once, bias read once, ids and
+    weights written once."""
+    b = 4 if wl.dtype == 0 else 2
+    return wl.N * wl.E * b + (4 * wl.E if wl.score_fn == 1 else 0) + 8 * wl.N * wl.K
+
+
+def path_bytes(wl, T: int, G: int, D: int) -> int:
+    """Compulsory HBM bytes of the whole path (each input read once, each output written once)."""
+    N, E, K, R, S, C = wl.N, wl.E, wl.K, wl.R, wl.S, wl.num_channels
+    epn = E // R
+    small = 4 * (E + (E + 1) + 2 * E)                              # layout per-expert outputs
+    small += 4 * (S * R * 2 + S * E + S * R * C + R + R * (epn + 1) + 2 * E + 2 * R + 2 * (R + 1))
+    return route_bytes(wl) + 4 * N * K + 4 * T + N * R + 4 * N * K + 12 * G + 4 * D + small
+
+
+def traffic_from_profile(kernel_src: str):
+    """Measured HBM bytes per routing launch, if a counter profile of the current kernel source
+    was committed (profiles/route_traffic.json); None otherwise."""
+    path = os.path.join(ROOT, "profiles", "route_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != h:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, seconds: float):
+    import oracle
+
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        ids, _ = oracle.route(inp.logits, wl.K, bias=inp.bias, score_fn=wl.score_fn,
+                              renormalize=wl.renormalize, n_group=wl.n_group,
+                              topk_group=wl.topk_group, group_topn=wl.group_topn,
+                              scale=wl.scale, dtype=wl.dtype)
+        L = oracle.layout(ids, wl.E, wl.alignment)
+        oracle.plan(ids, L.cu_seqlens, L.expanded_to_permuted, wl.E, wl.R, wl.S,
+                    wl.num_channels, wl.NvS)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or passes >= 1000:
+            break
+    return {"value": wl.N * passes / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%d full passes (route+layout+plan) over the %d-token workload, one thread, "
+                      "%.1f s" % (passes, wl.N, el)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from expert_dispatch_layout_amd import _binding as B
+    from expert_dispatch_layout_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.workload]
+    inp = synth.make_inputs(wl)
+    N, E, K, A, R, S, C = wl.N, wl.E, wl.K, wl.alignment, wl.R, wl.S, wl.num_channels
+    logits_bytes = inp.logits.nbytes
+    nsets = max(2, -(-(3 * LLC_BYTES // 2) // max(logits_bytes, 1)))   # > 1.5x the LLC
+    nsets = min(nsets, 64)
+
+    host = torch.from_numpy(inp.logits.view(np.int16) if wl.dtype == synth.BF16 else inp.logits)
+    sets = []
+    for _ in range(nsets):
+        x = host.to(dev)
+        if wl.dtype == synth.BF16:
+            x = x.view(torch.bfloat16)
+        ids = torch.empty((N, K), dtype=torch.int32, device=dev)
+        w = torch.empty((N, K), dtype=torch.float32, device=dev)
+        sets.append((x, ids, w, B.alloc_layout(N, E, K, A, dev), B.alloc_plan(N, E, K, R, S, C, dev)))
+    bias = torch.from_numpy(inp.bias).to(dev) if inp.bias is not None else None
+    params = B.route_params(wl.score_fn, wl.renormalize, wl.n_group, wl.topk_group,
+                            wl.group_topn, wl.scale)
+    ws_l = B.alloc_workspace(B.layout_workspace_size(N, E, K), dev)
+    ws_p = B.alloc_workspace(B.plan_workspace_size(N, E, K, R, S), dev)
+    NvS = wl.NvS
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        x, ids, w, L, P = sets[i % nsets]
+        if ev is not None:
+            ev[0].record(stream)
+        B.mep_route_topk(x, K, bias, params, ids, w, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        B.mep_build_layout(ids, E, A, L.tokens_per_expert, L.cu_seqlens, L.expanded_to_permuted,
+                           L.permuted_to_expanded, L.zero_fill, ws_l, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        B.mep_plan(ids, L.cu_seqlens, L.expanded_to_permuted, E, A, R, S, C, NvS, P, ws_p, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, per-call events inside, bracketed by synchronisation
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    route_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    layout_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    plan_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+
+    # sizes of this batch's layout and dedup lists (for the whole-path byte count)
+    L, P = sets[(args.warmup + args.steps - 1) % nsets][3:]
+    T = int(L.cu_seqlens[E].item())
+    G, D = [int(v) for v in P.dup_offsets[R].tolist()]
+    rb = route_bytes(wl)
+    achieved = rb / (route_ms * 1e-3) / 1e9
+    pb = path_bytes(wl, T, G, D)
+    traffic = traffic_from_profile(os.path.join(ROOT, "expert_dispatch_layout_amd", "csrc", "route.hip"))
+
+    out = {
+        "metric": "routed tokens/sec + achieved HBM GB/s (% of peak), N=65536 E=256 K=8",
+        "value": N / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32,i32",
+        "data": "synthetic",
+        "config": {"workload": "%s: N=%d E=%d K=%d %s logits, %s, A=%d, R=%d, num_src=%d, "
+                               "channels=%d" % (wl.name, N, E, K,
+                                                "bf16" if wl.dtype else "fp32",
+                                                "sigmoid+bias, 8 groups keep 4 (top-2 sum), "
+                                                "renorm x2.5" if wl.score_fn else "softmax top-K",
+                                                A, R, S, C),
+                   "buffer_sets": nsets},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "kernel": "route_kernel", "bytes_per_launch": rb},
+        "path": {"route_ms": route_ms, "layout_ms": layout_ms, "plan_ms": plan_ms,
+                 "algorithmic_bytes": pb, "GB_per_s": pb / (ms_step * 1e-3) / 1e9,
+                 "frac_of_peak": pb / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "slots_per_s": N * K / (ms_step * 1e-3), "T": T, "dedup_groups": G,
+                 "dedup_dups": D, "host_wall_s": wall},
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

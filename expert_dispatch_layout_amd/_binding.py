@@ -1,0 +1,276 @@
+"""ctypes binding of libmep.so.  Argument marshalling only: every step of the path runs in the
+HIP kernels behind the C ABI (include/mep.h).  PyTorch supplies device memory and the stream.
+
+The functions named like the C entry points take preallocated tensors; the convenience
+helpers ``route``, ``build_layout`` and ``plan`` allocate outputs and workspaces with torch.
+There is no CPU fallback: if the library is missing or no GPU is present, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmep.so")
+
+MEP_OK, MEP_ERR_INVALID_ARG, MEP_ERR_UNSUPPORTED, MEP_ERR_CAPACITY, MEP_ERR_DEVICE = 0, 1, 2, 3, 4
+MEP_F32, MEP_BF16 = 0, 1
+MEP_SOFTMAX, MEP_SIGMOID = 0, 1
+
+
+class MepError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__("%s failed: %s (%d)" % (where, status_string(code), code))
+        self.code = code
+
+
+class RouteParams(ctypes.Structure):
+    _fields_ = [("score_fn", ctypes.c_int), ("renormalize", ctypes.c_int),
+                ("n_group", ctypes.c_int), ("topk_group", ctypes.c_int),
+                ("group_topn", ctypes.c_int), ("scale", ctypes.c_float)]
+
+
+class PlanOutputs(ctypes.Structure):
+    _fields_ = [("is_token_in_rank", ctypes.c_void_p), ("num_tokens_per_rank", ctypes.c_void_p),
+                ("num_tokens_per_expert", ctypes.c_void_p), ("rank_prefix_matrix", ctypes.c_void_p),
+                ("channel_prefix_matrix", ctypes.c_void_p), ("recv_tokens", ctypes.c_void_p),
+                ("recv_cu_seqlens", ctypes.c_void_p), ("recv_zero_fill", ctypes.c_void_p),
+                ("dst", ctypes.c_void_p), ("dup_counts", ctypes.c_void_p),
+                ("dup_offsets", ctypes.c_void_p), ("dup_groups", ctypes.c_void_p),
+                ("cap_groups", ctypes.c_int64), ("dup_loffs", ctypes.c_void_p),
+                ("cap_dups", ctypes.c_int64)]
+
+
+EXPORTS = ("mep_route_topk", "mep_build_layout", "mep_layout_workspace_size", "mep_plan",
+           "mep_plan_workspace_size", "mep_status_string")
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib():
+    """Load libmep.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError("libmep.so is not built; run python -m expert_dispatch_layout_amd.build")
+                L = ctypes.CDLL(LIB_PATH)
+                P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+                L.mep_route_topk.argtypes = [P, I, I64, I, I, P, ctypes.POINTER(RouteParams), P, P, P]
+                L.mep_route_topk.restype = I
+                L.mep_build_layout.argtypes = [P, I64, I, I, I, P, P, P, P, I64, P, P, SZ, P]
+                L.mep_build_layout.restype = I
+                L.mep_layout_workspace_size.argtypes = [I64, I, I]
+                L.mep_layout_workspace_size.restype = SZ
+                L.mep_plan.argtypes = [P, P, P, I64, I, I, I, I, I, I, I64,
+                                       ctypes.POINTER(PlanOutputs), P, SZ, P]
+                L.mep_plan.restype = I
+                L.mep_plan_workspace_size.argtypes = [I64, I, I, I, I]
+                L.mep_plan_workspace_size.restype = SZ
+                L.mep_status_string.argtypes = [I]
+                L.mep_status_string.restype = ctypes.c_char_p
+                _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().mep_status_string(code).decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(rc: int, where: str):
+    if rc != MEP_OK:
+        raise MepError(rc, where)
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("device tensors are required")
+
+
+# ---------------------------------------------------------------------------------------------
+# Entry points with the C names (preallocated outputs)
+# ---------------------------------------------------------------------------------------------
+
+def mep_route_topk(logits, K, bias, params: RouteParams, topk_ids, topk_weights=None, stream=None):
+    _require_cuda(logits, bias, topk_ids, topk_weights)
+    dtype = MEP_BF16 if logits.dtype == torch.bfloat16 else MEP_F32
+    if logits.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("logits must be float32 or bfloat16")
+    N, E = logits.shape
+    rc = lib().mep_route_topk(_ptr(logits), dtype, N, E, K, _ptr(bias), ctypes.byref(params),
+                              _ptr(topk_ids), _ptr(topk_weights), _stream(stream))
+    _check(rc, "mep_route_topk")
+
+
+def mep_build_layout(topk_ids, E, alignment, tokens_per_expert, cu_seqlens, expanded_to_permuted,
+                     permuted_to_expanded, zero_fill, ws, stream=None):
+    _require_cuda(topk_ids, tokens_per_expert, cu_seqlens, expanded_to_permuted,
+                  permuted_to_expanded, zero_fill, ws)
+    N, K = topk_ids.shape
+    cap = permuted_to_expanded.numel() if permuted_to_expanded is not None else 0
+    rc = lib().mep_build_layout(_ptr(topk_ids), N, E, K, alignment, _ptr(tokens_per_expert),
+                                _ptr(cu_seqlens), _ptr(expanded_to_permuted),
+                                _ptr(permuted_to_expanded), cap, _ptr(zero_fill), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "mep_build_layout")
+
+
+def mep_plan(topk_ids, cu_seqlens, expanded_to_permuted, E, alignment, R, num_src, num_channels,
+             NvS, outputs: "PlanTensors", ws, stream=None):
+    _require_cuda(topk_ids, cu_seqlens, expanded_to_permuted, ws)
+    N, K = topk_ids.shape
+    po = outputs.as_struct()
+    rc = lib().mep_plan(_ptr(topk_ids), _ptr(cu_seqlens), _ptr(expanded_to_permuted), N, E, K,
+                        alignment, R, num_src, num_channels, NvS, ctypes.byref(po), _ptr(ws),
+                        ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "mep_plan")
+
+
+def layout_workspace_size(N, E, K) -> int:
+    return int(lib().mep_layout_workspace_size(N, E, K))
+
+
+def plan_workspace_size(N, E, K, R, num_src) -> int:
+    return int(lib().mep_plan_workspace_size(N, E, K, R, num_src))
+
+
+# ---------------------------------------------------------------------------------------------
+# Allocating helpers
+# ---------------------------------------------------------------------------------------------
+
+def alloc_workspace(nbytes: int, device=None) -> torch.Tensor:
+    """Zero-filled workspace (the library requires zero on first use and keeps it valid)."""
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device or "cuda")
+
+
+def route_params(score_fn=MEP_SOFTMAX, renormalize=True, n_group=1, topk_group=1, group_topn=2,
+                 scale=1.0) -> RouteParams:
+    return RouteParams(score_fn, int(renormalize), n_group, topk_group, group_topn, float(scale))
+
+
+def route(logits, K, *, bias=None, score_fn=MEP_SOFTMAX, renormalize=True, n_group=1,
+          topk_group=1, group_topn=2, scale=1.0, stream=None):
+    N = logits.shape[0]
+    ids = torch.empty((N, K), dtype=torch.int32, device=logits.device)
+    w = torch.empty((N, K), dtype=torch.float32, device=logits.device)
+    mep_route_topk(logits, K, bias, route_params(score_fn, renormalize, n_group, topk_group,
+                                                 group_topn, scale), ids, w, stream)
+    return ids, w
+
+
+@dataclass
+class LayoutTensors:
+    tokens_per_expert: torch.Tensor
+    cu_seqlens: torch.Tensor
+    expanded_to_permuted: torch.Tensor
+    permuted_to_expanded: torch.Tensor  # capacity-sized; first cu_seqlens[E] rows are valid
+    zero_fill: torch.Tensor
+
+
+def permuted_capacity(N, E, K, alignment) -> int:
+    nk = N * K
+    return nk + min(E, nk) * (alignment - 1)
+
+
+def alloc_layout(N, E, K, alignment, device="cuda") -> LayoutTensors:
+    cap = max(permuted_capacity(N, E, K, alignment), 1)
+    i32 = dict(dtype=torch.int32, device=device)
+    return LayoutTensors(torch.empty(E, **i32), torch.empty(E + 1, **i32),
+                         torch.empty(max(N * K, 1), **i32)[:N * K], torch.empty(cap, **i32),
+                         torch.empty((E, 2), **i32))
+
+
+def build_layout(topk_ids, E, alignment, *, out: LayoutTensors | None = None, ws=None,
+                 stream=None) -> LayoutTensors:
+    N, K = topk_ids.shape
+    out = out or alloc_layout(N, E, K, alignment, topk_ids.device)
+    ws = ws if ws is not None else alloc_workspace(layout_workspace_size(N, E, K), topk_ids.device)
+    mep_build_layout(topk_ids, E, alignment, out.tokens_per_expert, out.cu_seqlens,
+                     out.expanded_to_permuted, out.permuted_to_expanded, out.zero_fill, ws, stream)
+    return out
+
+
+@dataclass
+class PlanTensors:
+    is_token_in_rank: torch.Tensor | None
+    num_tokens_per_rank: torch.Tensor | None
+    num_tokens_per_expert: torch.Tensor | None
+    rank_prefix_matrix: torch.Tensor | None
+    channel_prefix_matrix: torch.Tensor | None
+    recv_tokens: torch.Tensor | None
+    recv_cu_seqlens: torch.Tensor | None
+    recv_zero_fill: torch.Tensor | None
+    dst: torch.Tensor | None
+    dup_counts: torch.Tensor | None
+    dup_offsets: torch.Tensor | None
+    dup_groups: torch.Tensor | None
+    dup_loffs: torch.Tensor | None
+
+    def as_struct(self) -> PlanOutputs:
+        cap_g = self.dup_groups.shape[0] if self.dup_groups is not None else 0
+        cap_d = self.dup_loffs.shape[0] if self.dup_loffs is not None else 0
+        return PlanOutputs(*(_addr(t) for t in (
+            self.is_token_in_rank, self.num_tokens_per_rank, self.num_tokens_per_expert,
+            self.rank_prefix_matrix, self.channel_prefix_matrix, self.recv_tokens,
+            self.recv_cu_seqlens, self.recv_zero_fill, self.dst, self.dup_counts,
+            self.dup_offsets, self.dup_groups)), cap_g, _addr(self.dup_loffs), cap_d)
+
+
+def _addr(t):
+    return None if t is None else t.data_ptr()
+
+
+def default_nvs(N, E, K, R, alignment) -> int:
+    epn = E // R
+    return N * min(K, epn) + epn * (alignment - 1)
+
+
+def dedup_capacity(N, E, K, R):
+    epn = E // R
+    g = N * min(K // 2, R) if epn >= 2 else 0
+    d = N * (K - (K + epn - 1) // epn)
+    return g, d
+
+
+def alloc_plan(N, E, K, R, num_src, num_channels, device="cuda") -> PlanTensors:
+    epn = E // R
+    i32 = dict(dtype=torch.int32, device=device)
+    cap_g, cap_d = dedup_capacity(N, E, K, R)
+    return PlanTensors(
+        torch.empty((max(N, 1), R), dtype=torch.uint8, device=device)[:N],
+        torch.empty((num_src, R), **i32), torch.empty((num_src, E), **i32),
+        torch.empty((num_src, R), **i32), torch.empty((num_src, R, num_channels), **i32),
+        torch.empty(R, **i32), torch.empty((R, epn + 1), **i32), torch.empty((E, 2), **i32),
+        torch.empty(max(N * K, 1), **i32)[:N * K], torch.empty((R, 2), **i32),
+        torch.empty((R + 1, 2), **i32), torch.empty((max(cap_g, 1), 3), **i32),
+        torch.empty(max(cap_d, 1), **i32))
+
+
+def plan(topk_ids, cu_seqlens, expanded_to_permuted, E, alignment, R, num_src, num_channels, *,
+         NvS=None, out: PlanTensors | None = None, ws=None, stream=None) -> PlanTensors:
+    N, K = topk_ids.shape
+    NvS = NvS if NvS is not None else default_nvs(N, E, K, R, alignment)
+    out = out or alloc_plan(N, E, K, R, num_src, num_channels, topk_ids.device)
+    ws = ws if ws is not None else alloc_workspace(plan_workspace_size(N, E, K, R, num_src),
+                                                   topk_ids.device)
+    mep_plan(topk_ids, cu_seqlens, expanded_to_permuted, E, alignment, R, num_src, num_channels,
+             NvS, out, ws, stream)
+    return out

@@ -1,0 +1,134 @@
+// Correctly rounded binary32 logistic sigmoid on gfx950.
+//
+// The sigmoid of the TensorRT-LLM RoutingKernel.cuh helpers (sigmoid_accurate) is the real
+// function 1/(1+exp(-x)); its rounding is not fixed there.  Selection keys are built from it, so
+// this library returns the correctly rounded value (round to nearest even, subnormals kept),
+// which is unique and therefore reproducible on any machine.
+//
+// Method (Ziv's onion-peeling strategy):
+//   fast path  evaluate in binary64 with the device libm exp and an IEEE divide (relative error
+//              well under 2^-50); widen by 2^-44 and accept when both ends round to the same
+//              binary32 value;
+//   slow path  evaluate in double-double arithmetic (Dekker's two-sum / two-product) to about
+//              2^-90 relative and decide the rounding from the double-double value, again with
+//              an interval check.  The exponential uses exp(t) = exp(t/2^12)^(2^12): an exact
+//              power-of-two scaling, a degree-16 Taylor polynomial and twelve squarings, so no
+//              split constant of ln 2 is needed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mep {
+
+struct dd_t {
+    double hi, lo;
+};
+
+__device__ __forceinline__ dd_t dd_two_sum(double a, double b) {
+    double s = a + b;
+    double bb = s - a;
+    double e = (a - (s - bb)) + (b - bb);
+    return {s, e};
+}
+
+// requires |a| >= |b| (or a == 0)
+__device__ __forceinline__ dd_t dd_quick_two_sum(double a, double b) {
+    double s = a + b;
+    return {s, b - (s - a)};
+}
+
+__device__ __forceinline__ dd_t dd_two_prod(double a, double b) {
+    double p = a * b;
+    return {p, __fma_rn(a, b, -p)};
+}
+
+__device__ __forceinline__ dd_t dd_add(dd_t a, dd_t b) {
+    dd_t s = dd_two_sum(a.hi, b.hi);
+    dd_t t = dd_two_sum(a.lo, b.lo);
+    s.lo += t.hi;
+    s = dd_quick_two_sum(s.hi, s.lo);
+    s.lo += t.lo;
+    return dd_quick_two_sum(s.hi, s.lo);
+}
+
+__device__ __forceinline__ dd_t dd_mul(dd_t a, dd_t b) {
+    dd_t p = dd_two_prod(a.hi, b.hi);
+    p.lo += a.hi * b.lo + a.lo * b.hi;
+    return dd_quick_two_sum(p.hi, p.lo);
+}
+
+__device__ __forceinline__ dd_t dd_mul_d(dd_t a, double b) {
+    dd_t p = dd_two_prod(a.hi, b);
+    p.lo += a.lo * b;
+    return dd_quick_two_sum(p.hi, p.lo);
+}
+
+__device__ __forceinline__ dd_t dd_div_d(dd_t a, double b) {
+    double q1 = a.hi / b;
+    dd_t p = dd_two_prod(q1, b);
+    double r = ((a.hi - p.hi) - p.lo) + a.lo;
+    return dd_quick_two_sum(q1, r / b);
+}
+
+// 1 / a for a >= 1
+__device__ __forceinline__ dd_t dd_recip(dd_t a) {
+    double y = 1.0 / a.hi;
+    // residual 1 - a*y in double-double, then one Newton correction
+    dd_t ay = dd_mul_d(a, y);
+    dd_t res = dd_add(dd_t{1.0, 0.0}, dd_t{-ay.hi, -ay.lo});
+    dd_t corr = dd_mul_d(res, y);
+    return dd_add(dd_t{y, 0.0}, corr);
+}
+
+// exp(t) for |t| <= 128 in double-double.
+__device__ __noinline__ dd_t dd_exp(double t) {
+    double u = t * 0x1p-12;  // exact
+    dd_t p = {1.0, 0.0};
+    for (int k = 16; k >= 1; --k) {
+        p = dd_div_d(dd_mul_d(p, u), (double)k);
+        p = dd_add(dd_t{1.0, 0.0}, p);
+    }
+    for (int i = 0; i < 12; ++i) p = dd_mul(p, p);
+    return p;
+}
+
+// Correct binary32 rounding (nearest, ties to even) of a non-negative double-double value.
+__device__ __forceinline__ float dd_round_f32(dd_t v) {
+    float f = (float)v.hi;
+    double fd = (double)f;
+    if (fd == v.hi) return f;
+    uint32_t fb = __float_as_uint(f);
+    float g = (v.hi > fd) ? __uint_as_float(fb + 1u) : __uint_as_float(fb - 1u);
+    double mid = 0.5 * (fd + (double)g);  // exact: both are binary32 neighbours
+    if (v.hi != mid || v.lo == 0.0) return f;
+    float up = fd > (double)g ? f : g;
+    float down = fd > (double)g ? g : f;
+    return v.lo > 0.0 ? up : down;
+}
+
+__device__ __noinline__ float sigmoid_cr_slow(float x) {
+    if (x != x) return x;
+    // sigmoid(x) < e^x <= e^-104 < 2^-150 rounds to 0; 1 - sigmoid(x) < e^-x <= e^-17.5 < 2^-25
+    // rounds to 1.
+    if (x <= -104.0f) return 0.0f;
+    if (x >= 17.5f) return 1.0f;
+    dd_t e = dd_exp(-(double)x);
+    dd_t s = dd_recip(dd_add(dd_t{1.0, 0.0}, e));
+    double tol = s.hi * 0x1p-80;
+    float lo = dd_round_f32(dd_quick_two_sum(s.hi, s.lo - tol));
+    float hi = dd_round_f32(dd_quick_two_sum(s.hi, s.lo + tol));
+    if (lo == hi) return lo;
+    return dd_round_f32(s);
+}
+
+__device__ __forceinline__ float sigmoid_cr(float x) {
+    double s = 1.0 / (1.0 + exp(-(double)x));
+    double tol = s * 0x1p-44;
+    float lo = (float)(s - tol);
+    float hi = (float)(s + tol);
+    if (lo == hi) return lo;
+    return sigmoid_cr_slow(x);
+}
+
+}  // namespace mep

@@ -28,9 +28,12 @@ SOFTMAX, SIGMOID = 0, 1
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (nearest, ties to even); return uint16 bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).copy()
+    lsb = (u >> 16) & np.uint32(1)
+    u += np.uint32(0x7FFF)      # no wrap for finite inputs: |bits| <= 0xFF7FFFFF
+    u += lsb
+    u >>= 16
+    return u.astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:

@@ -1,0 +1,129 @@
+"""Host-side checks of libmep.so that need no GPU: the library loads, exports every entry point
+include/mep.h declares, sizes its workspaces, and rejects bad arguments before touching memory.
+The pointers passed here are fake (never dereferenced: validation returns first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mep.h")
+
+pytest.importorskip("torch")
+from expert_dispatch_layout_amd import _binding as B  # noqa: E402
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(mep_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(B.LIB_PATH)
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    assert B.status_string(0) == "MEP_OK"
+    assert B.status_string(3) == "MEP_ERR_CAPACITY"
+    assert B.status_string(99) == "MEP_UNKNOWN_STATUS"
+
+
+def test_workspace_sizes():
+    assert B.layout_workspace_size(0, 8, 2) == 256
+    assert B.layout_workspace_size(65536, 256, 8) == 256 + 256 * 256 * 8
+    assert B.layout_workspace_size(1, 8, 2) == 256 + 8 * 8
+    s1 = B.plan_workspace_size(65536, 256, 8, 8, 8)
+    assert s1 == 256 + 8 * 32 * (3 * 8 + 256) * 8
+    assert B.plan_workspace_size(65536, 256, 8, 8, 1) == 256 + 256 * (3 * 8 + 256) * 8
+
+
+FAKE = 0x10000          # aligned, never dereferenced
+MIS = 0x10004           # 4-aligned but not 16-aligned
+
+
+def _route(logits=FAKE, dtype=0, N=16, E=8, K=2, bias=FAKE, score_fn=0, renorm=1, n_group=1,
+           topk_group=1, group_topn=2, scale=1.0, ids=FAKE, w=FAKE):
+    p = B.RouteParams(score_fn, renorm, n_group, topk_group, group_topn, scale)
+    return B.lib().mep_route_topk(logits, dtype, N, E, K, bias, ctypes.byref(p), ids, w, None)
+
+
+def test_route_validation():
+    assert _route(N=0) == B.MEP_OK                       # nothing to do, nothing launched
+    assert _route(logits=None) == B.MEP_ERR_INVALID_ARG
+    assert _route(ids=None) == B.MEP_ERR_INVALID_ARG
+    assert _route(logits=MIS) == B.MEP_ERR_INVALID_ARG
+    assert _route(dtype=7) == B.MEP_ERR_INVALID_ARG
+    assert _route(score_fn=5) == B.MEP_ERR_INVALID_ARG
+    assert _route(score_fn=1, bias=None) == B.MEP_ERR_INVALID_ARG
+    assert _route(N=-1) == B.MEP_ERR_INVALID_ARG
+    assert _route(scale=float("nan")) == B.MEP_ERR_INVALID_ARG
+    assert _route(E=1025, K=2) == B.MEP_ERR_UNSUPPORTED
+    assert _route(E=64, K=33) == B.MEP_ERR_UNSUPPORTED
+    assert _route(E=8, K=9) == B.MEP_ERR_UNSUPPORTED
+    assert _route(E=12, n_group=5) == B.MEP_ERR_UNSUPPORTED          # E % n_group
+    assert _route(E=64, n_group=64) == B.MEP_ERR_UNSUPPORTED         # > 32 groups
+    assert _route(E=16, n_group=4, topk_group=0) == B.MEP_ERR_INVALID_ARG
+    assert _route(E=16, n_group=4, topk_group=1, group_topn=3) == B.MEP_ERR_UNSUPPORTED
+    assert _route(E=16, K=8, n_group=4, topk_group=1) == B.MEP_ERR_UNSUPPORTED  # 4 eligible < K
+    assert _route(N=2 ** 28, E=64, K=16) == B.MEP_ERR_UNSUPPORTED    # N*K > INT32_MAX
+
+
+def _layout(N=16, E=8, K=2, A=4, tpe=FAKE, cu=FAKE, e2p=FAKE, p2e=FAKE, cap=None, zf=FAKE,
+            ws=FAKE, ws_bytes=1 << 20, ids=FAKE):
+    if cap is None:
+        cap = N * K + min(E, N * K) * (A - 1)
+    return B.lib().mep_build_layout(ids, N, E, K, A, tpe, cu, e2p, p2e, cap, zf, ws, ws_bytes, None)
+
+
+def test_layout_validation():
+    assert _layout(ids=None) == B.MEP_ERR_INVALID_ARG
+    assert _layout(cu=None) == B.MEP_ERR_INVALID_ARG
+    assert _layout(e2p=None) == B.MEP_ERR_INVALID_ARG
+    assert _layout(ws=None) == B.MEP_ERR_INVALID_ARG
+    assert _layout(e2p=FAKE + 2) == B.MEP_ERR_INVALID_ARG
+    assert _layout(ws=FAKE + 64) == B.MEP_ERR_INVALID_ARG             # workspace needs 256 B
+    assert _layout(A=0) == B.MEP_ERR_INVALID_ARG
+    assert _layout(E=2048) == B.MEP_ERR_UNSUPPORTED
+    assert _layout(K=9, E=8) == B.MEP_ERR_UNSUPPORTED
+    assert _layout(N=2 ** 28, K=8, E=64) == B.MEP_ERR_UNSUPPORTED
+    assert _layout(cap=16 * 2 + 8 * 3 - 1) == B.MEP_ERR_CAPACITY
+    assert _layout(ws_bytes=255) == B.MEP_ERR_CAPACITY
+
+
+def _plan(N=64, E=16, K=4, A=2, R=4, S=2, C=3, NvS=None, ws_bytes=1 << 24, cap_g=None,
+          cap_d=None, out_ptr=FAKE, **kw):
+    epn = E // R
+    if NvS is None:
+        NvS = N * min(K, epn) + epn * (A - 1)
+    g, d = B.dedup_capacity(N, E, K, R)
+    po = B.PlanOutputs(*([FAKE] * 12), g if cap_g is None else cap_g, FAKE,
+                       d if cap_d is None else cap_d)
+    for k, v in kw.items():
+        setattr(po, k, v)
+    return B.lib().mep_plan(FAKE, FAKE, FAKE, N, E, K, A, R, S, C, NvS, ctypes.byref(po), FAKE,
+                            ws_bytes, None)
+
+
+def test_plan_validation():
+    assert _plan(E=18, R=4) == B.MEP_ERR_UNSUPPORTED                  # E % R
+    assert _plan(R=129, E=129 * 2) == B.MEP_ERR_UNSUPPORTED
+    assert _plan(N=63, S=2) == B.MEP_ERR_INVALID_ARG                  # N % num_src
+    assert _plan(C=0) == B.MEP_ERR_INVALID_ARG
+    assert _plan(S=0) == B.MEP_ERR_INVALID_ARG
+    assert _plan(dst=FAKE + 1) == B.MEP_ERR_INVALID_ARG
+    assert _plan(NvS=64 * 4 + 4 * 1 - 1) == B.MEP_ERR_CAPACITY       # below the per-rank bound
+    assert _plan(N=2 ** 20, E=16, K=4, R=4, NvS=2 ** 30) == B.MEP_ERR_CAPACITY  # R*NvS > INT32_MAX
+    g, d = B.dedup_capacity(64, 16, 4, 4)
+    assert g == 64 * 2 and d == 64 * 3
+    assert _plan(cap_g=g - 1) == B.MEP_ERR_CAPACITY
+    assert _plan(cap_d=d - 1) == B.MEP_ERR_CAPACITY
+    assert _plan(ws_bytes=100) == B.MEP_ERR_CAPACITY
+    # epn == 1: no duplicates are possible, zero capacity is enough for both lists
+    assert B.dedup_capacity(64, 8, 2, 8) == (0, 0)

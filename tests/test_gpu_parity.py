@@ -1,0 +1,304 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Integers (ids, counts, offsets, permutations, plan and dedup structures) must match bit for bit;
+routing weights within 1e-6 relative for fp32 logits and 2e-3 for bf16 logits (the accuracy the
+weights are specified to; both sides compute them in binary64 from identical binary32 inputs, so
+the observed error is a few units in the last place).  Every workload runs at full size."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from expert_dispatch_layout_amd import _binding as B
+from expert_dispatch_layout_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def setup_module(module):
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    B.lib()
+
+
+def _note(msg):
+    print(msg, flush=True)
+
+
+def _to_dev_logits(logits, dtype):
+    if dtype == synth.BF16:
+        t = torch.from_numpy(logits.view(np.int16)).to(DEV)
+        return t.view(torch.bfloat16)
+    return torch.from_numpy(logits).to(DEV)
+
+
+def gpu_route(logits, K, dtype, *, bias=None, score_fn=0, renormalize=True, n_group=1,
+              topk_group=1, group_topn=2, scale=1.0):
+    x = _to_dev_logits(logits, dtype)
+    b = torch.from_numpy(bias).to(DEV) if bias is not None else None
+    ids, w = B.route(x, K, bias=b, score_fn=score_fn, renormalize=renormalize, n_group=n_group,
+                     topk_group=topk_group, group_topn=group_topn, scale=scale)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+def gpu_layout_plan(ids_np, E, A, R, S, C, NvS=None):
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np, np.int32)).to(DEV)
+    L = B.build_layout(ids, E, A)
+    P = B.plan(ids, L.cu_seqlens, L.expanded_to_permuted, E, A, R, S, C, NvS=NvS)
+    torch.cuda.synchronize()
+    return L, P
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+def check_route(inp_logits, K, dtype, **kw):
+    ids_g, w_g = gpu_route(inp_logits, K, dtype, **kw)
+    ids_o, w_o = oracle.route(inp_logits, K, dtype=dtype, **kw)
+    bad = np.nonzero((ids_g != ids_o).any(axis=1))[0]
+    assert bad.size == 0, "ids differ on %d tokens, first %s: gpu %s oracle %s" % (
+        bad.size, bad[:3], ids_g[bad[:3]], ids_o[bad[:3]])
+    tol = 2e-3 if dtype == synth.BF16 else 1e-6
+    err = np.abs(w_g.astype(np.float64) - w_o) / np.maximum(np.abs(w_o.astype(np.float64)), 1e-30)
+    assert float(err.max(initial=0.0)) <= tol, "weight rel err %g" % err.max()
+    return ids_o, float(err.max(initial=0.0))
+
+
+def check_layout_plan(ids, E, A, R, S, C, NvS=None):
+    N, K = ids.shape
+    epn = E // R
+    if NvS is None:
+        NvS = N * min(K, epn) + epn * (A - 1)
+    Lg, Pg = gpu_layout_plan(ids, E, A, R, S, C, NvS)
+    Lo = oracle.layout(ids, E, A)
+    T = int(Lo.cu_seqlens[E])
+    assert np.array_equal(_np(Lg.tokens_per_expert), Lo.tokens_per_expert)
+    assert np.array_equal(_np(Lg.cu_seqlens), Lo.cu_seqlens)
+    assert np.array_equal(_np(Lg.expanded_to_permuted), Lo.expanded_to_permuted)
+    assert np.array_equal(_np(Lg.permuted_to_expanded)[:T], Lo.permuted_to_expanded)
+    assert np.array_equal(_np(Lg.zero_fill), Lo.zero_fill)
+    Po = oracle.plan(ids, Lo.cu_seqlens, Lo.expanded_to_permuted, E, R, S, C, NvS)
+    G, D = int(Po.dup_offsets[R, 0]), int(Po.dup_offsets[R, 1])
+    for name in ("is_token_in_rank", "num_tokens_per_rank", "num_tokens_per_expert",
+                 "rank_prefix_matrix", "channel_prefix_matrix", "recv_tokens", "recv_cu_seqlens",
+                 "recv_zero_fill", "dst", "dup_counts", "dup_offsets"):
+        g = _np(getattr(Pg, name))
+        o = getattr(Po, name)
+        assert g.shape == o.shape, name
+        assert np.array_equal(g, o), name
+    assert np.array_equal(_np(Pg.dup_groups)[:G], Po.dup_groups)
+    assert np.array_equal(_np(Pg.dup_loffs)[:D], Po.dup_loffs)
+    return Lo, Po
+
+
+# -------------------------------------------------------------------------------------------
+# the five workloads at full size, end to end
+# -------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_workload_full_path(name):
+    wl = synth.WORKLOADS[name]
+    _note("workload %s N=%d E=%d K=%d" % (name, wl.N, wl.E, wl.K))
+    inp = synth.make_inputs(wl)
+    ids, err = check_route(inp.logits, wl.K, wl.dtype, bias=inp.bias, score_fn=wl.score_fn,
+                           renormalize=wl.renormalize, n_group=wl.n_group,
+                           topk_group=wl.topk_group, group_topn=wl.group_topn, scale=wl.scale)
+    _note("  route ok, max weight rel err %.3g" % err)
+    check_layout_plan(ids, wl.E, wl.alignment, wl.R, wl.S, wl.num_channels)
+    _note("  layout + plan ok (S=%d)" % wl.S)
+    check_layout_plan(ids, wl.E, wl.alignment, wl.R, 1, wl.num_channels)
+    _note("  layout + plan ok (S=1)")
+
+
+# -------------------------------------------------------------------------------------------
+# routing sweep: shapes, dtypes, modes, ragged E, K up to 32, ties
+# -------------------------------------------------------------------------------------------
+
+ROUTE_CASES = []
+for E, K in [(3, 2), (8, 1), (8, 8), (12, 5), (16, 4), (64, 8), (100, 7), (128, 16), (200, 3),
+             (256, 8), (256, 32), (512, 8), (1024, 8), (1024, 32)]:
+    for dtype in (synth.F32, synth.BF16):
+        ROUTE_CASES.append((E, K, dtype))
+
+
+@pytest.mark.parametrize("E,K,dtype", ROUTE_CASES)
+@pytest.mark.parametrize("mode", ["softmax", "softmax_full", "sigmoid", "sigmoid_group"])
+def test_route_sweep(E, K, dtype, mode):
+    rng = np.random.default_rng(E * 1000 + K * 10 + dtype)
+    N = 333
+    x = rng.standard_normal((N, E)).astype(np.float32)
+    x[::7, 1::3] = x[::7, 0:1]          # equal logits inside rows -> ties
+    x[5] = 0.0
+    x[6, : E // 2] = -0.0               # signed zeros tie with +0
+    logits = synth.f32_to_bf16_bits(x) if dtype == synth.BF16 else x
+    bias = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    kw = {}
+    if mode == "softmax_full":
+        kw = dict(renormalize=False)
+    elif mode == "sigmoid":
+        kw = dict(score_fn=1, bias=np.zeros(E, np.float32) if K % 2 else bias, scale=2.5)
+    elif mode == "sigmoid_group":
+        G = next((g for g in (8, 4, 2) if E % g == 0 and (E // g) >= 2), 1)
+        if G == 1:
+            pytest.skip("no group split")
+        TG = max(1, G // 2)
+        if TG * (E // G) < K:
+            TG = G
+        kw = dict(score_fn=1, bias=bias, n_group=G, topk_group=TG, group_topn=1 + (K % 2),
+                  scale=2.5, renormalize=bool(K % 3))
+    check_route(logits, K, dtype, **kw)
+
+
+def test_route_tiny_batches():
+    rng = np.random.default_rng(9)
+    for N in (1, 2, 3, 63, 65, 257):
+        x = rng.standard_normal((N, 256)).astype(np.float32)
+        check_route(x, 8, synth.F32, score_fn=1, bias=np.zeros(256, np.float32), n_group=8,
+                    topk_group=4, scale=2.5)
+
+
+# -------------------------------------------------------------------------------------------
+# sigmoid: every bf16 value, hard fp32 cases, a dense fp32 range
+# -------------------------------------------------------------------------------------------
+
+def _sigmoid_via_route(xs):
+    """sigmoid of each value, read back through routing with K = E = 32, no renormalisation and
+    unit scale: the weight of a selected expert is then exactly its sigmoid."""
+    n = -(-xs.size // 32) * 32
+    pad = np.zeros(n, np.float32)
+    pad[: xs.size] = xs
+    x = pad.reshape(-1, 32)
+    ids, w = gpu_route(x, 32, synth.F32, score_fn=1, bias=np.zeros(32, np.float32),
+                       renormalize=False, scale=1.0)
+    s = np.empty_like(x)
+    np.put_along_axis(s, ids.astype(np.int64), w, axis=1)
+    return s.reshape(-1)[: xs.size]
+
+
+def test_sigmoid_every_bf16_value():
+    b = np.arange(1 << 16, dtype=np.uint32)
+    finite = ((b >> 7) & 0xFF) != 0xFF
+    xs = (b[finite] << 16).view(np.float32)
+    got = _sigmoid_via_route(xs)
+    want = oracle.sigmoid(xs)
+    bad = np.nonzero(got.view(np.uint32) != want.view(np.uint32))[0]
+    assert bad.size == 0, (xs[bad[:5]], got[bad[:5]], want[bad[:5]])
+
+
+def test_sigmoid_fp32_range_and_hard_cases():
+    xs = (np.uint32(0x3F800000) + np.arange(1 << 22, dtype=np.uint32)).view(np.float32)
+    want, path = oracle.sigmoid(xs, with_path=True)
+    assert (path == 2).sum() > 0        # includes inputs that sit near a rounding midpoint
+    got = _sigmoid_via_route(xs)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    rng = np.random.default_rng(11)
+    xs = np.concatenate([rng.uniform(-110, 30, 1 << 18).astype(np.float32),
+                         np.array([0.0, -0.0, 1e-45, -1e-45, 17.5, -87.5, -103.9, -104.0, -150.0,
+                                   3e38, -3e38], np.float32)])
+    got = _sigmoid_via_route(xs)
+    want = oracle.sigmoid(xs)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+# -------------------------------------------------------------------------------------------
+# layout and plan sweeps on synthetic id rows
+# -------------------------------------------------------------------------------------------
+
+LAYOUT_CASES = [
+    # N, E, K, A, R, S, C
+    (0, 8, 2, 3, 2, 2, 4),
+    (1, 8, 2, 1, 2, 1, 24),
+    (1023, 8, 2, 128, 8, 1, 24),       # N*K = 2046: one ragged tile
+    (1024, 8, 2, 128, 8, 8, 24),       # N*K = 2048: exactly one tile
+    (1025, 8, 2, 128, 1, 5, 24),       # one slot into the second tile
+    (777, 16, 4, 3, 4, 3, 7),
+    (4096, 64, 8, 64, 8, 8, 24),
+    (5000, 128, 8, 1, 16, 8, 1),
+    (3000, 256, 8, 128, 32, 3, 1000),  # more channels than tokens per shard
+    (2048, 256, 8, 2, 128, 4, 24),     # R = 128 (epn = 2)
+    (999, 96, 6, 5, 12, 3, 10),
+    (640, 512, 16, 8, 8, 2, 24),       # K > 8 path
+    (300, 1024, 32, 16, 128, 3, 4),    # K = 32, E = 1024
+    (2000, 8, 8, 4, 8, 4, 24),         # epn = 1, K = E
+]
+
+
+@pytest.mark.parametrize("N,E,K,A,R,S,C", LAYOUT_CASES)
+def test_layout_plan_sweep(N, E, K, A, R, S, C):
+    _note("layout/plan N=%d E=%d K=%d A=%d R=%d S=%d C=%d" % (N, E, K, A, R, S, C))
+    ids = synth.random_ids(N, E, K, seed=N + 31 * E + K, hot=min(4, E))
+    check_layout_plan(ids, E, A, R, S, C)
+
+
+def test_plan_larger_nvs_stride():
+    ids = synth.random_ids(1000, 64, 8, seed=3, hot=4)
+    check_layout_plan(ids, 64, 16, 8, 4, 24, NvS=1000 * 8 + 8 * 15 + 12345)
+
+
+# -------------------------------------------------------------------------------------------
+# determinism, workspace reuse, optional outputs
+# -------------------------------------------------------------------------------------------
+
+def test_run_twice_is_byte_identical():
+    wl = synth.WORKLOADS["dsv3"]
+    inp = synth.make_inputs(wl)
+    outs = []
+    for _ in range(2):
+        ids, w = gpu_route(inp.logits, wl.K, wl.dtype, bias=inp.bias, score_fn=wl.score_fn,
+                           n_group=wl.n_group, topk_group=wl.topk_group, scale=wl.scale)
+        L, P = gpu_layout_plan(ids, wl.E, wl.alignment, wl.R, wl.S, wl.num_channels)
+        outs.append([ids, w] + [_np(t) for t in (L.expanded_to_permuted, L.permuted_to_expanded,
+                                                 P.dst, P.dup_groups, P.dup_loffs,
+                                                 P.channel_prefix_matrix)])
+    for a, b in zip(outs[0], outs[1]):
+        assert a.tobytes() == b.tobytes()
+
+
+def test_workspace_reuse_across_sizes():
+    E, K, A, R, S, C = 64, 8, 16, 8, 4, 24
+    ws_l = B.alloc_workspace(B.layout_workspace_size(8000, E, K), DEV)
+    ws_p = B.alloc_workspace(B.plan_workspace_size(8000, E, K, R, S), DEV)
+    for N in (8000, 40, 4000, 0, 8000, 1):
+        ids_np = synth.random_ids(N, E, K, seed=N, hot=2)
+        ids = torch.from_numpy(ids_np).to(DEV)
+        L = B.build_layout(ids, E, A, ws=ws_l)
+        P = B.plan(ids, L.cu_seqlens, L.expanded_to_permuted, E, A, R, S, C, ws=ws_p)
+        torch.cuda.synchronize()
+        Lo = oracle.layout(ids_np, E, A)
+        assert np.array_equal(_np(L.expanded_to_permuted), Lo.expanded_to_permuted)
+        Po = oracle.plan(ids_np, Lo.cu_seqlens, Lo.expanded_to_permuted, E, R, S, C,
+                         B.default_nvs(N, E, K, R, A))
+        assert np.array_equal(_np(P.dst), Po.dst)
+        assert np.array_equal(_np(P.channel_prefix_matrix), Po.channel_prefix_matrix)
+
+
+def test_optional_outputs_may_be_null():
+    E, K, A, R, S, C, N = 64, 8, 16, 8, 4, 24, 3000
+    ids_np = synth.random_ids(N, E, K, seed=5, hot=2)
+    ids = torch.from_numpy(ids_np).to(DEV)
+    out = B.alloc_layout(N, E, K, A, DEV)
+    ws = B.alloc_workspace(B.layout_workspace_size(N, E, K), DEV)
+    B.mep_build_layout(ids, E, A, None, out.cu_seqlens, out.expanded_to_permuted, None, None, ws)
+    Lo = oracle.layout(ids_np, E, A)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(out.expanded_to_permuted), Lo.expanded_to_permuted)
+    P = B.alloc_plan(N, E, K, R, S, C, DEV)
+    keep = B.PlanTensors(None, None, None, None, None, None, None, None, P.dst, None, None,
+                         None, P.dup_loffs)
+    wsp = B.alloc_workspace(B.plan_workspace_size(N, E, K, R, S), DEV)
+    B.mep_plan(ids, out.cu_seqlens, out.expanded_to_permuted, E, A, R, S, C,
+               B.default_nvs(N, E, K, R, A), keep, wsp)
+    torch.cuda.synchronize()
+    Po = oracle.plan(ids_np, Lo.cu_seqlens, Lo.expanded_to_permuted, E, R, S, C,
+                     B.default_nvs(N, E, K, R, A))
+    assert np.array_equal(_np(P.dst), Po.dst)
+    assert np.array_equal(_np(P.dup_loffs)[: Po.dup_loffs.size], Po.dup_loffs)
+    ids_o, w_o = oracle.route(np.zeros((4, 16), np.float32), 2)
+    t = torch.zeros((4, 16), device=DEV)
+    ids_g = torch.empty((4, 2), dtype=torch.int32, device=DEV)
+    B.mep_route_topk(t, 2, None, B.route_params(), ids_g, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(ids_g), ids_o)

@@ -199,7 +199,8 @@ extern "C" int mep_build_layout(const int32_t* topk_ids, int64_t N, int E, int K
                                 int64_t permuted_cap, int32_t* zero_fill, void* ws, size_t ws_bytes,
                                 void* stream) {
     using namespace mep;
-    if (!topk_ids || !cu_seqlens || !expanded_to_permuted || !ws) return MEP_ERR_INVALID_ARG;
+    if (!cu_seqlens || !ws) return MEP_ERR_INVALID_ARG;
+    if (N > 0 && (!topk_ids || !expanded_to_permuted)) return MEP_ERR_INVALID_ARG;  // N == 0 reads nothing
     if (N < 0 || E < 1 || K < 1 || alignment < 1) return MEP_ERR_INVALID_ARG;
     const void* ptrs[] = {topk_ids, tokens_per_expert, cu_seqlens, expanded_to_permuted,
                           permuted_to_expanded, zero_fill};

@@ -462,7 +462,8 @@ extern "C" int mep_plan(const int32_t* topk_ids, const int32_t* cu_seqlens,
                         int R, int num_src, int num_channels, int64_t NvS, const mep_plan_outputs* out,
                         void* ws, size_t ws_bytes, void* stream) {
     using namespace mep;
-    if (!topk_ids || !cu_seqlens || !expanded_to_permuted || !out || !ws) return MEP_ERR_INVALID_ARG;
+    if (!cu_seqlens || !out || !ws) return MEP_ERR_INVALID_ARG;
+    if (N > 0 && (!topk_ids || !expanded_to_permuted)) return MEP_ERR_INVALID_ARG;  // N == 0 reads nothing
     if (N < 0 || E < 1 || K < 1 || R < 1 || num_src < 1 || num_channels < 1 || alignment < 1)
         return MEP_ERR_INVALID_ARG;
     const void* p4[] = {topk_ids, cu_seqlens, expanded_to_permuted, out->is_token_in_rank,

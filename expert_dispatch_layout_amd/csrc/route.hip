@@ -354,13 +354,14 @@ extern "C" int mep_route_topk(const void* logits, int dtype, int64_t N, int E, i
                               const float* bias, const mep_route_params* p, int32_t* topk_ids,
                               float* topk_weights, void* stream) {
     using namespace mep;
-    if (!p || !logits || !topk_ids) return MEP_ERR_INVALID_ARG;
+    if (!p) return MEP_ERR_INVALID_ARG;
+    if (N > 0 && (!logits || !topk_ids)) return MEP_ERR_INVALID_ARG;  // N == 0 reads nothing
     if (dtype != MEP_F32 && dtype != MEP_BF16) return MEP_ERR_INVALID_ARG;
     if (p->score_fn != MEP_SOFTMAX && p->score_fn != MEP_SIGMOID) return MEP_ERR_INVALID_ARG;
     if (N < 0 || E < 1 || K < 1) return MEP_ERR_INVALID_ARG;
     if (!aligned(logits, 16) || !aligned(topk_ids, 4) || (topk_weights && !aligned(topk_weights, 4)))
         return MEP_ERR_INVALID_ARG;
-    if (p->score_fn == MEP_SIGMOID && (!bias || !aligned(bias, 4))) return MEP_ERR_INVALID_ARG;
+    if (p->score_fn == MEP_SIGMOID && ((N > 0 && !bias) || !aligned(bias, 4))) return MEP_ERR_INVALID_ARG;
     if (!(p->scale == p->scale) || p->scale > FLT_MAX || p->scale < -FLT_MAX) return MEP_ERR_INVALID_ARG;
     if (p->n_group < 1 || p->renormalize < 0 || p->renormalize > 1) return MEP_ERR_INVALID_ARG;
     if (E > 1024 || K > 32 || K > E) return MEP_ERR_UNSUPPORTED;

@@ -36,7 +36,8 @@
  *   - All checks run on the host before anything is enqueued.  On error
  *     nothing is written and nothing is launched.  Capacities are checked
  *     against worst-case bounds, so kernels have no error path.
- *   - Optional outputs are marked "nullable"; NULL skips them.
+ *   - Optional outputs are marked "nullable"; NULL skips them.  With N == 0 the per-slot
+ *     inputs and outputs (logits, ids, weights, permutation maps, dst) may be NULL.
  *   - No exceptions cross the ABI; mep_status_string names a return code.
  */
 #ifndef MEP_H_
@@ -144,7 +145,8 @@ int mep_route_topk(const void* logits, int dtype, int64_t N, int E, int K,
  *                        permuted_to_expanded is given, else ignored
  *   zero_fill            device int32[E,2] (nullable)
  *   ws, ws_bytes         workspace (see mep_layout_workspace_size)
- * Returns MEP_ERR_UNSUPPORTED for E > 1024 or N*K > INT32_MAX - E*alignment.
+ * Returns MEP_ERR_UNSUPPORTED for E > 1024, K > min(E, 32), or
+ * N*K + min(E, N*K)*(alignment-1) > INT32_MAX - 65536.
  */
 int mep_build_layout(const int32_t* topk_ids, int64_t N, int E, int K, int alignment,
                      int32_t* tokens_per_expert, int32_t* cu_seqlens,

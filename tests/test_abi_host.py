@@ -57,6 +57,7 @@ def _route(logits=FAKE, dtype=0, N=16, E=8, K=2, bias=FAKE, score_fn=0, renorm=1
 def test_route_validation():
     assert _route(N=0) == B.MEP_OK                       # nothing to do, nothing launched
     assert _route(logits=None) == B.MEP_ERR_INVALID_ARG
+    assert _route(N=0, logits=None, ids=None, w=None) == B.MEP_OK
     assert _route(ids=None) == B.MEP_ERR_INVALID_ARG
     assert _route(logits=MIS) == B.MEP_ERR_INVALID_ARG
     assert _route(dtype=7) == B.MEP_ERR_INVALID_ARG
@@ -84,6 +85,7 @@ def _layout(N=16, E=8, K=2, A=4, tpe=FAKE, cu=FAKE, e2p=FAKE, p2e=FAKE, cap=None
 
 def test_layout_validation():
     assert _layout(ids=None) == B.MEP_ERR_INVALID_ARG
+    assert _layout(N=0, ids=None, e2p=None, ws=None) == B.MEP_ERR_INVALID_ARG   # workspace needed
     assert _layout(cu=None) == B.MEP_ERR_INVALID_ARG
     assert _layout(e2p=None) == B.MEP_ERR_INVALID_ARG
     assert _layout(ws=None) == B.MEP_ERR_INVALID_ARG

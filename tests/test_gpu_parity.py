@@ -250,9 +250,12 @@ def test_run_twice_is_byte_identical():
         ids, w = gpu_route(inp.logits, wl.K, wl.dtype, bias=inp.bias, score_fn=wl.score_fn,
                            n_group=wl.n_group, topk_group=wl.topk_group, scale=wl.scale)
         L, P = gpu_layout_plan(ids, wl.E, wl.alignment, wl.R, wl.S, wl.num_channels)
-        outs.append([ids, w] + [_np(t) for t in (L.expanded_to_permuted, L.permuted_to_expanded,
-                                                 P.dst, P.dup_groups, P.dup_loffs,
-                                                 P.channel_prefix_matrix)])
+        T = int(L.cu_seqlens[wl.E].item())
+        G, D = [int(v) for v in P.dup_offsets[wl.R].tolist()]
+        # capacity-sized buffers: only their valid prefixes are defined
+        outs.append([ids, w, _np(L.expanded_to_permuted), _np(L.permuted_to_expanded)[:T],
+                     _np(P.dst), _np(P.dup_groups)[:G], _np(P.dup_loffs)[:D],
+                     _np(P.channel_prefix_matrix), _np(P.is_token_in_rank)])
     for a, b in zip(outs[0], outs[1]):
         assert a.tobytes() == b.tobytes()
 
@@ -261,7 +264,7 @@ def test_workspace_reuse_across_sizes():
     E, K, A, R, S, C = 64, 8, 16, 8, 4, 24
     ws_l = B.alloc_workspace(B.layout_workspace_size(8000, E, K), DEV)
     ws_p = B.alloc_workspace(B.plan_workspace_size(8000, E, K, R, S), DEV)
-    for N in (8000, 40, 4000, 0, 8000, 1):
+    for N in (8000, 40, 4000, 0, 8000, 4):
         ids_np = synth.random_ids(N, E, K, seed=N, hot=2)
         ids = torch.from_numpy(ids_np).to(DEV)
         L = B.build_layout(ids, E, A, ws=ws_l)

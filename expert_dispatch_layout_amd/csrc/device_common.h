@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mep {
 
 constexpr int kWave = 64;
@@ -141,5 +143,72 @@ __host__ __device__ constexpr int bits_for(int n_keys) {
     while ((1 << b) < n_keys) ++b;
     return b;
 }
+
+}  // namespace mep
+
+namespace mep {
+
+// ---- cross-lane exchange within aligned segments of S lanes (S a power of two <= 64) ----------
+// Partners: S>=2 lane^1, S>=4 lane^2 (DPP quad permutes), S>=8 the mirror lane within 8
+// (DPP row_half_mirror), S>=16 the mirror lane within 16 (DPP row_mirror), S>=32/64 lane^16 and
+// lane^32 through ds_bpermute.  Each step pairs lanes symmetrically, so folding a commutative
+// operation over the steps leaves every lane of the segment with the full result.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int STEP>
+__device__ __forceinline__ uint32_t seg_partner_u32(uint32_t v) {
+    if constexpr (STEP == 1) return dpp_u32<0xB1>(v);   // quad_perm [1,0,3,2]
+    else if constexpr (STEP == 2) return dpp_u32<0x4E>(v);  // quad_perm [2,3,0,1]
+    else if constexpr (STEP == 4) return dpp_u32<0x141>(v); // row_half_mirror
+    else if constexpr (STEP == 8) return dpp_u32<0x140>(v); // row_mirror
+    else return (uint32_t)__shfl_xor((int)v, STEP);
+}
+
+template <int STEP>
+__device__ __forceinline__ float seg_partner_f32(float v) {
+    return __uint_as_float(seg_partner_u32<STEP>(__float_as_uint(v)));
+}
+
+template <int STEP>
+__device__ __forceinline__ double seg_partner_f64(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = seg_partner_u32<STEP>((uint32_t)u);
+    const uint32_t hi = seg_partner_u32<STEP>((uint32_t)(u >> 32));
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// All-reduce over segments of S lanes; S is a run-time power of two (uniform) up to SMAX.
+template <int SMAX, typename T, typename Partner, typename Op>
+__device__ __forceinline__ T seg_allreduce(T v, int S, Partner partner, Op op) {
+    if constexpr (SMAX >= 2) if (S >= 2) v = op(v, partner(v, std::integral_constant<int, 1>{}));
+    if constexpr (SMAX >= 4) if (S >= 4) v = op(v, partner(v, std::integral_constant<int, 2>{}));
+    if constexpr (SMAX >= 8) if (S >= 8) v = op(v, partner(v, std::integral_constant<int, 4>{}));
+    if constexpr (SMAX >= 16) if (S >= 16) v = op(v, partner(v, std::integral_constant<int, 8>{}));
+    if constexpr (SMAX >= 32) if (S >= 32) v = op(v, partner(v, std::integral_constant<int, 16>{}));
+    if constexpr (SMAX >= 64) if (S >= 64) v = op(v, partner(v, std::integral_constant<int, 32>{}));
+    return v;
+}
+
+struct PartnerF32 {
+    template <int STEP>
+    __device__ __forceinline__ float operator()(float v, std::integral_constant<int, STEP>) const {
+        return seg_partner_f32<STEP>(v);
+    }
+};
+struct PartnerF64 {
+    template <int STEP>
+    __device__ __forceinline__ double operator()(double v, std::integral_constant<int, STEP>) const {
+        return seg_partner_f64<STEP>(v);
+    }
+};
+struct PartnerU32 {
+    template <int STEP>
+    __device__ __forceinline__ uint32_t operator()(uint32_t v, std::integral_constant<int, STEP>) const {
+        return seg_partner_u32<STEP>(v);
+    }
+};
 
 }  // namespace mep

@@ -1,0 +1,295 @@
+// Pieces shared by the routing kernels: arguments, the exact per-token selection (used by the
+// generic kernel for every token and by the fast kernel for tokens its filter cannot certify),
+// and the binary64 weight computation.
+//
+// Element layout used by both kernels: a token is handled by a segment of LPT lanes of one
+// wave64.  Lane `lseg` of the segment loads NV 16-byte chunks; chunk j holds experts
+// [(j*LPT + lseg)*W, +W) with W = 4 (fp32) or 8 (bf16), so each load instruction of a segment
+// reads one contiguous run of the row ("line" j = experts [j*LPT*W, (j+1)*LPT*W)).
+#pragma once
+
+#include <float.h>
+#include <limits.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "device_common.h"
+#include "host_common.h"
+#include "sigmoid_cr.h"
+
+namespace mep {
+
+struct RouteArgs {
+    const void* logits;
+    const float* bias;
+    int64_t N;
+    int E;
+    int K;
+    int score_fn;
+    int renormalize;
+    int n_group;
+    int topk_group;
+    int group_topn;
+    float scale;
+    float inv_gsize;  // 1 / (E / n_group)
+    int32_t* ids;
+    float* weights;
+    int vec;          // rows are 16-byte aligned and E is a multiple of the chunk width
+};
+
+constexpr int kRouteBlock = 256;
+constexpr int kMaxGroups = 32;
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0..N-1.
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int LPT>
+__device__ __forceinline__ uint32_t seg_max_u32(uint32_t v) {
+#pragma unroll
+    for (int o = LPT / 2; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, LPT));
+    return v;
+}
+
+template <int LPT>
+__device__ __forceinline__ uint32_t seg_min_u32(uint32_t v) {
+#pragma unroll
+    for (int o = LPT / 2; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, LPT));
+    return v;
+}
+
+template <int LPT>
+__device__ __forceinline__ double seg_sum_f64(double v) {
+#pragma unroll
+    for (int o = LPT / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, LPT);
+    return v;
+}
+
+// keep the two largest of (t1 >= t2) and the partner lane's pair
+template <int LPT>
+__device__ __forceinline__ void seg_top2_u32(uint32_t& t1, uint32_t& t2) {
+#pragma unroll
+    for (int o = LPT / 2; o >= 1; o >>= 1) {
+        uint32_t b1 = (uint32_t)__shfl_xor((int)t1, o, LPT);
+        uint32_t b2 = (uint32_t)__shfl_xor((int)t2, o, LPT);
+        uint32_t n2 = max(min(t1, b1), max(t2, b2));
+        t1 = max(t1, b1);
+        t2 = n2;
+    }
+}
+
+__device__ __forceinline__ int chunk_expert(int q, int W, int LPT, int lseg) {
+    return ((q / W) * LPT + lseg) * W + (q % W);
+}
+
+// Load the lane's NE = NV*W logits of token `tok` (as binary32; bf16 widening is exact).
+template <int LPT, int NV, bool BF16>
+__device__ __forceinline__ void load_row(const RouteArgs& a, int64_t tok, int lseg,
+                                         float (&x)[NV * (BF16 ? 8 : 4)]) {
+    constexpr int W = BF16 ? 8 : 4;
+    const int E = a.E;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int e0 = (j * LPT + lseg) * W;
+        if (a.vec && e0 < E) {
+            if constexpr (BF16) {
+                const uint4 v = *reinterpret_cast<const uint4*>(
+                    reinterpret_cast<const uint16_t*>(a.logits) + tok * E + e0);
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    x[j * W + 2 * q] = __uint_as_float(w4[q] << 16);
+                    x[j * W + 2 * q + 1] = __uint_as_float(w4[q] & 0xFFFF0000u);
+                }
+            } else {
+                const float4 v = *reinterpret_cast<const float4*>(
+                    reinterpret_cast<const float*>(a.logits) + tok * E + e0);
+                x[j * W + 0] = v.x;
+                x[j * W + 1] = v.y;
+                x[j * W + 2] = v.z;
+                x[j * W + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < W; ++i) {
+                const int e = e0 + i;
+                float v = 0.0f;
+                if (e < E) {
+                    if constexpr (BF16)
+                        v = __uint_as_float(
+                            (uint32_t)(reinterpret_cast<const uint16_t*>(a.logits)[tok * E + e]) << 16);
+                    else
+                        v = reinterpret_cast<const float*>(a.logits)[tok * E + e];
+                }
+                x[j * W + i] = v;
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ float load_logit(const RouteArgs& a, int64_t tok, int e, bool bf16) {
+    if (bf16)
+        return __uint_as_float((uint32_t)(reinterpret_cast<const uint16_t*>(a.logits)[tok * a.E + e])
+                               << 16);
+    return reinterpret_cast<const float*>(a.logits)[tok * a.E + e];
+}
+
+// Exact selection for one token by the LPT lanes of its segment: exact keys (logit, or
+// correctly rounded sigmoid + bias), exact group limit, then K rounds of a segmented arg-max
+// (max of the order-preserving key, then min expert index among the maxima).  On return the
+// lane owning output slot k (k % LPT == lseg) holds its expert in my_e[k / LPT]; every lane
+// holds the first selected logit in first_x (used by the softmax weights).
+template <int LPT, int NV, bool BF16, int KMAX>
+__device__ __forceinline__ void exact_select_token(const RouteArgs& a, const float* bias, int lseg,
+                                                   const float (&x)[NV * (BF16 ? 8 : 4)],
+                                                   int (&my_e)[(KMAX + LPT - 1) / LPT],
+                                                   float& first_x) {
+    constexpr int W = BF16 ? 8 : 4;
+    constexpr int NE = NV * W;
+    const int E = a.E;
+    const int K = a.K;
+    const bool sig = a.score_fn == MEP_SIGMOID;
+    uint32_t ok[NE];
+    uint32_t valid = 0;
+#pragma unroll
+    for (int q = 0; q < NE; ++q) {
+        const int e = chunk_expert(q, W, LPT, lseg);
+        const bool v = e < E;
+        valid |= (v ? 1u : 0u) << q;
+        float key = x[q];
+        if (sig) key = (v ? sigmoid_cr(x[q]) : 0.0f) + (v ? bias[e] : 0.0f);
+        ok[q] = v ? order_key(key) : 0u;
+    }
+    uint32_t eligible = valid;
+    if (a.n_group > 1) {
+        int grp[NE];
+#pragma unroll
+        for (int q = 0; q < NE; ++q)
+            grp[q] = (int)(((float)chunk_expert(q, W, LPT, lseg) + 0.5f) * a.inv_gsize);
+        uint32_t score[kMaxGroups];
+#pragma unroll
+        for (int g = 0; g < kMaxGroups; ++g) {
+            score[g] = 0;
+            if (g < a.n_group) {
+                uint32_t t1 = 0, t2 = 0;
+#pragma unroll
+                for (int q = 0; q < NE; ++q) {
+                    if (((valid >> q) & 1u) && grp[q] == g) {
+                        t2 = max(t2, min(t1, ok[q]));
+                        t1 = max(t1, ok[q]);
+                    }
+                }
+                seg_top2_u32<LPT>(t1, t2);
+                const float f1 = order_key_inv(t1);
+                score[g] = order_key((a.group_topn >= 2) ? (f1 + order_key_inv(t2)) : f1);
+            }
+        }
+        // keep topk_group groups by repeated extraction (score desc, group index asc)
+        uint32_t kept = 0;
+        for (int r = 0; r < a.topk_group; ++r) {
+            uint32_t bs = 0;
+            int bg = -1;
+#pragma unroll
+            for (int g = 0; g < kMaxGroups; ++g) {
+                if (g < a.n_group && !((kept >> g) & 1u) && (bg < 0 || score[g] > bs)) {
+                    bs = score[g];
+                    bg = g;
+                }
+            }
+            kept |= 1u << bg;
+        }
+        uint32_t el = 0;
+#pragma unroll
+        for (int q = 0; q < NE; ++q) el |= (((kept >> grp[q]) & 1u) ? 1u : 0u) << q;
+        eligible &= el;
+    }
+    uint32_t taken = 0;
+    first_x = 0.0f;
+    static_for<KMAX>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        if (k >= K) return;
+        uint32_t best = 0;
+        int best_q = -1;
+#pragma unroll
+        for (int q = 0; q < NE; ++q) {
+            // slots are visited in increasing expert index, so '>' keeps the lower index on ties
+            if ((((eligible & ~taken) >> q) & 1u) && (best_q < 0 || ok[q] > best)) {
+                best = ok[q];
+                best_q = q;
+            }
+        }
+        const int best_e = best_q < 0 ? INT_MAX : chunk_expert(best_q, W, LPT, lseg);
+        const uint32_t m = seg_max_u32<LPT>(best_q < 0 ? 0u : best);
+        const uint32_t cand = (best_q >= 0 && best == m) ? (uint32_t)best_e : 0xFFFFFFFFu;
+        const int e_sel = (int)seg_min_u32<LPT>(cand);
+        if (best_q >= 0 && best_e == e_sel) taken |= 1u << best_q;
+        if (k == 0) first_x = order_key_inv(m);  // softmax: the first selected logit
+        if ((k % LPT) == lseg) my_e[k / LPT] = e_sel;
+    });
+}
+
+// Weights from the selected experts of a token.  The lane owning output slot j (j % LPT == lseg)
+// holds v_j: the logit (softmax) or the correctly rounded sigmoid (sigmoid).  All arithmetic is
+// binary64, rounded once to binary32 (TensorRT-LLM RoutingKernel.cuh calcSoftmax, over the
+// selected lanes or over the full score vector; sigmoid weights renormalised and scaled).
+// For softmax without renormalisation `full_max`/`full_den` carry the max and the sum of
+// exp(x - max) over all E logits of the token.
+template <int LPT, int KPL>
+__device__ __forceinline__ void write_weights(const RouteArgs& a, int64_t tok, int lseg, bool live,
+                                              const int (&my_e)[KPL], const float (&my_v)[KPL],
+                                              double first_x, double full_max, double full_den) {
+    const bool sig = a.score_fn == MEP_SIGMOID;
+    const int K = a.K;
+    double term[KPL];
+    double den = 0.0;
+#pragma unroll
+    for (int m = 0; m < KPL; ++m) {
+        const int j = m * LPT + lseg;
+        double t = 0.0;
+        if (j < K) {
+            if (sig)
+                t = (double)my_v[m];
+            else if (a.renormalize)
+                t = exp((double)my_v[m] - first_x);
+            else
+                t = exp((double)my_v[m] - full_max);
+        }
+        term[m] = t;
+        den += t;
+    }
+    if (sig) {
+        if (a.renormalize) den = seg_sum_f64<LPT>(den);
+    } else if (a.renormalize) {
+        den = seg_sum_f64<LPT>(den);
+    } else {
+        den = full_den;
+    }
+    if (!live) return;
+#pragma unroll
+    for (int m = 0; m < KPL; ++m) {
+        const int j = m * LPT + lseg;
+        if (j < K) {
+            a.ids[tok * K + j] = my_e[m];
+            if (a.weights) {
+                double w;
+                if (sig && !a.renormalize)
+                    w = term[m];
+                else
+                    w = den > 0.0 ? term[m] / den : 0.0;
+                a.weights[tok * K + j] = (float)(w * (double)a.scale);
+            }
+        }
+    }
+}
+
+// Fast-kernel launcher (route_fast.hip).  Returns false when the shape is not covered.
+bool launch_route_fast(const RouteArgs& a, int dtype, hipStream_t st);
+
+}  // namespace mep

@@ -1,0 +1,45 @@
+// Shape dispatch of the fast routing kernel (route_fast.h): decides whether a routing call is
+// covered and with which group mapping and list depth.
+#include "route_fast.h"
+
+namespace mep {
+
+static int ilog2(int v) {
+    int l = 0;
+    while ((1 << l) < v) ++l;
+    return l;
+}
+
+bool launch_route_fast(const RouteArgs& a, int dtype, hipStream_t st) {
+    const bool bf16 = dtype == MEP_BF16;
+    if (a.E % kFastEPL != 0 || !a.vec) return false;
+    const int LPT = a.E / kFastEPL;
+    if (LPT != 2 && LPT != 4 && LPT != 8 && LPT != 16) return false;
+    FastCfg cfg{};
+    int units;
+    if (a.n_group <= 1) {
+        cfg.mode = 0;
+        units = LPT;
+    } else {
+        const int gsize = a.E / a.n_group;
+        if (gsize % kFastEPL == 0) {
+            cfg.mode = 1;  // a group spans gsize/32 lanes
+            cfg.S = gsize / kFastEPL;
+        } else {
+            return false;
+        }
+        cfg.log2S = ilog2(cfg.S);
+        if ((1 << cfg.log2S) != cfg.S) return false;
+        units = a.topk_group;
+    }
+    cfg.mt = (a.K + units - 1) / units;
+    const int M = (cfg.mode != 0 && cfg.mt < 2) ? 2 : cfg.mt;  // group scores need the top two
+    if (M > 4) return false;
+    if (bf16)
+        launch_fast_bf16(LPT, a, cfg, M, st);
+    else
+        launch_fast_f32(LPT, a, cfg, M, st);
+    return true;
+}
+
+}  // namespace mep

@@ -1,0 +1,15 @@
+// Instantiations of the fast routing kernel for binary32 logits.
+#include "route_fast.h"
+
+namespace mep {
+
+void launch_fast_f32(int LPT, const RouteArgs& a, const FastCfg& cfg, int M, hipStream_t st) {
+    switch (LPT) {
+        case 2: launch_fast_shape<2, false>(a, cfg, M, st); break;
+        case 4: launch_fast_shape<4, false>(a, cfg, M, st); break;
+        case 8: launch_fast_shape<8, false>(a, cfg, M, st); break;
+        default: launch_fast_shape<16, false>(a, cfg, M, st); break;
+    }
+}
+
+}  // namespace mep

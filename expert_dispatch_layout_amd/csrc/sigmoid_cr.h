@@ -132,3 +132,12 @@ __device__ __forceinline__ float sigmoid_cr(float x) {
 }
 
 }  // namespace mep
+
+namespace mep {
+
+// Out-of-line forms for paths that evaluate many independent values on rare occasions: a call
+// keeps the scheduler from interleaving (and holding registers for) all of them at once.
+__device__ __noinline__ float sigmoid_cr_call(float x) { return sigmoid_cr(x); }
+__device__ __noinline__ double exp_f64_call(double x) { return exp(x); }
+
+}  // namespace mep

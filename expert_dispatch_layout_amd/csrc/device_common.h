@@ -10,6 +10,24 @@ namespace mep {
 
 constexpr int kWave = 64;
 
+// Global-memory views of generic pointers.  Pointers that reach a kernel inside a struct are
+// generic to the compiler, which then emits flat instructions; those count against the LDS
+// counter as well, so every LDS wait would also wait for outstanding HBM loads.
+#define MEP_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ const MEP_GLOBAL T* gptr(const T* p) {
+    return (const MEP_GLOBAL T*)p;
+}
+template <typename T>
+__device__ __forceinline__ MEP_GLOBAL T* gptr(T* p) {
+    return (MEP_GLOBAL T*)p;
+}
+
+// Native 4 x 32-bit vector for 16-byte accesses: it loads from any address space and keeps
+// register buffers in registers (HIP's uint4 is a struct with unions, which can defeat the
+// promotion of a local array to registers).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // Order-preserving map from binary32 to uint32 (larger float -> larger integer).
 // -0 is folded onto +0 so that a signed-zero pair compares equal and is decided by index.
 __device__ __forceinline__ uint32_t order_key(float f) {

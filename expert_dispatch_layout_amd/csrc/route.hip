@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kRouteBlock) void route_generic_kernel(RouteArgs a)
         full_max = (double)order_key_inv(seg_max_u32<LPT>(order_key(fm)));
 #pragma unroll
         for (int q = 0; q < NE; ++q)
-            if (chunk_expert(q, W, LPT, lseg) < a.E) full_den += exp((double)x[q] - full_max);
+            if (chunk_expert(q, W, LPT, lseg) < a.E) full_den += exp_neg_f64((double)x[q] - full_max);
         full_den = seg_sum_f64<LPT>(full_den);
     }
     write_weights<LPT, KPL>(a, tok, lseg, live, my_e, my_v, (double)first_x, full_max, full_den);

@@ -100,8 +100,8 @@ __device__ __forceinline__ void load_row(const RouteArgs& a, int64_t tok, int ls
         const int e0 = (j * LPT + lseg) * W;
         if (a.vec && e0 < E) {
             if constexpr (BF16) {
-                const uint4 v = *reinterpret_cast<const uint4*>(
-                    reinterpret_cast<const uint16_t*>(a.logits) + tok * E + e0);
+                const u32x4 v = *reinterpret_cast<const MEP_GLOBAL u32x4*>(
+                    gptr(reinterpret_cast<const uint16_t*>(a.logits)) + tok * E + e0);
                 const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -109,12 +109,12 @@ __device__ __forceinline__ void load_row(const RouteArgs& a, int64_t tok, int ls
                     x[j * W + 2 * q + 1] = __uint_as_float(w4[q] & 0xFFFF0000u);
                 }
             } else {
-                const float4 v = *reinterpret_cast<const float4*>(
-                    reinterpret_cast<const float*>(a.logits) + tok * E + e0);
-                x[j * W + 0] = v.x;
-                x[j * W + 1] = v.y;
-                x[j * W + 2] = v.z;
-                x[j * W + 3] = v.w;
+                const u32x4 v = *reinterpret_cast<const MEP_GLOBAL u32x4*>(
+                    gptr(reinterpret_cast<const float*>(a.logits)) + tok * E + e0);
+                x[j * W + 0] = __uint_as_float(v.x);
+                x[j * W + 1] = __uint_as_float(v.y);
+                x[j * W + 2] = __uint_as_float(v.z);
+                x[j * W + 3] = __uint_as_float(v.w);
             }
         } else {
 #pragma unroll
@@ -124,9 +124,9 @@ __device__ __forceinline__ void load_row(const RouteArgs& a, int64_t tok, int ls
                 if (e < E) {
                     if constexpr (BF16)
                         v = __uint_as_float(
-                            (uint32_t)(reinterpret_cast<const uint16_t*>(a.logits)[tok * E + e]) << 16);
+                            (uint32_t)(gptr(reinterpret_cast<const uint16_t*>(a.logits))[tok * E + e]) << 16);
                     else
-                        v = reinterpret_cast<const float*>(a.logits)[tok * E + e];
+                        v = gptr(reinterpret_cast<const float*>(a.logits))[tok * E + e];
                 }
                 x[j * W + i] = v;
             }
@@ -136,9 +136,9 @@ __device__ __forceinline__ void load_row(const RouteArgs& a, int64_t tok, int ls
 
 __device__ __forceinline__ float load_logit(const RouteArgs& a, int64_t tok, int e, bool bf16) {
     if (bf16)
-        return __uint_as_float((uint32_t)(reinterpret_cast<const uint16_t*>(a.logits)[tok * a.E + e])
+        return __uint_as_float((uint32_t)(gptr(reinterpret_cast<const uint16_t*>(a.logits))[tok * a.E + e])
                                << 16);
-    return reinterpret_cast<const float*>(a.logits)[tok * a.E + e];
+    return gptr(reinterpret_cast<const float*>(a.logits))[tok * a.E + e];
 }
 
 // Exact selection for one token by the LPT lanes of its segment: exact keys (logit, or
@@ -237,7 +237,8 @@ __device__ __forceinline__ void exact_select_token(const RouteArgs& a, const flo
 
 // Weights from the selected experts of a token.  The lane owning output slot j (j % LPT == lseg)
 // holds v_j: the logit (softmax) or the correctly rounded sigmoid (sigmoid).  All arithmetic is
-// binary64, rounded once to binary32 (TensorRT-LLM RoutingKernel.cuh calcSoftmax, over the
+// binary64 (to within a few units of 2^-52), rounded once to binary32 (TensorRT-LLM
+// RoutingKernel.cuh calcSoftmax, over the
 // selected lanes or over the full score vector; sigmoid weights renormalised and scaled).
 // For softmax without renormalisation `full_max`/`full_den` carry the max and the sum of
 // exp(x - max) over all E logits of the token.
@@ -257,9 +258,9 @@ __device__ __forceinline__ void write_weights(const RouteArgs& a, int64_t tok, i
             if (sig)
                 t = (double)my_v[m];
             else if (a.renormalize)
-                t = exp((double)my_v[m] - first_x);
+                t = exp_neg_f64((double)my_v[m] - first_x);
             else
-                t = exp((double)my_v[m] - full_max);
+                t = exp_neg_f64((double)my_v[m] - full_max);
         }
         term[m] = t;
         den += t;
@@ -272,18 +273,20 @@ __device__ __forceinline__ void write_weights(const RouteArgs& a, int64_t tok, i
         den = full_den;
     }
     if (!live) return;
+    // w = term / den to within a few units of 2^-52 (a reciprocal refined twice, then a product)
+    const double inv_den = den > 0.0 ? recip_f64(den) : 0.0;
 #pragma unroll
     for (int m = 0; m < KPL; ++m) {
         const int j = m * LPT + lseg;
         if (j < K) {
-            a.ids[tok * K + j] = my_e[m];
+            gptr(a.ids)[tok * K + j] = my_e[m];
             if (a.weights) {
                 double w;
                 if (sig && !a.renormalize)
                     w = term[m];
                 else
-                    w = den > 0.0 ? term[m] / den : 0.0;
-                a.weights[tok * K + j] = (float)(w * (double)a.scale);
+                    w = den > 0.0 ? term[m] * inv_den : 0.0;
+                gptr(a.weights)[tok * K + j] = (float)(w * (double)a.scale);
             }
         }
     }

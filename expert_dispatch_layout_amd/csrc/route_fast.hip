@@ -1,8 +1,36 @@
 // Shape dispatch of the fast routing kernel (route_fast.h): decides whether a routing call is
 // covered and with which group mapping and list depth.
+#include <mutex>
+
 #include "route_fast.h"
 
 namespace mep {
+
+int resident_blocks(const void* kernel, int block_threads) {
+    struct Entry {
+        int device;
+        const void* kernel;
+        int blocks;
+    };
+    static std::mutex mu;
+    static Entry cache[64];
+    static int used = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (int i = 0; i < used; ++i)
+            if (cache[i].device == dev && cache[i].kernel == kernel) return cache[i].blocks;
+    }
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block_threads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    const int blocks = per_cu * cus;
+    std::lock_guard<std::mutex> lock(mu);
+    if (used < 64) cache[used++] = Entry{dev, kernel, blocks};
+    return blocks;
+}
 
 static int ilog2(int v) {
     int l = 0;

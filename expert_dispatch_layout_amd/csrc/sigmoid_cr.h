@@ -6,9 +6,8 @@
 // which is unique and therefore reproducible on any machine.
 //
 // Method (Ziv's onion-peeling strategy):
-//   fast path  evaluate in binary64 with the device libm exp and an IEEE divide (relative error
-//              well under 2^-50); widen by 2^-44 and accept when both ends round to the same
-//              binary32 value;
+//   fast path  evaluate in binary64 (relative error below 2^-48, see sigmoid_f64); widen by
+//              2^-44 and accept when both ends round to the same binary32 value;
 //   slow path  evaluate in double-double arithmetic (Dekker's two-sum / two-product) to about
 //              2^-90 relative and decide the rounding from the double-double value, again with
 //              an interval check.  The exponential uses exp(t) = exp(t/2^12)^(2^12): an exact
@@ -122,22 +121,79 @@ __device__ __noinline__ float sigmoid_cr_slow(float x) {
     return dd_round_f32(s);
 }
 
+// 2^y in binary64 for |y| <= 1100.  y = n + f with n = rint(y) and |f| <= 1/2 (exact); 2^f =
+// e^(f ln 2) by its Taylor series to degree 13, whose truncation error is below 2^-56 for
+// |f ln 2| <= 0.35, in Horner form (coefficients (ln 2)^k / k! rounded to binary64); then an
+// exact scaling by 2^n.  Relative error below 2^-51.
+__device__ __forceinline__ double exp2_f64(double y) {
+    const double n = __builtin_rint(y);
+    const double f = y - n;
+    double p = 0x1.816193166d0f9p-40;
+    p = __fma_rn(p, f, 0x1.c3bd650fc2986p-36);
+    p = __fma_rn(p, f, 0x1.e8cac7351bb25p-32);
+    p = __fma_rn(p, f, 0x1.e4cf5158b8ecap-28);
+    p = __fma_rn(p, f, 0x1.b5253d395e7c4p-24);
+    p = __fma_rn(p, f, 0x1.62c0223a5c824p-20);
+    p = __fma_rn(p, f, 0x1.ffcbfc588b0c7p-17);
+    p = __fma_rn(p, f, 0x1.430912f86c787p-13);
+    p = __fma_rn(p, f, 0x1.5d87fe78a6731p-10);
+    p = __fma_rn(p, f, 0x1.3b2ab6fba4e77p-7);
+    p = __fma_rn(p, f, 0x1.c6b08d704a0c0p-5);
+    p = __fma_rn(p, f, 0x1.ebfbdff82c58fp-3);
+    p = __fma_rn(p, f, 0x1.62e42fefa39efp-1);
+    p = __fma_rn(p, f, 1.0);
+    return __builtin_amdgcn_ldexp(p, (int)n);
+}
+
+// 1/d for a positive normal binary64 d whose reciprocal is normal: the hardware reciprocal
+// refined by two Newton steps
+// r <- r + r (1 - d r), each of which squares the relative error; result within 2^-52.
+__device__ __forceinline__ double recip_f64(double d) {
+    double r = __builtin_amdgcn_rcp(d);
+    double e = __fma_rn(-d, r, 1.0);
+    r = __fma_rn(r, e, r);
+    e = __fma_rn(-d, r, 1.0);
+    return __fma_rn(r, e, r);
+}
+
+// e^t in binary64 for t <= 0 (softmax terms): 2^(t log2 e), with relative error below
+// (|t| + 4) 2^-53 (the rounding of t log2 e dominates for large |t|); 0 or a subnormal below
+// about e^-734.
+__device__ __forceinline__ double exp_neg_f64(double t) {
+    const double y = fmax(t * 0x1.71547652b82fep+0, -1060.0);
+    return exp2_f64(y);
+}
+
+// sigma(x) = 1 / (1 + 2^y), y = -x log2(e), in binary64 with relative error below 2^-48.
+// y is formed as x * C_hi + x * C_lo with C_hi = -log2(e) rounded to 29 significant bits (so the
+// first product of a binary32 x is exact) and C_lo the binary64 remainder; y is clamped to
+// [-1060, 1000], where sigma is 1 or far below the smallest binary32 subnormal either way.
+__device__ __forceinline__ double sigmoid_f64(float x) {
+    const double xd = (double)x;
+    double y = __fma_rn(xd, 0x1.a8fa03d1105e0p-29, xd * -0x1.7154766p+0);
+    y = fmin(fmax(y, -1060.0), 1000.0);
+    return recip_f64(1.0 + exp2_f64(y));
+}
+
 __device__ __forceinline__ float sigmoid_cr(float x) {
-    double s = 1.0 / (1.0 + exp(-(double)x));
-    double tol = s * 0x1p-44;
+    const double s = sigmoid_f64(x);
+    const double tol = s * 0x1p-44;
     float lo = (float)(s - tol);
     float hi = (float)(s + tol);
     if (lo == hi) return lo;
     return sigmoid_cr_slow(x);
 }
 
+// The fast path alone: `ok` is false when the interval test cannot decide the binary32
+// rounding (about one value in 2^19); the caller then takes the exact path.
+__device__ __forceinline__ float sigmoid_cr_fast(float x, bool& ok) {
+    const double s = sigmoid_f64(x);
+    const double tol = s * 0x1p-44;
+    const float lo = (float)(s - tol);
+    const float hi = (float)(s + tol);
+    ok = lo == hi;
+    return lo;
+}
+
 }  // namespace mep
 
-namespace mep {
-
-// Out-of-line forms for paths that evaluate many independent values on rare occasions: a call
-// keeps the scheduler from interleaving (and holding registers for) all of them at once.
-__device__ __noinline__ float sigmoid_cr_call(float x) { return sigmoid_cr(x); }
-__device__ __noinline__ double exp_f64_call(double x) { return exp(x); }
-
-}  // namespace mep

@@ -49,23 +49,34 @@ __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 // Relaxed device-scope 64-bit status word access for cross-workgroup look-back.  The value is
 // carried inside the word, so no other data needs release/acquire ordering.
 __device__ __forceinline__ void status_store(uint64_t* p, uint64_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gptr(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t status_load(const uint64_t* p) {
-    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(gptr(const_cast<uint64_t*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 constexpr uint32_t kLookbackSpinLimit = 1u << 22;
 
-// Status word: high 32 bits = (epoch << 1) | inclusive_flag, low 32 bits = value.
+// Status word: high 32 bits = tag | inclusive_flag, low 32 bits = value.  The tag has bit 31 set
+// and carries the low 30 bits of the call's epoch, so neither a zero-filled workspace nor the
+// 32-bit counts that other calls with a different geometry store in the same bytes (always below
+// 2^31) can pass for a status word of the current call.
+__device__ __forceinline__ uint32_t status_tag(uint32_t epoch) {
+    return 0x80000000u | ((epoch & 0x3FFFFFFFu) << 1);
+}
 __device__ __forceinline__ uint64_t status_make(uint32_t epoch, bool inclusive, uint32_t value) {
-    return ((uint64_t)((epoch << 1) | (inclusive ? 1u : 0u)) << 32) | (uint64_t)value;
+    return ((uint64_t)(status_tag(epoch) | (inclusive ? 1u : 0u)) << 32) | (uint64_t)value;
 }
 
-// Decoupled look-back for one column: publish this tile's aggregate, walk predecessors until an
-// inclusive prefix is found, then publish this tile's inclusive prefix.  Tiles are numbered in
-// the order their workgroups started (atomic ticket), so every awaited predecessor is resident.
-// Returns the exclusive prefix of the column before this tile.
+// Decoupled look-back for one column (Merrill & Garland, "Single-pass Parallel Prefix Scan with
+// Decoupled Look-back", 2016): publish this tile's aggregate, walk predecessors until an inclusive
+// prefix is found, then publish this tile's inclusive prefix.  The walk reads a window of kLbWin
+// predecessors at once (independent loads in flight), consumes them nearest first, and stops at
+// the first inclusive one; a predecessor that has not published yet is re-read after a short
+// sleep.  Tiles are numbered in the order their workgroups started (atomic ticket), so every
+// awaited predecessor is resident.  Returns the exclusive prefix of the column before this tile.
+constexpr int kLbWin = 32;
+
 __device__ __forceinline__ uint32_t lookback_column(uint64_t* status, int tile, int ncols, int col,
                                                     uint32_t epoch, uint32_t aggregate) {
     uint64_t* mine = status + (size_t)tile * ncols + col;
@@ -74,22 +85,38 @@ __device__ __forceinline__ uint32_t lookback_column(uint64_t* status, int tile, 
         return 0u;
     }
     status_store(mine, status_make(epoch, false, aggregate));
+    const uint32_t want = status_tag(epoch);
     uint32_t excl = 0;
     int p = tile - 1;
     uint32_t spins = 0;
     while (p >= 0) {
-        uint64_t w = status_load(status + (size_t)p * ncols + col);
-        uint32_t hi = (uint32_t)(w >> 32);
-        if ((hi >> 1) != (epoch & 0x7FFFFFFFu)) {
-            // A predecessor always publishes; the bound only guarantees that a misused
-            // workspace (two calls sharing it at once) ends in wrong values, never in a hang.
+        uint64_t w[kLbWin];
+#pragma unroll
+        for (int i = 0; i < kLbWin; ++i)
+            w[i] = (p - i >= 0) ? status_load(status + (size_t)(p - i) * ncols + col)
+                                : status_make(epoch, true, 0u);
+        int consumed = 0;
+        bool done = false, stall = false;
+#pragma unroll
+        for (int i = 0; i < kLbWin; ++i) {
+            const uint32_t hi = (uint32_t)(w[i] >> 32);
+            const bool ready = (hi & ~1u) == want;
+            const bool take = !done && !stall && ready;
+            stall = stall || (!done && !ready);
+            if (take) {
+                excl += (uint32_t)w[i];
+                consumed = i + 1;
+                done = (hi & 1u) != 0u;
+            }
+        }
+        if (done) break;
+        p -= consumed;
+        if (stall) {
+            // A predecessor always publishes; the bound only guarantees that a misused workspace
+            // (two calls sharing it at once) ends in wrong values, never in a hang.
             if (++spins > kLookbackSpinLimit) break;
             __builtin_amdgcn_s_sleep(1);
-            continue;
         }
-        excl += (uint32_t)w;
-        if (hi & 1u) break;
-        --p;
     }
     status_store(mine, status_make(epoch, true, excl + aggregate));
     return excl;
@@ -97,6 +124,16 @@ __device__ __forceinline__ uint32_t lookback_column(uint64_t* status, int tile, 
 
 __device__ __forceinline__ uint32_t status_value(const uint64_t* status, int tile, int ncols, int col) {
     return (uint32_t)(status[(size_t)tile * ncols + col]);
+}
+
+// Value of a tagged word written in this call, re-read until its tag is current (bounded).
+__device__ __forceinline__ uint32_t tagged_value(const uint64_t* p, uint64_t v, uint32_t want) {
+    uint32_t spins = 0;
+    while (((uint32_t)(v >> 32) & ~1u) != want && ++spins < kLookbackSpinLimit) {
+        __builtin_amdgcn_s_sleep(1);
+        v = status_load(p);
+    }
+    return (uint32_t)v;
 }
 
 // Workspace header shared by the layout and plan calls (first 256 bytes of the workspace).
@@ -115,13 +152,17 @@ __device__ __forceinline__ int take_ticket(WsHeader* h, int ntiles) {
     return (int)(t % (uint32_t)ntiles);
 }
 
-// Stable rank of each lane's key among the lanes of this wave that share it:
-// returns the mask of lanes holding the same key (restricted to `active`).
-__device__ __forceinline__ uint64_t match_peers(uint32_t key, int nbits, uint64_t active) {
+// Lanes of this wave (restricted to `active`) holding the same key as the calling lane: one wave
+// ballot per key bit (a wave64 stand-in for a warp match).  NB = key bits, fixed at compile time
+// so the loop unrolls.
+template <int NB>
+__device__ __forceinline__ uint64_t match_peers(uint32_t key, uint64_t active) {
     uint64_t peers = active;
-    for (int b = 0; b < nbits; ++b) {
-        uint64_t ones = __ballot((key >> b) & 1u);
-        peers &= ((key >> b) & 1u) ? ones : ~ones;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const bool bit = (key >> b) & 1u;
+        const uint64_t ones = __ballot(bit);
+        peers &= bit ? ones : ~ones;
     }
     return peers;
 }
@@ -154,6 +195,13 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp, int& tota
     }
     __syncthreads();
     return off + incl - v;
+}
+
+// Sum over the 64 lanes of a wave (every lane gets the result).
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
 }
 
 __host__ __device__ constexpr int bits_for(int n_keys) {

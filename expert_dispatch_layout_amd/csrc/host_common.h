@@ -17,4 +17,6 @@ inline int launch_status() {
 
 inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 }  // namespace mep

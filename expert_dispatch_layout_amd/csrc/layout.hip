@@ -1,19 +1,23 @@
 // mep_build_layout: per-expert histogram, padded exclusive scan and the stable
 // expanded <-> permuted maps of the N*K routed slots.
 //
-// Two kernels over tiles of 2048 consecutive slots:
+// Two kernels.  Scatter tiles are 4096 consecutive slots; a count tile groups enough of them that
+// at most about 32 count tiles exist:
 //
-//   count   LDS-privatised per-tile histogram (one LDS atomic per slot, no global atomics), then
-//           a single-pass decoupled look-back per expert column (Merrill & Garland 2016) that
-//           publishes each tile's inclusive per-expert prefix.  Tiles take an atomic ticket so
-//           every awaited predecessor is already running.
+//   count   LDS-privatised histograms (one LDS atomic per slot, no global atomics), one per
+//           scatter tile, written to the workspace; their sum per expert column goes through a
+//           single-pass decoupled look-back (Merrill & Garland 2016) that publishes each count
+//           tile's inclusive per-expert prefix.  Count tiles take an atomic ticket so every
+//           awaited predecessor is already running, and the look-back reads all of them in one
+//           window, so the chain costs about one round trip between compute dies.
 //   scatter every tile reads the per-expert totals (last tile's inclusive prefix), forms the
 //           padded offsets cu_seqlens (ceil(count/A)*A, 0 for an empty expert: MoonEP
 //           planning.py Phase B2 padded group scan), and ranks its slots stably: within a wave
 //           the slots sharing an expert are found with one ballot per id bit (a wave64 stand-in
 //           for a warp match), counted per (wave, expert) in LDS and prefixed across waves --
 //           the same order MoonEP planning.py run_c1 passA produces, so the permutation is
-//           deterministic and stable in slot order.
+//           deterministic and stable in slot order.  The inverse is staged in LDS in expert
+//           order, so each expert's run of the tile is written as consecutive addresses.
 //
 // The inverse holds the slot index t*K+k; padding rows hold -1 (MoonEP's empty-slot sentinel).
 #include <limits.h>
@@ -23,35 +27,107 @@
 
 namespace mep {
 
-constexpr int kLayBlock = 256;
-constexpr int kLayPerThread = 8;
-constexpr int kLayTile = kLayBlock * kLayPerThread;  // slots per tile
-constexpr int kLayWaves = kLayBlock / kWave;
-constexpr int kLayPerWave = kLayTile / kLayWaves;    // 512
+constexpr int kLayTile = 4096;                       // slots per scatter tile
+constexpr int kScatBlock = 1024;
+constexpr int kScatWaves = kScatBlock / kWave;
+constexpr int kScatPerWave = kLayTile / kScatWaves;  // 256
 constexpr int kMaxExperts = 1024;
+constexpr int kCountBlock = 1024;
+constexpr int kCountTiles = 32;                      // count tiles aimed at (parallelism vs look-back length)
 
-__global__ __launch_bounds__(kLayBlock) void layout_count_kernel(const int32_t* __restrict__ ids,
-                                                                 int NK, int E, uint64_t* status,
-                                                                 WsHeader* hdr) {
+// Geometry: tiles of kLayTile slots (one workgroup each in both kernels); a count tile groups
+// `sub` consecutive tiles so that about kCountTiles count tiles take part in the look-back (one
+// window of predecessors).
+struct LayGeom {
+    int NK, E, nsub, sub, nct;
+    int ticketed;  // tiles in ticket order (when count tiles could outnumber resident groups)
+};
+
+// Only the last arriving workgroup of a count tile ever waits (on earlier count tiles).  With at
+// most this many count tiles, waiting workgroups can never fill the GPU, so every awaited one
+// gets to run and tiles can follow the workgroup index; beyond it they take a ticket.
+constexpr int kUnticketedCountTiles = 128;
+constexpr int kMaxCountTiles = 4096;  // arrival counters kept in the workspace
+
+static LayGeom lay_geom(int64_t NK, int E) {
+    LayGeom g;
+    g.NK = (int)NK;
+    g.E = E;
+    g.nsub = (int)ceil_div64(NK, kLayTile);
+    int sub = (int)ceil_div64(g.nsub, kCountTiles);
+    if (sub < (int)ceil_div64(g.nsub, kMaxCountTiles)) sub = (int)ceil_div64(g.nsub, kMaxCountTiles);
+    if (sub < 1) sub = 1;
+    g.sub = sub;
+    g.nct = (int)ceil_div64(g.nsub, sub);
+    g.ticketed = g.nct > kUnticketedCountTiles;
+    return g;
+}
+
+// Workspace of mep_build_layout after the header: arrival counters of count tiles (fixed place,
+// always left at zero), look-back words [nct][E], and the tagged histogram of every tile
+// [nsub][E].  Tagged words are written with single atomic stores and carry the call's epoch, so
+// a reader on another compute die needs no cache write-back fence: it re-reads until the tag is
+// current.
+struct LayWs {
+    uint32_t* arrive;
+    uint64_t* status;
+    uint64_t* tilehist;
+};
+
+// One tile per workgroup: LDS-privatised histogram (one LDS atomic per slot), written to the
+// workspace; the last tile of a count tile to arrive sums the count tile's histograms and takes
+// it through the look-back.
+__global__ __launch_bounds__(kCountBlock) void layout_count_kernel(const int32_t* __restrict__ ids,
+                                                                   LayGeom g, LayWs w, WsHeader* hdr) {
     __shared__ int hist[kMaxExperts];
     __shared__ int s_tile;
-    for (int e = threadIdx.x; e < E; e += kLayBlock) hist[e] = 0;
-    if (threadIdx.x == 0) s_tile = take_ticket(hdr, (int)gridDim.x);
+    __shared__ uint32_t s_arrived;
+    const int tid = threadIdx.x;
+    const int E = g.E;
+    for (int i = tid; i < E; i += kCountBlock) hist[i] = 0;
+    if (tid == 0) s_tile = g.ticketed ? take_ticket(hdr, (int)gridDim.x) : (int)blockIdx.x;
     __syncthreads();
     const int tile = s_tile;
-    const uint32_t epoch = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    const uint32_t epoch = __hip_atomic_load(&gptr(hdr)->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
     const int base = tile * kLayTile;
+    const MEP_GLOBAL int32_t* gids = gptr(ids);
+    constexpr int kPer = kLayTile / kCountBlock;
+    int v[kPer];
 #pragma unroll
-    for (int it = 0; it < kLayPerThread; ++it) {
-        const int i = base + it * kLayBlock + threadIdx.x;
-        if (i < NK) {
-            const int id = ids[i];
-            if ((unsigned)id < (unsigned)E) atomicAdd(&hist[id], 1);  // out-of-range ids are skipped
-        }
+    for (int j = 0; j < kPer; ++j) {
+        const int i = base + j * kCountBlock + tid;
+        v[j] = i < g.NK ? gids[i] : -1;
     }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+        if ((unsigned)v[j] < (unsigned)E) atomicAdd(&hist[v[j]], 1);  // out-of-range ids are skipped
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += kLayBlock)
-        lookback_column(status, tile, E, e, epoch, (uint32_t)hist[e]);
+    const uint32_t want = status_tag(epoch);
+    for (int e = tid; e < E; e += kCountBlock)
+        status_store(w.tilehist + (size_t)tile * E + e, status_make(epoch, false, (uint32_t)hist[e]));
+    // ---- arrival at the count tile; the last arriver continues ------------------------------
+    const int ct = tile / g.sub;
+    const int t0 = ct * g.sub;
+    const int nsub_here = min(g.sub, g.nsub - t0);
+    __syncthreads();
+    if (tid == 0)
+        s_arrived = __hip_atomic_fetch_add(gptr(w.arrive) + ct, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_arrived != (uint32_t)(nsub_here - 1)) return;
+    if (tid == 0) __hip_atomic_store(gptr(w.arrive) + ct, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int e = tid; e < E; e += kCountBlock) {
+        uint32_t agg = 0;
+        for (int b0 = 0; b0 < nsub_here; b0 += 8) {
+            uint64_t x[8];
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+                x[b] = b0 + b < nsub_here ? status_load(w.tilehist + (size_t)(t0 + b0 + b) * E + e) : 0;
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+                if (b0 + b < nsub_here) agg += tagged_value(w.tilehist + (size_t)(t0 + b0 + b) * E + e, x[b], want);
+        }
+        lookback_column(w.status, ct, E, e, epoch, agg);
+    }
 }
 
 struct LayoutOut {
@@ -63,63 +139,94 @@ struct LayoutOut {
     int p2e_cap;
 };
 
-__global__ __launch_bounds__(kLayBlock) void layout_scatter_kernel(const int32_t* __restrict__ ids,
-                                                                   int NK, int E, int A, int ntiles,
-                                                                   const uint64_t* status,
-                                                                   WsHeader* hdr, LayoutOut out) {
+template <int NB>
+__global__ __launch_bounds__(kScatBlock) void layout_scatter_kernel(const int32_t* __restrict__ ids,
+                                                                    LayGeom g, int A, LayWs lw,
+                                                                    WsHeader* hdr, LayoutOut out) {
+    constexpr int EPT = kMaxExperts / kScatBlock;  // experts per thread in the per-expert passes
     __shared__ int s_cu[kMaxExperts + 1];
     __shared__ int s_tot[kMaxExperts];
-    __shared__ int s_base[kMaxExperts];
-    __shared__ int s_cnt[kLayWaves][kMaxExperts];
-    __shared__ int s_tmp[kLayWaves];
+    __shared__ int s_base[kMaxExperts];   // cu[e] + slots of e in earlier tiles
+    __shared__ int s_loc[kMaxExperts];    // start of e in this tile's expert-ordered staging
+    __shared__ int s_cnt[kScatWaves][kMaxExperts];
+    __shared__ int s_tmp[kScatWaves];
+    __shared__ int s_slot[kLayTile];      // staging of the inverse in expert order
+    __shared__ int s_pos[kLayTile];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
     const int tile = blockIdx.x;
+    const int NK = g.NK, E = g.E, ntiles = g.nsub;
+    const MEP_GLOBAL int32_t* gids = gptr(ids);
+    MEP_GLOBAL int32_t* g_e2p = gptr(out.e2p);
+    MEP_GLOBAL int32_t* g_p2e = gptr(out.p2e);
+    const int wbase = tile * kLayTile + w * kScatPerWave;
+    int idv[kScatPerWave / kWave];  // this lane's ids, loaded first so the loads overlap the scan
+#pragma unroll
+    for (int it = 0; it < kScatPerWave / kWave; ++it) {
+        const int i = wbase + it * kWave + lane;
+        idv[it] = (tile < ntiles && i < NK) ? gids[i] : 0;
+    }
 
-    // ---- padded offsets from the per-expert totals (4 experts per thread) ----------------
-    int pad[4];
+    // ---- per-expert totals and the slots of each expert before this tile, all loads issued
+    // together: totals from the last count tile's inclusive prefix, earlier count tiles from the
+    // look-back, earlier scatter tiles of this count tile from their histograms
+    const int ct = tile / g.sub;
+    const int s0 = ct * g.sub;
+    const uint64_t* status = lw.status;
+    int tot[EPT], pre[EPT];
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+        const int e = tid * EPT + q;
+        tot[q] = (e < E && ntiles > 0) ? (int)status_value(status, g.nct - 1, E, e) : 0;
+        pre[q] = (e < E && tile < ntiles && ct > 0) ? (int)status_value(status, ct - 1, E, e) : 0;
+    }
+    for (int s2 = s0; s2 < tile && tile < ntiles; ++s2) {  // the earlier tiles of this count tile
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) {
+            const int e = tid * EPT + q;
+            if (e < E) pre[q] += (int)status_value(lw.tilehist, s2, E, e);
+        }
+    }
+    int pad[EPT];
     int mysum = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int e = tid * 4 + q;
-        int tot = 0;
-        if (e < E && ntiles > 0) tot = (int)status_value(status, ntiles - 1, E, e);
-        if (e < E) s_tot[e] = tot;
-        pad[q] = tot > 0 ? ((tot + A - 1) / A) * A : 0;
+    for (int q = 0; q < EPT; ++q) {
+        const int e = tid * EPT + q;
+        if (e < E) s_tot[e] = tot[q];
+        pad[q] = tot[q] > 0 ? ((tot[q] + A - 1) / A) * A : 0;
         mysum += pad[q];
     }
     int total;
-    int run = block_exclusive_scan<kLayBlock>(mysum, s_tmp, total);
+    int run = block_exclusive_scan<kScatBlock>(mysum, s_tmp, total);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int e = tid * 4 + q;
-        if (e < E) s_cu[e] = run;
+    for (int q = 0; q < EPT; ++q) {
+        const int e = tid * EPT + q;
+        if (e < E) {
+            s_cu[e] = run;
+            s_base[e] = run + pre[q];
+        }
         run += pad[q];
     }
     if (tid == 0) s_cu[E] = total;
-    for (int e = tid; e < E; e += kLayBlock)
+    for (int e = tid; e < E; e += kScatBlock)
 #pragma unroll
-        for (int ww = 0; ww < kLayWaves; ++ww) s_cnt[ww][e] = 0;
+        for (int ww = 0; ww < kScatWaves; ++ww) s_cnt[ww][e] = 0;
     __syncthreads();
-    for (int e = tid; e < E; e += kLayBlock)
-        s_base[e] = s_cu[e] + ((tile > 0 && tile < ntiles) ? (int)status_value(status, tile - 1, E, e) : 0);
 
     // ---- stable in-tile ranks: wave match + per-(wave, expert) counters -----------------
-    const int nbits = bits_for(E);
-    const int wbase = tile * kLayTile + w * kLayPerWave;
-    int key[kLayPerWave / kWave];
-    int rank[kLayPerWave / kWave];
+    int key[kScatPerWave / kWave];
+    int rank[kScatPerWave / kWave];
     if (tile < ntiles) {
 #pragma unroll
-        for (int it = 0; it < kLayPerWave / kWave; ++it) {
+        for (int it = 0; it < kScatPerWave / kWave; ++it) {
             const int i = wbase + it * kWave + lane;
-            int k = i < NK ? ids[i] : 0;
+            int k = idv[it];
             const bool valid = i < NK && (unsigned)k < (unsigned)E;
             if (!valid) k = 0;
             const uint64_t active = __ballot(valid);
-            const uint64_t peers = match_peers((uint32_t)k, nbits, active);
+            const uint64_t peers = match_peers<NB>((uint32_t)k, active);
             key[it] = valid ? k : -1;
             rank[it] = 0;
             if (valid) {
@@ -131,26 +238,53 @@ __global__ __launch_bounds__(kLayBlock) void layout_scatter_kernel(const int32_t
         }
     }
     __syncthreads();
-    for (int e = tid; e < E; e += kLayBlock) {
-        int r = 0;
+    // per expert: exclusive prefix over waves, and the tile's expert-ordered staging offsets
+    int my_tile_cnt[EPT];
+    int cnt_sum = 0;
 #pragma unroll
-        for (int ww = 0; ww < kLayWaves; ++ww) {
-            const int c = s_cnt[ww][e];
-            s_cnt[ww][e] = r;
-            r += c;
+    for (int q = 0; q < EPT; ++q) {
+        const int e = tid * EPT + q;
+        int r = 0;
+        if (e < E) {
+#pragma unroll
+            for (int ww = 0; ww < kScatWaves; ++ww) {
+                const int c = s_cnt[ww][e];
+                s_cnt[ww][e] = r;
+                r += c;
+            }
         }
+        my_tile_cnt[q] = r;
+        cnt_sum += r;
+    }
+    int tile_slots;
+    int loc = block_exclusive_scan<kScatBlock>(cnt_sum, s_tmp, tile_slots);
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+        const int e = tid * EPT + q;
+        if (e < E) s_loc[e] = loc;
+        loc += my_tile_cnt[q];
     }
     __syncthreads();
     if (tile < ntiles) {
 #pragma unroll
-        for (int it = 0; it < kLayPerWave / kWave; ++it) {
+        for (int it = 0; it < kScatPerWave / kWave; ++it) {
             const int i = wbase + it * kWave + lane;
             const int k = key[it];
             if (k >= 0) {
-                const int P = s_base[k] + s_cnt[w][k] + rank[it];
-                out.e2p[i] = P;
-                if (out.p2e && P < out.p2e_cap) out.p2e[P] = i;
+                const int within = s_cnt[w][k] + rank[it];
+                const int P = s_base[k] + within;
+                g_e2p[i] = P;
+                const int j = s_loc[k] + within;
+                s_slot[j] = i;
+                s_pos[j] = P;
             }
+        }
+    }
+    __syncthreads();
+    if (out.p2e && tile < ntiles) {
+        for (int j = tid; j < tile_slots; j += kScatBlock) {
+            const int P = s_pos[j];
+            if (P < out.p2e_cap) g_p2e[P] = s_slot[j];
         }
     }
 
@@ -159,38 +293,53 @@ __global__ __launch_bounds__(kLayBlock) void layout_scatter_kernel(const int32_t
         for (int e = blockIdx.x; e < E; e += gridDim.x) {
             const int start = s_cu[e] + s_tot[e];
             const int end = min(s_cu[e + 1], out.p2e_cap);
-            for (int p = start + tid; p < end; p += kLayBlock) out.p2e[p] = -1;
+            for (int p = start + tid; p < end; p += kScatBlock) g_p2e[p] = -1;
         }
     }
 
     // ---- per-expert outputs and workspace reset ------------------------------------------
     if (blockIdx.x == 0) {
-        for (int e = tid; e <= E; e += kLayBlock) out.cu_seqlens[e] = s_cu[e];
-        for (int e = tid; e < E; e += kLayBlock) {
+        MEP_GLOBAL int32_t* g_cu = gptr(out.cu_seqlens);
+        for (int e = tid; e <= E; e += kScatBlock) g_cu[e] = s_cu[e];
+        for (int e = tid; e < E; e += kScatBlock) {
             const int cnt = s_tot[e];
-            if (out.tokens_per_expert) out.tokens_per_expert[e] = cnt;
+            if (out.tokens_per_expert) gptr(out.tokens_per_expert)[e] = cnt;
             if (out.zero_fill) {
                 const int padded = s_cu[e + 1] - s_cu[e];
                 const bool z = cnt > 0 && padded > cnt;
-                out.zero_fill[2 * e] = z ? s_cu[e] + cnt : 0;
-                out.zero_fill[2 * e + 1] = z ? padded - cnt : 0;
+                gptr(out.zero_fill)[2 * e] = z ? s_cu[e] + cnt : 0;
+                gptr(out.zero_fill)[2 * e + 1] = z ? padded - cnt : 0;
             }
         }
         if (tid == 0) {
-            hdr->epoch = hdr->epoch + 1u;
-            hdr->ticket = 0u;
+            MEP_GLOBAL WsHeader* h = gptr(hdr);
+            h->epoch = h->epoch + 1u;
+            h->ticket = 0u;
         }
     }
 }
 
-static int64_t layout_tiles(int64_t NK) { return ceil_div64(NK, kLayTile); }
+}  // namespace mep
 
+namespace mep {
+// Workspace of mep_build_layout: header, arrival counters, look-back words, tile histograms.
+struct LayWsLayout {
+    size_t arrive, status, tilehist, bytes;
+};
+static LayWsLayout lay_ws_layout(const LayGeom& g) {
+    LayWsLayout l;
+    l.arrive = sizeof(WsHeader);
+    l.status = l.arrive + align256((size_t)kMaxCountTiles * sizeof(uint32_t));
+    l.tilehist = l.status + align256((size_t)g.nct * (size_t)g.E * sizeof(uint64_t));
+    l.bytes = l.tilehist + align256((size_t)g.nsub * (size_t)g.E * sizeof(uint64_t));
+    return l;
+}
 }  // namespace mep
 
 extern "C" size_t mep_layout_workspace_size(int64_t N, int E, int K) {
     using namespace mep;
-    if (N < 0 || E < 1 || K < 1) return sizeof(WsHeader);
-    return sizeof(WsHeader) + (size_t)layout_tiles(N * (int64_t)K) * (size_t)E * sizeof(uint64_t);
+    if (N < 0 || E < 1 || K < 1 || E > kMaxExperts) return sizeof(WsHeader);
+    return lay_ws_layout(lay_geom(N * (int64_t)K, E)).bytes;
 }
 
 extern "C" int mep_build_layout(const int32_t* topk_ids, int64_t N, int E, int K, int alignment,
@@ -215,15 +364,24 @@ extern "C" int mep_build_layout(const int32_t* topk_ids, int64_t N, int E, int K
     if (ws_bytes < mep_layout_workspace_size(N, E, K)) return MEP_ERR_CAPACITY;
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const LayGeom g = lay_geom(NK, E);
     WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
-    uint64_t* status = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + sizeof(WsHeader));
-    const int ntiles = (int)layout_tiles(NK);
-    if (ntiles > 0)
-        hipLaunchKernelGGL(layout_count_kernel, dim3(ntiles), dim3(kLayBlock), 0, st, topk_ids,
-                           (int)NK, E, status, hdr);
+    const LayWsLayout wl = lay_ws_layout(g);
+    char* wb = reinterpret_cast<char*>(ws);
+    const LayWs lw{reinterpret_cast<uint32_t*>(wb + wl.arrive), reinterpret_cast<uint64_t*>(wb + wl.status),
+                   reinterpret_cast<uint64_t*>(wb + wl.tilehist)};
+    if (g.nsub > 0)
+        hipLaunchKernelGGL(layout_count_kernel, dim3(g.nsub), dim3(kCountBlock), 0, st, topk_ids, g, lw, hdr);
     LayoutOut out{tokens_per_expert, cu_seqlens, expanded_to_permuted, permuted_to_expanded, zero_fill,
                   permuted_to_expanded ? (int)(permuted_cap < INT32_MAX ? permuted_cap : INT32_MAX) : 0};
-    hipLaunchKernelGGL(layout_scatter_kernel, dim3(ntiles > 0 ? ntiles : 1), dim3(kLayBlock), 0, st,
-                       topk_ids, (int)NK, E, alignment, ntiles, status, hdr, out);
+    const dim3 sgrid(g.nsub > 0 ? g.nsub : 1), sblock(kScatBlock);
+    if (E <= 16)
+        hipLaunchKernelGGL(layout_scatter_kernel<4>, sgrid, sblock, 0, st, topk_ids, g, alignment, lw, hdr, out);
+    else if (E <= 64)
+        hipLaunchKernelGGL(layout_scatter_kernel<6>, sgrid, sblock, 0, st, topk_ids, g, alignment, lw, hdr, out);
+    else if (E <= 256)
+        hipLaunchKernelGGL(layout_scatter_kernel<8>, sgrid, sblock, 0, st, topk_ids, g, alignment, lw, hdr, out);
+    else
+        hipLaunchKernelGGL(layout_scatter_kernel<10>, sgrid, sblock, 0, st, topk_ids, g, alignment, lw, hdr, out);
     return launch_status();
 }

@@ -1,6 +1,6 @@
 // mep_plan: expert-parallel dispatch plan over R virtual ranks, computed on one GPU's batch.
 //
-// Tokens are cut into tiles that never cross a source shard (TT tokens, TT*K <= 2048 slots).
+// Tokens are cut into tiles that never cross a source shard (TT tokens, TT*K <= 4096 slots).
 // Per token, with owner(e) = e / epn:
 //   c0[r]  1 if the token sends anything to r       (is_token_in_rank; DeepEP intranode.cu
 //                                                     notify_dispatch counts and prefixes these)
@@ -9,9 +9,14 @@
 //                                                     canonicalisation encodes them as -dst-1)
 //   cE[e]  1 if the token is routed to e            (per-shard expert counts)
 //
-//   count kernel  LDS histogram of the 3R+E columns per tile + decoupled look-back across tiles
-//                 (exclusive/inclusive prefix of every column at every tile boundary); also
-//                 writes is_token_in_rank.
+//   count kernel  per count tile (a few consecutive write tiles of one shard): LDS histograms of
+//                 the 3R+E columns per write tile; the 3R rank columns go to the workspace and,
+//                 summed, through a decoupled look-back across count tiles (about 32 of them,
+//                 read in one window), so the prefix of a rank column at any write-tile boundary
+//                 is a look-back value plus a few histograms; the E expert columns are needed
+//                 per shard only, so each count tile publishes one tagged aggregate and the last
+//                 count tile to start (every other one is then running) reduces them into the
+//                 per-shard expert counts and the expert totals.  Also writes is_token_in_rank.
 //   write kernel  dst with the duplicate encoding; dedup groups and duplicate offsets in a stable
 //                 (rank, token, k) order -- each slot is ranked among same-rank slots of its
 //                 wave by ballot-matching and per-(wave, rank) LDS counters, then offset by the
@@ -25,12 +30,19 @@
 
 namespace mep {
 
-constexpr int kPlanBlock = 256;
+constexpr int kPlanBlock = 512;
 constexpr int kPlanWaves = kPlanBlock / kWave;
-constexpr int kPlanSlots = 2048;  // slots per tile
+constexpr int kPlanSlots = 4096;  // slots per tile
 constexpr int kMaxRanks = 128;
 constexpr int kMaxE = 1024;
 constexpr int kMaxCols = 3 * kMaxRanks + kMaxE;
+
+constexpr int kMaxSources = 1024;   // virtual source shards (keeps count tiles <= kMaxCountTiles)
+// Only the last arriving workgroup of a count tile ever waits (on earlier count tiles).  With at
+// most this many count tiles, waiting workgroups can never fill the GPU, so every awaited one
+// gets to run and write tiles can follow the workgroup index; beyond it they take a ticket.
+constexpr int kUnticketedCountTiles = 128;
+constexpr int kCountTilesP = 32;    // count tiles aimed at (parallelism vs look-back length)
 
 static int plan_tile_tokens(int K) {
     int kp = 1;
@@ -39,10 +51,24 @@ static int plan_tile_tokens(int K) {
     return tt > kPlanBlock ? kPlanBlock : tt;
 }
 
+// Write tiles: TT tokens, never crossing a shard (tps per shard, ntiles in all).  Count tiles:
+// `sub` consecutive write tiles of one shard (ctps per shard, nct in all).
 struct PlanGeom {
     int N, E, K, R, epn, S, n, tps, ntiles, TT, ncols, C;
+    int sub, ctps, nct;
+    int ticketed;  // write tiles in ticket order (when count tiles could outnumber resident groups)
     int64_t NvS;
 };
+
+// count tile of write tile wt, and the first write tile of that count tile
+__device__ __forceinline__ int ct_of(const PlanGeom& g, int wt) {
+    const int sh = wt / g.tps;
+    return sh * g.ctps + (wt - sh * g.tps) / g.sub;
+}
+__device__ __forceinline__ int ct_first_wt(const PlanGeom& g, int ct) {
+    const int sh = ct / g.ctps;
+    return sh * g.tps + (ct - sh * g.ctps) * g.sub;
+}
 
 // Per-token view: owner ranks, hit counts and first-occurrence flags of its K slots.
 template <int KMAX>
@@ -55,12 +81,12 @@ struct TokenSlots {
 };
 
 template <int KMAX>
-__device__ __forceinline__ void token_slots(TokenSlots<KMAX>& ts, const int32_t* ids, int64_t t,
-                                            int K, int E, const int* s_owner) {
+__device__ __forceinline__ void token_slots(TokenSlots<KMAX>& ts, const int (&idk)[KMAX], int K, int E,
+                                            int R, const int* s_owner) {
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
         if (k < K) {
-            const int id = ids[t * K + k];
+            const int id = idk[k];
             ts.ok[k] = (unsigned)id < (unsigned)E;
             ts.id[k] = ts.ok[k] ? id : 0;
             ts.r[k] = ts.ok[k] ? s_owner[ts.id[k]] : -1;
@@ -70,76 +96,194 @@ __device__ __forceinline__ void token_slots(TokenSlots<KMAX>& ts, const int32_t*
             ts.r[k] = -1;
         }
     }
+    if (KMAX <= 8 && R <= 16) {
+        // slots per rank as 4-bit counters packed in one word; first slot per rank from a mask
+        uint64_t packed = 0;
+        uint32_t seen = 0;
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        int h = 0;
-        bool first = true;
-#pragma unroll
-        for (int k2 = 0; k2 < KMAX; ++k2) {
-            const bool same = ts.ok[k] && ts.ok[k2] && ts.r[k2] == ts.r[k];
-            h += same;
-            if (k2 < k && same) first = false;
+        for (int k = 0; k < KMAX; ++k) {
+            const int r = ts.ok[k] ? ts.r[k] : 0;
+            ts.first[k] = ts.ok[k] && !((seen >> r) & 1u);
+            if (ts.ok[k]) {
+                packed += 1ull << (4 * r);
+                seen |= 1u << r;
+            }
         }
-        ts.h[k] = h;
-        ts.first[k] = first;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            ts.h[k] = ts.ok[k] ? (int)((packed >> (4 * ts.r[k])) & 15u) : 0;
+    } else {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            int h = 0;
+            bool first = true;
+#pragma unroll
+            for (int k2 = 0; k2 < KMAX; ++k2) {
+                const bool same = ts.ok[k] && ts.ok[k2] && ts.r[k2] == ts.r[k];
+                h += same;
+                if (k2 < k && same) first = false;
+            }
+            ts.h[k] = h;
+            ts.first[k] = first;
+        }
     }
 }
 
 template <int KMAX>
+__device__ __forceinline__ void load_token_ids(int (&idk)[KMAX], const int32_t* ids, int64_t t, int K,
+                                               bool live) {
+    const MEP_GLOBAL int32_t* gids = gptr(ids);
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) idk[k] = (live && k < K) ? gids[t * K + k] : -1;
+}
+
+// Rank sets of a token as bit masks: RW 32-bit words (1 word when R <= 32, else 4).
+template <int RW>
+struct RankMask {
+    uint32_t w[RW];
+    __device__ __forceinline__ void clear() {
+#pragma unroll
+        for (int q = 0; q < RW; ++q) w[q] = 0u;
+    }
+    __device__ __forceinline__ bool test(int r) const {
+        if constexpr (RW == 1) return (w[0] >> r) & 1u;
+        uint32_t v = 0;
+#pragma unroll
+        for (int q = 0; q < RW; ++q) v |= ((r >> 5) == q) ? w[q] : 0u;
+        return (v >> (r & 31)) & 1u;
+    }
+    __device__ __forceinline__ void set(int r) {
+        if constexpr (RW == 1) {
+            w[0] |= 1u << r;
+        } else {
+#pragma unroll
+            for (int q = 0; q < RW; ++q) w[q] |= ((r >> 5) == q) ? (1u << (r & 31)) : 0u;
+        }
+    }
+};
+
+// Workspace of mep_plan after the header: arrival counters of count tiles (fixed place, always
+// left at zero), look-back words of the rank columns [nct][3R], tagged expert aggregates
+// [nct][E], and the tagged histograms of every write tile [ntiles][3R+E].
+// Tagged words are written with single atomic stores and carry the call's epoch, so a reader on
+// another compute die needs no cache write-back fence: it re-reads until the tag is current.
+struct PlanWs {
+    uint32_t* arrive;
+    uint64_t* status3;
+    uint64_t* statusE;
+    uint64_t* tilehist;
+};
+
+constexpr int kMaxCountTiles = 2048;
+
+// One write tile per workgroup.  Each writes its histograms; the last of the write tiles of a
+// count tile to arrive sums them, publishes the count tile's expert aggregates and takes its rank
+// columns through the look-back.
+template <int KMAX, int RW>
 __global__ __launch_bounds__(kPlanBlock) void plan_count_kernel(const int32_t* __restrict__ ids,
-                                                                PlanGeom g, uint64_t* status,
-                                                                WsHeader* hdr, uint8_t* itr) {
+                                                                PlanGeom g, PlanWs w, WsHeader* hdr,
+                                                                uint8_t* itr) {
     __shared__ int s_cnt[kMaxCols];
     __shared__ int s_owner[kMaxE];
     __shared__ int s_tile;
+    __shared__ uint32_t s_arrived;
     const int tid = threadIdx.x;
-    for (int c = tid; c < g.ncols; c += kPlanBlock) s_cnt[c] = 0;
-    for (int e = tid; e < g.E; e += kPlanBlock) s_owner[e] = e / g.epn;
-    if (tid == 0) s_tile = take_ticket(hdr, (int)gridDim.x);
-    __syncthreads();
-    const int tile = s_tile;
-    const uint32_t epoch = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-    const int sh = tile / g.tps;
-    const int ct = tile - sh * g.tps;
-    const int64_t t0 = (int64_t)sh * g.n + (int64_t)ct * g.TT;
-    const int64_t t1 = min(t0 + g.TT, (int64_t)(sh + 1) * g.n);
-    const int64_t t = t0 + tid;
+    const int lane = tid & 63;
+    const int nc = g.ncols;
     const int R = g.R;
-    if (tid < g.TT && t < t1) {
-        TokenSlots<KMAX> ts;
-        token_slots<KMAX>(ts, ids, t, g.K, g.E, s_owner);
-        uint32_t m[kMaxRanks / 32] = {0u, 0u, 0u, 0u};
+    const int E = g.E;
+    const int K = g.K;
+    const int n3 = 3 * R;
+    for (int c = tid; c < nc; c += kPlanBlock) s_cnt[c] = 0;
+    for (int e = tid; e < E; e += kPlanBlock) s_owner[e] = e / g.epn;
+    if (tid == 0) s_tile = g.ticketed ? take_ticket(hdr, (int)gridDim.x) : (int)blockIdx.x;
+    __syncthreads();
+    const int wt = s_tile;
+    const uint32_t epoch = __hip_atomic_load(&gptr(hdr)->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    const int sh = wt / g.tps;
+    const int64_t t = (int64_t)sh * g.n + (int64_t)(wt - sh * g.tps) * g.TT + tid;
+    const bool live = tid < g.TT && t < (int64_t)(sh + 1) * g.n;
+    int idk[KMAX];
+    load_token_ids<KMAX>(idk, ids, t, K, live);
+    {
+        RankMask<RW> seen, multi;  // ranks reached; ranks reached by >= 2 slots
+        seen.clear();
+        multi.clear();
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
-            if (!ts.ok[k]) continue;
-            const int r = ts.r[k];
-            atomicAdd(&s_cnt[3 * R + ts.id[k]], 1);
-            if (ts.first[k]) {
-                atomicAdd(&s_cnt[r], 1);
-                if (ts.h[k] >= 2) atomicAdd(&s_cnt[R + r], 1);
-#pragma unroll
-                for (int q = 0; q < kMaxRanks / 32; ++q) m[q] |= ((r >> 5) == q) ? (1u << (r & 31)) : 0u;
-            } else {
-                atomicAdd(&s_cnt[2 * R + r], 1);
+            const int id = idk[k];
+            if (k < K && (unsigned)id < (unsigned)E) {  // false for a lane without a token
+                atomicAdd(&s_cnt[n3 + id], 1);
+                const int r = s_owner[id];
+                if (seen.test(r)) multi.set(r);
+                seen.set(r);
             }
         }
-        if (itr) {
-            uint8_t* row = itr + t * R;
+        if (live && itr) {
+            MEP_GLOBAL uint8_t* row = gptr(itr) + t * R;
             if ((R & 3) == 0) {
-                for (int b = 0; b < R; b += 4) {
-                    const uint32_t bits = m[b >> 5] >> (b & 31);
-                    const uint32_t word = (bits & 1u) | (((bits >> 1) & 1u) << 8) |
-                                          (((bits >> 2) & 1u) << 16) | (((bits >> 3) & 1u) << 24);
-                    *reinterpret_cast<uint32_t*>(row + b) = word;
+                for (int bb = 0; bb < R; bb += 4) {
+                    const uint32_t word = (seen.test(bb) ? 1u : 0u) | (seen.test(bb + 1) ? 1u << 8 : 0u) |
+                                          (seen.test(bb + 2) ? 1u << 16 : 0u) | (seen.test(bb + 3) ? 1u << 24 : 0u);
+                    *reinterpret_cast<MEP_GLOBAL uint32_t*>(row + bb) = word;
                 }
             } else {
-                for (int b = 0; b < R; ++b) row[b] = (uint8_t)((m[b >> 5] >> (b & 31)) & 1u);
+                for (int bb = 0; bb < R; ++bb) row[bb] = seen.test(bb) ? 1 : 0;
+            }
+        }
+        // tokens per rank (c0) and tokens with >= 2 slots per rank (c1): wave ballots; lane r
+        // collects rank r's counts (one pass per 64 ranks), then one LDS add per lane
+        for (int r0 = 0; r0 < R; r0 += 64) {
+            int n0 = 0, n1 = 0;
+            const int rmax = min(64, R - r0);
+            for (int j = 0; j < rmax; ++j) {
+                const int c0 = popc64(__ballot(seen.test(r0 + j)));
+                const int c1 = popc64(__ballot(multi.test(r0 + j)));
+                n0 = lane == j ? c0 : n0;
+                n1 = lane == j ? c1 : n1;
+            }
+            if (lane < rmax) {
+                if (n0) atomicAdd(&s_cnt[r0 + lane], n0);
+                if (n1) atomicAdd(&s_cnt[R + r0 + lane], n1);
             }
         }
     }
     __syncthreads();
-    for (int c = tid; c < g.ncols; c += kPlanBlock)
-        lookback_column(status, tile, g.ncols, c, epoch, (uint32_t)s_cnt[c]);
+    // duplicates per rank (c2) = slots on the rank (its experts' counts) - tokens on the rank
+    for (int e = tid; e < E; e += kPlanBlock) {
+        const int c = s_cnt[n3 + e];
+        if (c) atomicAdd(&s_cnt[2 * R + s_owner[e]], c);
+    }
+    __syncthreads();
+    for (int r = tid; r < R; r += kPlanBlock) s_cnt[2 * R + r] -= s_cnt[r];
+    __syncthreads();
+    const uint32_t want = status_tag(epoch);
+    for (int c = tid; c < nc; c += kPlanBlock)
+        status_store(w.tilehist + (size_t)wt * nc + c, status_make(epoch, false, (uint32_t)s_cnt[c]));
+    // ---- arrival at the count tile; the last arriver continues ------------------------------
+    const int ct = ct_of(g, wt);
+    const int wt0 = ct_first_wt(g, ct);
+    const int nsub_here = min(g.sub, (ct / g.ctps + 1) * g.tps - wt0);
+    __syncthreads();
+    if (tid == 0)
+        s_arrived = __hip_atomic_fetch_add(gptr(w.arrive) + ct, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_arrived != (uint32_t)(nsub_here - 1)) return;
+    if (tid == 0) __hip_atomic_store(gptr(w.arrive) + ct, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int c = tid; c < nc; c += kPlanBlock) {
+        uint32_t agg = 0;
+        for (int b0 = 0; b0 < nsub_here; b0 += 8) {
+            uint64_t v[8];
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+                v[b] = b0 + b < nsub_here ? status_load(w.tilehist + (size_t)(wt0 + b0 + b) * nc + c) : 0;
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+                if (b0 + b < nsub_here) agg += tagged_value(w.tilehist + (size_t)(wt0 + b0 + b) * nc + c, v[b], want);
+        }
+        if (c < n3) lookback_column(w.status3, ct, n3, c, epoch, agg);
+        else status_store(w.statusE + (size_t)ct * E + (c - n3), status_make(epoch, false, agg));
+    }
 }
 
 struct PlanOutDev {
@@ -162,11 +306,10 @@ struct PlanOutDev {
 
 enum : uint32_t { kNone = 0, kHead = 1, kDup = 2 };
 
-template <int KMAX>
+template <int KMAX, int NB>
 __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ cu_seqlens,
-    const int32_t* __restrict__ e2p, PlanGeom g, const uint64_t* status, WsHeader* hdr,
-    PlanOutDev o) {
+    const int32_t* __restrict__ e2p, PlanGeom g, PlanWs pw, WsHeader* hdr, PlanOutDev o) {
     __shared__ int s_owner[kMaxE];
     __shared__ int s_cu_r[kMaxRanks + 1];
     __shared__ int s_excl[3 * kMaxRanks];
@@ -188,21 +331,40 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
     const int ct = tile >= 0 ? tile - sh * g.tps : 0;
     const int64_t t0 = (int64_t)sh * g.n + (int64_t)ct * g.TT;
     const int64_t t1 = tile >= 0 ? min(t0 + g.TT, (int64_t)(sh + 1) * g.n) : t0;
-    const int first_tile_of_shard = sh * g.tps;
+    const int ctile = tile >= 0 ? ct_of(g, tile) : 0;     // count tile of this write tile
+    const int ct_shard0 = sh * g.ctps;                      // first count tile of the shard
+    const int n3 = 3 * g.R;  // rank columns: look-back words and write-tile histograms
+    const uint64_t* status = pw.status3;
+
+    // this thread's token: ids and permuted positions, loaded before anything else
+    const int64_t my_t = t0 + tid;
+    const bool my_live = tile >= 0 && tid < g.TT && my_t < t1;
+    int idk[KMAX], pk[KMAX];
+    load_token_ids<KMAX>(idk, ids, my_t, g.K, my_live);
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) pk[k] = (my_live && k < g.K) ? gptr(e2p)[my_t * g.K + k] : 0;
 
     auto total_of = [&](int col) -> int {
-        return g.ntiles > 0 ? (int)status_value(status, g.ntiles - 1, g.ncols, col) : 0;
+        return g.ntiles > 0 ? (int)status_value(status, g.nct - 1, n3, col) : 0;
+    };
+    // global exclusive prefix of a column before this write tile: earlier count tiles (look-back)
+    // plus the earlier write tiles of this count tile (their histograms)
+    auto prefix_here = [&](int col) -> int {
+        int v = ctile > 0 ? (int)status_value(status, ctile - 1, n3, col) : 0;
+        for (int j0 = ct_first_wt(g, ctile); j0 < tile; j0 += 8) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (j0 + j < tile) v += (int)status_value(pw.tilehist, j0 + j, g.ncols, col);
+        }
+        return v;
     };
 
     // ---- prologue --------------------------------------------------------------------------
     for (int e = tid; e < g.E; e += kPlanBlock) s_owner[e] = e / g.epn;
     for (int r = tid; r <= R; r += kPlanBlock) s_cu_r[r] = cu_seqlens[r * g.epn];
-    for (int c = tid; c < 3 * R; c += kPlanBlock)
-        s_excl[c] = tile > 0 ? (int)status_value(status, tile - 1, g.ncols, c) : 0;
+    for (int c = tid; c < 3 * R; c += kPlanBlock) s_excl[c] = tile >= 0 ? prefix_here(c) : 0;
     for (int r = tid; r < R; r += kPlanBlock)
-        s_shard0[r] = first_tile_of_shard > 0
-                          ? (int)status_value(status, first_tile_of_shard - 1, g.ncols, r)
-                          : 0;
+        s_shard0[r] = ct_shard0 > 0 ? (int)status_value(status, ct_shard0 - 1, n3, r) : 0;
     for (int r = tid; r < R; r += kPlanBlock)
 #pragma unroll
         for (int ww = 0; ww < kPlanWaves; ++ww) {
@@ -231,12 +393,12 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
     // ---- per-token pass: dst, slot codes, is_token_in_rank ballots ------------------------
     const int nslots = (int)(t1 - t0) * g.K;
     if (tile >= 0 && tid < g.TT) {
-        const int64_t t = t0 + tid;
-        const bool live = t < t1;
+        const int64_t t = my_t;
+        const bool live = my_live;
         uint32_t m[kMaxRanks / 32] = {0u, 0u, 0u, 0u};
         if (live) {
             TokenSlots<KMAX> ts;
-            token_slots<KMAX>(ts, ids, t, g.K, g.E, s_owner);
+            token_slots<KMAX>(ts, idk, g.K, g.E, R, s_owner);
 #pragma unroll
             for (int k = 0; k < KMAX; ++k) {
                 if (k >= g.K) continue;
@@ -246,9 +408,9 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
                     continue;
                 }
                 const int r = ts.r[k];
-                const int loff = e2p[t * g.K + k] - s_cu_r[r];
+                const int loff = pk[k] - s_cu_r[r];
                 const int64_t raw = (int64_t)r * g.NvS + loff;
-                if (o.dst) o.dst[t * g.K + k] = (int32_t)(ts.first[k] ? raw : -raw - 1);
+                if (o.dst) gptr(o.dst)[t * g.K + k] = (int32_t)(ts.first[k] ? raw : -raw - 1);
                 const uint32_t type = ts.first[k] ? (ts.h[k] >= 2 ? kHead : kNone) : kDup;
                 s_code[si] = type | ((uint32_t)r << 2) | ((uint32_t)ts.h[k] << 10);
                 s_loff[si] = loff;
@@ -272,7 +434,6 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
     const int per_wave = (nslots + kPlanWaves - 1) / kPlanWaves;
     const int wbeg = w * per_wave;
     const int wend = min(nslots, wbeg + per_wave);
-    const int rbits = bits_for(R);
     int hrank[kIters];
     int drank[kIters];
     if (tile >= 0) {
@@ -287,7 +448,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
             const uint64_t act = __ballot(valid);
             const uint64_t hm = __ballot(valid && type == kHead);
             const uint64_t dm = __ballot(valid && type == kDup);
-            const uint64_t peers = match_peers((uint32_t)r, rbits, act);
+            const uint64_t peers = match_peers<NB>((uint32_t)r, act);
             hrank[it] = 0;
             drank[it] = 0;
             if (valid) {
@@ -332,13 +493,13 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
                 const int64_t gpos = (int64_t)s_doff[0][r] + s_excl[R + r] + s_hc[w][r] + hrank[it];
                 if (o.dup_groups && gpos < o.cap_g) {
                     const int h = (int)(code >> 10);
-                    o.dup_groups[3 * gpos + 0] = s_loff[si];
-                    o.dup_groups[3 * gpos + 1] = dup_local;
-                    o.dup_groups[3 * gpos + 2] = h - 1;
+                    gptr(o.dup_groups)[3 * gpos + 0] = s_loff[si];
+                    gptr(o.dup_groups)[3 * gpos + 1] = dup_local;
+                    gptr(o.dup_groups)[3 * gpos + 2] = h - 1;
                 }
             } else {
                 const int64_t dpos = (int64_t)s_doff[1][r] + dup_local;
-                if (o.dup_loffs && dpos < o.cap_d) o.dup_loffs[dpos] = s_loff[si];
+                if (o.dup_loffs && dpos < o.cap_d) gptr(o.dup_loffs)[dpos] = s_loff[si];
             }
         }
     }
@@ -362,24 +523,45 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
             for (int ww = 0; ww < wf; ++ww) cnt += popc64(s_mask[ww][r]);
             const int rem = L & 63;
             if (rem) cnt += popc64(s_mask[wf][r] & ((1ull << rem) - 1ull));
-            o.chan[((int64_t)sh * R + r) * g.C + c] = s_excl[r] + cnt - s_shard0[r];
+            gptr(o.chan)[((int64_t)sh * R + r) * g.C + c] = s_excl[r] + cnt - s_shard0[r];
         }
     }
 
     // ---- per-shard matrices from the last tile of each shard -----------------------------
     if (tile >= 0 && ct == g.tps - 1) {
+        // the count tile of a shard's last write tile ends at the shard's end
         for (int r = tid; r < R; r += kPlanBlock) {
-            const int incl = (int)status_value(status, tile, g.ncols, r);
-            if (o.rank_prefix) o.rank_prefix[(int64_t)sh * R + r] = incl;
-            if (o.ntpr) o.ntpr[(int64_t)sh * R + r] = incl - s_shard0[r];
+            const int incl = (int)status_value(status, ctile, n3, r);
+            if (o.rank_prefix) gptr(o.rank_prefix)[(int64_t)sh * R + r] = incl;
+            if (o.ntpr) gptr(o.ntpr)[(int64_t)sh * R + r] = incl - s_shard0[r];
         }
-        if (o.ntpe) {
-            for (int e = tid; e < g.E; e += kPlanBlock) {
-                const int col = 3 * R + e;
-                const int prev = first_tile_of_shard > 0
-                                     ? (int)status_value(status, first_tile_of_shard - 1, g.ncols, col)
-                                     : 0;
-                o.ntpe[(int64_t)sh * g.E + e] = (int)status_value(status, tile, g.ncols, col) - prev;
+    }
+
+    // ---- per-shard expert counts and expert totals, a slice of the experts per workgroup: sums
+    // of the count tiles' expert aggregates (written by the count kernel)
+    if (g.ntiles > 0) {
+        for (int e = blockIdx.x + (tid / 64) * gridDim.x; e < g.E; e += gridDim.x * kPlanWaves) {
+            // one wave per expert: lane j sums the count tiles of shards j, j + 64, ...
+            int tot = 0;
+            for (int s2 = lane; s2 < g.S; s2 += 64) {
+                int part = 0;
+                for (int c0 = s2 * g.ctps; c0 < (s2 + 1) * g.ctps; c0 += 4) {
+                    int v[4];
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        v[b] = c0 + b < (s2 + 1) * g.ctps ? (int)status_value(pw.statusE, c0 + b, g.E, e) : 0;
+                    part += v[0] + v[1] + v[2] + v[3];
+                }
+                if (o.ntpe) gptr(o.ntpe)[(int64_t)s2 * g.E + e] = part;
+                tot += part;
+            }
+            tot = wave_sum_i32(tot);
+            if (o.recv_zf && lane == 0) {
+                const int cnt = tot;
+                const int padded = cu_seqlens[e + 1] - cu_seqlens[e];
+                const bool z = cnt > 0 && padded > cnt;
+                gptr(o.recv_zf)[2 * e] = z ? cu_seqlens[e] + cnt - cu_seqlens[s_owner[e] * g.epn] : 0;
+                gptr(o.recv_zf)[2 * e + 1] = z ? padded - cnt : 0;
             }
         }
     }
@@ -387,44 +569,39 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
     // ---- block 0: per-rank outputs, empty-shard case, workspace reset ---------------------
     if (blockIdx.x == 0) {
         for (int r = tid; r < R; r += kPlanBlock) {
-            if (o.recv_tokens) o.recv_tokens[r] = total_of(r);
+            if (o.recv_tokens) gptr(o.recv_tokens)[r] = total_of(r);
             if (o.dup_counts) {
-                o.dup_counts[2 * r] = s_doff[0][r + 1] - s_doff[0][r];
-                o.dup_counts[2 * r + 1] = s_doff[1][r + 1] - s_doff[1][r];
+                gptr(o.dup_counts)[2 * r] = s_doff[0][r + 1] - s_doff[0][r];
+                gptr(o.dup_counts)[2 * r + 1] = s_doff[1][r + 1] - s_doff[1][r];
             }
         }
         if (o.dup_offsets)
             for (int r = tid; r <= R; r += kPlanBlock) {
-                o.dup_offsets[2 * r] = s_doff[0][r];
-                o.dup_offsets[2 * r + 1] = s_doff[1][r];
+                gptr(o.dup_offsets)[2 * r] = s_doff[0][r];
+                gptr(o.dup_offsets)[2 * r + 1] = s_doff[1][r];
             }
         if (o.recv_cu)
             for (int p = tid; p < R * (g.epn + 1); p += kPlanBlock) {
                 const int r = p / (g.epn + 1);
                 const int j = p - r * (g.epn + 1);
-                o.recv_cu[p] = cu_seqlens[r * g.epn + j] - s_cu_r[r];
+                gptr(o.recv_cu)[p] = cu_seqlens[r * g.epn + j] - s_cu_r[r];
             }
-        if (o.recv_zf)
-            for (int e = tid; e < g.E; e += kPlanBlock) {
-                const int cnt = total_of(3 * R + e);
-                const int padded = cu_seqlens[e + 1] - cu_seqlens[e];
-                const bool z = cnt > 0 && padded > cnt;
-                o.recv_zf[2 * e] = z ? cu_seqlens[e] + cnt - s_cu_r[s_owner[e]] : 0;
-                o.recv_zf[2 * e + 1] = z ? padded - cnt : 0;
-            }
+
         if (g.ntiles == 0) {  // no tokens: every per-shard matrix is zero
             for (int p = tid; p < g.S * R; p += kPlanBlock) {
-                if (o.rank_prefix) o.rank_prefix[p] = 0;
-                if (o.ntpr) o.ntpr[p] = 0;
+                if (o.rank_prefix) gptr(o.rank_prefix)[p] = 0;
+                if (o.ntpr) gptr(o.ntpr)[p] = 0;
             }
             if (o.ntpe)
-                for (int p = tid; p < g.S * g.E; p += kPlanBlock) o.ntpe[p] = 0;
+                for (int p = tid; p < g.S * g.E; p += kPlanBlock) gptr(o.ntpe)[p] = 0;
+            if (o.recv_zf)
+                for (int p = tid; p < 2 * g.E; p += kPlanBlock) gptr(o.recv_zf)[p] = 0;
             if (o.chan)
-                for (int64_t p = tid; p < (int64_t)g.S * R * g.C; p += kPlanBlock) o.chan[p] = 0;
+                for (int64_t p = tid; p < (int64_t)g.S * R * g.C; p += kPlanBlock) gptr(o.chan)[p] = 0;
         }
         if (tid == 0) {
-            hdr->epoch = hdr->epoch + 1u;
-            hdr->ticket = 0u;
+            gptr(hdr)->epoch = gptr(hdr)->epoch + 1u;
+            gptr(hdr)->ticket = 0u;
         }
     }
 }
@@ -444,17 +621,44 @@ static PlanGeom plan_geom(int64_t N, int E, int K, int R, int S, int C, int64_t 
     g.ncols = 3 * R + E;
     g.C = C;
     g.NvS = NvS;
+    int sub = (int)ceil_div64(g.ntiles, kCountTilesP);
+    if (sub < 1) sub = 1;
+    g.sub = sub;
+    g.ctps = (int)ceil_div64(g.tps, sub);
+    g.nct = S * g.ctps;
+    g.ticketed = g.nct > kUnticketedCountTiles;
     return g;
+}
+
+}  // namespace mep
+
+namespace mep {
+
+// Byte offsets of the parts of the plan workspace (each 256-byte aligned), and its size.
+struct PlanWsLayout {
+    size_t arrive, status3, statusE, tilehist, bytes;
+};
+
+
+
+static PlanWsLayout plan_ws_layout(const PlanGeom& g) {
+    PlanWsLayout L;
+    const size_t n3 = 3 * (size_t)g.R;
+    L.arrive = sizeof(WsHeader);
+    L.status3 = L.arrive + kMaxCountTiles * sizeof(uint32_t);
+    L.statusE = L.status3 + align256((size_t)g.nct * n3 * sizeof(uint64_t));
+    L.tilehist = L.statusE + align256((size_t)g.nct * g.E * sizeof(uint64_t));
+    L.bytes = L.tilehist + align256((size_t)g.ntiles * g.ncols * sizeof(uint64_t));
+    return L;
 }
 
 }  // namespace mep
 
 extern "C" size_t mep_plan_workspace_size(int64_t N, int E, int K, int R, int num_src) {
     using namespace mep;
-    if (N < 0 || E < 1 || K < 1 || R < 1 || num_src < 1) return sizeof(WsHeader);
-    const int TT = plan_tile_tokens(K);
-    const int64_t tps = ceil_div64(N / num_src, TT);
-    return sizeof(WsHeader) + (size_t)(num_src * tps) * (size_t)(3 * R + E) * sizeof(uint64_t);
+    if (N < 0 || E < 1 || K < 1 || R < 1 || num_src < 1 || R > kMaxRanks || E > kMaxE)
+        return sizeof(WsHeader);
+    return plan_ws_layout(plan_geom(N, E, K, R, num_src, 1, 0)).bytes;
 }
 
 extern "C" int mep_plan(const int32_t* topk_ids, const int32_t* cu_seqlens,
@@ -476,6 +680,7 @@ extern "C" int mep_plan(const int32_t* topk_ids, const int32_t* cu_seqlens,
     if (!aligned(ws, 256)) return MEP_ERR_INVALID_ARG;
     if (E > kMaxE || K > 32 || K > E || R > kMaxRanks) return MEP_ERR_UNSUPPORTED;
     if (E % R != 0) return MEP_ERR_UNSUPPORTED;
+    if (num_src > kMaxSources) return MEP_ERR_UNSUPPORTED;
     if (N % num_src != 0) return MEP_ERR_INVALID_ARG;
     const int64_t NK = N * (int64_t)K;
     const int64_t bound = NK + (NK < E ? NK : (int64_t)E) * (int64_t)(alignment - 1);
@@ -493,24 +698,30 @@ extern "C" int mep_plan(const int32_t* topk_ids, const int32_t* cu_seqlens,
     PlanGeom g = plan_geom(N, E, K, R, num_src, num_channels, NvS);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
-    uint64_t* status = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + sizeof(WsHeader));
+    const PlanWsLayout L = plan_ws_layout(g);
+    char* wsb = reinterpret_cast<char*>(ws);
+    const PlanWs pw{reinterpret_cast<uint32_t*>(wsb + L.arrive), reinterpret_cast<uint64_t*>(wsb + L.status3),
+                    reinterpret_cast<uint64_t*>(wsb + L.statusE), reinterpret_cast<uint64_t*>(wsb + L.tilehist)};
     PlanOutDev o{out->is_token_in_rank, out->num_tokens_per_rank, out->num_tokens_per_expert,
                  out->rank_prefix_matrix, out->channel_prefix_matrix, out->recv_tokens,
                  out->recv_cu_seqlens, out->recv_zero_fill, out->dst, out->dup_counts,
                  out->dup_offsets, out->dup_groups, out->cap_groups, out->dup_loffs, out->cap_dups};
     const int grid = g.ntiles > 0 ? g.ntiles : 1;
+    auto launch = [&](auto count_kernel, auto write_kernel) {
+        if (g.ntiles > 0)
+            hipLaunchKernelGGL(count_kernel, dim3(g.ntiles), dim3(kPlanBlock), 0, st, topk_ids, g, pw, hdr,
+                               o.itr);
+        hipLaunchKernelGGL(write_kernel, dim3(grid), dim3(kPlanBlock), 0, st, topk_ids, cu_seqlens,
+                           expanded_to_permuted, g, pw, hdr, o);
+    };
     if (K <= 8) {
-        if (g.ntiles > 0)
-            hipLaunchKernelGGL(plan_count_kernel<8>, dim3(g.ntiles), dim3(kPlanBlock), 0, st, topk_ids,
-                               g, status, hdr, o.itr);
-        hipLaunchKernelGGL(plan_write_kernel<8>, dim3(grid), dim3(kPlanBlock), 0, st, topk_ids,
-                           cu_seqlens, expanded_to_permuted, g, status, hdr, o);
+        if (R <= 8) launch(plan_count_kernel<8, 1>, plan_write_kernel<8, 3>);
+        else if (R <= 32) launch(plan_count_kernel<8, 1>, plan_write_kernel<8, 5>);
+        else launch(plan_count_kernel<8, 4>, plan_write_kernel<8, 7>);
     } else {
-        if (g.ntiles > 0)
-            hipLaunchKernelGGL(plan_count_kernel<32>, dim3(g.ntiles), dim3(kPlanBlock), 0, st, topk_ids,
-                               g, status, hdr, o.itr);
-        hipLaunchKernelGGL(plan_write_kernel<32>, dim3(grid), dim3(kPlanBlock), 0, st, topk_ids,
-                           cu_seqlens, expanded_to_permuted, g, status, hdr, o);
+        if (R <= 8) launch(plan_count_kernel<32, 1>, plan_write_kernel<32, 3>);
+        else if (R <= 32) launch(plan_count_kernel<32, 1>, plan_write_kernel<32, 5>);
+        else launch(plan_count_kernel<32, 4>, plan_write_kernel<32, 7>);
     }
     return launch_status();
 }

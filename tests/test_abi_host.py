@@ -36,13 +36,23 @@ def test_status_strings():
 
 
 def test_workspace_sizes():
-    assert B.layout_workspace_size(0, 8, 2) == 256
-    assert B.layout_workspace_size(65536, 256, 8) == 256 + 256 * 256 * 8
-    assert B.layout_workspace_size(1, 8, 2) == 256 + 8 * 8
-    s1 = B.plan_workspace_size(65536, 256, 8, 8, 8)
-    assert s1 == 256 + 8 * 32 * (3 * 8 + 256) * 8
-    assert B.plan_workspace_size(65536, 256, 8, 8, 1) == 256 + 256 * (3 * 8 + 256) * 8
+    # layout: header, arrival counters of up to 4096 count tiles (fixed region), then 4096-slot
+    # tiles grouped by 4 into 32 count tiles: one look-back word per (count tile, expert) and
+    # one tagged count per (tile, expert), each region 256-byte aligned
+    arrive = 4096 * 4
+    assert B.layout_workspace_size(0, 8, 2) == 256 + arrive
+    assert B.layout_workspace_size(65536, 256, 8) == 256 + arrive + 32 * 256 * 8 + 128 * 256 * 8
+    assert B.layout_workspace_size(1, 8, 2) == 256 + arrive + 256 + 256
+    # plan: write tiles of 4096 / K tokens that never cross a shard (128 here), grouped by 4
+    # into 32 count tiles; arrival counters (fixed region), look-back words for the 3R rank
+    # columns, tagged expert aggregates per count tile, and tagged 3R+E column histograms per
+    # write tile (each part 256-aligned)
+    def a256(x):
+        return (x + 255) // 256 * 256
 
+    want = 256 + 2048 * 4 + a256(32 * 24 * 8) + a256(32 * 256 * 8) + a256(128 * (24 + 256) * 8)
+    assert B.plan_workspace_size(65536, 256, 8, 8, 8) == want
+    assert B.plan_workspace_size(65536, 256, 8, 8, 1) == want
 
 FAKE = 0x10000          # aligned, never dereferenced
 MIS = 0x10004           # 4-aligned but not 16-aligned

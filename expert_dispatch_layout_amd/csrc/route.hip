@@ -133,6 +133,7 @@ extern "C" int mep_route_topk(const void* logits, int dtype, int64_t N, int E, i
     const int W = dtype == MEP_BF16 ? 8 : 4;
     a.vec = (E % W) == 0;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (launch_route_sig(a, dtype, st)) return launch_status();
     if (launch_route_fast(a, dtype, st)) return launch_status();
     return dtype == MEP_BF16 ? dispatch_generic<true>(a, st) : dispatch_generic<false>(a, st);
 }

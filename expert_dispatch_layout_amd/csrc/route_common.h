@@ -295,4 +295,7 @@ __device__ __forceinline__ void write_weights(const RouteArgs& a, int64_t tok, i
 // Fast-kernel launcher (route_fast.hip).  Returns false when the shape is not covered.
 bool launch_route_fast(const RouteArgs& a, int dtype, hipStream_t st);
 
+// Sigmoid routing kernel launcher (route_sig.hip).  Returns false when the shape is not covered.
+bool launch_route_sig(const RouteArgs& a, int dtype, hipStream_t st);
+
 }  // namespace mep

@@ -1,0 +1,48 @@
+// Shape dispatch of the sigmoid routing kernel (route_sig.h).
+#include "route_sig.h"
+
+namespace mep {
+
+template <int LPT, bool BF16, int MODE>
+static void launch_sig(const RouteArgs& a, hipStream_t st) {
+    SigCfg cfg;
+    cfg.nsets = ceil_div64(a.N, FastGeom<LPT, BF16>::TPW);
+    cfg.tg = MODE == 1 ? a.topk_group : LPT;
+    auto kernel = route_sig_kernel<LPT, BF16, MODE>;
+    const int64_t need = ceil_div64(cfg.nsets, kFastWaves);
+    int64_t grid = resident_blocks(reinterpret_cast<const void*>(kernel), kFastBlock);
+    if (grid > need) grid = need;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kFastBlock), 0, st, a, cfg);
+}
+
+template <bool BF16, int MODE>
+static void launch_sig_lpt(int LPT, const RouteArgs& a, hipStream_t st) {
+    switch (LPT) {
+        case 2: launch_sig<2, BF16, MODE>(a, st); break;
+        case 4: launch_sig<4, BF16, MODE>(a, st); break;
+        case 8: launch_sig<8, BF16, MODE>(a, st); break;
+        default: launch_sig<16, BF16, MODE>(a, st); break;
+    }
+}
+
+bool launch_route_sig(const RouteArgs& a, int dtype, hipStream_t st) {
+    if (a.score_fn != MEP_SIGMOID || !a.vec || a.K > 8 || a.E % kFastEPL != 0) return false;
+    const int LPT = a.E / kFastEPL;
+    if (LPT != 2 && LPT != 4 && LPT != 8 && LPT != 16) return false;
+    int mode;
+    if (a.n_group <= 1) mode = 0;
+    else if (a.n_group == LPT) mode = 1;
+    else return false;
+    const bool bf16 = dtype == MEP_BF16;
+    if (bf16) {
+        if (mode == 0) launch_sig_lpt<true, 0>(LPT, a, st);
+        else launch_sig_lpt<true, 1>(LPT, a, st);
+    } else {
+        if (mode == 0) launch_sig_lpt<false, 0>(LPT, a, st);
+        else launch_sig_lpt<false, 1>(LPT, a, st);
+    }
+    return true;
+}
+
+}  // namespace mep

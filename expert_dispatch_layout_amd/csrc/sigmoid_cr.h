@@ -121,6 +121,14 @@ __device__ __noinline__ float sigmoid_cr_slow(float x) {
     return dd_round_f32(s);
 }
 
+// A binary64 constant placed in scalar registers where it is used.  The empty volatile asm keeps
+// the compiler from hoisting the constant out of loops into vector registers (where, under
+// register pressure, it would be spilled and reloaded from scratch memory instead).
+__device__ __forceinline__ double sreg(double v) {
+    asm volatile("" : "+s"(v));
+    return v;
+}
+
 // 2^y in binary64 for |y| <= 1100.  y = n + f with n = rint(y) and |f| <= 1/2 (exact); 2^f =
 // e^(f ln 2) by its Taylor series to degree 13, whose truncation error is below 2^-56 for
 // |f ln 2| <= 0.35, in Horner form (coefficients (ln 2)^k / k! rounded to binary64); then an
@@ -128,19 +136,19 @@ __device__ __noinline__ float sigmoid_cr_slow(float x) {
 __device__ __forceinline__ double exp2_f64(double y) {
     const double n = __builtin_rint(y);
     const double f = y - n;
-    double p = 0x1.816193166d0f9p-40;
-    p = __fma_rn(p, f, 0x1.c3bd650fc2986p-36);
-    p = __fma_rn(p, f, 0x1.e8cac7351bb25p-32);
-    p = __fma_rn(p, f, 0x1.e4cf5158b8ecap-28);
-    p = __fma_rn(p, f, 0x1.b5253d395e7c4p-24);
-    p = __fma_rn(p, f, 0x1.62c0223a5c824p-20);
-    p = __fma_rn(p, f, 0x1.ffcbfc588b0c7p-17);
-    p = __fma_rn(p, f, 0x1.430912f86c787p-13);
-    p = __fma_rn(p, f, 0x1.5d87fe78a6731p-10);
-    p = __fma_rn(p, f, 0x1.3b2ab6fba4e77p-7);
-    p = __fma_rn(p, f, 0x1.c6b08d704a0c0p-5);
-    p = __fma_rn(p, f, 0x1.ebfbdff82c58fp-3);
-    p = __fma_rn(p, f, 0x1.62e42fefa39efp-1);
+    double p = sreg(0x1.816193166d0f9p-40);
+    p = __fma_rn(p, f, sreg(0x1.c3bd650fc2986p-36));
+    p = __fma_rn(p, f, sreg(0x1.e8cac7351bb25p-32));
+    p = __fma_rn(p, f, sreg(0x1.e4cf5158b8ecap-28));
+    p = __fma_rn(p, f, sreg(0x1.b5253d395e7c4p-24));
+    p = __fma_rn(p, f, sreg(0x1.62c0223a5c824p-20));
+    p = __fma_rn(p, f, sreg(0x1.ffcbfc588b0c7p-17));
+    p = __fma_rn(p, f, sreg(0x1.430912f86c787p-13));
+    p = __fma_rn(p, f, sreg(0x1.5d87fe78a6731p-10));
+    p = __fma_rn(p, f, sreg(0x1.3b2ab6fba4e77p-7));
+    p = __fma_rn(p, f, sreg(0x1.c6b08d704a0c0p-5));
+    p = __fma_rn(p, f, sreg(0x1.ebfbdff82c58fp-3));
+    p = __fma_rn(p, f, sreg(0x1.62e42fefa39efp-1));
     p = __fma_rn(p, f, 1.0);
     return __builtin_amdgcn_ldexp(p, (int)n);
 }

@@ -152,6 +152,38 @@ def test_route_sweep(E, K, dtype, mode):
     check_route(logits, K, dtype, **kw)
 
 
+# one expert group of 32 per lane (E = 32 * G), or no group limit, sigmoid scoring: the
+# register-resident selection with certified margins; near ties, a group holding most of the top
+# keys (list refill), equal logits (exact fallback) and a wide bias range (larger margins)
+LANE_GROUP_CASES = []
+for G in (2, 4, 8, 16):
+    for K in (1, 2, 5, 8):
+        for dtype in (synth.F32, synth.BF16):
+            LANE_GROUP_CASES.append((G, K, dtype))
+
+
+@pytest.mark.parametrize("G,K,dtype", LANE_GROUP_CASES)
+def test_route_sigmoid_lane_groups(G, K, dtype):
+    E = 32 * G
+    rng = np.random.default_rng(G * 100 + K * 10 + dtype)
+    N = 1000
+    x = rng.standard_normal((N, E)).astype(np.float32)
+    x[::11, :12] = 4.0 + rng.standard_normal((len(x[::11]), 12)).astype(np.float32) * 0.1  # one group wins
+    x[3::13, 1::5] = x[3::13, 0:1]                 # equal logits
+    x[7::17] = np.float32(0.5) + np.float32(2.0 ** -20) * rng.integers(0, 4, (len(x[7::17]), E))  # near ties
+    logits = synth.f32_to_bf16_bits(x) if dtype == synth.BF16 else x
+    for bias_scale in (0.1, 3.0):
+        bias = rng.uniform(-bias_scale, bias_scale, E).astype(np.float32)
+        for tg in sorted({1, max(1, G // 2), G}):
+            if tg * 32 < K:
+                continue
+            _note("G=%d K=%d dtype=%d bias=%g tg=%d" % (G, K, dtype, bias_scale, tg))
+            check_route(logits, K, dtype, score_fn=1, bias=bias, n_group=G, topk_group=tg,
+                        group_topn=1 + (K % 2), scale=2.5, renormalize=K > 1)
+        _note("G=%d K=%d dtype=%d bias=%g no group limit" % (G, K, dtype, bias_scale))
+        check_route(logits, K, dtype, score_fn=1, bias=bias, scale=1.0, renormalize=False)
+
+
 def test_route_tiny_batches():
     rng = np.random.default_rng(9)
     for N in (1, 2, 3, 63, 65, 257):

@@ -17,20 +17,21 @@
 //      signed integers, in reverse, and -inf is below every key in both readings, so the
 //      selection below is integer min / float med3 on the same bits (a median is the same
 //      element in either order) with -inf as the empty entry, and no NaN canonicalisation;
-//   2. a sorted list of the lane's 5 largest keys, one med3 per entry and key;
+//   2. a sorted list of the lane's 6 largest keys, one med3 per entry and key;
 //   3. group score = sum of the group's top keys (list entries 0 and 1), with the group index in
 //      its 3 (4 for 16 groups) low significand bits so that a lower index wins a tie; the rank of
 //      each group among the segment's groups from the other lanes' scores (DPP),
 //      kept = rank < topk_group;
 //   4. K + 1 extraction rounds over the kept lanes' list heads (segment max through DPP); the
-//      winning lane pops its head; a lane that empties its list refills it from its keys below
-//      the value it last gave up (rare: a group holding more than 5 of the top K + 1);
+//      winning lane pops its head (a lane whose list runs dry before the last round, i.e. a group
+//      holding more than 6 of the top K + 1, about one token in 10^4, takes the exact path);
 //   5. certification: the selection on the exact keys (correctly rounded sigmoid plus bias, both
 //      binary32) is the same when the last kept and first dropped group scores, and each pair
 //      of consecutive extracted keys, differ by more than the error bounds below, and every
 //      round had exactly one winner.  A token that fails is redone at once by the whole wave
 //      from the row still in LDS, on exact keys (exact_token_sig).
-// The K selected experts then get the correctly rounded sigmoid in binary64 and the weights.
+// The K selected experts then get their sigmoid in binary64 (relative error below 2^-30) for the
+// weights.
 //
 // Error bounds.  Let S = RN(sigma(x)) and k = RN(S + b) be the exact key, s~ the binary32
 // sigmoid (|s~ - sigma| <= 3.23 * 2^-23, see route_fast.h), b' = RN(b - c), k'' = RN(s~ + b'),
@@ -51,7 +52,7 @@
 
 namespace mep {
 
-constexpr int kSigT = 5;                          // list depth per lane
+constexpr int kSigT = 6;                          // list depth per lane
 constexpr int kSigEmpty = (int)0xFF800000u;       // -inf: below every key as float and as integer
 
 // LDS row layout: lane group g of a token (its CPL chunks) starts at chunk g * (CPL + 1).
@@ -127,8 +128,17 @@ __device__ __forceinline__ uint64_t partner_u64(uint64_t v, P partner) {
     return ((uint64_t)partner((uint32_t)(v >> 32)) << 32) | partner((uint32_t)v);
 }
 
-// Wave-wide maximum of a 64-bit value (uniform result): DPP within rows of 16 lanes, then the
-// four row maxima through lane reads.
+// Wave-wide maximum of a 64-bit value (uniform result): DPP butterflies within rows of 16 lanes,
+// then the row broadcasts (lane 15 of a row into the next row, lane 31 into the upper two rows)
+// leave the maximum in lane 63, which is read once.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_keep_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v, CTRL, ROWS, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), CTRL,
+                                                              ROWS, 0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     uint64_t w;
     w = partner_u64(v, [](uint32_t u) { return seg_partner_u32<1>(u); });
@@ -139,24 +149,25 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     v = w > v ? w : v;
     w = partner_u64(v, [](uint32_t u) { return seg_partner_u32<8>(u); });
     v = w > v ? w : v;
-    uint64_t r = 0;
-#pragma unroll
-    for (int row = 0; row < 4; ++row) {
-        const uint64_t x = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), row * 16) << 32) |
-                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, row * 16);
-        r = x > r ? x : r;
-    }
-    return r;
+    w = dpp_keep_u64<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = w > v ? w : v;
+    w = dpp_keep_u64<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    v = w > v ? w : v;
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), 63) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
 }
 
 // Exact routing of token `tok` whose row is at `row` in LDS (SigGeom layout), by the whole wave:
 // lane l takes experts [l*NPL, (l+1)*NPL); a key is the correctly rounded sigmoid plus the bias,
 // ordered by (key desc, expert asc) as one 64-bit word; group scores (binary32 sums of the top
 // keys) and ranks (score desc, group asc) as in the fast path but exact; then K rounds of a
-// wave-wide arg-max.  Writes the K ids and weights.
+// wave-wide arg-max over the heads of the lanes' sorted keys.  Writes the K ids and weights.
+// Out of line, so that its registers do not add to those of the set loop it is rarely called
+// from; the arguments are taken by value (a reference to a kernel argument would put a copy of
+// it in scratch memory).
 template <int LPT, bool BF16, int MODE>
-__device__ __forceinline__ void exact_token_sig(const RouteArgs& a, const u32x4* row, int64_t tok,
-                                                int tg, int wl) {
+__device__ __noinline__ void exact_token_sig(const RouteArgs a, const u32x4* row, int64_t tok, int tg,
+                                             int wl) {
     using G = SigGeom<LPT, BF16>;
     constexpr int W = G::W;
     constexpr int E = kFastEPL * LPT;
@@ -164,28 +175,28 @@ __device__ __forceinline__ void exact_token_sig(const RouteArgs& a, const u32x4*
     constexpr int S = 32 / NPL;    // lanes per group of 32 experts
     const int K = a.K;
     const char* rb = reinterpret_cast<const char*>(row);
-    uint64_t pk[NPL];
-    float sg[NPL];
+    auto logit = [&](int e) -> float {
+        const char* p = rb + G::pos(e / W) * 16 + (e % W) * (BF16 ? 2 : 4);
+        return BF16 ? __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t*>(p)) << 16)
+                    : *reinterpret_cast<const float*>(p);
+    };
+    uint64_t P[NPL];  // the lane's keys, sorted descending
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
         const int e = wl * NPL + i;
-        const char* p = rb + G::pos(e / W) * 16 + (e % W) * (BF16 ? 2 : 4);
-        const float x = BF16 ? __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t*>(p)) << 16)
-                             : *reinterpret_cast<const float*>(p);
-        sg[i] = sigmoid_cr(x);
-        const float key = sg[i] + gptr(a.bias)[e];
-        pk[i] = ((uint64_t)order_key(key) << 32) | (uint32_t)~(uint32_t)e;
+        const float key = sigmoid_cr(logit(e)) + gptr(a.bias)[e];
+        uint64_t v = ((uint64_t)order_key(key) << 32) | (uint32_t)~(uint32_t)e;
+#pragma unroll
+        for (int j = 0; j < i; ++j) {  // insertion into the sorted prefix
+            const uint64_t hi = P[j] > v ? P[j] : v;
+            v = P[j] > v ? v : P[j];
+            P[j] = hi;
+        }
+        P[i] = v;
     }
     bool kept = true;
     if constexpr (MODE == 1) {
-        uint64_t t1 = 0, t2 = 0;  // the group's two largest keys (0 is below every key)
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) {
-            const uint64_t v = pk[i];
-            const uint64_t lo = v < t1 ? v : t1;
-            t2 = lo > t2 ? lo : t2;
-            t1 = v > t1 ? v : t1;
-        }
+        uint64_t t1 = P[0], t2 = NPL > 1 ? P[NPL > 1 ? 1 : 0] : 0;  // the group's two largest keys
         auto merge = [&](auto partner) {
             const uint64_t b1 = partner_u64(t1, partner), b2 = partner_u64(t2, partner);
             const uint64_t lo = t1 < b1 ? t1 : b1;
@@ -211,47 +222,35 @@ __device__ __forceinline__ void exact_token_sig(const RouteArgs& a, const u32x4*
         }
         kept = rank < tg;
     }
-    uint32_t taken = 0;
-    int my_e = 0;
-    float my_s = 0.0f;
-    double den = 0.0;
-    for (int r = 0; r < K; ++r) {
-        uint64_t best = 0;
-        int bi = -1;
-        float bs = 0.0f;
+    if (!kept) {
 #pragma unroll
-        for (int i = 0; i < NPL; ++i) {
-            if (kept && !((taken >> i) & 1u) && pk[i] > best) {
-                best = pk[i];
-                bi = i;
-                bs = sg[i];
-            }
-        }
-        const uint64_t mx = wave_max_u64(best);
-        const bool win = bi >= 0 && best == mx;
-        if (win) taken |= 1u << bi;
-        const uint64_t wmask = __ballot(win);
-        const int wlane = wmask ? __builtin_ctzll(wmask) : 0;
-        const float s_r = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(bs), wlane));
-        const int e_r = (int)~(uint32_t)mx;
-        den += (double)s_r;
-        if (wl == r) {
-            my_e = e_r;
-            my_s = s_r;
-        }
+        for (int i = 0; i < NPL; ++i) P[i] = 0;  // 0 is below every key
     }
+    int my_e = 0;
+    for (int r = 0; r < K; ++r) {
+        const uint64_t mx = wave_max_u64(P[0]);
+        const bool win = P[0] == mx;
+#pragma unroll
+        for (int i = 0; i < NPL - 1; ++i) P[i] = win ? P[i + 1] : P[i];
+        P[NPL - 1] = win ? 0 : P[NPL - 1];
+        if (wl == r) my_e = (int)~(uint32_t)mx;
+    }
+    // weights from the correctly rounded sigmoid of the selected experts (lanes 0..K-1)
+    const double v = wl < K ? (double)sigmoid_cr(logit(my_e)) : 0.0;
+    const double den = seg_allreduce<8>(v, 8, PartnerF64{}, [](double x, double y) { return x + y; });
     if (wl < K) {
         const double inv = a.renormalize ? (den > 0.0 ? recip_f64(den) : 0.0) : 1.0;
         gptr(a.ids)[tok * K + wl] = my_e;
-        if (a.weights) gptr(a.weights)[tok * K + wl] = (float)(((double)my_s * inv) * (double)a.scale);
+        if (a.weights) gptr(a.weights)[tok * K + wl] = (float)((v * inv) * (double)a.scale);
     }
 }
 
 // ---- the kernel -----------------------------------------------------------------------------------
 
 // MODE 0: no group limit; MODE 1: lane lseg of a segment is group lseg (n_group == LPT).
-template <int LPT, bool BF16, int MODE>
-__global__ __launch_bounds__(kFastBlock, BF16 ? 4 : 3) void route_sig_kernel(RouteArgs a, SigCfg cfg) {
+// NW waves per workgroup, each independent after the prologue.
+template <int LPT, bool BF16, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_kernel(RouteArgs a, SigCfg cfg) {
     using G = SigGeom<LPT, BF16>;
     constexpr int W = G::W;
     constexpr int CPL = G::CPL;
@@ -264,7 +263,8 @@ __global__ __launch_bounds__(kFastBlock, BF16 ? 4 : 3) void route_sig_kernel(Rou
     static_assert(CPL * W == NE, "32 experts per lane");
     static_assert(FastGeom<LPT, BF16>::TPW == TPW && FastGeom<LPT, BF16>::CPL == CPL, "load geometry");
 
-    __shared__ u32x4 s_rows[kFastWaves][TPW * RS];
+    constexpr int NT = 64 * NW;
+    __shared__ u32x4 s_rows[NW][TPW * RS];
     __shared__ float4 s_bsh4[LPT * kFastEPL / 4];  // b - c
     __shared__ float s_bconst[2];                   // constant terms of the two margins
 
@@ -274,8 +274,8 @@ __global__ __launch_bounds__(kFastBlock, BF16 ? 4 : 3) void route_sig_kernel(Rou
     const int tw = wl / LPT;
     const int lseg = wl % LPT;
     const int K = a.K;
-    const int64_t waves = (int64_t)gridDim.x * kFastWaves;
-    const int64_t first_set = (int64_t)blockIdx.x * kFastWaves + wv;
+    const int64_t waves = (int64_t)gridDim.x * NW;
+    const int64_t first_set = (int64_t)blockIdx.x * NW + wv;
 
     u32x4 buf[CPL];
     if (first_set < cfg.nsets) fast_load_set<LPT, BF16>(a, first_set, wl, buf);
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(kFastBlock, BF16 ? 4 : 3) void route_sig_kernel(Rou
         s_bconst[1] = (float)((4.0 * D + 2.0 * H * 0x1p-24) * (1.0 + 0x1p-19));
     }
     const int e0 = lseg * NE;
-    for (int e = tid; e < LPT * NE; e += kFastBlock) reinterpret_cast<float*>(s_bsh4)[e] = gb[e] - c;
+    for (int e = tid; e < LPT * NE; e += NT) reinterpret_cast<float*>(s_bsh4)[e] = gb[e] - c;
     __syncthreads();
 
     u32x4* my_rows = s_rows[wv];
@@ -350,9 +350,9 @@ __global__ __launch_bounds__(kFastBlock, BF16 ? 4 : 3) void route_sig_kernel(Rou
         if (set + waves < cfg.nsets) fast_load_set<LPT, BF16>(a, set + waves, wl, buf);
         wave_lds_sync();
 
-        const int64_t tok_raw = set * TPW + tw;
-        const bool live = tok_raw < a.N;
-        const int64_t tok = live ? tok_raw : (a.N - 1);
+        const int tok_raw = (int)set * TPW + tw;  // N * K < 2^31
+        const bool live = tok_raw < (int)a.N;
+        const int tok = live ? tok_raw : (int)a.N - 1;
         const float b_gap = *reinterpret_cast<volatile const float*>(&s_bconst[0]);
         const float b_grp = *reinterpret_cast<volatile const float*>(&s_bconst[1]);
 
@@ -391,79 +391,68 @@ __global__ __launch_bounds__(kFastBlock, BF16 ? 4 : 3) void route_sig_kernel(Rou
         }
 
         // ---- K + 1 extraction rounds ---------------------------------------------------------------
-        uint32_t wm = 0;  // rounds this lane won
-        int wins = 0;
-        int myM[KPL];     // extracted value of round lseg + q * LPT
+        // All KMAX + 1 rounds run whatever K is (rounds past K only feed bits that are masked off),
+        // so no round depends on a run-time condition.  `slot_bits` marks this lane's output slots;
+        // it is derived from the set index (the shift is always 0) so that the compiler forms the
+        // per-round lane tests inside the loop instead of hoisting them all into scalar registers.
+        const uint32_t slot_bits = (1u << lseg) << (uint32_t)(set >> 40);
+        uint32_t wm = 0;      // rounds this lane won
+        uint32_t gapbad = 0;  // rounds whose value is too close to the previous one
+        int myM[KPL];         // value extracted in round lseg + q * LPT
+        int myW[KPL];         // lane (within the segment) that won that round
 #pragma unroll
-        for (int q = 0; q < KPL; ++q) myM[q] = kSigEmpty;
+        for (int q = 0; q < KPL; ++q) {
+            myM[q] = kSigEmpty;
+            myW[q] = 0;
+        }
         int prev = 0;
-#pragma unroll 1
-        for (int r = 0; r <= K; ++r) {
+        static_for<KMAX + 1>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
             const int m = seg_min_i32<LPT>(L[0]);
-#pragma unroll
-            for (int q = 0; q < KPL; ++q) myM[q] = (r == lseg + q * LPT) ? m : myM[q];
-            if (r > 0) {
+            const bool win = L[0] == m;
+            if constexpr (r < KMAX) {
+                const int wr = seg_max_i32<LPT>(win ? lseg : 0);
+                constexpr int q = r / LPT;
+                const bool mine = (slot_bits >> (r - q * LPT)) & 1u;
+                myM[q] = mine ? m : myM[q];
+                myW[q] = mine ? wr : myW[q];
+            }
+            if constexpr (r > 0) {
+                // certification of the order: consecutive extracted values far enough apart
                 const float fp = __int_as_float(prev), fm = __int_as_float(m);
-                fail = fail || !(fp - fm > fmaf(-(fp + fm), a_gap, b_gap));
+                gapbad |= (fp - fm > fmaf(-(fp + fm), a_gap, b_gap)) ? 0u : (1u << r);
             }
             prev = m;
-            const bool win = L[0] == m;
 #pragma unroll
             for (int i = 0; i < kSigT - 1; ++i) L[i] = win ? L[i + 1] : L[i];
             L[kSigT - 1] = win ? kSigEmpty : L[kSigT - 1];
-            wins += win ? 1 : 0;
             wm |= win ? (1u << r) : 0u;
-            const bool empty = win && wins == kSigT && r < K;
-            if (__ballot(empty) != 0ull) {
-                if (empty) {
-                    // the lane's keys below the value it just gave up
-#pragma unroll 1
-                    for (int j = 0; j < CPL; ++j) {
-                        int k[W];
-                        chunk_keys(j, k);
-#pragma unroll
-                        for (int i = 0; i < W; ++i)
-                            if (k[i] > m) list_insert(L, k[i]);
-                    }
-                }
-            }
-        }
-        // every round had exactly one winner in the segment
+        });
+        // every round up to K had exactly one winner in the segment, consecutive values were far
+        // enough apart, and no list ran dry before round K (a group holding more than kSigT of the
+        // top K + 1 is left to the exact path)
         const uint32_t all = (2u << K) - 1u;
-        if (seg_or_u32<LPT>(wm) != all || seg_add_u32<LPT>((uint32_t)__popc(wm)) != (uint32_t)(K + 1))
-            fail = true;
+        wm &= all;
+        const int nw = __popc(wm);
+        if ((gapbad & all) != 0u) fail = true;
+        if (nw >= kSigT && (wm >> K) == 0u) fail = true;
+        if (seg_or_u32<LPT>(wm) != all || seg_add_u32<LPT>((uint32_t)nw) != (uint32_t)(K + 1)) fail = true;
 
         // ---- experts of this lane's output slots, weights ------------------------------------------
-        int wlane[KPL];
-#pragma unroll
-        for (int q = 0; q < KPL; ++q) wlane[q] = 0;
-        static_for<LPT>([&](auto oc) {
-            constexpr int o = decltype(oc)::value;
-            const uint32_t wo = seg_xor_u32<o>(wm);
-#pragma unroll
-            for (int q = 0; q < KPL; ++q)
-                if ((wo >> (lseg + q * LPT)) & 1u) wlane[q] = lseg ^ o;
-        });
         int my_e[KPL];
-        float my_v[KPL];
+        double my_v[KPL];
 #pragma unroll
         for (int q = 0; q < KPL; ++q) {
             const int j = lseg + q * LPT;
-            const int e = wlane[q] * NE + (int)((uint32_t)myM[q] & 31u);
+            const int e = myW[q] * NE + (int)((uint32_t)myM[q] & 31u);
             my_e[q] = e;
-            float v = 0.0f;
-            if (j < K) {
-                bool ok;
-                v = sigmoid_cr_fast(row_logit(e), ok);
-                fail = fail || !ok;
-            }
-            my_v[q] = v;
+            my_v[q] = j < K ? sigmoid_f64_weight(row_logit(e)) : 0.0;
         }
         fail = seg_or_u32<LPT>(fail ? 1u : 0u) != 0u;
         // (v / sum(v)) * scale (renormalised) or v * scale, in binary64, rounded once
         double den = 0.0;
 #pragma unroll
-        for (int q = 0; q < KPL; ++q) den += (double)my_v[q];
+        for (int q = 0; q < KPL; ++q) den += my_v[q];
         den = seg_allreduce<LPT>(den, LPT, PartnerF64{}, [](double u, double w) { return u + w; });
         const double inv = a.renormalize ? (den > 0.0 ? recip_f64(den) : 0.0) : 1.0;
         if (live && !fail) {
@@ -472,7 +461,7 @@ __global__ __launch_bounds__(kFastBlock, BF16 ? 4 : 3) void route_sig_kernel(Rou
                 const int j = lseg + q * LPT;
                 if (j < K) {
                     gptr(a.ids)[tok * K + j] = my_e[q];
-                    if (a.weights) gptr(a.weights)[tok * K + j] = (float)(((double)my_v[q] * inv) * (double)a.scale);
+                    if (a.weights) gptr(a.weights)[tok * K + j] = (float)((my_v[q] * inv) * (double)a.scale);
                 }
             }
         }

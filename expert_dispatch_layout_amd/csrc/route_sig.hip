@@ -8,12 +8,13 @@ static void launch_sig(const RouteArgs& a, hipStream_t st) {
     SigCfg cfg;
     cfg.nsets = ceil_div64(a.N, FastGeom<LPT, BF16>::TPW);
     cfg.tg = MODE == 1 ? a.topk_group : LPT;
-    auto kernel = route_sig_kernel<LPT, BF16, MODE>;
-    const int64_t need = ceil_div64(cfg.nsets, kFastWaves);
-    int64_t grid = resident_blocks(reinterpret_cast<const void*>(kernel), kFastBlock);
+    constexpr int NW = 4;
+    auto kernel = route_sig_kernel<LPT, BF16, MODE, NW>;
+    const int64_t need = ceil_div64(cfg.nsets, NW);
+    int64_t grid = resident_blocks(reinterpret_cast<const void*>(kernel), 64 * NW);
     if (grid > need) grid = need;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kFastBlock), 0, st, a, cfg);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * NW), 0, st, a, cfg);
 }
 
 template <bool BF16, int MODE>

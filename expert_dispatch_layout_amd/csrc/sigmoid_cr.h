@@ -129,29 +129,38 @@ __device__ __forceinline__ double sreg(double v) {
     return v;
 }
 
-// 2^y in binary64 for |y| <= 1100.  y = n + f with n = rint(y) and |f| <= 1/2 (exact); 2^f =
-// e^(f ln 2) by its Taylor series to degree 13, whose truncation error is below 2^-56 for
-// |f ln 2| <= 0.35, in Horner form (coefficients (ln 2)^k / k! rounded to binary64); then an
-// exact scaling by 2^n.  Relative error below 2^-51.
-__device__ __forceinline__ double exp2_f64(double y) {
+// Coefficients of 2^f = e^(f ln 2) for |f| <= 1/2: the Taylor series to degree 13, (ln 2)^k / k!
+// rounded to binary64, highest degree first (the constant term 1 is added separately).  The
+// truncation error is below 2^-56 for |f ln 2| <= 0.35.
+constexpr int kExp2Terms = 13;
+constexpr double kExp2Coef[kExp2Terms] = {
+    0x1.816193166d0f9p-40, 0x1.c3bd650fc2986p-36, 0x1.e8cac7351bb25p-32, 0x1.e4cf5158b8ecap-28,
+    0x1.b5253d395e7c4p-24, 0x1.62c0223a5c824p-20, 0x1.ffcbfc588b0c7p-17, 0x1.430912f86c787p-13,
+    0x1.5d87fe78a6731p-10, 0x1.3b2ab6fba4e77p-7,  0x1.c6b08d704a0c0p-5,  0x1.ebfbdff82c58fp-3,
+    0x1.62e42fefa39efp-1};
+
+// Coefficient source: scalar-register constants (the default).
+struct Exp2CoefConst {
+    __device__ __forceinline__ double operator()(int i) const { return sreg(kExp2Coef[i]); }
+};
+
+// 2^y in binary64 for |y| <= 1100.  y = n + f with n = rint(y) and |f| <= 1/2 (exact); 2^f by
+// the series above in Horner form, then an exact scaling by 2^n.  Relative error below 2^-51.
+// `coef(i)` supplies kExp2Coef[i].  FIRST > 0 drops the FIRST highest-degree terms: FIRST = 5
+// keeps degree 8, whose truncation error is below 2^-31 (enough where only about 2^-30 relative
+// accuracy is needed, with fewer constants to hold).
+template <int FIRST = 0, typename C>
+__device__ __forceinline__ double exp2_f64_c(double y, C coef) {
     const double n = __builtin_rint(y);
     const double f = y - n;
-    double p = sreg(0x1.816193166d0f9p-40);
-    p = __fma_rn(p, f, sreg(0x1.c3bd650fc2986p-36));
-    p = __fma_rn(p, f, sreg(0x1.e8cac7351bb25p-32));
-    p = __fma_rn(p, f, sreg(0x1.e4cf5158b8ecap-28));
-    p = __fma_rn(p, f, sreg(0x1.b5253d395e7c4p-24));
-    p = __fma_rn(p, f, sreg(0x1.62c0223a5c824p-20));
-    p = __fma_rn(p, f, sreg(0x1.ffcbfc588b0c7p-17));
-    p = __fma_rn(p, f, sreg(0x1.430912f86c787p-13));
-    p = __fma_rn(p, f, sreg(0x1.5d87fe78a6731p-10));
-    p = __fma_rn(p, f, sreg(0x1.3b2ab6fba4e77p-7));
-    p = __fma_rn(p, f, sreg(0x1.c6b08d704a0c0p-5));
-    p = __fma_rn(p, f, sreg(0x1.ebfbdff82c58fp-3));
-    p = __fma_rn(p, f, sreg(0x1.62e42fefa39efp-1));
+    double p = coef(FIRST);
+#pragma unroll
+    for (int i = FIRST + 1; i < kExp2Terms; ++i) p = __fma_rn(p, f, coef(i));
     p = __fma_rn(p, f, 1.0);
     return __builtin_amdgcn_ldexp(p, (int)n);
 }
+
+__device__ __forceinline__ double exp2_f64(double y) { return exp2_f64_c(y, Exp2CoefConst{}); }
 
 // 1/d for a positive normal binary64 d whose reciprocal is normal: the hardware reciprocal
 // refined by two Newton steps
@@ -176,12 +185,19 @@ __device__ __forceinline__ double exp_neg_f64(double t) {
 // y is formed as x * C_hi + x * C_lo with C_hi = -log2(e) rounded to 29 significant bits (so the
 // first product of a binary32 x is exact) and C_lo the binary64 remainder; y is clamped to
 // [-1060, 1000], where sigma is 1 or far below the smallest binary32 subnormal either way.
-__device__ __forceinline__ double sigmoid_f64(float x) {
+template <int FIRST = 0, typename C>
+__device__ __forceinline__ double sigmoid_f64_c(float x, C coef) {
     const double xd = (double)x;
     double y = __fma_rn(xd, 0x1.a8fa03d1105e0p-29, xd * -0x1.7154766p+0);
     y = fmin(fmax(y, -1060.0), 1000.0);
-    return recip_f64(1.0 + exp2_f64(y));
+    return recip_f64(1.0 + exp2_f64_c<FIRST>(y, coef));
 }
+
+__device__ __forceinline__ double sigmoid_f64(float x) { return sigmoid_f64_c(x, Exp2CoefConst{}); }
+
+// sigma(x) in binary64 with relative error below 2^-30: the degree-8 exponential.  For routing
+// weights, which are compared at 1e-6 relative, not for selection keys.
+__device__ __forceinline__ double sigmoid_f64_weight(float x) { return sigmoid_f64_c<5>(x, Exp2CoefConst{}); }
 
 __device__ __forceinline__ float sigmoid_cr(float x) {
     const double s = sigmoid_f64(x);
@@ -194,8 +210,9 @@ __device__ __forceinline__ float sigmoid_cr(float x) {
 
 // The fast path alone: `ok` is false when the interval test cannot decide the binary32
 // rounding (about one value in 2^19); the caller then takes the exact path.
-__device__ __forceinline__ float sigmoid_cr_fast(float x, bool& ok) {
-    const double s = sigmoid_f64(x);
+template <typename C>
+__device__ __forceinline__ float sigmoid_cr_fast_c(float x, bool& ok, C coef) {
+    const double s = sigmoid_f64_c(x, coef);
     const double tol = s * 0x1p-44;
     const float lo = (float)(s - tol);
     const float hi = (float)(s + tol);
@@ -203,5 +220,8 @@ __device__ __forceinline__ float sigmoid_cr_fast(float x, bool& ok) {
     return lo;
 }
 
-}  // namespace mep
+__device__ __forceinline__ float sigmoid_cr_fast(float x, bool& ok) {
+    return sigmoid_cr_fast_c(x, ok, Exp2CoefConst{});
+}
 
+}  // namespace mep

@@ -172,7 +172,9 @@ def test_route_sigmoid_lane_groups(G, K, dtype):
     x[3::13, 1::5] = x[3::13, 0:1]                 # equal logits
     x[7::17] = np.float32(0.5) + np.float32(2.0 ** -20) * rng.integers(0, 4, (len(x[7::17]), E))  # near ties
     logits = synth.f32_to_bf16_bits(x) if dtype == synth.BF16 else x
-    for bias_scale in (0.1, 3.0):
+    # a bias beyond 2^20 in magnitude sends every token through the exact path (and makes keys
+    # tie: the sigmoid is absorbed by the bias)
+    for bias_scale in (0.1, 3.0, 2.0 ** 21):
         bias = rng.uniform(-bias_scale, bias_scale, E).astype(np.float32)
         for tg in sorted({1, max(1, G // 2), G}):
             if tg * 32 < K:

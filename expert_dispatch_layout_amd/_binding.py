@@ -46,7 +46,7 @@ class PlanOutputs(ctypes.Structure):
 
 
 EXPORTS = ("mep_route_topk", "mep_build_layout", "mep_layout_workspace_size", "mep_plan",
-           "mep_plan_workspace_size", "mep_status_string")
+           "mep_plan_workspace_size", "mep_layout_plan", "mep_status_string")
 
 _lib = None
 _lock = threading.Lock()
@@ -73,6 +73,9 @@ def lib():
                 L.mep_plan.restype = I
                 L.mep_plan_workspace_size.argtypes = [I64, I, I, I, I]
                 L.mep_plan_workspace_size.restype = SZ
+                L.mep_layout_plan.argtypes = [P, I64, I, I, I, P, P, P, P, I64, P,
+                                              I, I, I, I64, ctypes.POINTER(PlanOutputs), P, SZ, P]
+                L.mep_layout_plan.restype = I
                 L.mep_status_string.argtypes = [I]
                 L.mep_status_string.restype = ctypes.c_char_p
                 _lib = L
@@ -142,6 +145,89 @@ def mep_plan(topk_ids, cu_seqlens, expanded_to_permuted, E, alignment, R, num_sr
                         alignment, R, num_src, num_channels, NvS, ctypes.byref(po), _ptr(ws),
                         ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "mep_plan")
+
+
+# ---------------------------------------------------------------------------------------------
+# Prepared calls: the same entry points with their arguments converted once, for loops that
+# issue the same call many times (a zero-argument callable per call; each call checks the
+# return code).  Tensors must stay alive and in place while the callable is used.
+# ---------------------------------------------------------------------------------------------
+
+def _bound(fn_name, args, where):
+    fn = getattr(lib(), fn_name)
+    args = tuple(args)
+
+    def call():
+        rc = fn(*args)
+        if rc != MEP_OK:
+            raise MepError(rc, where)
+    return call
+
+
+def bound_route_topk(logits, K, bias, params: RouteParams, topk_ids, topk_weights=None, stream=None):
+    _require_cuda(logits, bias, topk_ids, topk_weights)
+    if logits.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("logits must be float32 or bfloat16")
+    dtype = MEP_BF16 if logits.dtype == torch.bfloat16 else MEP_F32
+    N, E = logits.shape
+    return _bound("mep_route_topk", (_ptr(logits), dtype, N, E, K, _ptr(bias), ctypes.byref(params),
+                                     _ptr(topk_ids), _ptr(topk_weights), _stream(stream)),
+                  "mep_route_topk")
+
+
+def bound_build_layout(topk_ids, E, alignment, tokens_per_expert, cu_seqlens, expanded_to_permuted,
+                       permuted_to_expanded, zero_fill, ws, stream=None):
+    _require_cuda(topk_ids, tokens_per_expert, cu_seqlens, expanded_to_permuted,
+                  permuted_to_expanded, zero_fill, ws)
+    N, K = topk_ids.shape
+    cap = permuted_to_expanded.numel() if permuted_to_expanded is not None else 0
+    return _bound("mep_build_layout", (_ptr(topk_ids), N, E, K, alignment, _ptr(tokens_per_expert),
+                                       _ptr(cu_seqlens), _ptr(expanded_to_permuted),
+                                       _ptr(permuted_to_expanded), cap, _ptr(zero_fill), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream(stream)),
+                  "mep_build_layout")
+
+
+def bound_plan(topk_ids, cu_seqlens, expanded_to_permuted, E, alignment, R, num_src, num_channels,
+               NvS, outputs: "PlanTensors", ws, stream=None):
+    _require_cuda(topk_ids, cu_seqlens, expanded_to_permuted, ws)
+    N, K = topk_ids.shape
+    po = outputs.as_struct()
+    call = _bound("mep_plan", (_ptr(topk_ids), _ptr(cu_seqlens), _ptr(expanded_to_permuted), N, E, K,
+                               alignment, R, num_src, num_channels, NvS, ctypes.byref(po), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(stream)), "mep_plan")
+    call.outputs = po  # keeps the struct referenced by the byref alive
+    return call
+
+
+def _layout_plan_args(topk_ids, E, alignment, layout, R, num_src, num_channels, NvS, po, ws, stream):
+    N, K = topk_ids.shape
+    cap = layout.permuted_to_expanded.numel() if layout.permuted_to_expanded is not None else 0
+    return (_ptr(topk_ids), N, E, K, alignment, _ptr(layout.tokens_per_expert), _ptr(layout.cu_seqlens),
+            _ptr(layout.expanded_to_permuted), _ptr(layout.permuted_to_expanded), cap,
+            _ptr(layout.zero_fill), R, num_src, num_channels, NvS, ctypes.byref(po), _ptr(ws),
+            ws.numel() * ws.element_size(), _stream(stream))
+
+
+def mep_layout_plan(topk_ids, E, alignment, layout: "LayoutTensors", R, num_src, num_channels, NvS,
+                    outputs: "PlanTensors", ws, stream=None):
+    """mep_build_layout + mep_plan in one call; `ws` is a plan workspace."""
+    _require_cuda(topk_ids, ws)
+    po = outputs.as_struct()
+    rc = lib().mep_layout_plan(*_layout_plan_args(topk_ids, E, alignment, layout, R, num_src,
+                                                  num_channels, NvS, po, ws, stream))
+    _check(rc, "mep_layout_plan")
+
+
+def bound_layout_plan(topk_ids, E, alignment, layout: "LayoutTensors", R, num_src, num_channels,
+                      NvS, outputs: "PlanTensors", ws, stream=None):
+    _require_cuda(topk_ids, ws)
+    po = outputs.as_struct()
+    call = _bound("mep_layout_plan", _layout_plan_args(topk_ids, E, alignment, layout, R, num_src,
+                                                       num_channels, NvS, po, ws, stream),
+                  "mep_layout_plan")
+    call.outputs = po
+    return call
 
 
 def layout_workspace_size(N, E, K) -> int:

@@ -24,6 +24,7 @@
 
 #include "device_common.h"
 #include "host_common.h"
+#include "calls.h"
 
 namespace mep {
 
@@ -35,13 +36,6 @@ constexpr int kMaxExperts = 1024;
 constexpr int kCountBlock = 1024;
 constexpr int kCountTiles = 32;                      // count tiles aimed at (parallelism vs look-back length)
 
-// Geometry: tiles of kLayTile slots (one workgroup each in both kernels); a count tile groups
-// `sub` consecutive tiles so that about kCountTiles count tiles take part in the look-back (one
-// window of predecessors).
-struct LayGeom {
-    int NK, E, nsub, sub, nct;
-    int ticketed;  // tiles in ticket order (when count tiles could outnumber resident groups)
-};
 
 // Only the last arriving workgroup of a count tile ever waits (on earlier count tiles).  With at
 // most this many count tiles, waiting workgroups can never fill the GPU, so every awaited one
@@ -63,16 +57,6 @@ static LayGeom lay_geom(int64_t NK, int E) {
     return g;
 }
 
-// Workspace of mep_build_layout after the header: arrival counters of count tiles (fixed place,
-// always left at zero), look-back words [nct][E], and the tagged histogram of every tile
-// [nsub][E].  Tagged words are written with single atomic stores and carry the call's epoch, so
-// a reader on another compute die needs no cache write-back fence: it re-reads until the tag is
-// current.
-struct LayWs {
-    uint32_t* arrive;
-    uint64_t* status;
-    uint64_t* tilehist;
-};
 
 // One tile per workgroup: LDS-privatised histogram (one LDS atomic per slot), written to the
 // workspace; the last tile of a count tile to arrive sums the count tile's histograms and takes
@@ -130,19 +114,11 @@ __global__ __launch_bounds__(kCountBlock) void layout_count_kernel(const int32_t
     }
 }
 
-struct LayoutOut {
-    int32_t* tokens_per_expert;
-    int32_t* cu_seqlens;
-    int32_t* e2p;
-    int32_t* p2e;
-    int32_t* zero_fill;
-    int p2e_cap;
-};
 
 template <int NB>
-__global__ __launch_bounds__(kScatBlock) void layout_scatter_kernel(const int32_t* __restrict__ ids,
-                                                                    LayGeom g, int A, LayWs lw,
-                                                                    WsHeader* hdr, LayoutOut out) {
+__global__ __launch_bounds__(kScatBlock) void layout_scatter_kernel(const int32_t* __restrict__ ids, int E,
+                                                                    int A, ScatterSrc src, WsHeader* hdr,
+                                                                    LayoutOut out) {
     constexpr int EPT = kMaxExperts / kScatBlock;  // experts per thread in the per-expert passes
     __shared__ int s_cu[kMaxExperts + 1];
     __shared__ int s_tot[kMaxExperts];
@@ -157,36 +133,64 @@ __global__ __launch_bounds__(kScatBlock) void layout_scatter_kernel(const int32_
     const int lane = tid & 63;
     const int w = tid >> 6;
     const int tile = blockIdx.x;
-    const int NK = g.NK, E = g.E, ntiles = g.nsub;
+    // the tile's slots [s_beg, s_end), its count tile and the source of the prefix data
+    int ntiles, s_beg, s_end, ct, first, nct, th_stride, th_off;
+    const uint64_t *status, *th;
+    if (!src.plan) {
+        const LayGeom& g = src.lg;
+        ntiles = g.nsub;
+        s_beg = tile * kLayTile;
+        s_end = min(s_beg + kLayTile, g.NK);
+        ct = tile / g.sub;
+        first = ct * g.sub;
+        nct = g.nct;
+        status = src.lw.status;
+        th = src.lw.tilehist;
+        th_stride = E;
+        th_off = 0;
+    } else {
+        const PlanGeom& g = src.pg;
+        ntiles = g.ntiles;
+        const int sh = tile / g.tps;
+        const int64_t t0 = (int64_t)sh * g.n + (int64_t)(tile - sh * g.tps) * g.TT;
+        const int64_t t1 = min(t0 + g.TT, (int64_t)(sh + 1) * g.n);
+        s_beg = (int)(t0 * g.K);
+        s_end = (int)(t1 * g.K);
+        ct = tile < ntiles ? ct_of(g, tile) : 0;
+        first = tile < ntiles ? ct_first_wt(g, ct) : 0;
+        nct = g.nct;
+        status = src.pw.statusE;
+        th = src.pw.tilehist;
+        th_stride = g.ncols;
+        th_off = 3 * g.R;
+    }
+    if (tile >= ntiles) s_end = s_beg;  // the single workgroup of an empty call
     const MEP_GLOBAL int32_t* gids = gptr(ids);
     MEP_GLOBAL int32_t* g_e2p = gptr(out.e2p);
     MEP_GLOBAL int32_t* g_p2e = gptr(out.p2e);
-    const int wbase = tile * kLayTile + w * kScatPerWave;
+    const int wbase = s_beg + w * kScatPerWave;
     int idv[kScatPerWave / kWave];  // this lane's ids, loaded first so the loads overlap the scan
 #pragma unroll
     for (int it = 0; it < kScatPerWave / kWave; ++it) {
         const int i = wbase + it * kWave + lane;
-        idv[it] = (tile < ntiles && i < NK) ? gids[i] : 0;
+        idv[it] = i < s_end ? gids[i] : 0;
     }
 
     // ---- per-expert totals and the slots of each expert before this tile, all loads issued
     // together: totals from the last count tile's inclusive prefix, earlier count tiles from the
-    // look-back, earlier scatter tiles of this count tile from their histograms
-    const int ct = tile / g.sub;
-    const int s0 = ct * g.sub;
-    const uint64_t* status = lw.status;
+    // look-back, earlier tiles of this count tile from their histograms
     int tot[EPT], pre[EPT];
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
         const int e = tid * EPT + q;
-        tot[q] = (e < E && ntiles > 0) ? (int)status_value(status, g.nct - 1, E, e) : 0;
+        tot[q] = (e < E && ntiles > 0) ? (int)status_value(status, nct - 1, E, e) : 0;
         pre[q] = (e < E && tile < ntiles && ct > 0) ? (int)status_value(status, ct - 1, E, e) : 0;
     }
-    for (int s2 = s0; s2 < tile && tile < ntiles; ++s2) {  // the earlier tiles of this count tile
+    for (int s2 = first; s2 < tile && tile < ntiles; ++s2) {  // the earlier tiles of this count tile
 #pragma unroll
         for (int q = 0; q < EPT; ++q) {
             const int e = tid * EPT + q;
-            if (e < E) pre[q] += (int)status_value(lw.tilehist, s2, E, e);
+            if (e < E) pre[q] += (int)status_value(th, s2, th_stride, th_off + e);
         }
     }
     int pad[EPT];
@@ -223,7 +227,7 @@ __global__ __launch_bounds__(kScatBlock) void layout_scatter_kernel(const int32_
         for (int it = 0; it < kScatPerWave / kWave; ++it) {
             const int i = wbase + it * kWave + lane;
             int k = idv[it];
-            const bool valid = i < NK && (unsigned)k < (unsigned)E;
+            const bool valid = i < s_end && (unsigned)k < (unsigned)E;
             if (!valid) k = 0;
             const uint64_t active = __ballot(valid);
             const uint64_t peers = match_peers<NB>((uint32_t)k, active);
@@ -311,7 +315,7 @@ __global__ __launch_bounds__(kScatBlock) void layout_scatter_kernel(const int32_
                 gptr(out.zero_fill)[2 * e + 1] = z ? padded - cnt : 0;
             }
         }
-        if (tid == 0) {
+        if (tid == 0 && !src.plan) {  // (the plan's writing pass resets its own workspace)
             MEP_GLOBAL WsHeader* h = gptr(hdr);
             h->epoch = h->epoch + 1u;
             h->ticket = 0u;
@@ -342,46 +346,101 @@ extern "C" size_t mep_layout_workspace_size(int64_t N, int E, int K) {
     return lay_ws_layout(lay_geom(N * (int64_t)K, E)).bytes;
 }
 
-extern "C" int mep_build_layout(const int32_t* topk_ids, int64_t N, int E, int K, int alignment,
-                                int32_t* tokens_per_expert, int32_t* cu_seqlens,
-                                int32_t* expanded_to_permuted, int32_t* permuted_to_expanded,
-                                int64_t permuted_cap, int32_t* zero_fill, void* ws, size_t ws_bytes,
-                                void* stream) {
-    using namespace mep;
-    if (!cu_seqlens || !ws) return MEP_ERR_INVALID_ARG;
+namespace mep {
+
+// Checks of mep_build_layout's ids and outputs, and the launch arguments that do not involve
+// its workspace; MEP_OK or the error code.
+int layout_prepare_outputs(const int32_t* topk_ids, int64_t N, int E, int K, int alignment,
+                           int32_t* tokens_per_expert, int32_t* cu_seqlens, int32_t* expanded_to_permuted,
+                           int32_t* permuted_to_expanded, int64_t permuted_cap, int32_t* zero_fill,
+                           LayoutCall& c) {
+    if (!cu_seqlens) return MEP_ERR_INVALID_ARG;
     if (N > 0 && (!topk_ids || !expanded_to_permuted)) return MEP_ERR_INVALID_ARG;  // N == 0 reads nothing
     if (N < 0 || E < 1 || K < 1 || alignment < 1) return MEP_ERR_INVALID_ARG;
     const void* ptrs[] = {topk_ids, tokens_per_expert, cu_seqlens, expanded_to_permuted,
                           permuted_to_expanded, zero_fill};
     for (const void* q : ptrs)
         if (q && !aligned(q, 4)) return MEP_ERR_INVALID_ARG;
-    if (!aligned(ws, 256)) return MEP_ERR_INVALID_ARG;
     if (E > kMaxExperts || K > 32 || K > E) return MEP_ERR_UNSUPPORTED;
     const int64_t NK = N * (int64_t)K;
     const int64_t bound = NK + (NK < E ? NK : (int64_t)E) * (int64_t)(alignment - 1);
     if (bound > INT32_MAX - (1 << 16)) return MEP_ERR_UNSUPPORTED;
     if (permuted_to_expanded && permuted_cap < bound) return MEP_ERR_CAPACITY;
-    if (ws_bytes < mep_layout_workspace_size(N, E, K)) return MEP_ERR_CAPACITY;
+    c.g = lay_geom(NK, E);
+    c.ids = topk_ids;
+    c.A = alignment;
+    c.hdr = nullptr;
+    c.lw = LayWs{nullptr, nullptr, nullptr};
+    c.out = LayoutOut{tokens_per_expert, cu_seqlens, expanded_to_permuted, permuted_to_expanded, zero_fill,
+                      permuted_to_expanded ? (int)(permuted_cap < INT32_MAX ? permuted_cap : INT32_MAX) : 0};
+    return MEP_OK;
+}
 
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const LayGeom g = lay_geom(NK, E);
-    WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
-    const LayWsLayout wl = lay_ws_layout(g);
+// All checks of mep_build_layout and its launch arguments.
+int layout_prepare(const int32_t* topk_ids, int64_t N, int E, int K, int alignment,
+                   int32_t* tokens_per_expert, int32_t* cu_seqlens, int32_t* expanded_to_permuted,
+                   int32_t* permuted_to_expanded, int64_t permuted_cap, int32_t* zero_fill, void* ws,
+                   size_t ws_bytes, LayoutCall& c) {
+    if (!ws) return MEP_ERR_INVALID_ARG;
+    const int rc = layout_prepare_outputs(topk_ids, N, E, K, alignment, tokens_per_expert, cu_seqlens,
+                                          expanded_to_permuted, permuted_to_expanded, permuted_cap, zero_fill, c);
+    if (rc != MEP_OK) return rc;
+    if (!aligned(ws, 256)) return MEP_ERR_INVALID_ARG;
+    if (ws_bytes < mep_layout_workspace_size(N, E, K)) return MEP_ERR_CAPACITY;
+    c.hdr = reinterpret_cast<WsHeader*>(ws);
+    const LayWsLayout wl = lay_ws_layout(c.g);
     char* wb = reinterpret_cast<char*>(ws);
-    const LayWs lw{reinterpret_cast<uint32_t*>(wb + wl.arrive), reinterpret_cast<uint64_t*>(wb + wl.status),
-                   reinterpret_cast<uint64_t*>(wb + wl.tilehist)};
-    if (g.nsub > 0)
-        hipLaunchKernelGGL(layout_count_kernel, dim3(g.nsub), dim3(kCountBlock), 0, st, topk_ids, g, lw, hdr);
-    LayoutOut out{tokens_per_expert, cu_seqlens, expanded_to_permuted, permuted_to_expanded, zero_fill,
-                  permuted_to_expanded ? (int)(permuted_cap < INT32_MAX ? permuted_cap : INT32_MAX) : 0};
-    const dim3 sgrid(g.nsub > 0 ? g.nsub : 1), sblock(kScatBlock);
+    c.lw = LayWs{reinterpret_cast<uint32_t*>(wb + wl.arrive), reinterpret_cast<uint64_t*>(wb + wl.status),
+                 reinterpret_cast<uint64_t*>(wb + wl.tilehist)};
+    return MEP_OK;
+}
+
+static void launch_scatter(const LayoutCall& c, const ScatterSrc& src, int ntiles, WsHeader* hdr,
+                           hipStream_t st) {
+    const dim3 sgrid(ntiles > 0 ? ntiles : 1), sblock(kScatBlock);
+    const int E = c.g.E;
     if (E <= 16)
-        hipLaunchKernelGGL(layout_scatter_kernel<4>, sgrid, sblock, 0, st, topk_ids, g, alignment, lw, hdr, out);
+        hipLaunchKernelGGL(layout_scatter_kernel<4>, sgrid, sblock, 0, st, c.ids, E, c.A, src, hdr, c.out);
     else if (E <= 64)
-        hipLaunchKernelGGL(layout_scatter_kernel<6>, sgrid, sblock, 0, st, topk_ids, g, alignment, lw, hdr, out);
+        hipLaunchKernelGGL(layout_scatter_kernel<6>, sgrid, sblock, 0, st, c.ids, E, c.A, src, hdr, c.out);
     else if (E <= 256)
-        hipLaunchKernelGGL(layout_scatter_kernel<8>, sgrid, sblock, 0, st, topk_ids, g, alignment, lw, hdr, out);
+        hipLaunchKernelGGL(layout_scatter_kernel<8>, sgrid, sblock, 0, st, c.ids, E, c.A, src, hdr, c.out);
     else
-        hipLaunchKernelGGL(layout_scatter_kernel<10>, sgrid, sblock, 0, st, topk_ids, g, alignment, lw, hdr, out);
+        hipLaunchKernelGGL(layout_scatter_kernel<10>, sgrid, sblock, 0, st, c.ids, E, c.A, src, hdr, c.out);
+}
+
+void layout_launch(const LayoutCall& c, hipStream_t st) {
+    const LayGeom& g = c.g;
+    if (g.nsub > 0)
+        hipLaunchKernelGGL(layout_count_kernel, dim3(g.nsub), dim3(kCountBlock), 0, st, c.ids, g, c.lw, c.hdr);
+    ScatterSrc src{};
+    src.plan = 0;
+    src.lg = g;
+    src.lw = c.lw;
+    launch_scatter(c, src, g.nsub, c.hdr, st);
+}
+
+void layout_launch_scatter_from_plan(const LayoutCall& lc, const PlanCall& pc, hipStream_t st) {
+    ScatterSrc src{};
+    src.plan = 1;
+    src.pg = pc.g;
+    src.pw = pc.pw;
+    launch_scatter(lc, src, pc.g.ntiles, pc.hdr, st);
+}
+
+}  // namespace mep
+
+extern "C" int mep_build_layout(const int32_t* topk_ids, int64_t N, int E, int K, int alignment,
+                                int32_t* tokens_per_expert, int32_t* cu_seqlens,
+                                int32_t* expanded_to_permuted, int32_t* permuted_to_expanded,
+                                int64_t permuted_cap, int32_t* zero_fill, void* ws, size_t ws_bytes,
+                                void* stream) {
+    using namespace mep;
+    LayoutCall c;
+    const int rc = layout_prepare(topk_ids, N, E, K, alignment, tokens_per_expert, cu_seqlens,
+                                  expanded_to_permuted, permuted_to_expanded, permuted_cap, zero_fill, ws,
+                                  ws_bytes, c);
+    if (rc != MEP_OK) return rc;
+    layout_launch(c, reinterpret_cast<hipStream_t>(stream));
     return launch_status();
 }

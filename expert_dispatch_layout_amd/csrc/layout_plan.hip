@@ -1,0 +1,29 @@
+// mep_layout_plan: the layout and the plan of one batch in one call, three kernels instead of
+// four: the plan's counting pass also takes the per-expert counts of its tiles through a
+// look-back, which gives the layout's totals and prefixes, so the layout's own counting pass is
+// not needed; the layout's scatter pass then runs over the plan's tiles, and the plan's writing
+// pass follows.  The results are those of mep_build_layout followed by mep_plan.
+#include "calls.h"
+#include "host_common.h"
+
+extern "C" int mep_layout_plan(const int32_t* topk_ids, int64_t N, int E, int K, int alignment,
+                               int32_t* tokens_per_expert, int32_t* cu_seqlens, int32_t* expanded_to_permuted,
+                               int32_t* permuted_to_expanded, int64_t permuted_cap, int32_t* zero_fill, int R,
+                               int num_src, int num_channels, int64_t NvS, const mep_plan_outputs* out, void* ws,
+                               size_t ws_bytes, void* stream) {
+    using namespace mep;
+    PlanCall pc;
+    int rc = plan_prepare(topk_ids, cu_seqlens, expanded_to_permuted, N, E, K, alignment, R, num_src, num_channels,
+                          NvS, out, ws, ws_bytes, pc);
+    if (rc != MEP_OK) return rc;
+    // the layout's checks and outputs; its workspace is not used (the plan's serves both)
+    LayoutCall lc;
+    rc = layout_prepare_outputs(topk_ids, N, E, K, alignment, tokens_per_expert, cu_seqlens, expanded_to_permuted,
+                                permuted_to_expanded, permuted_cap, zero_fill, lc);
+    if (rc != MEP_OK) return rc;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    plan_launch_count(pc, st);
+    layout_launch_scatter_from_plan(lc, pc, st);
+    plan_launch_write(pc, st);
+    return launch_status();
+}

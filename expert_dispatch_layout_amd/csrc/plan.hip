@@ -27,6 +27,7 @@
 
 #include "device_common.h"
 #include "host_common.h"
+#include "calls.h"
 
 namespace mep {
 
@@ -51,24 +52,7 @@ static int plan_tile_tokens(int K) {
     return tt > kPlanBlock ? kPlanBlock : tt;
 }
 
-// Write tiles: TT tokens, never crossing a shard (tps per shard, ntiles in all).  Count tiles:
-// `sub` consecutive write tiles of one shard (ctps per shard, nct in all).
-struct PlanGeom {
-    int N, E, K, R, epn, S, n, tps, ntiles, TT, ncols, C;
-    int sub, ctps, nct;
-    int ticketed;  // write tiles in ticket order (when count tiles could outnumber resident groups)
-    int64_t NvS;
-};
 
-// count tile of write tile wt, and the first write tile of that count tile
-__device__ __forceinline__ int ct_of(const PlanGeom& g, int wt) {
-    const int sh = wt / g.tps;
-    return sh * g.ctps + (wt - sh * g.tps) / g.sub;
-}
-__device__ __forceinline__ int ct_first_wt(const PlanGeom& g, int ct) {
-    const int sh = ct / g.ctps;
-    return sh * g.tps + (ct - sh * g.ctps) * g.sub;
-}
 
 // Per-token view: owner ranks, hit counts and first-occurrence flags of its K slots.
 template <int KMAX>
@@ -162,23 +146,12 @@ struct RankMask {
     }
 };
 
-// Workspace of mep_plan after the header: arrival counters of count tiles (fixed place, always
-// left at zero), look-back words of the rank columns [nct][3R], tagged expert aggregates
-// [nct][E], and the tagged histograms of every write tile [ntiles][3R+E].
-// Tagged words are written with single atomic stores and carry the call's epoch, so a reader on
-// another compute die needs no cache write-back fence: it re-reads until the tag is current.
-struct PlanWs {
-    uint32_t* arrive;
-    uint64_t* status3;
-    uint64_t* statusE;
-    uint64_t* tilehist;
-};
 
 constexpr int kMaxCountTiles = 2048;
 
 // One write tile per workgroup.  Each writes its histograms; the last of the write tiles of a
-// count tile to arrive sums them, publishes the count tile's expert aggregates and takes its rank
-// columns through the look-back.
+// count tile to arrive sums them and takes the rank columns and the expert columns through the
+// look-back (the expert prefixes also serve the layout in mep_layout_plan).
 template <int KMAX, int RW>
 __global__ __launch_bounds__(kPlanBlock) void plan_count_kernel(const int32_t* __restrict__ ids,
                                                                 PlanGeom g, PlanWs w, WsHeader* hdr,
@@ -282,27 +255,10 @@ __global__ __launch_bounds__(kPlanBlock) void plan_count_kernel(const int32_t* _
                 if (b0 + b < nsub_here) agg += tagged_value(w.tilehist + (size_t)(wt0 + b0 + b) * nc + c, v[b], want);
         }
         if (c < n3) lookback_column(w.status3, ct, n3, c, epoch, agg);
-        else status_store(w.statusE + (size_t)ct * E + (c - n3), status_make(epoch, false, agg));
+        else lookback_column(w.statusE, ct, E, c - n3, epoch, agg);
     }
 }
 
-struct PlanOutDev {
-    uint8_t* itr;
-    int32_t* ntpr;
-    int32_t* ntpe;
-    int32_t* rank_prefix;
-    int32_t* chan;
-    int32_t* recv_tokens;
-    int32_t* recv_cu;
-    int32_t* recv_zf;
-    int32_t* dst;
-    int32_t* dup_counts;
-    int32_t* dup_offsets;
-    int32_t* dup_groups;
-    int64_t cap_g;
-    int32_t* dup_loffs;
-    int64_t cap_d;
-};
 
 enum : uint32_t { kNone = 0, kHead = 1, kDup = 2 };
 
@@ -537,27 +493,18 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
         }
     }
 
-    // ---- per-shard expert counts and expert totals, a slice of the experts per workgroup: sums
-    // of the count tiles' expert aggregates (written by the count kernel)
+    // ---- per-shard expert counts and expert totals, a slice of the experts per workgroup:
+    // differences of the expert look-back's inclusive prefixes at the shards' last count tiles
     if (g.ntiles > 0) {
         for (int e = blockIdx.x + (tid / 64) * gridDim.x; e < g.E; e += gridDim.x * kPlanWaves) {
-            // one wave per expert: lane j sums the count tiles of shards j, j + 64, ...
-            int tot = 0;
+            // one wave per expert: lane j takes shards j, j + 64, ...
             for (int s2 = lane; s2 < g.S; s2 += 64) {
-                int part = 0;
-                for (int c0 = s2 * g.ctps; c0 < (s2 + 1) * g.ctps; c0 += 4) {
-                    int v[4];
-#pragma unroll
-                    for (int b = 0; b < 4; ++b)
-                        v[b] = c0 + b < (s2 + 1) * g.ctps ? (int)status_value(pw.statusE, c0 + b, g.E, e) : 0;
-                    part += v[0] + v[1] + v[2] + v[3];
-                }
-                if (o.ntpe) gptr(o.ntpe)[(int64_t)s2 * g.E + e] = part;
-                tot += part;
+                const int hi = (int)status_value(pw.statusE, (s2 + 1) * g.ctps - 1, g.E, e);
+                const int lo = s2 > 0 ? (int)status_value(pw.statusE, s2 * g.ctps - 1, g.E, e) : 0;
+                if (o.ntpe) gptr(o.ntpe)[(int64_t)s2 * g.E + e] = hi - lo;
             }
-            tot = wave_sum_i32(tot);
             if (o.recv_zf && lane == 0) {
-                const int cnt = tot;
+                const int cnt = (int)status_value(pw.statusE, g.nct - 1, g.E, e);
                 const int padded = cu_seqlens[e + 1] - cu_seqlens[e];
                 const bool z = cnt > 0 && padded > cnt;
                 gptr(o.recv_zf)[2 * e] = z ? cu_seqlens[e] + cnt - cu_seqlens[s_owner[e] * g.epn] : 0;
@@ -661,11 +608,12 @@ extern "C" size_t mep_plan_workspace_size(int64_t N, int E, int K, int R, int nu
     return plan_ws_layout(plan_geom(N, E, K, R, num_src, 1, 0)).bytes;
 }
 
-extern "C" int mep_plan(const int32_t* topk_ids, const int32_t* cu_seqlens,
-                        const int32_t* expanded_to_permuted, int64_t N, int E, int K, int alignment,
-                        int R, int num_src, int num_channels, int64_t NvS, const mep_plan_outputs* out,
-                        void* ws, size_t ws_bytes, void* stream) {
-    using namespace mep;
+namespace mep {
+
+// Checks of mep_plan and the launch arguments; MEP_OK or the error code.
+int plan_prepare(const int32_t* topk_ids, const int32_t* cu_seqlens, const int32_t* expanded_to_permuted,
+                 int64_t N, int E, int K, int alignment, int R, int num_src, int num_channels, int64_t NvS,
+                 const mep_plan_outputs* out, void* ws, size_t ws_bytes, PlanCall& c) {
     if (!cu_seqlens || !out || !ws) return MEP_ERR_INVALID_ARG;
     if (N > 0 && (!topk_ids || !expanded_to_permuted)) return MEP_ERR_INVALID_ARG;  // N == 0 reads nothing
     if (N < 0 || E < 1 || K < 1 || R < 1 || num_src < 1 || num_channels < 1 || alignment < 1)
@@ -695,33 +643,70 @@ extern "C" int mep_plan(const int32_t* topk_ids, const int32_t* cu_seqlens,
     if (out->dup_loffs && out->cap_dups < d_max) return MEP_ERR_CAPACITY;
     if (ws_bytes < mep_plan_workspace_size(N, E, K, R, num_src)) return MEP_ERR_CAPACITY;
 
-    PlanGeom g = plan_geom(N, E, K, R, num_src, num_channels, NvS);
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
-    const PlanWsLayout L = plan_ws_layout(g);
+    c.g = plan_geom(N, E, K, R, num_src, num_channels, NvS);
+    c.ids = topk_ids;
+    c.cu = cu_seqlens;
+    c.e2p = expanded_to_permuted;
+    c.hdr = reinterpret_cast<WsHeader*>(ws);
+    const PlanWsLayout L = plan_ws_layout(c.g);
     char* wsb = reinterpret_cast<char*>(ws);
-    const PlanWs pw{reinterpret_cast<uint32_t*>(wsb + L.arrive), reinterpret_cast<uint64_t*>(wsb + L.status3),
-                    reinterpret_cast<uint64_t*>(wsb + L.statusE), reinterpret_cast<uint64_t*>(wsb + L.tilehist)};
-    PlanOutDev o{out->is_token_in_rank, out->num_tokens_per_rank, out->num_tokens_per_expert,
-                 out->rank_prefix_matrix, out->channel_prefix_matrix, out->recv_tokens,
-                 out->recv_cu_seqlens, out->recv_zero_fill, out->dst, out->dup_counts,
-                 out->dup_offsets, out->dup_groups, out->cap_groups, out->dup_loffs, out->cap_dups};
-    const int grid = g.ntiles > 0 ? g.ntiles : 1;
-    auto launch = [&](auto count_kernel, auto write_kernel) {
-        if (g.ntiles > 0)
-            hipLaunchKernelGGL(count_kernel, dim3(g.ntiles), dim3(kPlanBlock), 0, st, topk_ids, g, pw, hdr,
-                               o.itr);
-        hipLaunchKernelGGL(write_kernel, dim3(grid), dim3(kPlanBlock), 0, st, topk_ids, cu_seqlens,
-                           expanded_to_permuted, g, pw, hdr, o);
+    c.pw = PlanWs{reinterpret_cast<uint32_t*>(wsb + L.arrive), reinterpret_cast<uint64_t*>(wsb + L.status3),
+                  reinterpret_cast<uint64_t*>(wsb + L.statusE), reinterpret_cast<uint64_t*>(wsb + L.tilehist)};
+    c.o = PlanOutDev{out->is_token_in_rank, out->num_tokens_per_rank, out->num_tokens_per_expert,
+                     out->rank_prefix_matrix, out->channel_prefix_matrix, out->recv_tokens,
+                     out->recv_cu_seqlens, out->recv_zero_fill, out->dst, out->dup_counts,
+                     out->dup_offsets, out->dup_groups, out->cap_groups, out->dup_loffs, out->cap_dups};
+    return MEP_OK;
+}
+
+// The counting pass (reads the ids only) and the writing pass (also the layout's cu_seqlens and
+// expanded_to_permuted), launched separately so that the counting pass can run alongside the
+// layout kernels.
+void plan_launch_count(const PlanCall& c, hipStream_t st) {
+    const PlanGeom& g = c.g;
+    if (g.ntiles == 0) return;
+    auto launch = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(g.ntiles), dim3(kPlanBlock), 0, st, c.ids, g, c.pw, c.hdr, c.o.itr);
     };
-    if (K <= 8) {
-        if (R <= 8) launch(plan_count_kernel<8, 1>, plan_write_kernel<8, 3>);
-        else if (R <= 32) launch(plan_count_kernel<8, 1>, plan_write_kernel<8, 5>);
-        else launch(plan_count_kernel<8, 4>, plan_write_kernel<8, 7>);
+    if (g.K <= 8) {
+        if (g.R <= 32) launch(plan_count_kernel<8, 1>);
+        else launch(plan_count_kernel<8, 4>);
     } else {
-        if (R <= 8) launch(plan_count_kernel<32, 1>, plan_write_kernel<32, 3>);
-        else if (R <= 32) launch(plan_count_kernel<32, 1>, plan_write_kernel<32, 5>);
-        else launch(plan_count_kernel<32, 4>, plan_write_kernel<32, 7>);
+        if (g.R <= 32) launch(plan_count_kernel<32, 1>);
+        else launch(plan_count_kernel<32, 4>);
     }
+}
+
+void plan_launch_write(const PlanCall& c, hipStream_t st) {
+    const PlanGeom& g = c.g;
+    const int grid = g.ntiles > 0 ? g.ntiles : 1;
+    auto launch = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kPlanBlock), 0, st, c.ids, c.cu, c.e2p, g, c.pw, c.hdr, c.o);
+    };
+    if (g.K <= 8) {
+        if (g.R <= 8) launch(plan_write_kernel<8, 3>);
+        else if (g.R <= 32) launch(plan_write_kernel<8, 5>);
+        else launch(plan_write_kernel<8, 7>);
+    } else {
+        if (g.R <= 8) launch(plan_write_kernel<32, 3>);
+        else if (g.R <= 32) launch(plan_write_kernel<32, 5>);
+        else launch(plan_write_kernel<32, 7>);
+    }
+}
+
+}  // namespace mep
+
+extern "C" int mep_plan(const int32_t* topk_ids, const int32_t* cu_seqlens,
+                        const int32_t* expanded_to_permuted, int64_t N, int E, int K, int alignment,
+                        int R, int num_src, int num_channels, int64_t NvS, const mep_plan_outputs* out,
+                        void* ws, size_t ws_bytes, void* stream) {
+    using namespace mep;
+    PlanCall c;
+    const int rc = plan_prepare(topk_ids, cu_seqlens, expanded_to_permuted, N, E, K, alignment, R, num_src,
+                                num_channels, NvS, out, ws, ws_bytes, c);
+    if (rc != MEP_OK) return rc;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    plan_launch_count(c, st);
+    plan_launch_write(c, st);
     return launch_status();
 }

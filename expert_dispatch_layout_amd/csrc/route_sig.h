@@ -248,7 +248,9 @@ __device__ __noinline__ void exact_token_sig(const RouteArgs a, const u32x4* row
 // ---- the kernel -----------------------------------------------------------------------------------
 
 // MODE 0: no group limit; MODE 1: lane lseg of a segment is group lseg (n_group == LPT).
-// NW waves per workgroup, each independent after the prologue.
+// NW waves per workgroup, each independent after the prologue.  A workgroup owns a contiguous
+// range of sets and its waves take them one at a time from an LDS counter, so a wave that spends
+// time on an uncertified token takes fewer sets and the workgroup still finishes with its peers.
 template <int LPT, bool BF16, int MODE, int NW>
 __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_kernel(RouteArgs a, SigCfg cfg) {
     using G = SigGeom<LPT, BF16>;
@@ -274,11 +276,16 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
     const int tw = wl / LPT;
     const int lseg = wl % LPT;
     const int K = a.K;
-    const int64_t waves = (int64_t)gridDim.x * NW;
-    const int64_t first_set = (int64_t)blockIdx.x * NW + wv;
+    // this workgroup's sets [set_lo, set_hi); wave wv starts with set_lo + wv
+    const int64_t spb = (cfg.nsets + gridDim.x - 1) / gridDim.x;
+    const int64_t set_lo = (int64_t)blockIdx.x * spb;
+    const int64_t set_hi = min(set_lo + spb, cfg.nsets);
+    const int64_t first_set = set_lo + wv;
+    __shared__ int s_next;  // next unclaimed set of this workgroup, relative to set_lo
+    if (tid == 0) s_next = NW;
 
     u32x4 buf[CPL];
-    if (first_set < cfg.nsets) fast_load_set<LPT, BF16>(a, first_set, wl, buf);
+    if (first_set < set_hi) fast_load_set<LPT, BF16>(a, first_set, wl, buf);
 
     // ---- shift c, the error-bound constants, and the shifted biases --------------------------------
     const MEP_GLOBAL float* gb = gptr(a.bias);
@@ -338,7 +345,8 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
         }
     };
 
-    for (int64_t set = first_set; set < cfg.nsets; set += waves) {
+    int64_t next_set = first_set;
+    for (int64_t set = first_set; set < set_hi; set = next_set) {
         // ---- registers -> this wave's LDS rows; refill with the next set --------------------------
         wave_lds_sync();
 #pragma unroll
@@ -347,7 +355,12 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
             const int r = q / CPR;
             my_rows[r * RS + G::pos(q - r * CPR)] = buf[cc];
         }
-        if (set + waves < cfg.nsets) fast_load_set<LPT, BF16>(a, set + waves, wl, buf);
+        {
+            int claimed = 0;
+            if (wl == 0) claimed = atomicAdd(&s_next, 1);
+            next_set = set_lo + __builtin_amdgcn_readfirstlane(claimed);
+        }
+        if (next_set < set_hi) fast_load_set<LPT, BF16>(a, next_set, wl, buf);
         wave_lds_sync();
 
         const int tok_raw = (int)set * TPW + tw;  // N * K < 2^31

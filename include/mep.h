@@ -11,6 +11,8 @@
  *   mep_plan         ids + layout -> expert-parallel plan over R virtual
  *                    ranks (membership, counts, prefix matrices, rank-tagged
  *                    destinations with duplicate encoding, dedup lists)
+ *   mep_layout_plan  the two calls above in one (three kernels instead of
+ *                    four)
  *
  * Sources, cited by page title and section:
  *   [TRT]  TensorRT-LLM RoutingKernel.cuh (blockScaleMoe routing helpers,
@@ -226,6 +228,27 @@ int mep_plan(const int32_t* topk_ids, const int32_t* cu_seqlens,
              const mep_plan_outputs* out, void* ws, size_t ws_bytes, void* stream);
 
 size_t mep_plan_workspace_size(int64_t N, int E, int K, int R, int num_src);
+
+/*
+ * mep_layout_plan -- mep_build_layout followed by mep_plan in one call, with
+ * the results of the two calls and the checks of both (the layout's
+ * cu_seqlens and expanded_to_permuted are outputs of the first part and inputs
+ * of the second, so both are required).  Three kernels instead of four: the
+ * plan's counting pass also produces the per-expert totals and prefixes the
+ * layout needs, so the layout's own counting pass is not run.
+ *
+ * Arguments as mep_build_layout (without its workspace) and mep_plan; `ws` is
+ * a workspace of mep_plan_workspace_size(N, E, K, R, num_src) bytes, the only
+ * scratch of the call, with the rules of every workspace (zero-filled before
+ * first use, calls sharing it ordered).  It may be shared with mep_plan calls
+ * but not with mep_build_layout calls.
+ */
+int mep_layout_plan(const int32_t* topk_ids, int64_t N, int E, int K, int alignment,
+                    int32_t* tokens_per_expert, int32_t* cu_seqlens,
+                    int32_t* expanded_to_permuted, int32_t* permuted_to_expanded,
+                    int64_t permuted_cap, int32_t* zero_fill, int R, int num_src,
+                    int num_channels, int64_t NvS, const mep_plan_outputs* out, void* ws,
+                    size_t ws_bytes, void* stream);
 
 /* Static, NUL-terminated name of a return code. */
 const char* mep_status_string(int code);

@@ -43,10 +43,21 @@ def gpu_route(logits, K, dtype, *, bias=None, score_fn=0, renormalize=True, n_gr
     return ids.cpu().numpy(), w.cpu().numpy()
 
 
-def gpu_layout_plan(ids_np, E, A, R, S, C, NvS=None):
+def gpu_layout_plan(ids_np, E, A, R, S, C, NvS=None, combined=False, ws=None):
+    """Layout and plan through the two calls, or through mep_layout_plan (`combined`); `ws` is an
+    optional (layout, plan) workspace pair to reuse."""
     ids = torch.from_numpy(np.ascontiguousarray(ids_np, np.int32)).to(DEV)
-    L = B.build_layout(ids, E, A)
-    P = B.plan(ids, L.cu_seqlens, L.expanded_to_permuted, E, A, R, S, C, NvS=NvS)
+    if not combined:
+        L = B.build_layout(ids, E, A, ws=ws[0] if ws else None)
+        P = B.plan(ids, L.cu_seqlens, L.expanded_to_permuted, E, A, R, S, C, NvS=NvS,
+                   ws=ws[1] if ws else None)
+    else:
+        N, K = ids.shape
+        L = B.alloc_layout(N, E, K, A, DEV)
+        P = B.alloc_plan(N, E, K, R, S, C, DEV)
+        wp_ = ws[1] if ws else B.alloc_workspace(B.plan_workspace_size(N, E, K, R, S), DEV)
+        nvs = NvS if NvS is not None else B.default_nvs(N, E, K, R, A)
+        B.mep_layout_plan(ids, E, A, L, R, S, C, nvs, P, wp_)
     torch.cuda.synchronize()
     return L, P
 
@@ -67,12 +78,12 @@ def check_route(inp_logits, K, dtype, **kw):
     return ids_o, float(err.max(initial=0.0))
 
 
-def check_layout_plan(ids, E, A, R, S, C, NvS=None):
+def check_layout_plan(ids, E, A, R, S, C, NvS=None, combined=False, ws=None):
     N, K = ids.shape
     epn = E // R
     if NvS is None:
         NvS = N * min(K, epn) + epn * (A - 1)
-    Lg, Pg = gpu_layout_plan(ids, E, A, R, S, C, NvS)
+    Lg, Pg = gpu_layout_plan(ids, E, A, R, S, C, NvS, combined=combined, ws=ws)
     Lo = oracle.layout(ids, E, A)
     T = int(Lo.cu_seqlens[E])
     assert np.array_equal(_np(Lg.tokens_per_expert), Lo.tokens_per_expert)
@@ -111,6 +122,22 @@ def test_workload_full_path(name):
     _note("  layout + plan ok (S=%d)" % wl.S)
     check_layout_plan(ids, wl.E, wl.alignment, wl.R, 1, wl.num_channels)
     _note("  layout + plan ok (S=1)")
+    check_layout_plan(ids, wl.E, wl.alignment, wl.R, wl.S, wl.num_channels, combined=True)
+    _note("  combined layout + plan ok")
+
+
+def test_layout_plan_combined_reuse_across_sizes():
+    """mep_layout_plan on one workspace, sized for the largest call, over calls of shrinking and
+    growing size, each checked against the oracle."""
+    E, K, A, R, S, C = 256, 8, 128, 8, 8, 24
+    big = 8192
+    ws = (B.alloc_workspace(B.layout_workspace_size(big, E, K), DEV),
+          B.alloc_workspace(B.plan_workspace_size(big, E, K, R, S), DEV))
+    rng = np.random.default_rng(77)
+    for N in (8192, 8, 4096, 1, 8192, 808):
+        ids = np.argsort(rng.random((N, E)), axis=1)[:, :K].astype(np.int32)
+        _note("combined N=%d" % N)
+        check_layout_plan(ids, E, A, R, S if N % S == 0 else 1, C, combined=True, ws=ws)
 
 
 # -------------------------------------------------------------------------------------------

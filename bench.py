@@ -10,8 +10,8 @@ Input and output buffers rotate over several distinct sets (together larger than
 Infinity Cache) so every step reads logits from HBM, not from the last-level cache.
 
 Prints one JSON line.  `roofline` describes the dominant kernel (routing): algorithmic bytes per
-launch / its average duration, timed with HIP events on the launch stream inside the timed
-region.  `cpu_baseline` is the CPU oracle timed on this host on a bounded sample.
+launch / its average duration, timed inside the timed region with HIP events that the kernel's
+launch on the bench stream stamps itself (mep_route_topk_timed).  `cpu_baseline` is the CPU oracle timed on this host on a bounded sample.
 """
 from __future__ import annotations
 
@@ -37,6 +37,13 @@ def parse():
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time for the oracle baseline (0 disables it)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, copy MIB mebibytes device to device three times "
+                         "(a plain copy kernel of known size, to scale HBM counters)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: read two rocprofv3 counter CSVs (FETCH_SIZE, WRITE_SIZE) of "
+                         "runs with --copy-calibration MIB (give the same MIB here) and write "
+                         "profiles/route_traffic.json")
     return ap.parse_args()
 
 
@@ -67,17 +74,77 @@ def route_kernel_name(wl) -> str:
     return "route_fast_kernel"
 
 
-def traffic_from_profile(kernel_src: str):
-    """Measured HBM bytes per routing launch, if a counter profile of the current kernel source
-    was committed (profiles/route_traffic.json); None otherwise."""
-    path = os.path.join(ROOT, "profiles", "route_traffic.json")
-    if not os.path.exists(path):
+# sources of the routing kernels; a counter profile is valid only while their text is unchanged
+ROUTE_SOURCES = ["route.hip", "route_common.h", "route_sig.hip", "route_sig.h", "sigmoid_cr.h",
+                 "route_fast.h", "route_fast.hip", "route_fast_f32.hip", "route_fast_bf16.hip"]
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "route_traffic.json")
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def route_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for name in ROUTE_SOURCES:
+        h.update(open(os.path.join(ROOT, "expert_dispatch_layout_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
+
+
+def traffic_from_profile():
+    """Measured HBM bytes per routing launch, if a counter profile of the current routing
+    sources was committed (profiles/route_traffic.json); None otherwise."""
+    if not os.path.exists(TRAFFIC_JSON):
         return None
-    rec = json.load(open(path))
-    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != h:
+    rec = json.load(open(TRAFFIC_JSON))
+    if rec.get("source_sha256") != route_sources_sha256():
         return None
     return rec.get("bytes_per_launch")
+
+
+def read_counter_csv(path: str, counter: str):
+    """Per-kernel lists of one counter's per-dispatch values (KiB) from a rocprofv3 CSV."""
+    import csv
+
+    per = {}
+    for row in csv.DictReader(open(path)):
+        if row["Counter_Name"] != counter:
+            continue
+        per.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return per
+
+
+def record_traffic(fetch_csv: str, write_csv: str, copy_mib: int, wl):
+    """Scale the routing kernel's FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the same
+    counters read for the plain copy kernel of --copy-calibration (known bytes), and store the
+    result with the hash of the routing sources."""
+    fetch = read_counter_csv(fetch_csv, "FETCH_SIZE")
+    write = read_counter_csv(write_csv, "WRITE_SIZE")
+    name = route_kernel_name(wl)
+    rk = [k for k in fetch if name.split("<")[0] in k]
+    assert len(rk) == 1, "routing kernel %s not unique in %s: %s" % (name, fetch_csv, list(fetch))
+    rk = rk[0]
+    # the copy kernel's dispatches of the calibration size are its largest ones
+    cf = max(fetch[COPY_KERNEL])
+    cw = max(write[COPY_KERNEL])
+    copy_kib = copy_mib * 1024.0
+    f_fac = copy_kib / cf
+    w_fac = copy_kib / cw
+    fk = sum(fetch[rk]) / len(fetch[rk])
+    wk = sum(write[rk]) / len(write[rk])
+    per = {}
+    for k in fetch:
+        if k in write and k != COPY_KERNEL:
+            per[k] = {"fetch_bytes": 1024 * f_fac * sum(fetch[k]) / len(fetch[k]),
+                      "write_bytes": 1024 * w_fac * sum(write[k]) / len(write[k]),
+                      "dispatches": len(fetch[k])}
+    rec = {"source_sha256": route_sources_sha256(), "kernel": rk,
+           "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+           "copy_kib": copy_kib, "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "fetch_scale": f_fac, "write_scale": w_fac,
+           "bytes_per_launch": 1024 * (fk * f_fac + wk * w_fac),
+           "algorithmic_bytes_per_launch": route_bytes(wl), "kernels": per}
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps({k: rec[k] for k in rec if k != "kernels"}))
 
 
 def cpu_baseline(wl, inp, seconds: float):
@@ -104,6 +171,12 @@ def cpu_baseline(wl, inp, seconds: float):
 
 def main():
     args = parse()
+    if args.record_traffic:
+        from expert_dispatch_layout_amd import synth
+
+        assert args.copy_calibration > 0, "--record-traffic needs the --copy-calibration size of the run"
+        record_traffic(*args.record_traffic, args.copy_calibration, synth.WORKLOADS[args.workload])
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -143,41 +216,39 @@ def main():
 
     # one prepared call per buffer set and entry point (arguments converted once): routing, then
     # layout + plan in one call (mep_layout_plan: three kernels, the plan's counting pass also
-    # serving the layout)
+    # serving the layout).  Timed steps route through mep_route_topk_timed with a pair of
+    # events per step, which the routing kernel's launch itself stamps with its start and end.
     calls = []
     for x, ids, w, L, P in sets:
         calls.append((B.bound_route_topk(x, K, bias, params, ids, w, stream),
                       B.bound_layout_plan(ids, E, A, L, R, S, C, NvS, P, ws_p, stream)))
-
-    def step(i, ev=None):
-        route, layout_plan = calls[i % nsets]
-        if ev is not None:
-            ev[0].record(stream)
-        route()
-        if ev is not None:
-            ev[1].record(stream)
-        layout_plan()
+    timers = [B.KernelTimer() for _ in range(args.steps)]
+    timed = []
+    for i in range(args.steps):
+        x, ids, w = sets[(args.warmup + i) % nsets][:3]
+        timed.append(B.bound_route_topk(x, K, bias, params, ids, w, stream, timer=timers[i]))
 
     for i in range(args.warmup):
-        step(i)
+        route, layout_plan = calls[i % nsets]
+        route()
+        layout_plan()
     torch.cuda.synchronize()
 
-    # timed region: K steps bracketed by synchronisation; HIP events on the launch stream around
-    # each routing call give its average duration
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    # timed region: K steps bracketed by synchronisation
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        timed[i]()
+        calls[(args.warmup + i) % nsets][1]()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
-    route_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    route_ms = sum(t.elapsed_ms() for t in timers) / args.steps
 
     # sizes of this batch's layout and dedup lists (for the whole-path byte count)
     L, P = sets[(args.warmup + args.steps - 1) % nsets][3:]
@@ -186,7 +257,7 @@ def main():
     rb = route_bytes(wl)
     achieved = rb / (route_ms * 1e-3) / 1e9
     pb = path_bytes(wl, T, G, D)
-    traffic = traffic_from_profile(os.path.join(ROOT, "expert_dispatch_layout_amd", "csrc", "route.hip"))
+    traffic = traffic_from_profile()
 
     out = {
         "metric": "routed tokens/sec + achieved HBM GB/s (% of peak), N=65536 E=256 K=8",
@@ -217,6 +288,14 @@ def main():
                  "slots_per_s": N * K / (ms_step * 1e-3), "T": T, "dedup_groups": G,
                  "dedup_dups": D, "host_wall_s": wall},
     }
+    if args.copy_calibration > 0:
+        nbytes = args.copy_calibration << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -45,7 +45,7 @@ class PlanOutputs(ctypes.Structure):
                 ("cap_dups", ctypes.c_int64)]
 
 
-EXPORTS = ("mep_route_topk", "mep_build_layout", "mep_layout_workspace_size", "mep_plan",
+EXPORTS = ("mep_route_topk", "mep_route_topk_timed", "mep_build_layout", "mep_layout_workspace_size", "mep_plan",
            "mep_plan_workspace_size", "mep_layout_plan", "mep_status_string")
 
 _lib = None
@@ -64,6 +64,9 @@ def lib():
                 P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
                 L.mep_route_topk.argtypes = [P, I, I64, I, I, P, ctypes.POINTER(RouteParams), P, P, P]
                 L.mep_route_topk.restype = I
+                L.mep_route_topk_timed.argtypes = [P, I, I64, I, I, P, ctypes.POINTER(RouteParams),
+                                                   P, P, P, P, P]
+                L.mep_route_topk_timed.restype = I
                 L.mep_build_layout.argtypes = [P, I64, I, I, I, P, P, P, P, I64, P, P, SZ, P]
                 L.mep_build_layout.restype = I
                 L.mep_layout_workspace_size.argtypes = [I64, I, I]
@@ -164,15 +167,59 @@ def _bound(fn_name, args, where):
     return call
 
 
-def bound_route_topk(logits, K, bias, params: RouteParams, topk_ids, topk_weights=None, stream=None):
+def bound_route_topk(logits, K, bias, params: RouteParams, topk_ids, topk_weights=None, stream=None,
+                     timer: "KernelTimer" = None):
+    """With `timer`, the call is mep_route_topk_timed: the routing kernel's own launch updates
+    the timer's two events with its start and end."""
     _require_cuda(logits, bias, topk_ids, topk_weights)
     if logits.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("logits must be float32 or bfloat16")
     dtype = MEP_BF16 if logits.dtype == torch.bfloat16 else MEP_F32
     N, E = logits.shape
-    return _bound("mep_route_topk", (_ptr(logits), dtype, N, E, K, _ptr(bias), ctypes.byref(params),
-                                     _ptr(topk_ids), _ptr(topk_weights), _stream(stream)),
-                  "mep_route_topk")
+    args = (_ptr(logits), dtype, N, E, K, _ptr(bias), ctypes.byref(params), _ptr(topk_ids),
+            _ptr(topk_weights), _stream(stream))
+    if timer is None:
+        return _bound("mep_route_topk", args, "mep_route_topk")
+    return _bound("mep_route_topk_timed", args + (timer.start, timer.stop), "mep_route_topk_timed")
+
+
+class KernelTimer:
+    """Two HIP events (created through the HIP runtime that torch and libmep share) for
+    mep_route_topk_timed; elapsed_ms() is hipEventElapsedTime once the work has completed.
+    The events are timing-only (hipEventDisableSystemFence): recording them performs no
+    system-scope cache write-back, which would otherwise delay the work that follows."""
+
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self, flags: int = DISABLE_SYSTEM_FENCE):
+        if KernelTimer._hip is None:
+            h = ctypes.CDLL("libamdhip64.so.7")
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                              ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            KernelTimer._hip = h
+        self.start = ctypes.c_void_p()
+        self.stop = ctypes.c_void_p()
+        for e in (self.start, self.stop):
+            rc = KernelTimer._hip.hipEventCreateWithFlags(ctypes.byref(e), flags)
+            if rc != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed (%d)" % rc)
+
+    def elapsed_ms(self) -> float:
+        ms = ctypes.c_float()
+        rc = KernelTimer._hip.hipEventElapsedTime(ctypes.byref(ms), self.start, self.stop)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+        return ms.value
+
+    def __del__(self):
+        h = KernelTimer._hip
+        if h is not None:
+            for e in (self.start, self.stop):
+                if e:
+                    h.hipEventDestroy(e)
 
 
 def bound_build_layout(topk_ids, E, alignment, tokens_per_expert, cu_seqlens, expanded_to_permuted,

@@ -60,19 +60,19 @@ __global__ __launch_bounds__(kRouteBlock) void route_generic_kernel(RouteArgs a)
 }
 
 template <int LPT, int NV, bool BF16>
-static void launch_generic(const RouteArgs& a, hipStream_t st) {
+static void launch_generic(const RouteArgs& a, const Launch& st) {
     const int tpb = kRouteBlock / LPT;
     const int64_t blocks = ceil_div64(a.N, tpb);
     if (a.K <= 8)
-        hipLaunchKernelGGL((route_generic_kernel<LPT, NV, BF16, 8>), dim3((unsigned)blocks),
+        launch_kernel((route_generic_kernel<LPT, NV, BF16, 8>), dim3((unsigned)blocks),
                            dim3(kRouteBlock), 0, st, a);
     else
-        hipLaunchKernelGGL((route_generic_kernel<LPT, NV, BF16, 32>), dim3((unsigned)blocks),
+        launch_kernel((route_generic_kernel<LPT, NV, BF16, 32>), dim3((unsigned)blocks),
                            dim3(kRouteBlock), 0, st, a);
 }
 
 template <bool BF16>
-static int dispatch_generic(const RouteArgs& a, hipStream_t st) {
+static int dispatch_generic(const RouteArgs& a, const Launch& st) {
     constexpr int W = BF16 ? 8 : 4;
     const int nchunks = (a.E + W - 1) / W;
     if (nchunks <= 1) launch_generic<1, 1, BF16>(a, st);
@@ -90,10 +90,11 @@ static int dispatch_generic(const RouteArgs& a, hipStream_t st) {
 
 }  // namespace mep
 
-extern "C" int mep_route_topk(const void* logits, int dtype, int64_t N, int E, int K,
-                              const float* bias, const mep_route_params* p, int32_t* topk_ids,
-                              float* topk_weights, void* stream) {
-    using namespace mep;
+namespace mep {
+
+static int route_topk(const void* logits, int dtype, int64_t N, int E, int K, const float* bias,
+                      const mep_route_params* p, int32_t* topk_ids, float* topk_weights,
+                      const Launch& st) {
     if (!p) return MEP_ERR_INVALID_ARG;
     if (N > 0 && (!logits || !topk_ids)) return MEP_ERR_INVALID_ARG;  // N == 0 reads nothing
     if (dtype != MEP_F32 && dtype != MEP_BF16) return MEP_ERR_INVALID_ARG;
@@ -132,8 +133,26 @@ extern "C" int mep_route_topk(const void* logits, int dtype, int64_t N, int E, i
     a.weights = topk_weights;
     const int W = dtype == MEP_BF16 ? 8 : 4;
     a.vec = (E % W) == 0;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (launch_route_sig(a, dtype, st)) return launch_status();
     if (launch_route_fast(a, dtype, st)) return launch_status();
     return dtype == MEP_BF16 ? dispatch_generic<true>(a, st) : dispatch_generic<false>(a, st);
+}
+
+}  // namespace mep
+
+extern "C" int mep_route_topk(const void* logits, int dtype, int64_t N, int E, int K,
+                              const float* bias, const mep_route_params* p, int32_t* topk_ids,
+                              float* topk_weights, void* stream) {
+    const mep::Launch l{reinterpret_cast<hipStream_t>(stream), nullptr, nullptr};
+    return mep::route_topk(logits, dtype, N, E, K, bias, p, topk_ids, topk_weights, l);
+}
+
+extern "C" int mep_route_topk_timed(const void* logits, int dtype, int64_t N, int E, int K,
+                                    const float* bias, const mep_route_params* p,
+                                    int32_t* topk_ids, float* topk_weights, void* stream,
+                                    void* start_event, void* stop_event) {
+    const mep::Launch l{reinterpret_cast<hipStream_t>(stream),
+                        reinterpret_cast<hipEvent_t>(start_event),
+                        reinterpret_cast<hipEvent_t>(stop_event)};
+    return mep::route_topk(logits, dtype, N, E, K, bias, p, topk_ids, topk_weights, l);
 }

@@ -9,6 +9,7 @@
 #pragma once
 
 #include <float.h>
+#include <hip/hip_ext.h>
 #include <limits.h>
 
 #include <type_traits>
@@ -37,6 +38,22 @@ struct RouteArgs {
     float* weights;
     int vec;          // rows are 16-byte aligned and E is a multiple of the chunk width
 };
+
+// Where a routing kernel is launched: the caller's stream and two optional events that the
+// launch itself updates with the kernel's start and end times (hipExtLaunchKernel), so the
+// kernel can be timed without marker packets between it and its neighbours on the stream.
+// Every routing path launches exactly one kernel.
+struct Launch {
+    hipStream_t st;
+    hipEvent_t start;  // may be null
+    hipEvent_t stop;   // may be null
+};
+
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t shmem, const Launch& l,
+                          Args... args) {
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, l.st, l.start, l.stop, 0, args...);
+}
 
 constexpr int kRouteBlock = 256;
 constexpr int kMaxGroups = 32;
@@ -293,9 +310,9 @@ __device__ __forceinline__ void write_weights(const RouteArgs& a, int64_t tok, i
 }
 
 // Fast-kernel launcher (route_fast.hip).  Returns false when the shape is not covered.
-bool launch_route_fast(const RouteArgs& a, int dtype, hipStream_t st);
+bool launch_route_fast(const RouteArgs& a, int dtype, const Launch& st);
 
 // Sigmoid routing kernel launcher (route_sig.hip).  Returns false when the shape is not covered.
-bool launch_route_sig(const RouteArgs& a, int dtype, hipStream_t st);
+bool launch_route_sig(const RouteArgs& a, int dtype, const Launch& st);
 
 }  // namespace mep

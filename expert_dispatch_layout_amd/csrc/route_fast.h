@@ -561,7 +561,7 @@ __global__ __launch_bounds__(kFastBlock, 3) void route_fast_kernel(RouteArgs a, 
 int resident_blocks(const void* kernel, int block_threads);
 
 template <int LPT, bool BF16, int MODE, int SCORE>
-void launch_fast_mode(const RouteArgs& a, const FastCfg& cfg_in, int M, hipStream_t st) {
+void launch_fast_mode(const RouteArgs& a, const FastCfg& cfg_in, int M, const Launch& st) {
     FastCfg cfg = cfg_in;
     cfg.nsets = ceil_div64(a.N, FastGeom<LPT, BF16>::TPW);
     auto launch = [&](auto kernel) {
@@ -569,7 +569,7 @@ void launch_fast_mode(const RouteArgs& a, const FastCfg& cfg_in, int M, hipStrea
         int64_t grid = resident_blocks(reinterpret_cast<const void*>(kernel), kFastBlock);
         if (grid > need) grid = need;
         if (grid < 1) grid = 1;
-        hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kFastBlock), 0, st, a, cfg);
+        launch_kernel(kernel, dim3((unsigned)grid), dim3(kFastBlock), 0, st, a, cfg);
     };
     if (a.K <= 8) {
         if (M <= 2) launch(route_fast_kernel<LPT, BF16, 8, 2, MODE, SCORE>);
@@ -581,7 +581,7 @@ void launch_fast_mode(const RouteArgs& a, const FastCfg& cfg_in, int M, hipStrea
 }
 
 template <int LPT, bool BF16>
-void launch_fast_shape(const RouteArgs& a, const FastCfg& cfg, int M, hipStream_t st) {
+void launch_fast_shape(const RouteArgs& a, const FastCfg& cfg, int M, const Launch& st) {
     if (a.score_fn == MEP_SIGMOID) {
         if (cfg.mode == 0) launch_fast_mode<LPT, BF16, 0, 2>(a, cfg, M, st);
         else launch_fast_mode<LPT, BF16, 1, 2>(a, cfg, M, st);
@@ -594,7 +594,7 @@ void launch_fast_shape(const RouteArgs& a, const FastCfg& cfg, int M, hipStream_
     }
 }
 
-void launch_fast_f32(int LPT, const RouteArgs& a, const FastCfg& cfg, int M, hipStream_t st);
-void launch_fast_bf16(int LPT, const RouteArgs& a, const FastCfg& cfg, int M, hipStream_t st);
+void launch_fast_f32(int LPT, const RouteArgs& a, const FastCfg& cfg, int M, const Launch& st);
+void launch_fast_bf16(int LPT, const RouteArgs& a, const FastCfg& cfg, int M, const Launch& st);
 
 }  // namespace mep

@@ -38,7 +38,7 @@ static int ilog2(int v) {
     return l;
 }
 
-bool launch_route_fast(const RouteArgs& a, int dtype, hipStream_t st) {
+bool launch_route_fast(const RouteArgs& a, int dtype, const Launch& st) {
     const bool bf16 = dtype == MEP_BF16;
     if (a.E % kFastEPL != 0 || !a.vec) return false;
     const int LPT = a.E / kFastEPL;

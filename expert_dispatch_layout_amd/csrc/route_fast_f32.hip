@@ -3,7 +3,7 @@
 
 namespace mep {
 
-void launch_fast_f32(int LPT, const RouteArgs& a, const FastCfg& cfg, int M, hipStream_t st) {
+void launch_fast_f32(int LPT, const RouteArgs& a, const FastCfg& cfg, int M, const Launch& st) {
     switch (LPT) {
         case 2: launch_fast_shape<2, false>(a, cfg, M, st); break;
         case 4: launch_fast_shape<4, false>(a, cfg, M, st); break;

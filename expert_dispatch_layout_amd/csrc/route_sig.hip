@@ -4,7 +4,7 @@
 namespace mep {
 
 template <int LPT, bool BF16, int MODE>
-static void launch_sig(const RouteArgs& a, hipStream_t st) {
+static void launch_sig(const RouteArgs& a, const Launch& st) {
     SigCfg cfg;
     cfg.nsets = ceil_div64(a.N, FastGeom<LPT, BF16>::TPW);
     cfg.tg = MODE == 1 ? a.topk_group : LPT;
@@ -14,11 +14,11 @@ static void launch_sig(const RouteArgs& a, hipStream_t st) {
     int64_t grid = resident_blocks(reinterpret_cast<const void*>(kernel), 64 * NW);
     if (grid > need) grid = need;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * NW), 0, st, a, cfg);
+    launch_kernel(kernel, dim3((unsigned)grid), dim3(64 * NW), 0, st, a, cfg);
 }
 
 template <bool BF16, int MODE>
-static void launch_sig_lpt(int LPT, const RouteArgs& a, hipStream_t st) {
+static void launch_sig_lpt(int LPT, const RouteArgs& a, const Launch& st) {
     switch (LPT) {
         case 2: launch_sig<2, BF16, MODE>(a, st); break;
         case 4: launch_sig<4, BF16, MODE>(a, st); break;
@@ -27,7 +27,7 @@ static void launch_sig_lpt(int LPT, const RouteArgs& a, hipStream_t st) {
     }
 }
 
-bool launch_route_sig(const RouteArgs& a, int dtype, hipStream_t st) {
+bool launch_route_sig(const RouteArgs& a, int dtype, const Launch& st) {
     if (a.score_fn != MEP_SIGMOID || !a.vec || a.K > 8 || a.E % kFastEPL != 0) return false;
     const int LPT = a.E / kFastEPL;
     if (LPT != 2 && LPT != 4 && LPT != 8 && LPT != 16) return false;

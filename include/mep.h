@@ -117,6 +117,23 @@ int mep_route_topk(const void* logits, int dtype, int64_t N, int E, int K,
                    int32_t* topk_ids, float* topk_weights, void* stream);
 
 /*
+ * mep_route_topk_timed -- mep_route_topk with kernel timing.
+ *
+ * Computes exactly what mep_route_topk computes (same arguments, checks and
+ * errors).  Every routing shape runs as one kernel; start_event and
+ * stop_event (hipEvent_t created by the caller, either may be NULL) are
+ * updated by that kernel's launch itself with its start and end times
+ * (hipExtLaunchKernel), so hipEventElapsedTime(start, stop) is the kernel's
+ * duration with no marker packet on the stream.  For measuring the kernel
+ * in place inside a larger stream of work.  Events are left untouched when
+ * the call returns an error or N == 0.
+ */
+int mep_route_topk_timed(const void* logits, int dtype, int64_t N, int E, int K,
+                         const float* bias, const mep_route_params* p,
+                         int32_t* topk_ids, float* topk_weights, void* stream,
+                         void* start_event, void* stop_event);
+
+/*
  * mep_build_layout -- padded per-expert layout of the N*K routed slots.
  *
  * Slot i = t*K + k holds expert e = topk_ids[i].

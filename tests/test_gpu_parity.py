@@ -221,6 +221,29 @@ def test_route_tiny_batches():
                     topk_group=4, scale=2.5)
 
 
+@pytest.mark.parametrize("score_fn,E,dtype", [(1, 256, synth.F32), (0, 128, synth.BF16),
+                                               (0, 40, synth.F32)])
+def test_route_timed_matches_untimed(score_fn, E, dtype):
+    """mep_route_topk_timed writes the same bytes as mep_route_topk on the sigmoid, fast and
+    generic routing paths, and its events bracket the kernel (positive elapsed time)."""
+    rng = np.random.default_rng(11)
+    N, K = 3000, 8
+    x = _to_dev_logits(rng.standard_normal((N, E)).astype(np.float32), dtype)
+    bias = torch.from_numpy(rng.uniform(-0.1, 0.1, E).astype(np.float32)).to(DEV)
+    p = B.route_params(score_fn, 1, 8 if score_fn else 1, 4, 2, 2.5)
+    outs = []
+    timer = B.KernelTimer()
+    for t in (None, timer):
+        ids = torch.full((N, K), -7, dtype=torch.int32, device=DEV)
+        w = torch.full((N, K), -7.0, dtype=torch.float32, device=DEV)
+        B.bound_route_topk(x, K, bias, p, ids, w, timer=t)()
+        torch.cuda.synchronize()
+        outs.append((ids.cpu().numpy(), w.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1].view(np.int32), outs[1][1].view(np.int32))
+    assert timer.elapsed_ms() > 0.0
+
+
 # -------------------------------------------------------------------------------------------
 # sigmoid: every bf16 value, hard fp32 cases, a dense fp32 range
 # -------------------------------------------------------------------------------------------

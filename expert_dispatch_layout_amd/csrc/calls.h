@@ -12,11 +12,9 @@
 namespace mep {
 
 // Geometry: tiles of kLayTile slots (one workgroup each in both kernels); a count tile groups
-// `sub` consecutive tiles so that about kCountTiles count tiles take part in the look-back (one
-// window of predecessors).
+// `sub` consecutive tiles so that at most kCountTiles count tiles exist.
 struct LayGeom {
     int NK, E, nsub, sub, nct;
-    int ticketed;  // tiles in ticket order (when count tiles could outnumber resident groups)
 };
 
 // Workspace of mep_build_layout after the header: arrival counters of count tiles (fixed place,
@@ -54,6 +52,8 @@ struct PlanGeom {
     int N, E, K, R, epn, S, n, tps, ntiles, TT, ncols, C;
     int sub, ctps, nct;
     int ticketed;  // write tiles in ticket order (when count tiles could outnumber resident groups)
+    int direct;    // count-tile prefixes by the last count tile's scan (nct <= kDirectCountTiles),
+                   // else by the decoupled look-back
     int64_t NvS;
 };
 

@@ -138,9 +138,10 @@ __device__ __forceinline__ uint32_t tagged_value(const uint64_t* p, uint64_t v, 
 
 // Workspace header shared by the layout and plan calls (first 256 bytes of the workspace).
 struct WsHeader {
-    uint32_t epoch;   // epoch of the last completed call
-    uint32_t ticket;  // tile ticket counter, reset to 0 by the consuming kernel
-    uint32_t pad[62];
+    uint32_t epoch;    // epoch of the last completed call
+    uint32_t ticket;   // tile ticket counter, reset to 0 by the consuming kernel
+    uint32_t ct_done;  // count tiles whose totals are stored; reset to 0 by the last of them
+    uint32_t pad[61];
 };
 static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 
@@ -150,6 +151,49 @@ static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 __device__ __forceinline__ int take_ticket(WsHeader* h, int ntiles) {
     const uint32_t t = __hip_atomic_fetch_add(&h->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return (int)(t % (uint32_t)ntiles);
+}
+
+// When the counting kernel ends, word c of every column holds the inclusive prefix through count
+// tile c.  It gets there in one of two ways.  With at most kDirectCountTiles count tiles, every
+// count tile stores its own totals and counts itself done; the last one to do so (all others have
+// then stored) scans every column in place -- no workgroup ever waits for another.  With more,
+// the totals go through the decoupled look-back below.
+constexpr int kDirectCountTiles = 64;
+
+// Inclusive scan in place of one column over count tiles 0..nct-1 whose words hold tagged totals
+// of this call (re-read until current: their stores may still be in flight from other dies).
+__device__ __forceinline__ void scan_count_column(uint64_t* status, int nct, int ncols, int col,
+                                                  uint32_t epoch) {
+    const uint32_t want = status_tag(epoch);
+    uint32_t run = 0;
+    for (int j0 = 0; j0 < nct; j0 += 16) {
+        uint64_t v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            v[j] = status_load(status + (size_t)min(j0 + j, nct - 1) * ncols + col);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (j0 + j >= nct) break;
+            uint64_t* p = status + (size_t)(j0 + j) * ncols + col;
+            run += tagged_value(p, v[j], want);
+            status_store(p, status_make(epoch, true, run));
+        }
+    }
+}
+
+// Counts the calling workgroup's count tile as done; true in the last of the nct count tiles,
+// which then resets the counter.  Call from every thread after the tile's words are stored.
+__device__ __forceinline__ bool last_count_tile(WsHeader* hdr, int nct, uint32_t* s_flag) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t d = __hip_atomic_fetch_add(&gptr(hdr)->ct_done, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = d == (uint32_t)(nct - 1);
+        if (last) __hip_atomic_store(&gptr(hdr)->ct_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = last ? 1u : 0u;
+    }
+    __syncthreads();
+    return *s_flag != 0u;
 }
 
 // Lanes of this wave (restricted to `active`) holding the same key as the calling lane: one wave

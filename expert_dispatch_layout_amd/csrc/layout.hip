@@ -5,11 +5,10 @@
 // at most about 32 count tiles exist:
 //
 //   count   LDS-privatised histograms (one LDS atomic per slot, no global atomics), one per
-//           scatter tile, written to the workspace; their sum per expert column goes through a
-//           single-pass decoupled look-back (Merrill & Garland 2016) that publishes each count
-//           tile's inclusive per-expert prefix.  Count tiles take an atomic ticket so every
-//           awaited predecessor is already running, and the look-back reads all of them in one
-//           window, so the chain costs about one round trip between compute dies.
+//           scatter tile, written to the workspace; the last tile of a count tile (at most 32
+//           of them) to arrive sums them and stores the count tile's totals, and the last count
+//           tile to do so turns every expert column into inclusive prefixes over count tiles.
+//           No workgroup waits for another.
 //   scatter every tile reads the per-expert totals (last tile's inclusive prefix), forms the
 //           padded offsets cu_seqlens (ceil(count/A)*A, 0 for an empty expert: MoonEP
 //           planning.py Phase B2 padded group scan), and ranks its slots stably: within a wave
@@ -34,14 +33,9 @@ constexpr int kScatWaves = kScatBlock / kWave;
 constexpr int kScatPerWave = kLayTile / kScatWaves;  // 256
 constexpr int kMaxExperts = 1024;
 constexpr int kCountBlock = 1024;
-constexpr int kCountTiles = 32;                      // count tiles aimed at (parallelism vs look-back length)
-
-
-// Only the last arriving workgroup of a count tile ever waits (on earlier count tiles).  With at
-// most this many count tiles, waiting workgroups can never fill the GPU, so every awaited one
-// gets to run and tiles can follow the workgroup index; beyond it they take a ticket.
-constexpr int kUnticketedCountTiles = 128;
+constexpr int kCountTiles = 32;                      // count tiles at most
 constexpr int kMaxCountTiles = 4096;  // arrival counters kept in the workspace
+static_assert(kCountTiles <= kDirectCountTiles, "the last layout count tile scans them all");
 
 static LayGeom lay_geom(int64_t NK, int E) {
     LayGeom g;
@@ -49,29 +43,25 @@ static LayGeom lay_geom(int64_t NK, int E) {
     g.E = E;
     g.nsub = (int)ceil_div64(NK, kLayTile);
     int sub = (int)ceil_div64(g.nsub, kCountTiles);
-    if (sub < (int)ceil_div64(g.nsub, kMaxCountTiles)) sub = (int)ceil_div64(g.nsub, kMaxCountTiles);
     if (sub < 1) sub = 1;
     g.sub = sub;
-    g.nct = (int)ceil_div64(g.nsub, sub);
-    g.ticketed = g.nct > kUnticketedCountTiles;
+    g.nct = (int)ceil_div64(g.nsub, sub);  // <= kCountTiles
     return g;
 }
 
 
 // One tile per workgroup: LDS-privatised histogram (one LDS atomic per slot), written to the
-// workspace; the last tile of a count tile to arrive sums the count tile's histograms and takes
-// it through the look-back.
+// workspace; the last tile of a count tile to arrive sums the count tile's histograms and stores
+// the count tile's totals; the last count tile to finish scans them.
 __global__ __launch_bounds__(kCountBlock) void layout_count_kernel(const int32_t* __restrict__ ids,
                                                                    LayGeom g, LayWs w, WsHeader* hdr) {
     __shared__ int hist[kMaxExperts];
-    __shared__ int s_tile;
     __shared__ uint32_t s_arrived;
     const int tid = threadIdx.x;
     const int E = g.E;
     for (int i = tid; i < E; i += kCountBlock) hist[i] = 0;
-    if (tid == 0) s_tile = g.ticketed ? take_ticket(hdr, (int)gridDim.x) : (int)blockIdx.x;
     __syncthreads();
-    const int tile = s_tile;
+    const int tile = blockIdx.x;
     const uint32_t epoch = __hip_atomic_load(&gptr(hdr)->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
     const int base = tile * kLayTile;
     const MEP_GLOBAL int32_t* gids = gptr(ids);
@@ -110,8 +100,10 @@ __global__ __launch_bounds__(kCountBlock) void layout_count_kernel(const int32_t
             for (int b = 0; b < 8; ++b)
                 if (b0 + b < nsub_here) agg += tagged_value(w.tilehist + (size_t)(t0 + b0 + b) * E + e, x[b], want);
         }
-        lookback_column(w.status, ct, E, e, epoch, agg);
+        status_store(w.status + (size_t)ct * E + e, status_make(epoch, false, agg));
     }
+    if (last_count_tile(hdr, g.nct, &s_arrived))
+        for (int e = tid; e < E; e += kCountBlock) scan_count_column(w.status, g.nct, E, e, epoch);
 }
 
 
@@ -176,21 +168,28 @@ __global__ __launch_bounds__(kScatBlock) void layout_scatter_kernel(const int32_
         idv[it] = i < s_end ? gids[i] : 0;
     }
 
-    // ---- per-expert totals and the slots of each expert before this tile, all loads issued
-    // together: totals from the last count tile's inclusive prefix, earlier count tiles from the
-    // look-back, earlier tiles of this count tile from their histograms
+    // ---- per-expert totals (the last count tile's inclusive prefix) and the slots of each expert
+    // before this tile (the inclusive prefix of the count tile before this one plus the
+    // histograms of the earlier tiles of this count tile), all loads issued together
     int tot[EPT], pre[EPT];
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
         const int e = tid * EPT + q;
-        tot[q] = (e < E && ntiles > 0) ? (int)status_value(status, nct - 1, E, e) : 0;
-        pre[q] = (e < E && tile < ntiles && ct > 0) ? (int)status_value(status, ct - 1, E, e) : 0;
-    }
-    for (int s2 = first; s2 < tile && tile < ntiles; ++s2) {  // the earlier tiles of this count tile
+        tot[q] = 0;
+        pre[q] = 0;
+        if (e >= E || tile >= ntiles) continue;
+        const MEP_GLOBAL uint64_t* gs = gptr(status) + e;
+        const MEP_GLOBAL uint64_t* gt = gptr(th) + (size_t)first * th_stride + th_off + e;
+        const int nwt = tile - first;  // earlier tiles of this count tile
+        tot[q] = (int)(uint32_t)gs[(size_t)(nct - 1) * E];
+        pre[q] = (int)(uint32_t)gs[(size_t)(ct > 0 ? ct - 1 : 0) * E];
+        if (ct == 0) pre[q] = 0;
+        int v[8];
+        for (int j0 = 0; j0 < nwt; j0 += 8) {  // rows past the end re-read the last one, counted 0
 #pragma unroll
-        for (int q = 0; q < EPT; ++q) {
-            const int e = tid * EPT + q;
-            if (e < E) pre[q] += (int)status_value(th, s2, th_stride, th_off + e);
+            for (int j = 0; j < 8; ++j) v[j] = (int)(uint32_t)gt[(size_t)min(j0 + j, nwt - 1) * th_stride];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pre[q] += j0 + j < nwt ? v[j] : 0;
         }
     }
     int pad[EPT];

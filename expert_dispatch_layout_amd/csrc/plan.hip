@@ -9,14 +9,16 @@
 //                                                     canonicalisation encodes them as -dst-1)
 //   cE[e]  1 if the token is routed to e            (per-shard expert counts)
 //
-//   count kernel  per count tile (a few consecutive write tiles of one shard): LDS histograms of
-//                 the 3R+E columns per write tile; the 3R rank columns go to the workspace and,
-//                 summed, through a decoupled look-back across count tiles (about 32 of them,
-//                 read in one window), so the prefix of a rank column at any write-tile boundary
-//                 is a look-back value plus a few histograms; the E expert columns are needed
-//                 per shard only, so each count tile publishes one tagged aggregate and the last
-//                 count tile to start (every other one is then running) reduces them into the
-//                 per-shard expert counts and the expert totals.  Also writes is_token_in_rank.
+//   count kernel  one write tile per workgroup: LDS histograms of the 3R+E columns, stored to
+//                 the workspace; the last write tile of a count tile (a few consecutive write
+//                 tiles of one shard) to arrive sums them.  With at most kDirectCountTiles count
+//                 tiles (about 32 are aimed at) it stores that count tile's totals, and the last
+//                 count tile to do so scans every column into inclusive prefixes (no workgroup
+//                 ever waits); with more, the sums go through a decoupled look-back across count
+//                 tiles.  Either way the prefix of a column at any write-tile boundary is a
+//                 count-tile inclusive prefix plus a few write-tile histograms; the expert
+//                 columns also give the layout's totals and prefixes in mep_layout_plan.  Also
+//                 writes is_token_in_rank.
 //   write kernel  dst with the duplicate encoding; dedup groups and duplicate offsets in a stable
 //                 (rank, token, k) order -- each slot is ranked among same-rank slots of its
 //                 wave by ballot-matching and per-(wave, rank) LDS counters, then offset by the
@@ -113,12 +115,31 @@ __device__ __forceinline__ void token_slots(TokenSlots<KMAX>& ts, const int (&id
     }
 }
 
+// The K entries of token t's row (ids or permuted positions): two 16-byte loads when `vec8`
+// (K == 8 and 16-byte aligned rows), else K 4-byte loads; `fill` where there is no token.
 template <int KMAX>
-__device__ __forceinline__ void load_token_ids(int (&idk)[KMAX], const int32_t* ids, int64_t t, int K,
-                                               bool live) {
-    const MEP_GLOBAL int32_t* gids = gptr(ids);
+__device__ __forceinline__ void load_token_row(int (&v)[KMAX], const int32_t* p, int64_t t, int K,
+                                               bool live, bool vec8, int fill) {
+    const MEP_GLOBAL int32_t* gp = gptr(p);
+    if constexpr (KMAX == 8) {
+        if (vec8) {
+            if (live) {
+                const MEP_GLOBAL u32x4* q = reinterpret_cast<const MEP_GLOBAL u32x4*>(gp + t * 8);
+                const u32x4 a = q[0], b = q[1];
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) idk[k] = (live && k < K) ? gids[t * K + k] : -1;
+                for (int k = 0; k < 4; ++k) {
+                    v[k] = (int)a[k];
+                    v[4 + k] = (int)b[k];
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) v[k] = fill;
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) v[k] = (live && k < K) ? gp[t * K + k] : fill;
 }
 
 // Rank sets of a token as bit masks: RW 32-bit words (1 word when R <= 32, else 4).
@@ -177,7 +198,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_count_kernel(const int32_t* _
     const int64_t t = (int64_t)sh * g.n + (int64_t)(wt - sh * g.tps) * g.TT + tid;
     const bool live = tid < g.TT && t < (int64_t)(sh + 1) * g.n;
     int idk[KMAX];
-    load_token_ids<KMAX>(idk, ids, t, K, live);
+    load_token_row<KMAX>(idk, ids, t, K, live, K == 8 && (((uintptr_t)ids) & 15u) == 0, -1);
     {
         RankMask<RW> seen, multi;  // ranks reached; ranks reached by >= 2 slots
         seen.clear();
@@ -254,8 +275,20 @@ __global__ __launch_bounds__(kPlanBlock) void plan_count_kernel(const int32_t* _
             for (int b = 0; b < 8; ++b)
                 if (b0 + b < nsub_here) agg += tagged_value(w.tilehist + (size_t)(wt0 + b0 + b) * nc + c, v[b], want);
         }
-        if (c < n3) lookback_column(w.status3, ct, n3, c, epoch, agg);
-        else lookback_column(w.statusE, ct, E, c - n3, epoch, agg);
+        if (g.direct) {
+            uint64_t* word = c < n3 ? w.status3 + (size_t)ct * n3 + c : w.statusE + (size_t)ct * E + (c - n3);
+            status_store(word, status_make(epoch, false, agg));
+        } else if (c < n3) {
+            lookback_column(w.status3, ct, n3, c, epoch, agg);
+        } else {
+            lookback_column(w.statusE, ct, E, c - n3, epoch, agg);
+        }
+    }
+    if (g.direct && last_count_tile(hdr, g.nct, &s_arrived)) {
+        for (int c = tid; c < nc; c += kPlanBlock) {
+            if (c < n3) scan_count_column(w.status3, g.nct, n3, c, epoch);
+            else scan_count_column(w.statusE, g.nct, E, c - n3, epoch);
+        }
     }
 }
 
@@ -269,7 +302,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
     __shared__ int s_owner[kMaxE];
     __shared__ int s_cu_r[kMaxRanks + 1];
     __shared__ int s_excl[3 * kMaxRanks];
-    __shared__ int s_shard0[kMaxRanks];
+    __shared__ int s_ctp[3][3 * kMaxRanks];  // count-tile prefixes of the rank columns (kCt*)
     __shared__ int s_doff[2][kMaxRanks + 1];
     __shared__ uint32_t s_code[kPlanSlots];
     __shared__ int s_loff[kPlanSlots];
@@ -292,35 +325,12 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
     const int n3 = 3 * g.R;  // rank columns: look-back words and write-tile histograms
     const uint64_t* status = pw.status3;
 
-    // this thread's token: ids and permuted positions, loaded before anything else
-    const int64_t my_t = t0 + tid;
-    const bool my_live = tile >= 0 && tid < g.TT && my_t < t1;
-    int idk[KMAX], pk[KMAX];
-    load_token_ids<KMAX>(idk, ids, my_t, g.K, my_live);
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) pk[k] = (my_live && k < g.K) ? gptr(e2p)[my_t * g.K + k] : 0;
-
-    auto total_of = [&](int col) -> int {
-        return g.ntiles > 0 ? (int)status_value(status, g.nct - 1, n3, col) : 0;
-    };
-    // global exclusive prefix of a column before this write tile: earlier count tiles (look-back)
-    // plus the earlier write tiles of this count tile (their histograms)
-    auto prefix_here = [&](int col) -> int {
-        int v = ctile > 0 ? (int)status_value(status, ctile - 1, n3, col) : 0;
-        for (int j0 = ct_first_wt(g, ctile); j0 < tile; j0 += 8) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (j0 + j < tile) v += (int)status_value(pw.tilehist, j0 + j, g.ncols, col);
-        }
-        return v;
-    };
-
-    // ---- prologue --------------------------------------------------------------------------
+    // ---- prologue: every load the tile needs before its per-token pass, issued together ------
+    // Prefixes of the 3R rank columns: s_excl = before this write tile (the count tiles before
+    // its count tile plus the earlier write tiles of its count tile), and three count-tile
+    // prefixes (before the shard's first count tile, through this count tile, all).
+    enum { kCtShard0 = 0, kCtIncl = 1, kCtTotal = 2 };
     for (int e = tid; e < g.E; e += kPlanBlock) s_owner[e] = e / g.epn;
-    for (int r = tid; r <= R; r += kPlanBlock) s_cu_r[r] = cu_seqlens[r * g.epn];
-    for (int c = tid; c < 3 * R; c += kPlanBlock) s_excl[c] = tile >= 0 ? prefix_here(c) : 0;
-    for (int r = tid; r < R; r += kPlanBlock)
-        s_shard0[r] = ct_shard0 > 0 ? (int)status_value(status, ct_shard0 - 1, n3, r) : 0;
     for (int r = tid; r < R; r += kPlanBlock)
 #pragma unroll
         for (int ww = 0; ww < kPlanWaves; ++ww) {
@@ -328,10 +338,66 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
             s_dc[ww][r] = 0;
             s_mask[ww][r] = 0ull;
         }
+
+    // this thread's token: ids and permuted positions
+    const int64_t my_t = t0 + tid;
+    const bool my_live = tile >= 0 && tid < g.TT && my_t < t1;
+    const bool vec8 = g.K == 8 && ((((uintptr_t)ids) | ((uintptr_t)e2p)) & 15u) == 0;
+    int idk[KMAX], pk[KMAX];
+    load_token_row<KMAX>(idk, ids, my_t, g.K, my_live, vec8, -1);
+    load_token_row<KMAX>(pk, e2p, my_t, g.K, my_live, vec8, 0);
+    const int cu_r = tid <= R ? cu_seqlens[tid * g.epn] : 0;
+    // the per-expert tail's first expert of this wave: its inclusive prefixes at the shards' last
+    // count tiles (lane s2 < S) and at the last count tile, and its cu_seqlens entries
+    const int e_first = (int)blockIdx.x + w * (int)gridDim.x;
+    const bool tail_pref = g.ntiles > 0 && e_first < g.E && g.S <= 64;
+    int tail_hi = 0, tail_lo = 0, tail_tot = 0, tail_cu0 = 0, tail_cu1 = 0, tail_cuo = 0;
+    if (tail_pref) {
+        if (lane < g.S) {
+            tail_hi = (int)status_value(pw.statusE, (lane + 1) * g.ctps - 1, g.E, e_first);
+            tail_lo = lane > 0 ? (int)status_value(pw.statusE, lane * g.ctps - 1, g.E, e_first) : 0;
+        }
+        if (lane == 0) {
+            tail_tot = (int)status_value(pw.statusE, g.nct - 1, g.E, e_first);
+            tail_cu0 = cu_seqlens[e_first];
+            tail_cu1 = cu_seqlens[e_first + 1];
+            tail_cuo = cu_seqlens[(e_first / g.epn) * g.epn];
+        }
+    }
+    // the earlier write tiles of this count tile
+    const int first_wt = tile >= 0 ? ct_first_wt(g, ctile) : 0;
+    const int nwt = tile >= 0 ? tile - first_wt : 0;
+    for (int c = tid; c < n3; c += kPlanBlock) {
+        // inclusive count-tile prefixes at the four count tiles, plus the earlier write tiles
+        int sx = 0, s0 = 0, si = 0, stt = 0;
+        if (tile >= 0) {
+            const MEP_GLOBAL uint64_t* gs = gptr(status) + c;
+            const MEP_GLOBAL uint64_t* gt = gptr(pw.tilehist) + (size_t)first_wt * g.ncols + c;
+            sx = (int)(uint32_t)gs[(size_t)(ctile > 0 ? ctile - 1 : 0) * n3];
+            s0 = (int)(uint32_t)gs[(size_t)(ct_shard0 > 0 ? ct_shard0 - 1 : 0) * n3];
+            si = (int)(uint32_t)gs[(size_t)ctile * n3];
+            stt = (int)(uint32_t)gs[(size_t)(g.nct - 1) * n3];
+            if (ctile == 0) sx = 0;
+            if (ct_shard0 == 0) s0 = 0;
+            int v[8];
+            for (int j0 = 0; j0 < nwt; j0 += 8) {  // rows past the end re-read the last one
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = (int)(uint32_t)gt[(size_t)min(j0 + j, nwt - 1) * g.ncols];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) sx += j0 + j < nwt ? v[j] : 0;
+            }
+        }
+        s_excl[c] = sx;
+        s_ctp[kCtShard0][c] = s0;
+        s_ctp[kCtIncl][c] = si;
+        s_ctp[kCtTotal][c] = stt;
+    }
+    if (tid <= R) s_cu_r[tid] = cu_r;
+    __syncthreads();
     {
         // segment starts of every rank's groups and duplicates (exclusive prefix over ranks)
-        const int ng = tid < R ? total_of(R + tid) : 0;
-        const int nd = tid < R ? total_of(2 * R + tid) : 0;
+        const int ng = tid < R ? s_ctp[kCtTotal][R + tid] : 0;
+        const int nd = tid < R ? s_ctp[kCtTotal][2 * R + tid] : 0;
         int tg, td;
         const int eg = block_exclusive_scan<kPlanBlock>(ng, s_tmp, tg);
         const int ed = block_exclusive_scan<kPlanBlock>(nd, s_tmp, td);
@@ -479,7 +545,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
             for (int ww = 0; ww < wf; ++ww) cnt += popc64(s_mask[ww][r]);
             const int rem = L & 63;
             if (rem) cnt += popc64(s_mask[wf][r] & ((1ull << rem) - 1ull));
-            gptr(o.chan)[((int64_t)sh * R + r) * g.C + c] = s_excl[r] + cnt - s_shard0[r];
+            gptr(o.chan)[((int64_t)sh * R + r) * g.C + c] = s_excl[r] + cnt - s_ctp[kCtShard0][r];
         }
     }
 
@@ -487,28 +553,31 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
     if (tile >= 0 && ct == g.tps - 1) {
         // the count tile of a shard's last write tile ends at the shard's end
         for (int r = tid; r < R; r += kPlanBlock) {
-            const int incl = (int)status_value(status, ctile, n3, r);
+            const int incl = s_ctp[kCtIncl][r];
             if (o.rank_prefix) gptr(o.rank_prefix)[(int64_t)sh * R + r] = incl;
-            if (o.ntpr) gptr(o.ntpr)[(int64_t)sh * R + r] = incl - s_shard0[r];
+            if (o.ntpr) gptr(o.ntpr)[(int64_t)sh * R + r] = incl - s_ctp[kCtShard0][r];
         }
     }
 
-    // ---- per-shard expert counts and expert totals, a slice of the experts per workgroup:
-    // differences of the expert look-back's inclusive prefixes at the shards' last count tiles
+    // ---- per-shard expert counts and expert totals, one wave per expert, a slice of the
+    // experts per workgroup: differences of the inclusive prefixes at the shards' last count tiles
     if (g.ntiles > 0) {
-        for (int e = blockIdx.x + (tid / 64) * gridDim.x; e < g.E; e += gridDim.x * kPlanWaves) {
-            // one wave per expert: lane j takes shards j, j + 64, ...
+        for (int e = e_first; e < g.E; e += gridDim.x * kPlanWaves) {
+            const bool pref = tail_pref && e == e_first;
             for (int s2 = lane; s2 < g.S; s2 += 64) {
-                const int hi = (int)status_value(pw.statusE, (s2 + 1) * g.ctps - 1, g.E, e);
-                const int lo = s2 > 0 ? (int)status_value(pw.statusE, s2 * g.ctps - 1, g.E, e) : 0;
+                const int hi = pref ? tail_hi : (int)status_value(pw.statusE, (s2 + 1) * g.ctps - 1, g.E, e);
+                const int lo = pref ? tail_lo : s2 > 0 ? (int)status_value(pw.statusE, s2 * g.ctps - 1, g.E, e) : 0;
                 if (o.ntpe) gptr(o.ntpe)[(int64_t)s2 * g.E + e] = hi - lo;
             }
             if (o.recv_zf && lane == 0) {
-                const int cnt = (int)status_value(pw.statusE, g.nct - 1, g.E, e);
-                const int padded = cu_seqlens[e + 1] - cu_seqlens[e];
-                const bool z = cnt > 0 && padded > cnt;
-                gptr(o.recv_zf)[2 * e] = z ? cu_seqlens[e] + cnt - cu_seqlens[s_owner[e] * g.epn] : 0;
-                gptr(o.recv_zf)[2 * e + 1] = z ? padded - cnt : 0;
+                const int total = pref ? tail_tot : (int)status_value(pw.statusE, g.nct - 1, g.E, e);
+                const int cu0 = pref ? tail_cu0 : cu_seqlens[e];
+                const int cu1 = pref ? tail_cu1 : cu_seqlens[e + 1];
+                const int cuo = pref ? tail_cuo : cu_seqlens[s_owner[e] * g.epn];
+                const int padded = cu1 - cu0;
+                const bool z = total > 0 && padded > total;
+                gptr(o.recv_zf)[2 * e] = z ? cu0 + total - cuo : 0;
+                gptr(o.recv_zf)[2 * e + 1] = z ? padded - total : 0;
             }
         }
     }
@@ -516,7 +585,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
     // ---- block 0: per-rank outputs, empty-shard case, workspace reset ---------------------
     if (blockIdx.x == 0) {
         for (int r = tid; r < R; r += kPlanBlock) {
-            if (o.recv_tokens) gptr(o.recv_tokens)[r] = total_of(r);
+            if (o.recv_tokens) gptr(o.recv_tokens)[r] = s_ctp[kCtTotal][r];
             if (o.dup_counts) {
                 gptr(o.dup_counts)[2 * r] = s_doff[0][r + 1] - s_doff[0][r];
                 gptr(o.dup_counts)[2 * r + 1] = s_doff[1][r + 1] - s_doff[1][r];
@@ -574,6 +643,7 @@ static PlanGeom plan_geom(int64_t N, int E, int K, int R, int S, int C, int64_t 
     g.ctps = (int)ceil_div64(g.tps, sub);
     g.nct = S * g.ctps;
     g.ticketed = g.nct > kUnticketedCountTiles;
+    g.direct = g.nct <= kDirectCountTiles;
     return g;
 }
 

@@ -307,6 +307,8 @@ LAYOUT_CASES = [
     (640, 512, 16, 8, 8, 2, 24),       # K > 8 path
     (300, 1024, 32, 16, 128, 3, 4),    # K = 32, E = 1024
     (2000, 8, 8, 4, 8, 4, 24),         # epn = 1, K = E
+    (6000, 64, 4, 8, 8, 120, 3),       # 120 count tiles: plan prefixes through the look-back
+    (9000, 32, 2, 4, 4, 300, 2),       # 300 count tiles: look-back in ticket order
 ]
 
 
@@ -315,6 +317,7 @@ def test_layout_plan_sweep(N, E, K, A, R, S, C):
     _note("layout/plan N=%d E=%d K=%d A=%d R=%d S=%d C=%d" % (N, E, K, A, R, S, C))
     ids = synth.random_ids(N, E, K, seed=N + 31 * E + K, hot=min(4, E))
     check_layout_plan(ids, E, A, R, S, C)
+    check_layout_plan(ids, E, A, R, S, C, combined=True)
 
 
 def test_plan_larger_nvs_stride():

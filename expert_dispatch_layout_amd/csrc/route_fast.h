@@ -142,27 +142,23 @@ struct FastGeom {
     static constexpr int TPB = kFastWaves * TPW;  // token slots per block
 };
 
-// Issue the CPL coalesced 16-byte loads of token set `set`.  A complete set is one contiguous
-// run: a wave-uniform base plus a per-lane offset.  The last set clamps its rows to N - 1.
+// Issue the CPL coalesced 16-byte loads of token set `set` (rows are CPR 16-byte chunks, so a
+// complete set is one contiguous run).  Rows past the last token re-read row N - 1.  One
+// straight-line path: the loads of the two cases never compete for registers, so waiting for
+// them never has to wait for other loads in flight.
 template <int LPT, bool BF16>
 __device__ __forceinline__ void fast_load_set(const RouteArgs& a, int64_t set, int wl,
                                               u32x4 (&buf)[FastGeom<LPT, BF16>::CPL]) {
     using G = FastGeom<LPT, BF16>;
-    const int64_t row_bytes = (int64_t)a.E * (BF16 ? 2 : 4);
-    const MEP_GLOBAL char* base = gptr(reinterpret_cast<const char*>(a.logits));
-    if ((set + 1) * G::TPW <= a.N) {
-        const MEP_GLOBAL char* sb = base + set * G::TPW * row_bytes;
+    const MEP_GLOBAL u32x4* base = gptr(reinterpret_cast<const u32x4*>(a.logits));
+    const int64_t t0 = set * G::TPW;
+    const int64_t last = a.N - 1;
 #pragma unroll
-        for (int c = 0; c < G::CPL; ++c)
-            buf[c] = *reinterpret_cast<const MEP_GLOBAL u32x4*>(sb + (c * 64 + wl) * 16);
-    } else {
-#pragma unroll
-        for (int c = 0; c < G::CPL; ++c) {
-            const int q = c * 64 + wl;  // chunk of the set
-            const int r = q / G::CPR;
-            const int64_t t = min(set * G::TPW + r, a.N - 1);
-            buf[c] = *reinterpret_cast<const MEP_GLOBAL u32x4*>(base + t * row_bytes + (int64_t)(q - r * G::CPR) * 16);
-        }
+    for (int c = 0; c < G::CPL; ++c) {
+        const int q = c * 64 + wl;  // chunk of the set
+        const int r = q / G::CPR;   // its row (a shift: CPR is a power of two)
+        const int64_t t = min(t0 + r, last);
+        buf[c] = base[t * G::CPR + (q - r * G::CPR)];
     }
 }
 

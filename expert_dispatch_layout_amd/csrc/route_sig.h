@@ -28,8 +28,9 @@
 //   5. certification: the selection on the exact keys (correctly rounded sigmoid plus bias, both
 //      binary32) is the same when the last kept and first dropped group scores, and each pair
 //      of consecutive extracted keys, differ by more than the error bounds below, and every
-//      round had exactly one winner.  A token that fails is redone at once by the whole wave
-//      from the row still in LDS, on exact keys (exact_token_sig).
+//      round had exactly one winner.  A token that fails is recorded in LDS and redone after
+//      the streaming loop by a whole wave, on exact keys, from its row read again from global
+//      memory (exact_token_sig), so the loop itself holds no call.
 // The K selected experts then get their sigmoid in binary64 (relative error below 2^-30) for the
 // weights.
 //
@@ -53,6 +54,7 @@
 namespace mep {
 
 constexpr int kSigT = 6;                          // list depth per lane
+constexpr int kSigMaxSetsPerGroup = 4096;         // sets per workgroup at most (16 KB of LDS)
 constexpr int kSigEmpty = (int)0xFF800000u;       // -inf: below every key as float and as integer
 
 // LDS row layout: lane group g of a token (its CPL chunks) starts at chunk g * (CPL + 1).
@@ -67,6 +69,14 @@ struct SigGeom {
     // position in the row of chunk ch
     static __device__ __forceinline__ int pos(int ch) { return (ch / CPL) * GS + ch % CPL; }
 };
+
+// A volatile read of an LDS float, re-done wherever it stands (so the compiler does not keep the
+// value in a register across a loop).  The pointer is cast to the LDS address space: a generic
+// volatile access would become a flat load, which counts against the vector-memory counter and
+// would make the wait for it also wait for every global load in flight.
+__device__ __forceinline__ float lds_volatile_load(const float* p) {
+    return *(volatile const __attribute__((address_space(3))) float*)p;
+}
 
 struct SigCfg {
     int64_t nsets;  // token sets of 64 / LPT tokens
@@ -166,19 +176,18 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 // from; the arguments are taken by value (a reference to a kernel argument would put a copy of
 // it in scratch memory).
 template <int LPT, bool BF16, int MODE>
-__device__ __noinline__ void exact_token_sig(const RouteArgs a, const u32x4* row, int64_t tok, int tg,
-                                             int wl) {
-    using G = SigGeom<LPT, BF16>;
-    constexpr int W = G::W;
+__device__ __noinline__ void exact_token_sig(const RouteArgs a, int64_t tok, int tg, int wl) {
     constexpr int E = kFastEPL * LPT;
     constexpr int NPL = E / 64;    // 1, 2, 4 or 8 experts per lane
     constexpr int S = 32 / NPL;    // lanes per group of 32 experts
     const int K = a.K;
-    const char* rb = reinterpret_cast<const char*>(row);
+    // the token's row, read again from global memory
+    const MEP_GLOBAL char* rb = gptr(reinterpret_cast<const char*>(a.logits)) + tok * E * (BF16 ? 2 : 4);
     auto logit = [&](int e) -> float {
-        const char* p = rb + G::pos(e / W) * 16 + (e % W) * (BF16 ? 2 : 4);
-        return BF16 ? __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t*>(p)) << 16)
-                    : *reinterpret_cast<const float*>(p);
+        if constexpr (BF16)
+            return __uint_as_float((uint32_t)reinterpret_cast<const MEP_GLOBAL uint16_t*>(rb)[e] << 16);
+        else
+            return reinterpret_cast<const MEP_GLOBAL float*>(rb)[e];
     };
     uint64_t P[NPL];  // the lane's keys, sorted descending
 #pragma unroll
@@ -271,7 +280,7 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
     __shared__ float s_bconst[2];                   // constant terms of the two margins
 
     const int tid = threadIdx.x;
-    const int wv = tid >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the set loop is not divergent
     const int wl = tid & 63;
     const int tw = wl / LPT;
     const int lseg = wl % LPT;
@@ -283,14 +292,27 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
     const int64_t first_set = set_lo + wv;
     __shared__ int s_next;  // next unclaimed set of this workgroup, relative to set_lo
     if (tid == 0) s_next = NW;
+    // per set of this workgroup: its tokens that the filter could not certify (bit t = token t);
+    // they are redone exactly after the streaming loop, so the loop holds no call
+    extern __shared__ uint32_t s_fail[];
+    for (int i = tid; i < (int)(set_hi - set_lo); i += NT) s_fail[i] = 0u;
 
+    // the bias first (so that waiting for it does not also wait for the logits), then the first set
+    constexpr int BPL = LPT * NE / 64;  // bias entries per lane
+    const MEP_GLOBAL float* gb = gptr(a.bias);
+    float bv[BPL];
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) bv[i] = gb[i * 64 + wl];
+    __builtin_amdgcn_sched_barrier(0);  // keep the bias loads ahead of the logits loads
     u32x4 buf[CPL];
-    if (first_set < set_hi) fast_load_set<LPT, BF16>(a, first_set, wl, buf);
+    // loads are issued unconditionally (past the range: an earlier set again), so every path has
+    // the same loads in flight and a wait for one set never waits for another
+    fast_load_set<LPT, BF16>(a, min(first_set, max(set_hi - 1, (int64_t)0)), wl, buf);
 
     // ---- shift c, the error-bound constants, and the shifted biases --------------------------------
-    const MEP_GLOBAL float* gb = gptr(a.bias);
     float mb = 0.0f;
-    for (int e = wl; e < LPT * NE; e += 64) mb = fmaxf(mb, fabsf(gb[e]));
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) mb = fmaxf(mb, fabsf(bv[i]));
     const float maxb = wave_max_nonneg(mb);
     const bool finite = maxb < 0x1p20f;  // false for inf / NaN: every token takes the exact path
     const float c = 1.0f + maxb + 0x1p-10f;
@@ -304,7 +326,10 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
         s_bconst[1] = (float)((4.0 * D + 2.0 * H * 0x1p-24) * (1.0 + 0x1p-19));
     }
     const int e0 = lseg * NE;
-    for (int e = tid; e < LPT * NE; e += NT) reinterpret_cast<float*>(s_bsh4)[e] = gb[e] - c;
+    if (wv == 0) {
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) reinterpret_cast<float*>(s_bsh4)[i * 64 + wl] = bv[i] - c;
+    }
     __syncthreads();
 
     u32x4* my_rows = s_rows[wv];
@@ -360,14 +385,14 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
             if (wl == 0) claimed = atomicAdd(&s_next, 1);
             next_set = set_lo + __builtin_amdgcn_readfirstlane(claimed);
         }
-        if (next_set < set_hi) fast_load_set<LPT, BF16>(a, next_set, wl, buf);
+        fast_load_set<LPT, BF16>(a, next_set < set_hi ? next_set : set, wl, buf);
         wave_lds_sync();
 
         const int tok_raw = (int)set * TPW + tw;  // N * K < 2^31
         const bool live = tok_raw < (int)a.N;
         const int tok = live ? tok_raw : (int)a.N - 1;
-        const float b_gap = *reinterpret_cast<volatile const float*>(&s_bconst[0]);
-        const float b_grp = *reinterpret_cast<volatile const float*>(&s_bconst[1]);
+        const float b_gap = lds_volatile_load(&s_bconst[0]);
+        const float b_grp = lds_volatile_load(&s_bconst[1]);
 
         // ---- keys and the lane's top list ------------------------------------------------------
         int L[kSigT];
@@ -479,12 +504,26 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
             }
         }
 
-        // ---- uncertified tokens: exact, by the whole wave, from the row in LDS ------------------------
-        uint64_t fm = __ballot(fail && live && lseg == 0);
-        while (fm) {
-            const int t = __builtin_ctzll(fm) / LPT;
-            fm &= fm - 1;
-            exact_token_sig<LPT, BF16, MODE>(a, &my_rows[t * RS], set * TPW + t, cfg.tg, wl);
+        // ---- uncertified tokens: recorded for the exact pass after the loop ------------------------
+        const uint64_t fm = __ballot(fail && live && lseg == 0);
+        if (fm != 0ull && wl == 0) {
+            uint32_t m = 0u;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) m |= (uint32_t)((fm >> (t * LPT)) & 1ull) << t;
+            s_fail[set - set_lo] = m;
+        }
+    }
+
+    // ---- uncertified tokens of this workgroup's sets: exact, one token per wave in turn ----------
+    __syncthreads();
+    int idx = 0;
+    for (int i = 0; i < (int)(set_hi - set_lo); ++i) {
+        uint32_t m = s_fail[i];
+        while (m) {
+            const int t = __builtin_ctz(m);
+            m &= m - 1u;
+            if (idx % NW == wv) exact_token_sig<LPT, BF16, MODE>(a, (set_lo + i) * TPW + t, cfg.tg, wl);
+            ++idx;
         }
     }
 }

@@ -12,9 +12,13 @@ static void launch_sig(const RouteArgs& a, const Launch& st) {
     auto kernel = route_sig_kernel<LPT, BF16, MODE, NW>;
     const int64_t need = ceil_div64(cfg.nsets, NW);
     int64_t grid = resident_blocks(reinterpret_cast<const void*>(kernel), 64 * NW);
+    // more workgroups than fit at once when a workgroup would own more sets than its LDS list of
+    // uncertified tokens holds
+    if (grid < ceil_div64(cfg.nsets, kSigMaxSetsPerGroup)) grid = ceil_div64(cfg.nsets, kSigMaxSetsPerGroup);
     if (grid > need) grid = need;
     if (grid < 1) grid = 1;
-    launch_kernel(kernel, dim3((unsigned)grid), dim3(64 * NW), 0, st, a, cfg);
+    const int64_t spb = ceil_div64(cfg.nsets, grid);  // sets per workgroup (as the kernel computes)
+    launch_kernel(kernel, dim3((unsigned)grid), dim3(64 * NW), (uint32_t)(spb * sizeof(uint32_t)), st, a, cfg);
 }
 
 template <bool BF16, int MODE>

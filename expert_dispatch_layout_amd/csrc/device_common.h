@@ -166,13 +166,13 @@ __device__ __forceinline__ void scan_count_column(uint64_t* status, int nct, int
                                                   uint32_t epoch) {
     const uint32_t want = status_tag(epoch);
     uint32_t run = 0;
-    for (int j0 = 0; j0 < nct; j0 += 16) {
-        uint64_t v[16];
+    for (int j0 = 0; j0 < nct; j0 += 32) {  // 32 loads in flight (one round trip at <= 32 count tiles)
+        uint64_t v[32];
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
+        for (int j = 0; j < 32; ++j)
             v[j] = status_load(status + (size_t)min(j0 + j, nct - 1) * ncols + col);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < 32; ++j) {
             if (j0 + j >= nct) break;
             uint64_t* p = status + (size_t)(j0 + j) * ncols + col;
             run += tagged_value(p, v[j], want);

@@ -167,33 +167,56 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
 }
 
-// Exact routing of token `tok` whose row is at `row` in LDS (SigGeom layout), by the whole wave:
-// lane l takes experts [l*NPL, (l+1)*NPL); a key is the correctly rounded sigmoid plus the bias,
-// ordered by (key desc, expert asc) as one 64-bit word; group scores (binary32 sums of the top
-// keys) and ranks (score desc, group asc) as in the fast path but exact; then K rounds of a
-// wave-wide arg-max over the heads of the lanes' sorted keys.  Writes the K ids and weights.
-// Out of line, so that its registers do not add to those of the set loop it is rarely called
-// from; the arguments are taken by value (a reference to a kernel argument would put a copy of
-// it in scratch memory).
+// Exact routing of token `tok` by the whole wave, from its row in global memory: lane l takes
+// experts [l*NPL, (l+1)*NPL); a key is the correctly rounded sigmoid plus the bias, ordered by
+// (key desc, expert asc) as one 64-bit word; group scores (binary32 sums of the top keys) and
+// ranks (score desc, group asc) as in the fast path but exact; then K rounds of a wave-wide
+// arg-max over the heads of the lanes' sorted keys.  Writes the K ids and weights.  Out of line,
+// so that its registers do not add to those of the kernel; the fields it needs are passed one by
+// one (a structure passed by value goes through scratch memory, a round trip per field).
 template <int LPT, bool BF16, int MODE>
-__device__ __noinline__ void exact_token_sig(const RouteArgs a, int64_t tok, int tg, int wl) {
+__device__ __forceinline__ void exact_token_sig(const void* logits, const float* bias, int32_t* ids,
+                                             float* weights, int K, int group_topn, int renormalize,
+                                             float scale, int64_t tok, int tg, int wl,
+                                             const u32x4* lds_row) {
     constexpr int E = kFastEPL * LPT;
     constexpr int NPL = E / 64;    // 1, 2, 4 or 8 experts per lane
     constexpr int S = 32 / NPL;    // lanes per group of 32 experts
-    const int K = a.K;
-    // the token's row, read again from global memory
-    const MEP_GLOBAL char* rb = gptr(reinterpret_cast<const char*>(a.logits)) + tok * E * (BF16 ? 2 : 4);
+    // the token's row: a copy in LDS (`lds_row`, plain layout), else read again from global memory
+    const MEP_GLOBAL char* rb = gptr(reinterpret_cast<const char*>(logits)) + tok * E * (BF16 ? 2 : 4);
+    const char* lb = reinterpret_cast<const char*>(lds_row);
     auto logit = [&](int e) -> float {
+        if (lb) {
+            if constexpr (BF16)
+                return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(lb)[e] << 16);
+            else
+                return reinterpret_cast<const float*>(lb)[e];
+        }
         if constexpr (BF16)
             return __uint_as_float((uint32_t)reinterpret_cast<const MEP_GLOBAL uint16_t*>(rb)[e] << 16);
         else
             return reinterpret_cast<const MEP_GLOBAL float*>(rb)[e];
     };
+    // every load first (the sigmoid's rare slow path is a call, which later loads could not pass)
+    float xs[NPL], bs[NPL], sv[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        xs[i] = logit(wl * NPL + i);
+        bs[i] = gptr(bias)[wl * NPL + i];
+    }
+    // the correctly rounded sigmoids: every fast path first (independent chains the compiler can
+    // interleave), then the rare values the binary64 interval could not decide
+    bool ok[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) sv[i] = sigmoid_cr_fast(xs[i], ok[i]);
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+        if (!ok[i]) sv[i] = sigmoid_cr_slow(xs[i]);
     uint64_t P[NPL];  // the lane's keys, sorted descending
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
         const int e = wl * NPL + i;
-        const float key = sigmoid_cr(logit(e)) + gptr(a.bias)[e];
+        const float key = sv[i] + bs[i];
         uint64_t v = ((uint64_t)order_key(key) << 32) | (uint32_t)~(uint32_t)e;
 #pragma unroll
         for (int j = 0; j < i; ++j) {  // insertion into the sorted prefix
@@ -219,7 +242,7 @@ __device__ __noinline__ void exact_token_sig(const RouteArgs a, int64_t tok, int
         if constexpr (S >= 16) merge([](uint32_t u) { return seg_partner_u32<8>(u); });
         if constexpr (S >= 32) merge([](uint32_t u) { return seg_partner_u32<16>(u); });
         const float f1 = order_key_inv((uint32_t)(t1 >> 32));
-        const float score = a.group_topn >= 2 ? f1 + order_key_inv((uint32_t)(t2 >> 32)) : f1;
+        const float score = group_topn >= 2 ? f1 + order_key_inv((uint32_t)(t2 >> 32)) : f1;
         const int g = wl / S;
         const uint64_t gk = ((uint64_t)order_key(score) << 32) | (uint32_t)~(uint32_t)g;
         int rank = 0;
@@ -244,13 +267,20 @@ __device__ __noinline__ void exact_token_sig(const RouteArgs a, int64_t tok, int
         P[NPL - 1] = win ? 0 : P[NPL - 1];
         if (wl == r) my_e = (int)~(uint32_t)mx;
     }
-    // weights from the correctly rounded sigmoid of the selected experts (lanes 0..K-1)
-    const double v = wl < K ? (double)sigmoid_cr(logit(my_e)) : 0.0;
+    // weights from the correctly rounded sigmoid of the selected experts (lanes 0..K-1), taken
+    // from the lane that holds each
+    float s_sel = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const float u = __shfl(sv[i], (my_e / NPL) & 63);
+        s_sel = (my_e % NPL) == i ? u : s_sel;
+    }
+    const double v = wl < K ? (double)s_sel : 0.0;
     const double den = seg_allreduce<8>(v, 8, PartnerF64{}, [](double x, double y) { return x + y; });
     if (wl < K) {
-        const double inv = a.renormalize ? (den > 0.0 ? recip_f64(den) : 0.0) : 1.0;
-        gptr(a.ids)[tok * K + wl] = my_e;
-        if (a.weights) gptr(a.weights)[tok * K + wl] = (float)((v * inv) * (double)a.scale);
+        const double inv = renormalize ? (den > 0.0 ? recip_f64(den) : 0.0) : 1.0;
+        gptr(ids)[tok * K + wl] = my_e;
+        if (weights) gptr(weights)[tok * K + wl] = (float)((v * inv) * (double)scale);
     }
 }
 
@@ -292,6 +322,12 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
     const int64_t first_set = set_lo + wv;
     __shared__ int s_next;  // next unclaimed set of this workgroup, relative to set_lo
     if (tid == 0) s_next = NW;
+    // a copy of the first uncertified token's row (when the LDS budget of four workgroups per CU
+    // leaves room), so the exact pass usually reads no row from global memory
+    constexpr bool kStash = (NW * TPW * RS + LPT * kFastEPL / 4 + CPR) * 16 + 1024 <= 40 * 1024;
+    __shared__ u32x4 s_xrow[kStash ? CPR : 1];
+    __shared__ int s_xtok;  // its token, or -1
+    if (tid == 0) s_xtok = -1;
     // per set of this workgroup: its tokens that the filter could not certify (bit t = token t);
     // they are redone exactly after the streaming loop, so the loop holds no call
     extern __shared__ uint32_t s_fail[];
@@ -506,11 +542,21 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
 
         // ---- uncertified tokens: recorded for the exact pass after the loop ------------------------
         const uint64_t fm = __ballot(fail && live && lseg == 0);
-        if (fm != 0ull && wl == 0) {
-            uint32_t m = 0u;
+        if (fm != 0ull) {
+            if (wl == 0) {
+                uint32_t m = 0u;
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) m |= (uint32_t)((fm >> (t * LPT)) & 1ull) << t;
-            s_fail[set - set_lo] = m;
+                for (int t = 0; t < TPW; ++t) m |= (uint32_t)((fm >> (t * LPT)) & 1ull) << t;
+                s_fail[set - set_lo] = m;
+            }
+            if constexpr (kStash) {
+                const int t0 = __builtin_ctzll(fm) / LPT;
+                int won = 0;
+                if (wl == 0) won = atomicCAS(&s_xtok, -1, (int)(set * TPW + t0)) == -1;
+                if (__builtin_amdgcn_readfirstlane(won)) {
+                    for (int ch = wl; ch < CPR; ch += 64) s_xrow[ch] = my_rows[t0 * RS + G::pos(ch)];
+                }
+            }
         }
     }
 
@@ -522,7 +568,13 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
         while (m) {
             const int t = __builtin_ctz(m);
             m &= m - 1u;
-            if (idx % NW == wv) exact_token_sig<LPT, BF16, MODE>(a, (set_lo + i) * TPW + t, cfg.tg, wl);
+            if (idx % NW == wv) {
+                const int64_t tok = (set_lo + i) * TPW + t;
+                const bool stashed = kStash && tok == (int64_t)s_xtok;
+                exact_token_sig<LPT, BF16, MODE>(a.logits, a.bias, a.ids, a.weights, K, a.group_topn,
+                                                 a.renormalize, a.scale, tok, cfg.tg, wl,
+                                                 stashed ? s_xrow : nullptr);
+            }
             ++idx;
         }
     }

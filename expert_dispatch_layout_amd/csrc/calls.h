@@ -138,6 +138,9 @@ void layout_launch(const LayoutCall& c, hipStream_t st);
 // The layout's scatter pass over the plan's tiles, from the plan's counting pass (mep_layout_plan).
 void layout_launch_scatter_from_plan(const LayoutCall& lc, const PlanCall& pc, hipStream_t st);
 void plan_launch_count(const PlanCall& c, hipStream_t st);
+// The scatter and write passes of mep_layout_plan in one kernel (after plan_launch_count); two
+// kernels for K > 8.
+void plan_launch_scatter_write(const LayoutCall& lc, const PlanCall& pc, hipStream_t st);
 void plan_launch_write(const PlanCall& c, hipStream_t st);
 
 }  // namespace mep

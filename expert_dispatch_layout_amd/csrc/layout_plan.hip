@@ -1,8 +1,9 @@
-// mep_layout_plan: the layout and the plan of one batch in one call, three kernels instead of
-// four: the plan's counting pass also takes the per-expert counts of its tiles through a
-// look-back, which gives the layout's totals and prefixes, so the layout's own counting pass is
-// not needed; the layout's scatter pass then runs over the plan's tiles, and the plan's writing
-// pass follows.  The results are those of mep_build_layout followed by mep_plan.
+// mep_layout_plan: the layout and the plan of one batch in one call, two kernels instead of
+// four: the plan's counting pass also takes the per-expert counts of its tiles, which gives the
+// layout's totals and prefixes, so the layout's own counting pass is not needed; then one kernel
+// scatters each of the plan's tiles (the layout) and writes that tile's part of the plan from the
+// ids and permuted positions it keeps in LDS.  The results are those of mep_build_layout
+// followed by mep_plan.
 #include "calls.h"
 #include "host_common.h"
 
@@ -23,7 +24,6 @@ extern "C" int mep_layout_plan(const int32_t* topk_ids, int64_t N, int E, int K,
     if (rc != MEP_OK) return rc;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     plan_launch_count(pc, st);
-    layout_launch_scatter_from_plan(lc, pc, st);
-    plan_launch_write(pc, st);
+    plan_launch_scatter_write(lc, pc, st);
     return launch_status();
 }

@@ -30,6 +30,7 @@
 #include "device_common.h"
 #include "host_common.h"
 #include "calls.h"
+#include "layout_scatter.h"
 
 namespace mep {
 
@@ -295,21 +296,70 @@ __global__ __launch_bounds__(kPlanBlock) void plan_count_kernel(const int32_t* _
 
 enum : uint32_t { kNone = 0, kHead = 1, kDup = 2 };
 
-template <int KMAX, int NB>
-__global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
-    const int32_t* __restrict__ ids, const int32_t* __restrict__ cu_seqlens,
-    const int32_t* __restrict__ e2p, PlanGeom g, PlanWs pw, WsHeader* hdr, PlanOutDev o) {
-    __shared__ int s_owner[kMaxE];
-    __shared__ int s_cu_r[kMaxRanks + 1];
-    __shared__ int s_excl[3 * kMaxRanks];
-    __shared__ int s_ctp[3][3 * kMaxRanks];  // count-tile prefixes of the rank columns (kCt*)
-    __shared__ int s_doff[2][kMaxRanks + 1];
-    __shared__ uint32_t s_code[kPlanSlots];
-    __shared__ int s_loff[kPlanSlots];
-    __shared__ int s_hc[kPlanWaves][kMaxRanks];
-    __shared__ int s_dc[kPlanWaves][kMaxRanks];
-    __shared__ uint64_t s_mask[kPlanWaves][kMaxRanks];
-    __shared__ int s_tmp[kPlanWaves];
+// LDS of one write tile.
+struct WriteLds {
+    int* owner;                   // [kMaxE] owner rank of each expert
+    int* cu_r;                    // [kMaxRanks + 1] cu_seqlens at each rank's first expert
+    int* excl;                    // [3 * kMaxRanks] rank-column prefixes before this write tile
+    int (*ctp)[3 * kMaxRanks];    // [3] count-tile prefixes of the rank columns (kCt*)
+    int (*doff)[kMaxRanks + 1];   // [2] segment starts of the groups / duplicates per rank
+    uint32_t* code;               // [kPlanSlots] slot codes
+    int* loff;                    // [kPlanSlots] rank-local offsets
+    int (*hc)[kMaxRanks];         // [waves] per-(wave, rank) head counters
+    int (*dc)[kMaxRanks];         // [waves] per-(wave, rank) duplicate counters
+    uint64_t (*mask)[kMaxRanks];  // [waves] per-(wave, rank) token ballots
+    int* tmp;                     // [waves]
+};
+
+// Where a write tile takes its tokens' ids and permuted positions and the cu_seqlens entries:
+// global memory (mep_plan), or the LDS that the scatter phase of the same workgroup left them in
+// (the fused kernel of mep_layout_plan: ids and positions by slot of the tile, cu_seqlens whole).
+struct WriteSrcGlobal {
+    const int32_t* ids;
+    const int32_t* pos;
+    const int32_t* cu;
+    template <int KMAX>
+    __device__ __forceinline__ void token(int (&idk)[KMAX], int (&pk)[KMAX], int64_t t, int /*li*/, int K,
+                                          bool live) const {
+        const bool vec8 = K == 8 && ((((uintptr_t)ids) | ((uintptr_t)pos)) & 15u) == 0;
+        load_token_row<KMAX>(idk, ids, t, K, live, vec8, -1);
+        load_token_row<KMAX>(pk, pos, t, K, live, vec8, 0);
+    }
+    __device__ __forceinline__ int cuv(int i) const { return gptr(cu)[i]; }
+};
+struct WriteSrcLds {
+    const int* ids;  // [tokens of the tile * K] by slot of the tile
+    const int* pos;
+    const int* cu;   // [E + 1]
+    template <int KMAX>
+    __device__ __forceinline__ void token(int (&idk)[KMAX], int (&pk)[KMAX], int64_t /*t*/, int li, int K,
+                                          bool live) const {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            idk[k] = (live && k < K) ? ids[li * K + k] : -1;
+            pk[k] = (live && k < K) ? pos[li * K + k] : 0;
+        }
+    }
+    __device__ __forceinline__ int cuv(int i) const { return cu[i]; }
+};
+
+// One write tile by a workgroup of NT threads (NT / 64 waves, one thread per token of the tile).
+template <int KMAX, int NB, int NT, class Src>
+__device__ __forceinline__ void plan_write_tile(const Src& src, const PlanGeom& g, const PlanWs& pw,
+                                                WsHeader* hdr, const PlanOutDev& o, const WriteLds& L) {
+    constexpr int kWTWaves = NT / kWave;
+    static_assert(NT >= kPlanBlock, "a thread per token");
+    int* s_owner = L.owner;
+    int* s_cu_r = L.cu_r;
+    int* s_excl = L.excl;
+    int (*s_ctp)[3 * kMaxRanks] = L.ctp;
+    int (*s_doff)[kMaxRanks + 1] = L.doff;
+    uint32_t* s_code = L.code;
+    int* s_loff = L.loff;
+    int (*s_hc)[kMaxRanks] = L.hc;
+    int (*s_dc)[kMaxRanks] = L.dc;
+    uint64_t (*s_mask)[kMaxRanks] = L.mask;
+    int* s_tmp = L.tmp;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -330,10 +380,10 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
     // its count tile plus the earlier write tiles of its count tile), and three count-tile
     // prefixes (before the shard's first count tile, through this count tile, all).
     enum { kCtShard0 = 0, kCtIncl = 1, kCtTotal = 2 };
-    for (int e = tid; e < g.E; e += kPlanBlock) s_owner[e] = e / g.epn;
-    for (int r = tid; r < R; r += kPlanBlock)
+    for (int e = tid; e < g.E; e += NT) s_owner[e] = e / g.epn;
+    for (int r = tid; r < R; r += NT)
 #pragma unroll
-        for (int ww = 0; ww < kPlanWaves; ++ww) {
+        for (int ww = 0; ww < kWTWaves; ++ww) {
             s_hc[ww][r] = 0;
             s_dc[ww][r] = 0;
             s_mask[ww][r] = 0ull;
@@ -342,11 +392,9 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
     // this thread's token: ids and permuted positions
     const int64_t my_t = t0 + tid;
     const bool my_live = tile >= 0 && tid < g.TT && my_t < t1;
-    const bool vec8 = g.K == 8 && ((((uintptr_t)ids) | ((uintptr_t)e2p)) & 15u) == 0;
     int idk[KMAX], pk[KMAX];
-    load_token_row<KMAX>(idk, ids, my_t, g.K, my_live, vec8, -1);
-    load_token_row<KMAX>(pk, e2p, my_t, g.K, my_live, vec8, 0);
-    const int cu_r = tid <= R ? cu_seqlens[tid * g.epn] : 0;
+    src.template token<KMAX>(idk, pk, my_t, tid, g.K, my_live);
+    const int cu_r = tid <= R ? src.cuv(tid * g.epn) : 0;
     // the per-expert tail's first expert of this wave: its inclusive prefixes at the shards' last
     // count tiles (lane s2 < S) and at the last count tile, and its cu_seqlens entries
     const int e_first = (int)blockIdx.x + w * (int)gridDim.x;
@@ -359,15 +407,15 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
         }
         if (lane == 0) {
             tail_tot = (int)status_value(pw.statusE, g.nct - 1, g.E, e_first);
-            tail_cu0 = cu_seqlens[e_first];
-            tail_cu1 = cu_seqlens[e_first + 1];
-            tail_cuo = cu_seqlens[(e_first / g.epn) * g.epn];
+            tail_cu0 = src.cuv(e_first);
+            tail_cu1 = src.cuv(e_first + 1);
+            tail_cuo = src.cuv((e_first / g.epn) * g.epn);
         }
     }
     // the earlier write tiles of this count tile
     const int first_wt = tile >= 0 ? ct_first_wt(g, ctile) : 0;
     const int nwt = tile >= 0 ? tile - first_wt : 0;
-    for (int c = tid; c < n3; c += kPlanBlock) {
+    for (int c = tid; c < n3; c += NT) {
         // inclusive count-tile prefixes at the four count tiles, plus the earlier write tiles
         int sx = 0, s0 = 0, si = 0, stt = 0;
         if (tile >= 0) {
@@ -399,8 +447,8 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
         const int ng = tid < R ? s_ctp[kCtTotal][R + tid] : 0;
         const int nd = tid < R ? s_ctp[kCtTotal][2 * R + tid] : 0;
         int tg, td;
-        const int eg = block_exclusive_scan<kPlanBlock>(ng, s_tmp, tg);
-        const int ed = block_exclusive_scan<kPlanBlock>(nd, s_tmp, td);
+        const int eg = block_exclusive_scan<NT>(ng, s_tmp, tg);
+        const int ed = block_exclusive_scan<NT>(nd, s_tmp, td);
         if (tid < R) {
             s_doff[0][tid] = eg;
             s_doff[1][tid] = ed;
@@ -452,8 +500,8 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
     __syncthreads();
 
     // ---- slot pass 1: stable ranks among same-rank heads / duplicates of this wave --------
-    constexpr int kIters = kPlanSlots / kPlanWaves / kWave;  // 8
-    const int per_wave = (nslots + kPlanWaves - 1) / kPlanWaves;
+    constexpr int kIters = kPlanSlots / kWTWaves / kWave;  // 8
+    const int per_wave = (nslots + kWTWaves - 1) / kWTWaves;
     const int wbeg = w * per_wave;
     const int wend = min(nslots, wbeg + per_wave);
     int hrank[kIters];
@@ -487,10 +535,10 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
         }
     }
     __syncthreads();
-    for (int r = tid; r < R; r += kPlanBlock) {
+    for (int r = tid; r < R; r += NT) {
         int hr = 0, dr = 0;
 #pragma unroll
-        for (int ww = 0; ww < kPlanWaves; ++ww) {
+        for (int ww = 0; ww < kWTWaves; ++ww) {
             const int hc = s_hc[ww][r], dc = s_dc[ww][r];
             s_hc[ww][r] = hr;
             s_dc[ww][r] = dr;
@@ -536,7 +584,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
         int c_hi = c_lo;
         while (c_hi < g.C && min((int64_t)(c_hi + 1) * q, (int64_t)g.n) <= tl1) ++c_hi;
         const int npairs = (c_hi - c_lo) * R;
-        for (int p = tid; p < npairs; p += kPlanBlock) {
+        for (int p = tid; p < npairs; p += NT) {
             const int c = c_lo + p / R;
             const int r = p - (p / R) * R;
             const int L = (int)(min((int64_t)(c + 1) * q, (int64_t)g.n) - tl0);  // tokens before the end
@@ -552,7 +600,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
     // ---- per-shard matrices from the last tile of each shard -----------------------------
     if (tile >= 0 && ct == g.tps - 1) {
         // the count tile of a shard's last write tile ends at the shard's end
-        for (int r = tid; r < R; r += kPlanBlock) {
+        for (int r = tid; r < R; r += NT) {
             const int incl = s_ctp[kCtIncl][r];
             if (o.rank_prefix) gptr(o.rank_prefix)[(int64_t)sh * R + r] = incl;
             if (o.ntpr) gptr(o.ntpr)[(int64_t)sh * R + r] = incl - s_ctp[kCtShard0][r];
@@ -562,7 +610,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
     // ---- per-shard expert counts and expert totals, one wave per expert, a slice of the
     // experts per workgroup: differences of the inclusive prefixes at the shards' last count tiles
     if (g.ntiles > 0) {
-        for (int e = e_first; e < g.E; e += gridDim.x * kPlanWaves) {
+        for (int e = e_first; e < g.E; e += gridDim.x * kWTWaves) {
             const bool pref = tail_pref && e == e_first;
             for (int s2 = lane; s2 < g.S; s2 += 64) {
                 const int hi = pref ? tail_hi : (int)status_value(pw.statusE, (s2 + 1) * g.ctps - 1, g.E, e);
@@ -571,9 +619,9 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
             }
             if (o.recv_zf && lane == 0) {
                 const int total = pref ? tail_tot : (int)status_value(pw.statusE, g.nct - 1, g.E, e);
-                const int cu0 = pref ? tail_cu0 : cu_seqlens[e];
-                const int cu1 = pref ? tail_cu1 : cu_seqlens[e + 1];
-                const int cuo = pref ? tail_cuo : cu_seqlens[s_owner[e] * g.epn];
+                const int cu0 = pref ? tail_cu0 : src.cuv(e);
+                const int cu1 = pref ? tail_cu1 : src.cuv(e + 1);
+                const int cuo = pref ? tail_cuo : src.cuv(s_owner[e] * g.epn);
                 const int padded = cu1 - cu0;
                 const bool z = total > 0 && padded > total;
                 gptr(o.recv_zf)[2 * e] = z ? cu0 + total - cuo : 0;
@@ -584,7 +632,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
 
     // ---- block 0: per-rank outputs, empty-shard case, workspace reset ---------------------
     if (blockIdx.x == 0) {
-        for (int r = tid; r < R; r += kPlanBlock) {
+        for (int r = tid; r < R; r += NT) {
             if (o.recv_tokens) gptr(o.recv_tokens)[r] = s_ctp[kCtTotal][r];
             if (o.dup_counts) {
                 gptr(o.dup_counts)[2 * r] = s_doff[0][r + 1] - s_doff[0][r];
@@ -592,34 +640,96 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
             }
         }
         if (o.dup_offsets)
-            for (int r = tid; r <= R; r += kPlanBlock) {
+            for (int r = tid; r <= R; r += NT) {
                 gptr(o.dup_offsets)[2 * r] = s_doff[0][r];
                 gptr(o.dup_offsets)[2 * r + 1] = s_doff[1][r];
             }
         if (o.recv_cu)
-            for (int p = tid; p < R * (g.epn + 1); p += kPlanBlock) {
+            for (int p = tid; p < R * (g.epn + 1); p += NT) {
                 const int r = p / (g.epn + 1);
                 const int j = p - r * (g.epn + 1);
-                gptr(o.recv_cu)[p] = cu_seqlens[r * g.epn + j] - s_cu_r[r];
+                gptr(o.recv_cu)[p] = src.cuv(r * g.epn + j) - s_cu_r[r];
             }
 
         if (g.ntiles == 0) {  // no tokens: every per-shard matrix is zero
-            for (int p = tid; p < g.S * R; p += kPlanBlock) {
+            for (int p = tid; p < g.S * R; p += NT) {
                 if (o.rank_prefix) gptr(o.rank_prefix)[p] = 0;
                 if (o.ntpr) gptr(o.ntpr)[p] = 0;
             }
             if (o.ntpe)
-                for (int p = tid; p < g.S * g.E; p += kPlanBlock) gptr(o.ntpe)[p] = 0;
+                for (int p = tid; p < g.S * g.E; p += NT) gptr(o.ntpe)[p] = 0;
             if (o.recv_zf)
-                for (int p = tid; p < 2 * g.E; p += kPlanBlock) gptr(o.recv_zf)[p] = 0;
+                for (int p = tid; p < 2 * g.E; p += NT) gptr(o.recv_zf)[p] = 0;
             if (o.chan)
-                for (int64_t p = tid; p < (int64_t)g.S * R * g.C; p += kPlanBlock) gptr(o.chan)[p] = 0;
+                for (int64_t p = tid; p < (int64_t)g.S * R * g.C; p += NT) gptr(o.chan)[p] = 0;
         }
         if (tid == 0) {
             gptr(hdr)->epoch = gptr(hdr)->epoch + 1u;
             gptr(hdr)->ticket = 0u;
         }
     }
+}
+
+
+template <int KMAX, int NB>
+__global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ e2p, PlanGeom g, PlanWs pw, WsHeader* hdr, PlanOutDev o) {
+    __shared__ int s_owner[kMaxE];
+    __shared__ int s_cu_r[kMaxRanks + 1];
+    __shared__ int s_excl[3 * kMaxRanks];
+    __shared__ int s_ctp[3][3 * kMaxRanks];
+    __shared__ int s_doff[2][kMaxRanks + 1];
+    __shared__ uint32_t s_code[kPlanSlots];
+    __shared__ int s_loff[kPlanSlots];
+    __shared__ int s_hc[kPlanWaves][kMaxRanks];
+    __shared__ int s_dc[kPlanWaves][kMaxRanks];
+    __shared__ uint64_t s_mask[kPlanWaves][kMaxRanks];
+    __shared__ int s_tmp[kPlanWaves];
+    const WriteLds L{s_owner, s_cu_r, s_excl, s_ctp, s_doff, s_code, s_loff, s_hc, s_dc, s_mask, s_tmp};
+    plan_write_tile<KMAX, NB, kPlanBlock>(WriteSrcGlobal{ids, e2p, cu_seqlens}, g, pw, hdr, o, L);
+}
+
+// The scatter and write passes of mep_layout_plan in one kernel: a workgroup scatters its plan
+// tile (layout_scatter.h), keeps the tile's ids and permuted positions in LDS, and writes its
+// part of the plan from them (cu_seqlens from its own padded scan).  The write phase's large LDS
+// arrays reuse the scatter phase's per-(wave, expert) counters, free by then.
+template <int NBE, int KMAX, int NB>
+__global__ __launch_bounds__(kScatBlock) void plan_scatter_write_kernel(const int32_t* __restrict__ ids, int A,
+                                                                        ScatterSrc src, WsHeader* hdr,
+                                                                        LayoutOut lout, PlanOutDev o) {
+    constexpr int kW = kScatBlock / kWave;
+    __shared__ int s_cu[kMaxExperts + 1];
+    __shared__ int s_tot[kMaxExperts];
+    __shared__ int s_base[kMaxExperts];
+    __shared__ int s_loc[kMaxExperts];
+    __shared__ __align__(16) int s_cnt[kScatWaves][kMaxExperts];
+    __shared__ int s_tmp[kScatWaves];
+    __shared__ int s_slot[kLayTile];
+    __shared__ int s_pos[kLayTile];
+    __shared__ int s_owner[kMaxE];
+    __shared__ int s_cu_r[kMaxRanks + 1];
+    __shared__ int s_excl[3 * kMaxRanks];
+    __shared__ int s_ctp[3][3 * kMaxRanks];
+    __shared__ int s_doff[2][kMaxRanks + 1];
+    __shared__ int s_wtmp[kW];
+    // the write phase's slot codes, offsets and per-wave counters inside s_cnt
+    static_assert(sizeof(uint32_t) * kPlanSlots * 2 + (sizeof(int) * 2 + sizeof(uint64_t)) * kW * kMaxRanks <=
+                      sizeof(int) * kScatWaves * kMaxExperts,
+                  "the write arrays fit in the scatter counters");
+    static_assert(kLayTile >= kPlanSlots, "a plan tile fits a scatter tile");
+    char* big = reinterpret_cast<char*>(&s_cnt[0][0]);
+    uint32_t* w_code = reinterpret_cast<uint32_t*>(big);
+    int* w_loff = reinterpret_cast<int*>(big + 4 * kPlanSlots);
+    int (*w_hc)[kMaxRanks] = reinterpret_cast<int (*)[kMaxRanks]>(big + 8 * kPlanSlots);
+    int (*w_dc)[kMaxRanks] = reinterpret_cast<int (*)[kMaxRanks]>(big + 8 * kPlanSlots + 4 * kW * kMaxRanks);
+    uint64_t (*w_mask)[kMaxRanks] = reinterpret_cast<uint64_t (*)[kMaxRanks]>(big + 8 * kPlanSlots + 8 * kW * kMaxRanks);
+
+    const ScatterLds SL{s_cu, s_tot, s_base, s_loc, s_cnt, s_tmp, s_slot, s_pos};
+    scatter_tile<NBE>(ids, src.pg.E, A, src, hdr, lout, SL, s_slot, s_pos);
+    __syncthreads();
+    const WriteLds WL{s_owner, s_cu_r, s_excl, s_ctp, s_doff, w_code, w_loff, w_hc, w_dc, w_mask, s_wtmp};
+    plan_write_tile<KMAX, NB, kScatBlock>(WriteSrcLds{s_slot, s_pos, s_cu}, src.pg, src.pw, hdr, o, WL);
 }
 
 static PlanGeom plan_geom(int64_t N, int E, int K, int R, int S, int C, int64_t NvS) {
@@ -745,6 +855,27 @@ void plan_launch_count(const PlanCall& c, hipStream_t st) {
         if (g.R <= 32) launch(plan_count_kernel<32, 1>);
         else launch(plan_count_kernel<32, 4>);
     }
+}
+
+void plan_launch_scatter_write(const LayoutCall& lc, const PlanCall& c, hipStream_t st) {
+    const PlanGeom& g = c.g;
+    if (g.K > 8) {  // the per-token arrays of K up to 32 need the registers of 512-thread groups
+        layout_launch_scatter_from_plan(lc, c, st);
+        plan_launch_write(c, st);
+        return;
+    }
+    ScatterSrc src{};
+    src.plan = 1;
+    src.pg = g;
+    src.pw = c.pw;
+    const int grid = g.ntiles > 0 ? g.ntiles : 1;
+    auto launch = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kScatBlock), 0, st, c.ids, lc.A, src, c.hdr, lc.out, c.o);
+    };
+    const bool wideE = g.E > 256;  // expert ids need 10 bits for the scatter's wave matching
+    if (g.R <= 8) wideE ? launch(plan_scatter_write_kernel<10, 8, 3>) : launch(plan_scatter_write_kernel<8, 8, 3>);
+    else if (g.R <= 32) wideE ? launch(plan_scatter_write_kernel<10, 8, 5>) : launch(plan_scatter_write_kernel<8, 8, 5>);
+    else wideE ? launch(plan_scatter_write_kernel<10, 8, 7>) : launch(plan_scatter_write_kernel<8, 8, 7>);
 }
 
 void plan_launch_write(const PlanCall& c, hipStream_t st) {

@@ -341,8 +341,8 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
     for (int i = 0; i < BPL; ++i) bv[i] = gb[i * 64 + wl];
     __builtin_amdgcn_sched_barrier(0);  // keep the bias loads ahead of the logits loads
     u32x4 buf[CPL];
-    // loads are issued unconditionally (past the range: an earlier set again), so every path has
-    // the same loads in flight and a wait for one set never waits for another
+    // (a wave without a set of its own loads the workgroup's last one, unused, so that the loads
+    // in flight are the same on every path into the loop)
     fast_load_set<LPT, BF16>(a, min(first_set, max(set_hi - 1, (int64_t)0)), wl, buf);
 
     // ---- shift c, the error-bound constants, and the shifted biases --------------------------------
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
             if (wl == 0) claimed = atomicAdd(&s_next, 1);
             next_set = set_lo + __builtin_amdgcn_readfirstlane(claimed);
         }
-        fast_load_set<LPT, BF16>(a, next_set < set_hi ? next_set : set, wl, buf);
+        if (next_set < set_hi) fast_load_set<LPT, BF16>(a, next_set, wl, buf);
         wave_lds_sync();
 
         const int tok_raw = (int)set * TPW + tw;  // N * K < 2^31

@@ -196,6 +196,11 @@ __device__ __forceinline__ bool last_count_tile(WsHeader* hdr, int nct, uint32_t
     return *s_flag != 0u;
 }
 
+// Index into an LDS array of per-slot values with one pad word after every 64: a lane writing
+// slot (lane * K + k) of a token-per-lane layout and a lane reading slot (base + lane) then both
+// hit 64 different banks.  Arrays need n + n / 64 words.
+__device__ __forceinline__ int slot_pad(int i) { return i + (i >> 6); }
+
 // Lanes of this wave (restricted to `active`) holding the same key as the calling lane: one wave
 // ballot per key bit (a wave64 stand-in for a warp match).  NB = key bits, fixed at compile time
 // so the loop unrolls.

@@ -29,9 +29,9 @@ struct ScatterLds {
 // One scatter tile (one workgroup of kScatBlock threads): the padded scan of the expert totals,
 // stable in-tile ranks, the tile's expanded_to_permuted and permuted_to_expanded entries, a
 // slice of the padding rows, and (workgroup 0) the per-expert outputs.  With `keep_ids` and
-// `keep_pos` (kLayTile ints each in LDS), it leaves the tile's ids and permuted positions there
-// by slot (-1 / 0 where there is no valid slot) for a later phase of the same workgroup; their
-// storage may be L.slot and L.pos, which are free by then.
+// `keep_pos` (kLayTile + kLayTile / 64 ints each in LDS), it leaves the tile's ids and permuted
+// positions there by slot, at slot_pad(slot) (-1 / 0 where there is no valid slot), for a later
+// phase of the same workgroup; their storage may be L.slot and L.pos, which are free by then.
 template <int NB>
 __device__ __forceinline__ void scatter_tile(const int32_t* __restrict__ ids, int E, int A,
                                              const ScatterSrc& src, WsHeader* hdr,
@@ -225,8 +225,8 @@ __device__ __forceinline__ void scatter_tile(const int32_t* __restrict__ ids, in
 #pragma unroll
             for (int it = 0; it < kScatPerWave / kWave; ++it) {
                 const int li = w * kScatPerWave + it * kWave + lane;  // slot - s_beg
-                keep_ids[li] = key[it];
-                keep_pos[li] = Pv[it];
+                keep_ids[slot_pad(li)] = key[it];
+                keep_pos[slot_pad(li)] = Pv[it];
             }
         }
     }

@@ -303,8 +303,8 @@ struct WriteLds {
     int* excl;                    // [3 * kMaxRanks] rank-column prefixes before this write tile
     int (*ctp)[3 * kMaxRanks];    // [3] count-tile prefixes of the rank columns (kCt*)
     int (*doff)[kMaxRanks + 1];   // [2] segment starts of the groups / duplicates per rank
-    uint32_t* code;               // [kPlanSlots] slot codes
-    int* loff;                    // [kPlanSlots] rank-local offsets
+    uint32_t* code;               // [kPlanSlots + kPlanSlots / 64] slot codes, at slot_pad(slot)
+    int* loff;                    // [kPlanSlots + kPlanSlots / 64] rank-local offsets, likewise
     int (*hc)[kMaxRanks];         // [waves] per-(wave, rank) head counters
     int (*dc)[kMaxRanks];         // [waves] per-(wave, rank) duplicate counters
     uint64_t (*mask)[kMaxRanks];  // [waves] per-(wave, rank) token ballots
@@ -328,7 +328,7 @@ struct WriteSrcGlobal {
     __device__ __forceinline__ int cuv(int i) const { return gptr(cu)[i]; }
 };
 struct WriteSrcLds {
-    const int* ids;  // [tokens of the tile * K] by slot of the tile
+    const int* ids;  // by slot of the tile, at slot_pad(slot)
     const int* pos;
     const int* cu;   // [E + 1]
     template <int KMAX>
@@ -336,8 +336,8 @@ struct WriteSrcLds {
                                           bool live) const {
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
-            idk[k] = (live && k < K) ? ids[li * K + k] : -1;
-            pk[k] = (live && k < K) ? pos[li * K + k] : 0;
+            idk[k] = (live && k < K) ? ids[slot_pad(li * K + k)] : -1;
+            pk[k] = (live && k < K) ? pos[slot_pad(li * K + k)] : 0;
         }
     }
     __device__ __forceinline__ int cuv(int i) const { return cu[i]; }
@@ -469,24 +469,43 @@ __device__ __forceinline__ void plan_write_tile(const Src& src, const PlanGeom& 
         if (live) {
             TokenSlots<KMAX> ts;
             token_slots<KMAX>(ts, idk, g.K, g.E, R, s_owner);
+            // branch-free over the slots (k < K is uniform): every LDS read first, then the codes
+            int32_t dv[KMAX];
+            int cr[KMAX];
+            bool all_ok = true;
 #pragma unroll
             for (int k = 0; k < KMAX; ++k) {
-                if (k >= g.K) continue;
-                const int si = tid * g.K + k;
-                if (!ts.ok[k]) {
-                    s_code[si] = kNone;
-                    continue;
-                }
-                const int r = ts.r[k];
-                const int loff = pk[k] - s_cu_r[r];
-                const int64_t raw = (int64_t)r * g.NvS + loff;
-                if (o.dst) gptr(o.dst)[t * g.K + k] = (int32_t)(ts.first[k] ? raw : -raw - 1);
-                const uint32_t type = ts.first[k] ? (ts.h[k] >= 2 ? kHead : kNone) : kDup;
-                s_code[si] = type | ((uint32_t)r << 2) | ((uint32_t)ts.h[k] << 10);
-                s_loff[si] = loff;
-                if (ts.first[k]) {
+                const bool v = k < g.K && ts.ok[k];
+                cr[k] = s_cu_r[v ? ts.r[k] : 0];
+                all_ok = all_ok && (k >= g.K || ts.ok[k]);
+            }
 #pragma unroll
-                    for (int q = 0; q < kMaxRanks / 32; ++q) m[q] |= ((r >> 5) == q) ? (1u << (r & 31)) : 0u;
+            for (int k = 0; k < KMAX; ++k) {
+                dv[k] = 0;
+                if (k >= g.K) continue;
+                const bool v = ts.ok[k];
+                const int si = tid * g.K + k;
+                const int r = v ? ts.r[k] : 0;
+                const int loff = pk[k] - cr[k];
+                const int64_t raw = (int64_t)r * g.NvS + loff;
+                dv[k] = (int32_t)(ts.first[k] ? raw : -raw - 1);
+                const uint32_t type = ts.first[k] ? (ts.h[k] >= 2 ? kHead : kNone) : kDup;
+                s_code[slot_pad(si)] = v ? (type | ((uint32_t)r << 2) | ((uint32_t)ts.h[k] << 10)) : kNone;
+                s_loff[slot_pad(si)] = loff;
+                const bool mark = v && ts.first[k];
+#pragma unroll
+                for (int q = 0; q < kMaxRanks / 32; ++q) m[q] |= (mark && (r >> 5) == q) ? (1u << (r & 31)) : 0u;
+            }
+            if (o.dst) {  // the token's K entries: two 16-byte stores when K == 8 and all are valid
+                MEP_GLOBAL int32_t* drow = gptr(o.dst) + t * g.K;
+                if (KMAX == 8 && g.K == 8 && all_ok && (((uintptr_t)o.dst) & 15u) == 0) {
+                    MEP_GLOBAL u32x4* d4 = reinterpret_cast<MEP_GLOBAL u32x4*>(drow);
+                    d4[0] = u32x4{(uint32_t)dv[0], (uint32_t)dv[1], (uint32_t)dv[2], (uint32_t)dv[3]};
+                    d4[1] = u32x4{(uint32_t)dv[4 % KMAX], (uint32_t)dv[5 % KMAX], (uint32_t)dv[6 % KMAX], (uint32_t)dv[7 % KMAX]};
+                } else {
+#pragma unroll
+                    for (int k = 0; k < KMAX; ++k)
+                        if (k < g.K && ts.ok[k]) drow[k] = dv[k];
                 }
             }
         }
@@ -511,7 +530,7 @@ __device__ __forceinline__ void plan_write_tile(const Src& src, const PlanGeom& 
         for (int it = 0; it < kIters; ++it) {
             const int si = wbeg + it * kWave + lane;
             const bool inb = si < wend;
-            const uint32_t code = inb ? s_code[si] : kNone;
+            const uint32_t code = inb ? s_code[slot_pad(si)] : kNone;
             const uint32_t type = code & 3u;
             const bool valid = type != kNone;
             const int r = valid ? (int)((code >> 2) & 0xFFu) : 0;
@@ -554,7 +573,7 @@ __device__ __forceinline__ void plan_write_tile(const Src& src, const PlanGeom& 
         for (int it = 0; it < kIters; ++it) {
             const int si = wbeg + it * kWave + lane;
             if (si >= wend) continue;
-            const uint32_t code = s_code[si];
+            const uint32_t code = s_code[slot_pad(si)];
             const uint32_t type = code & 3u;
             if (type == kNone) continue;
             const int r = (int)((code >> 2) & 0xFFu);
@@ -563,13 +582,13 @@ __device__ __forceinline__ void plan_write_tile(const Src& src, const PlanGeom& 
                 const int64_t gpos = (int64_t)s_doff[0][r] + s_excl[R + r] + s_hc[w][r] + hrank[it];
                 if (o.dup_groups && gpos < o.cap_g) {
                     const int h = (int)(code >> 10);
-                    gptr(o.dup_groups)[3 * gpos + 0] = s_loff[si];
+                    gptr(o.dup_groups)[3 * gpos + 0] = s_loff[slot_pad(si)];
                     gptr(o.dup_groups)[3 * gpos + 1] = dup_local;
                     gptr(o.dup_groups)[3 * gpos + 2] = h - 1;
                 }
             } else {
                 const int64_t dpos = (int64_t)s_doff[1][r] + dup_local;
-                if (o.dup_loffs && dpos < o.cap_d) gptr(o.dup_loffs)[dpos] = s_loff[si];
+                if (o.dup_loffs && dpos < o.cap_d) gptr(o.dup_loffs)[dpos] = s_loff[slot_pad(si)];
             }
         }
     }
@@ -680,8 +699,8 @@ __global__ __launch_bounds__(kPlanBlock) void plan_write_kernel(
     __shared__ int s_excl[3 * kMaxRanks];
     __shared__ int s_ctp[3][3 * kMaxRanks];
     __shared__ int s_doff[2][kMaxRanks + 1];
-    __shared__ uint32_t s_code[kPlanSlots];
-    __shared__ int s_loff[kPlanSlots];
+    __shared__ uint32_t s_code[kPlanSlots + kPlanSlots / 64];
+    __shared__ int s_loff[kPlanSlots + kPlanSlots / 64];
     __shared__ int s_hc[kPlanWaves][kMaxRanks];
     __shared__ int s_dc[kPlanWaves][kMaxRanks];
     __shared__ uint64_t s_mask[kPlanWaves][kMaxRanks];
@@ -699,31 +718,33 @@ __global__ __launch_bounds__(kScatBlock) void plan_scatter_write_kernel(const in
                                                                         ScatterSrc src, WsHeader* hdr,
                                                                         LayoutOut lout, PlanOutDev o) {
     constexpr int kW = kScatBlock / kWave;
+    constexpr int kPadSlots = kPlanSlots + kPlanSlots / 64;
+    // one region for the scatter phase's per-(wave, expert) counters and, later, the write
+    // phase's slot codes, offsets and per-wave counters
+    constexpr int kWriteBytes = 8 * kPadSlots + (4 + 4 + 8) * kW * kMaxRanks;
+    constexpr int kScatBytes = 4 * kScatWaves * kMaxExperts;
+    constexpr int kBigBytes = kWriteBytes > kScatBytes ? kWriteBytes : kScatBytes;
+    static_assert(kLayTile >= kPlanSlots, "a plan tile fits a scatter tile");
+    __shared__ __align__(16) char s_big[kBigBytes];
     __shared__ int s_cu[kMaxExperts + 1];
     __shared__ int s_tot[kMaxExperts];
     __shared__ int s_base[kMaxExperts];
     __shared__ int s_loc[kMaxExperts];
-    __shared__ __align__(16) int s_cnt[kScatWaves][kMaxExperts];
     __shared__ int s_tmp[kScatWaves];
-    __shared__ int s_slot[kLayTile];
-    __shared__ int s_pos[kLayTile];
+    __shared__ int s_slot[kLayTile + kLayTile / 64];
+    __shared__ int s_pos[kLayTile + kLayTile / 64];
     __shared__ int s_owner[kMaxE];
     __shared__ int s_cu_r[kMaxRanks + 1];
     __shared__ int s_excl[3 * kMaxRanks];
     __shared__ int s_ctp[3][3 * kMaxRanks];
     __shared__ int s_doff[2][kMaxRanks + 1];
     __shared__ int s_wtmp[kW];
-    // the write phase's slot codes, offsets and per-wave counters inside s_cnt
-    static_assert(sizeof(uint32_t) * kPlanSlots * 2 + (sizeof(int) * 2 + sizeof(uint64_t)) * kW * kMaxRanks <=
-                      sizeof(int) * kScatWaves * kMaxExperts,
-                  "the write arrays fit in the scatter counters");
-    static_assert(kLayTile >= kPlanSlots, "a plan tile fits a scatter tile");
-    char* big = reinterpret_cast<char*>(&s_cnt[0][0]);
-    uint32_t* w_code = reinterpret_cast<uint32_t*>(big);
-    int* w_loff = reinterpret_cast<int*>(big + 4 * kPlanSlots);
-    int (*w_hc)[kMaxRanks] = reinterpret_cast<int (*)[kMaxRanks]>(big + 8 * kPlanSlots);
-    int (*w_dc)[kMaxRanks] = reinterpret_cast<int (*)[kMaxRanks]>(big + 8 * kPlanSlots + 4 * kW * kMaxRanks);
-    uint64_t (*w_mask)[kMaxRanks] = reinterpret_cast<uint64_t (*)[kMaxRanks]>(big + 8 * kPlanSlots + 8 * kW * kMaxRanks);
+    int (*s_cnt)[kMaxExperts] = reinterpret_cast<int (*)[kMaxExperts]>(s_big);
+    uint32_t* w_code = reinterpret_cast<uint32_t*>(s_big);
+    int* w_loff = reinterpret_cast<int*>(s_big + 4 * kPadSlots);
+    int (*w_hc)[kMaxRanks] = reinterpret_cast<int (*)[kMaxRanks]>(s_big + 8 * kPadSlots);
+    int (*w_dc)[kMaxRanks] = reinterpret_cast<int (*)[kMaxRanks]>(s_big + 8 * kPadSlots + 4 * kW * kMaxRanks);
+    uint64_t (*w_mask)[kMaxRanks] = reinterpret_cast<uint64_t (*)[kMaxRanks]>(s_big + 8 * kPadSlots + 8 * kW * kMaxRanks);
 
     const ScatterLds SL{s_cu, s_tot, s_base, s_loc, s_cnt, s_tmp, s_slot, s_pos};
     scatter_tile<NBE>(ids, src.pg.E, A, src, hdr, lout, SL, s_slot, s_pos);

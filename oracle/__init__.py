@@ -51,6 +51,8 @@ def load(path: str):
     L.oracle_plan.argtypes = ([P, P, P, i64, i32, i32, i32, i32, i32, i64]
                               + [P] * 11 + [P, i64, P, i64])
     L.oracle_plan.restype = i32
+    L.oracle_tile_map.argtypes = [P, i32, i32, P, P, i64, P, P]
+    L.oracle_tile_map.restype = i32
     return L
 
 
@@ -120,6 +122,30 @@ def layout(ids: np.ndarray, E: int, alignment: int) -> Layout:
         raise ValueError("oracle_layout failed (code %d)" % rc)
     T = int(cu[E])
     return Layout(tpe, cu, e2p, p2e[:T].copy(), zf)
+
+
+@dataclass
+class TileMap:
+    cta_to_expert: np.ndarray  # [num_ctas]
+    mn_limit: np.ndarray       # [num_ctas]
+    permuted_idx_size: int
+    num_ctas: int
+
+
+def tile_map(counts: np.ndarray, alignment: int) -> TileMap:
+    """Grouped-GEMM tile maps of per-expert counts ([TRT] routingPermutation CTA maps)."""
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    E = counts.shape[0]
+    cap = int(np.sum((counts.astype(np.int64) + alignment - 1) // alignment)) if E else 0
+    c2e = np.empty(max(cap, 1), np.int32)
+    lim = np.empty(max(cap, 1), np.int32)
+    pis = np.zeros(1, np.int32)
+    nc = np.zeros(1, np.int32)
+    rc = lib().oracle_tile_map(_p(counts), E, alignment, _p(c2e), _p(lim), cap, _p(pis), _p(nc))
+    if rc != 0:
+        raise ValueError("oracle_tile_map failed (code %d)" % rc)
+    n = int(nc[0])
+    return TileMap(c2e[:n].copy(), lim[:n].copy(), int(pis[0]), n)
 
 
 @dataclass

@@ -1,8 +1,8 @@
 /*
  * mep_oracle.c -- TEST INFRASTRUCTURE ONLY.
  *
- * A plain, slow, single-threaded CPU oracle for MoE routing, dispatch layout
- * and expert-parallel planning.  Only tests, the smoke check and the CPU
+ * A plain, slow, single-threaded CPU oracle for MoE routing, dispatch layout,
+ * expert-parallel planning and grouped-GEMM tile maps.  Only tests, the smoke check and the CPU
  * baseline leg of the benchmark may load it; the product path never does.
  * It shares no code, header, table or constant with the HIP library.
  *
@@ -19,7 +19,8 @@
  * Readings taken where the pages are silent are listed next to the code
  * that takes them.  Parity status: every function here is pinned by the
  * CPU tests (brute force, exact-arithmetic sigmoid, closed forms,
- * stable-sort equivalence, plan invariants); none is "parity unpinned".
+ * stable-sort equivalence, plan invariants, row-by-row tile enumeration);
+ * none is "parity unpinned".
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math -shared -fPIC
  *        mep_oracle.c -lquadmath -lm
@@ -502,4 +503,55 @@ int oracle_plan(const int32_t* ids, const int32_t* cu_seqlens,
     }
     free(itr); free(ntpr); free(ntpe); free(ng); free(nd);
     return rc;
+}
+
+/*
+ * Grouped-GEMM tile maps, [TRT] routingPermutation / routingIndicesOffsetsKernel
+ * (the per-expert CTA bookkeeping that follows the histogram).
+ *   per expert e with count c_e: numCta_e = ceil(c_e / A) tiles of A rows;
+ *   ctaOffset_e = exclusive prefix sum of numCta over experts, and the total
+ *   (numNonExitingCtas) is the sum over all experts;
+ *   for every tile index cta in [0, numCta_e), at position ctaOffset_e + cta:
+ *     cta_to_expert = e   (the index of e within `counts`)
+ *     mn_limit      = min((ctaOffset_e + cta + 1) * A, ctaOffset_e * A + c_e)
+ *   permuted_idx_size = numNonExitingCtas * A.
+ * Entries at and beyond the total are left untouched.  A negative count is
+ * an argument error; a total above cap is OR_ERR_CAP with nothing written.
+ * Pinned by the tile-map tests in test_oracle_pins.py.
+ */
+int oracle_tile_map(const int32_t* counts, int E, int A, int32_t* cta_to_expert,
+                    int32_t* mn_limit, int64_t cap, int32_t* permuted_idx_size,
+                    int32_t* num_ctas) {
+    if (E <= 0 || A <= 0 || cap < 0) return OR_ERR_ARG;
+    for (int e = 0; e < E; ++e)
+        if (counts[e] < 0) return OR_ERR_ARG;
+    int64_t* num_cta = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    int64_t* cta_offset = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    /* step 1: tiles per expert */
+    for (int e = 0; e < E; ++e) num_cta[e] = ((int64_t)counts[e] + A - 1) / A;
+    /* step 2: exclusive sum and its total */
+    int64_t total = 0;
+    for (int e = 0; e < E; ++e) {
+        cta_offset[e] = total;
+        total += num_cta[e];
+    }
+    if (total > cap) {
+        free(num_cta);
+        free(cta_offset);
+        return OR_ERR_CAP;
+    }
+    /* step 3: each expert fills its own tiles */
+    for (int e = 0; e < E; ++e)
+        for (int64_t cta = 0; cta < num_cta[e]; ++cta) {
+            int64_t lim1 = (cta_offset[e] + cta + 1) * (int64_t)A;
+            int64_t lim2 = cta_offset[e] * (int64_t)A + counts[e];
+            if (cta_to_expert) cta_to_expert[cta_offset[e] + cta] = e;
+            if (mn_limit) mn_limit[cta_offset[e] + cta] = (int32_t)(lim1 < lim2 ? lim1 : lim2);
+        }
+    /* step 4: the two scalars */
+    if (permuted_idx_size) *permuted_idx_size = (int32_t)(total * A);
+    if (num_ctas) *num_ctas = (int32_t)total;
+    free(num_cta);
+    free(cta_offset);
+    return OR_OK;
 }

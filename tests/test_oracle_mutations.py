@@ -55,6 +55,12 @@ MUTANTS = [
      "recv_cu_seqlens[r * (epn + 1) + j] = cu_seqlens[r * epn + j] - cu_seqlens[r];"),
     ("dup_offsets_inclusive", "gtot += ng[r];\n        dtot += nd[r];\n    }",
      "gtot += ng[r];\n        dtot += nd[r];\n        if (dup_offsets) { dup_offsets[2 * r] = (int32_t)gtot; }\n    }"),
+    ("tile_count_floor", "num_cta[e] = ((int64_t)counts[e] + A - 1) / A;",
+     "num_cta[e] = ((int64_t)counts[e]) / A;"),
+    ("tile_limit_exclusive_end", "int64_t lim1 = (cta_offset[e] + cta + 1) * (int64_t)A;",
+     "int64_t lim1 = (cta_offset[e] + cta) * (int64_t)A;"),
+    ("tile_limit_ignores_count", "int64_t lim2 = cta_offset[e] * (int64_t)A + counts[e];",
+     "int64_t lim2 = (cta_offset[e] + num_cta[e]) * (int64_t)A;"),
 ]
 
 
@@ -76,6 +82,10 @@ def _battery():
     for args in [(128, 8, 2, 2, 2, 24, 1), (96, 8, 2, 8, 8, 5, 128), (256, 64, 8, 8, 4, 24, 16),
                  (240, 32, 6, 4, 3, 7, 3)]:
         pins.test_plan_invariants(*args)
+    pins.test_tile_map_hand_example()
+    for seed in range(2):
+        for E, A in [(5, 4), (16, 3)]:
+            pins.test_tile_map_matches_row_enumeration(seed, E, A)
 
 
 def test_real_oracle_passes_battery():

@@ -399,3 +399,78 @@ def test_workload_prefix_end_to_end(name):
     assert all(len(set(r)) == wl.K for r in ids.tolist())
     np.testing.assert_allclose(w.astype(np.float64).sum(axis=1), wl.scale, rtol=1e-6)
     _check_plan(ids, wl.E, wl.R, wl.S, wl.num_channels, wl.alignment)
+
+
+# ---------------------------------------------------------------------------------------------
+# Grouped-GEMM tile maps: a row-level enumeration and the layout's permuted rows
+# ---------------------------------------------------------------------------------------------
+
+def test_tile_map_hand_example():
+    for c in json.load(open(GOLDEN))["tile_map"]["cases"]:
+        tm = oracle.tile_map(np.array(c["counts"], np.int32), c["alignment"])
+        assert tm.cta_to_expert.tolist() == c["cta_to_expert"]
+        assert tm.mn_limit.tolist() == c["mn_limit"]
+        assert (tm.permuted_idx_size, tm.num_ctas) == (c["permuted_idx_size"], c["num_ctas"])
+
+
+def _rows_of(counts, A):
+    """Permuted rows listed one by one: (owner, is_real) per row, experts back to back, each
+    padded with dummy rows to a whole number of A-row tiles."""
+    rows = []
+    for e, c in enumerate(counts):
+        real = [(e, True)] * int(c)
+        while len(real) % A:
+            real.append((e, False))
+        rows += real
+    return rows
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("E,A", [(1, 1), (5, 4), (16, 3), (64, 128), (33, 1)])
+def test_tile_map_matches_row_enumeration(seed, E, A):
+    rng = np.random.default_rng(1000 + seed)
+    counts = rng.integers(0, 3 * A + 2, E).astype(np.int32)
+    counts[rng.random(E) < 0.3] = 0
+    counts[rng.random(E) < 0.2] = A * rng.integers(1, 3)
+    tm = oracle.tile_map(counts, A)
+    rows = _rows_of(counts, A)
+    assert len(rows) % A == 0
+    assert tm.num_ctas == len(rows) // A and tm.permuted_idx_size == len(rows)
+    for j in range(tm.num_ctas):
+        tile = rows[j * A:(j + 1) * A]
+        assert len({o for o, _ in tile}) == 1  # a tile never straddles two experts
+        assert tm.cta_to_expert[j] == tile[0][0]
+        real = sum(r for _, r in tile)
+        assert real >= 1 and tm.mn_limit[j] == j * A + real
+
+
+def test_tile_map_alignment_one_is_repeat():
+    counts = np.array([3, 0, 1, 7, 0, 2], np.int32)
+    tm = oracle.tile_map(counts, 1)
+    assert tm.cta_to_expert.tolist() == np.repeat(np.arange(6), counts).tolist()
+    assert tm.mn_limit.tolist() == list(range(1, int(counts.sum()) + 1))
+
+
+def test_tile_map_empty_and_invalid():
+    tm = oracle.tile_map(np.zeros(7, np.int32), 5)
+    assert tm.num_ctas == 0 and tm.permuted_idx_size == 0
+    with pytest.raises(ValueError):
+        oracle.tile_map(np.array([1, -1], np.int32), 2)
+
+
+@pytest.mark.parametrize("N,E,K,A", [(37, 8, 2, 4), (300, 16, 4, 3), (129, 64, 8, 128)])
+def test_tile_map_tiles_cover_layout_rows(N, E, K, A):
+    """Tile j spans permuted rows [jA, (j+1)A) of the stable layout: rows below its limit hold
+    slots of its expert, the rest are padding."""
+    rng = np.random.default_rng(N)
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(N)]).astype(np.int32)
+    L = oracle.layout(ids, E, A)
+    tm = oracle.tile_map(L.tokens_per_expert, A)
+    assert tm.permuted_idx_size == int(L.cu_seqlens[E])
+    flat = ids.reshape(-1)
+    for j in range(tm.num_ctas):
+        lim = int(tm.mn_limit[j])
+        assert j * A < lim <= (j + 1) * A
+        real = L.permuted_to_expanded[j * A:lim]
+        assert np.all(real >= 0) and np.all(flat[real] == tm.cta_to_expert[j])
+        assert np.all(L.permuted_to_expanded[lim:(j + 1) * A] == -1)

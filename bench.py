@@ -169,6 +169,33 @@ def cpu_baseline(wl, inp, seconds: float):
                       "%.1f s" % (passes, wl.N, el)}
 
 
+def tile_map_leg(B, torch, L, wl, steps: int, stream):
+    """Grouped-GEMM tile maps of the last step's histogram, timed on their own (not part of the
+    step): `steps` back-to-back calls between two events on the launch stream."""
+    N, E, K, A = wl.N, wl.E, wl.K, wl.alignment
+    cap = B.tile_map_capacity(N * K, E, A)
+    dev = L.tokens_per_expert.device
+    c2e = torch.empty(cap, dtype=torch.int32, device=dev)
+    lim = torch.empty(cap, dtype=torch.int32, device=dev)
+    sc = torch.empty(2, dtype=torch.int32, device=dev)
+    call = B.bound_tile_map(L.tokens_per_expert, N * K, A, c2e, lim, sc[:1], sc[1:], stream)
+    for _ in range(3):
+        call()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(steps):
+        call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / steps
+    tiles = int(sc[1].item())
+    nbytes = 4 * E + 8 * tiles + 8   # counts in; expert and row limit per tile, two scalars out
+    return {"us_per_call": us, "tiles": tiles, "algorithmic_bytes": nbytes,
+            "GB_per_s": nbytes / (us * 1e-6) / 1e9}
+
+
 def main():
     args = parse()
     if args.record_traffic:
@@ -215,7 +242,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     # one prepared call per buffer set and entry point (arguments converted once): routing, then
-    # layout + plan in one call (mep_layout_plan: three kernels, the plan's counting pass also
+    # layout + plan in one call (mep_layout_plan: two kernels, the plan's counting pass also
     # serving the layout).  Timed steps route through mep_route_topk_timed with a pair of
     # events per step, which the routing kernel's launch itself stamps with its start and end.
     calls = []
@@ -288,6 +315,7 @@ def main():
                  "slots_per_s": N * K / (ms_step * 1e-3), "T": T, "dedup_groups": G,
                  "dedup_dups": D, "host_wall_s": wall},
     }
+    out["next_rows"] = {"tile_map": tile_map_leg(B, torch, L, wl, args.steps, stream)}
     if args.copy_calibration > 0:
         nbytes = args.copy_calibration << 20
         src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)

@@ -46,7 +46,7 @@ class PlanOutputs(ctypes.Structure):
 
 
 EXPORTS = ("mep_route_topk", "mep_route_topk_timed", "mep_build_layout", "mep_layout_workspace_size", "mep_plan",
-           "mep_plan_workspace_size", "mep_layout_plan", "mep_status_string")
+           "mep_plan_workspace_size", "mep_layout_plan", "mep_tile_map", "mep_status_string")
 
 _lib = None
 _lock = threading.Lock()
@@ -79,6 +79,8 @@ def lib():
                 L.mep_layout_plan.argtypes = [P, I64, I, I, I, P, P, P, P, I64, P,
                                               I, I, I, I64, ctypes.POINTER(PlanOutputs), P, SZ, P]
                 L.mep_layout_plan.restype = I
+                L.mep_tile_map.argtypes = [P, I, I64, I, P, P, I64, P, P, P]
+                L.mep_tile_map.restype = I
                 L.mep_status_string.argtypes = [I]
                 L.mep_status_string.restype = ctypes.c_char_p
                 _lib = L
@@ -155,6 +157,34 @@ def mep_plan(topk_ids, cu_seqlens, expanded_to_permuted, E, alignment, R, num_sr
 # issue the same call many times (a zero-argument callable per call; each call checks the
 # return code).  Tensors must stay alive and in place while the callable is used.
 # ---------------------------------------------------------------------------------------------
+
+def tile_map_capacity(num_slots: int, E: int, tile: int) -> int:
+    """Tiles that `num_slots` slots over E experts can need at most (the bound mep_tile_map
+    checks cap_ctas against)."""
+    return (num_slots + min(E, num_slots) * (tile - 1)) // tile
+
+
+def mep_tile_map(tokens_per_expert, num_slots, tile, cta_to_expert=None, cta_mn_limit=None,
+                 permuted_idx_size=None, num_ctas=None, stream=None):
+    _require_cuda(tokens_per_expert, cta_to_expert, cta_mn_limit, permuted_idx_size, num_ctas)
+    E = tokens_per_expert.numel()
+    caps = [t.numel() for t in (cta_to_expert, cta_mn_limit) if t is not None]
+    cap = min(caps) if caps else 0
+    rc = lib().mep_tile_map(_ptr(tokens_per_expert), E, num_slots, tile, _ptr(cta_to_expert),
+                            _ptr(cta_mn_limit), cap, _ptr(permuted_idx_size), _ptr(num_ctas),
+                            _stream(stream))
+    _check(rc, "mep_tile_map")
+
+
+def bound_tile_map(tokens_per_expert, num_slots, tile, cta_to_expert=None, cta_mn_limit=None,
+                   permuted_idx_size=None, num_ctas=None, stream=None):
+    _require_cuda(tokens_per_expert, cta_to_expert, cta_mn_limit, permuted_idx_size, num_ctas)
+    caps = [t.numel() for t in (cta_to_expert, cta_mn_limit) if t is not None]
+    return _bound("mep_tile_map", (_ptr(tokens_per_expert), tokens_per_expert.numel(), num_slots,
+                                   tile, _ptr(cta_to_expert), _ptr(cta_mn_limit),
+                                   min(caps) if caps else 0, _ptr(permuted_idx_size),
+                                   _ptr(num_ctas), _stream(stream)), "mep_tile_map")
+
 
 def _bound(fn_name, args, where):
     fn = getattr(lib(), fn_name)

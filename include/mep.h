@@ -11,8 +11,10 @@
  *   mep_plan         ids + layout -> expert-parallel plan over R virtual
  *                    ranks (membership, counts, prefix matrices, rank-tagged
  *                    destinations with duplicate encoding, dedup lists)
- *   mep_layout_plan  the two calls above in one (three kernels instead of
+ *   mep_layout_plan  the two calls above in one (two kernels instead of
  *                    four)
+ *   mep_tile_map     per-expert counts -> grouped-GEMM tile maps (the expert
+ *                    and the row limit of every padded tile)
  *
  * Sources, cited by page title and section:
  *   [TRT]  TensorRT-LLM RoutingKernel.cuh (blockScaleMoe routing helpers,
@@ -250,9 +252,10 @@ size_t mep_plan_workspace_size(int64_t N, int E, int K, int R, int num_src);
  * mep_layout_plan -- mep_build_layout followed by mep_plan in one call, with
  * the results of the two calls and the checks of both (the layout's
  * cu_seqlens and expanded_to_permuted are outputs of the first part and inputs
- * of the second, so both are required).  Three kernels instead of four: the
+ * of the second, so both are required).  Two kernels instead of four: the
  * plan's counting pass also produces the per-expert totals and prefixes the
- * layout needs, so the layout's own counting pass is not run.
+ * layout needs, so the layout's own counting pass is not run, and one kernel
+ * both scatters the layout and writes the plan.
  *
  * Arguments as mep_build_layout (without its workspace) and mep_plan; `ws` is
  * a workspace of mep_plan_workspace_size(N, E, K, R, num_src) bytes, the only
@@ -266,6 +269,43 @@ int mep_layout_plan(const int32_t* topk_ids, int64_t N, int E, int K, int alignm
                     int64_t permuted_cap, int32_t* zero_fill, int R, int num_src,
                     int num_channels, int64_t NvS, const mep_plan_outputs* out, void* ws,
                     size_t ws_bytes, void* stream);
+
+/*
+ * mep_tile_map -- grouped-GEMM tile maps of a per-expert histogram
+ * ([TRT] routingPermutation / routingIndicesOffsetsKernel: the per-expert
+ * CTA bookkeeping after the histogram).
+ *
+ * With c_e = tokens_per_expert[e] and A = tile:
+ *   tiles_e = ceil(c_e / A); off_e = sum_{e' < e} tiles_e'; T = sum of all
+ *   for every j = off_e + i, 0 <= i < tiles_e:
+ *     cta_to_expert[j] = e
+ *     cta_mn_limit[j]  = min((j + 1) * A, off_e * A + c_e)
+ *   permuted_idx_size[0] = T * A, num_ctas[0] = T
+ * With the same A as mep_build_layout's alignment, tile j covers the permuted
+ * rows [j*A, (j+1)*A) of that layout (off_e * A == cu_seqlens[e]): the rows
+ * below its limit hold expert e's slots, the rest are padding.  Entries at and
+ * beyond T are not written.  For the experts of one rank of mep_plan, pass
+ * tokens_per_expert + r*epn with E = epn: the expert index is then rank-local
+ * (the pages' local expert index with stride 1) and the tiles cover
+ * recv_cu_seqlens[r].
+ *
+ * Arguments
+ *   tokens_per_expert device int32[E], every count >= 0 (a negative count
+ *                     counts as 0), summing to at most num_slots
+ *   E                 1 .. 1024
+ *   num_slots         >= sum of the counts (N*K for a whole layout)
+ *   tile              A >= 1
+ *   cta_to_expert, cta_mn_limit  device int32[cap_ctas] (nullable)
+ *   cap_ctas          >= (num_slots + min(E, num_slots)*(A-1)) / A when
+ *                     either array is given
+ *   permuted_idx_size, num_ctas  device int32[1] (nullable)
+ * Returns MEP_ERR_UNSUPPORTED for E > 1024 or
+ * num_slots + min(E, num_slots)*(A-1) > INT32_MAX - 65536.  Counts that sum
+ * above num_slots give unspecified values but no write beyond cap_ctas.
+ */
+int mep_tile_map(const int32_t* tokens_per_expert, int E, int64_t num_slots, int tile,
+                 int32_t* cta_to_expert, int32_t* cta_mn_limit, int64_t cap_ctas,
+                 int32_t* permuted_idx_size, int32_t* num_ctas, void* stream);
 
 /* Static, NUL-terminated name of a return code. */
 const char* mep_status_string(int code);

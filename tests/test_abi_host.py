@@ -139,3 +139,27 @@ def test_plan_validation():
     assert _plan(ws_bytes=100) == B.MEP_ERR_CAPACITY
     # epn == 1: no duplicates are possible, zero capacity is enough for both lists
     assert B.dedup_capacity(64, 8, 2, 8) == (0, 0)
+
+
+def _tile(E=8, M=64, A=4, tpe=FAKE, c2e=FAKE, lim=FAKE, cap=None, pis=FAKE, nct=FAKE):
+    if cap is None:
+        cap = B.tile_map_capacity(M, E, A) if A > 0 else 0
+    return B.lib().mep_tile_map(tpe, E, M, A, c2e, lim, cap, pis, nct, None)
+
+
+def test_tile_map_validation():
+    assert B.tile_map_capacity(64, 8, 4) == (64 + 8 * 3) // 4
+    assert B.tile_map_capacity(3, 8, 4) == (3 + 3 * 3) // 4      # at most 3 experts hold slots
+    assert B.tile_map_capacity(0, 8, 4) == 0
+    assert _tile(tpe=None) == B.MEP_ERR_INVALID_ARG
+    assert _tile(E=0) == B.MEP_ERR_INVALID_ARG
+    assert _tile(A=0) == B.MEP_ERR_INVALID_ARG
+    assert _tile(M=-1, cap=0) == B.MEP_ERR_INVALID_ARG
+    assert _tile(cap=-1) == B.MEP_ERR_INVALID_ARG
+    assert _tile(lim=FAKE + 2) == B.MEP_ERR_INVALID_ARG
+    assert _tile(E=1025) == B.MEP_ERR_UNSUPPORTED
+    assert _tile(M=2 ** 31, A=1, cap=2 ** 31) == B.MEP_ERR_UNSUPPORTED
+    assert _tile(cap=(64 + 8 * 3) // 4 - 1) == B.MEP_ERR_CAPACITY
+    assert _tile(c2e=None, cap=(64 + 8 * 3) // 4 - 1) == B.MEP_ERR_CAPACITY  # either array
+    # nothing to write: accepted without a launch
+    assert _tile(c2e=None, lim=None, pis=None, nct=None, cap=0) == B.MEP_OK

@@ -53,6 +53,10 @@ def load(path: str):
     L.oracle_plan.restype = i32
     L.oracle_tile_map.argtypes = [P, i32, i32, P, P, i64, P, P]
     L.oracle_tile_map.restype = i32
+    L.oracle_permute_rows.argtypes = [P, i32, i64, i64, i32, P, P, i32, P, i64]
+    L.oracle_permute_rows.restype = i32
+    L.oracle_combine_rows.argtypes = [P, i32, i64, i64, i32, P, P, P, i64]
+    L.oracle_combine_rows.restype = i32
     return L
 
 
@@ -146,6 +150,48 @@ def tile_map(counts: np.ndarray, alignment: int) -> TileMap:
         raise ValueError("oracle_tile_map failed (code %d)" % rc)
     n = int(nc[0])
     return TileMap(c2e[:n].copy(), lim[:n].copy(), int(pis[0]), n)
+
+
+def _row_dtype(a: np.ndarray) -> int:
+    """0 for fp32 rows, 1 for bf16 rows (held as uint16 bit patterns)."""
+    if a.dtype == np.float32:
+        return 0
+    if a.dtype == np.uint16:
+        return 1
+    raise ValueError("rows must be float32 or uint16 (bf16 bits)")
+
+
+def permute_rows(x: np.ndarray, expanded_to_permuted: np.ndarray, zero_fill: np.ndarray,
+                 T: int, fill=None) -> np.ndarray:
+    """Rows of x [N, H] copied to their permuted rows [T, H]; padding ranges zeroed.  Rows that
+    neither step writes keep `fill` (default: an all-ones bit pattern, so they stand out)."""
+    x = np.ascontiguousarray(x)
+    N, H = x.shape
+    K = expanded_to_permuted.size // max(N, 1) if N else 1
+    e2p = np.ascontiguousarray(expanded_to_permuted, np.int32)
+    zf = None if zero_fill is None else np.ascontiguousarray(zero_fill, np.int32)
+    out = np.empty((T, H), x.dtype)
+    out.view(np.uint8)[...] = 0xFF if fill is None else fill
+    E = 1 if zf is None else zf.shape[0]
+    rc = lib().oracle_permute_rows(_p(x), _row_dtype(x), N, H, K, _p(e2p), _p(zf), E, _p(out), T)
+    if rc != 0:
+        raise ValueError("oracle_permute_rows failed (code %d)" % rc)
+    return out
+
+
+def combine_rows(y: np.ndarray, expanded_to_permuted: np.ndarray, K: int,
+                 topk_weights: np.ndarray = None) -> np.ndarray:
+    """out[t] = sum over k (in order, binary32) of w[t,k] * y[P[t,k]], cast to y's type."""
+    y = np.ascontiguousarray(y)
+    T, H = y.shape
+    e2p = np.ascontiguousarray(expanded_to_permuted, np.int32).reshape(-1)
+    N = e2p.size // K
+    w = None if topk_weights is None else np.ascontiguousarray(topk_weights, np.float32)
+    out = np.empty((N, H), y.dtype)
+    rc = lib().oracle_combine_rows(_p(y), _row_dtype(y), N, H, K, _p(e2p), _p(w), _p(out), T)
+    if rc != 0:
+        raise ValueError("oracle_combine_rows failed (code %d)" % rc)
+    return out
 
 
 @dataclass

@@ -2,7 +2,8 @@
  * mep_oracle.c -- TEST INFRASTRUCTURE ONLY.
  *
  * A plain, slow, single-threaded CPU oracle for MoE routing, dispatch layout,
- * expert-parallel planning and grouped-GEMM tile maps.  Only tests, the smoke check and the CPU
+ * expert-parallel planning, grouped-GEMM tile maps and the local permute /
+ * combine of hidden-state rows.  Only tests, the smoke check and the CPU
  * baseline leg of the benchmark may load it; the product path never does.
  * It shares no code, header, table or constant with the HIP library.
  *
@@ -19,7 +20,8 @@
  * Readings taken where the pages are silent are listed next to the code
  * that takes them.  Parity status: every function here is pinned by the
  * CPU tests (brute force, exact-arithmetic sigmoid, closed forms,
- * stable-sort equivalence, plan invariants, row-by-row tile enumeration);
+ * stable-sort equivalence, plan invariants, row-by-row tile enumeration,
+ * exact permute/combine round trips and sums, bf16 rounding against torch);
  * none is "parity unpinned".
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math -shared -fPIC
@@ -553,5 +555,90 @@ int oracle_tile_map(const int32_t* counts, int E, int A, int32_t* cta_to_expert,
     if (num_ctas) *num_ctas = (int32_t)total;
     free(num_cta);
     free(cta_offset);
+    return OR_OK;
+}
+
+/*
+ * Local permute and combine of hidden-state rows: one GPU's share of
+ * [DEEP] intranode dispatch (each token's row copied to the slot of every
+ * rank it goes to) and combine (a token's received rows summed in fp32 in
+ * order, then cast back to the row type).  Here the destinations are the
+ * permuted rows of the layout instead of per-rank channel buffers.
+ *   permute:  out[expanded_to_permuted[t*K+k]] = x[t]  for every t, k;
+ *             the zero-fill range (start, len) of every expert is set to 0.
+ *   combine:  out[t] = cast(acc), acc = 0.0f then, for k = 0 .. K-1 in
+ *             order, acc = acc + w[t*K+k] * y[expanded_to_permuted[t*K+k]]
+ *             (or acc + y[...] when w is NULL), each step one binary32
+ *             multiply and one binary32 add.
+ * dtype 0 = fp32 rows, 1 = bf16 rows; H = elements per row.  The cast to
+ * bf16 rounds to nearest, ties to even; a NaN stays a (quiet) NaN.
+ */
+static uint16_t bf16_round_nearest_even(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0)
+        return (uint16_t)((u >> 16) | 0x0040u); /* NaN: keep sign, force quiet */
+    uint32_t upper = u >> 16;
+    uint32_t lower = u & 0xffffu;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1; /* carries into exponent */
+    return (uint16_t)upper;
+}
+
+static float row_value(const void* rows, int dtype, int64_t idx) {
+    if (dtype == 0) return ((const float*)rows)[idx];
+    uint32_t u = (uint32_t)((const uint16_t*)rows)[idx] << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+int oracle_permute_rows(const void* x, int dtype, int64_t N, int64_t H, int K,
+                        const int32_t* expanded_to_permuted, const int32_t* zero_fill, int E,
+                        void* out, int64_t T) {
+    if (N < 0 || H <= 0 || K <= 0 || E <= 0 || T < 0) return OR_ERR_ARG;
+    if (dtype != 0 && dtype != 1) return OR_ERR_ARG;
+    size_t row = (size_t)H * (dtype == 0 ? 4 : 2);
+    for (int64_t t = 0; t < N; ++t)
+        for (int k = 0; k < K; ++k) {
+            int64_t p = expanded_to_permuted[t * K + k];
+            if (p < 0 || p >= T) return OR_ERR_ARG;
+            memcpy((char*)out + (size_t)p * row, (const char*)x + (size_t)t * row, row);
+        }
+    if (zero_fill)
+        for (int e = 0; e < E; ++e) {
+            int64_t start = zero_fill[2 * e], len = zero_fill[2 * e + 1];
+            if (len == 0) continue;
+            if (start < 0 || start + len > T) return OR_ERR_ARG;
+            memset((char*)out + (size_t)start * row, 0, (size_t)len * row);
+        }
+    return OR_OK;
+}
+
+int oracle_combine_rows(const void* y, int dtype, int64_t N, int64_t H, int K,
+                        const int32_t* expanded_to_permuted, const float* topk_weights,
+                        void* out, int64_t T) {
+    if (N < 0 || H <= 0 || K <= 0 || T < 0) return OR_ERR_ARG;
+    if (dtype != 0 && dtype != 1) return OR_ERR_ARG;
+    for (int64_t t = 0; t < N; ++t)
+        for (int k = 0; k < K; ++k) {
+            int64_t p = expanded_to_permuted[t * K + k];
+            if (p < 0 || p >= T) return OR_ERR_ARG;
+        }
+    for (int64_t t = 0; t < N; ++t)
+        for (int64_t h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int k = 0; k < K; ++k) {
+                int64_t p = expanded_to_permuted[t * K + k];
+                float v = row_value(y, dtype, p * H + h);
+                if (topk_weights) {
+                    float prod = topk_weights[t * K + k] * v;
+                    acc = acc + prod;
+                } else {
+                    acc = acc + v;
+                }
+            }
+            if (dtype == 0) ((float*)out)[t * H + h] = acc;
+            else ((uint16_t*)out)[t * H + h] = bf16_round_nearest_even(acc);
+        }
     return OR_OK;
 }

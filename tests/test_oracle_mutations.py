@@ -61,6 +61,16 @@ MUTANTS = [
      "int64_t lim1 = (cta_offset[e] + cta) * (int64_t)A;"),
     ("tile_limit_ignores_count", "int64_t lim2 = cta_offset[e] * (int64_t)A + counts[e];",
      "int64_t lim2 = (cta_offset[e] + num_cta[e]) * (int64_t)A;"),
+    ("permute_wrong_token", "(const char*)x + (size_t)t * row, row);",
+     "(const char*)x + (size_t)((t * K + k) % N) * row, row);"),
+    ("permute_no_zero_fill", "if (len == 0) continue;", "continue;"),
+    ("combine_drops_weight", "float prod = topk_weights[t * K + k] * v;", "float prod = v;"),
+    ("combine_weight_reversed", "float prod = topk_weights[t * K + k] * v;",
+     "float prod = topk_weights[t * K + (K - 1 - k)] * v;"),
+    ("combine_reverse_order", "for (int k = 0; k < K; ++k) {\n                int64_t p = expanded_to_permuted[t * K + k];\n                float v",
+     "for (int k = K - 1; k >= 0; --k) {\n                int64_t p = expanded_to_permuted[t * K + k];\n                float v"),
+    ("bf16_truncates_ties", "if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1;",
+     "if (lower > 0x8000u) upper += 1;"),
 ]
 
 
@@ -86,6 +96,11 @@ def _battery():
     for seed in range(2):
         for E, A in [(5, 4), (16, 3)]:
             pins.test_tile_map_matches_row_enumeration(seed, E, A)
+    for dtype in ("f32", "bf16"):
+        pins.test_permute_then_combine_round_trip(dtype, 37, 8, 2, 4, 16)
+        pins.test_combine_small_integers_exact(dtype)
+    pins.test_combine_sums_in_slot_order()
+    pins.test_combine_bf16_rounding_matches_torch()
 
 
 def test_real_oracle_passes_battery():

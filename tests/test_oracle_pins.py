@@ -474,3 +474,100 @@ def test_tile_map_tiles_cover_layout_rows(N, E, K, A):
         real = L.permuted_to_expanded[j * A:lim]
         assert np.all(real >= 0) and np.all(flat[real] == tm.cta_to_expert[j])
         assert np.all(L.permuted_to_expanded[lim:(j + 1) * A] == -1)
+
+
+# ---------------------------------------------------------------------------------------------
+# Local permute / combine of hidden rows: round trips, exact small-integer sums, the binary32
+# summation order and the bf16 rounding (checked against torch's CPU conversion)
+# ---------------------------------------------------------------------------------------------
+
+def _bf16_bits(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+
+
+def _bf16_to_f32(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _rand_layout(rng, N, E, K, A):
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(N)]).astype(np.int32)
+    return ids, oracle.layout(ids, E, A)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N,E,K,A,H", [(1, 4, 1, 1, 8), (37, 8, 2, 4, 16), (64, 16, 4, 3, 24),
+                                       (50, 32, 8, 8, 8)])
+def test_permute_then_combine_round_trip(dtype, N, E, K, A, H):
+    rng = np.random.default_rng(N * 31 + K)
+    # values with at most 4 significant bits, so every partial sum j*x (j <= 8) is exact
+    xf = (rng.integers(-15, 16, (N, H)) * np.exp2(rng.integers(-6, 7, (N, H)))).astype(np.float32)
+    x = xf if dtype == "f32" else _bf16_bits(xf)
+    ids, L = _rand_layout(rng, N, E, K, A)
+    T = int(L.cu_seqlens[E])
+    xp = oracle.permute_rows(x, L.expanded_to_permuted, L.zero_fill, T)
+    # every row of [0, T) written: a slot's token row, or zeros on padding
+    pad = np.ones(T, bool)
+    pad[L.expanded_to_permuted] = False
+    assert np.all(xp[pad].view(np.uint8) == 0)
+    tok = L.permuted_to_expanded[~pad] // K
+    assert np.array_equal(xp[~pad], x[tok])
+    # K copies summed in order: exactly K * x
+    y = oracle.combine_rows(xp, L.expanded_to_permuted, K)
+    xv = xf if dtype == "f32" else _bf16_to_f32(x)
+    got = y if dtype == "f32" else _bf16_to_f32(y)
+    assert np.array_equal(got, xv * np.float32(K))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_combine_small_integers_exact(dtype):
+    """Integer rows and power-of-two weights: every partial sum is exact, so the result is the
+    exact weighted sum."""
+    from fractions import Fraction
+    rng = np.random.default_rng(3)
+    N, E, K, A, H = 40, 16, 8, 4, 12
+    ids, L = _rand_layout(rng, N, E, K, A)
+    T = int(L.cu_seqlens[E])
+    yv = rng.integers(-4, 5, (T, H)).astype(np.float32)
+    w = rng.choice(np.array([0.25, 0.5, 1.0, 2.0, -1.0], np.float32), (N, K))
+    y = yv if dtype == "f32" else _bf16_bits(yv)
+    out = oracle.combine_rows(y, L.expanded_to_permuted, K, w)
+    outv = out if dtype == "f32" else _bf16_to_f32(out)
+    P = L.expanded_to_permuted.reshape(N, K)
+    for t in range(N):
+        for h in range(H):
+            exact = sum(Fraction(float(w[t, k])) * Fraction(float(yv[P[t, k], h])) for k in range(K))
+            assert Fraction(float(outv[t, h])) == exact
+
+
+def test_combine_sums_in_slot_order():
+    """1 + 2^-24 rounds back to 1 in binary32 (tie to even), so adding two 2^-24 terms after the
+    1 leaves 1, while adding them first gives 1 + 2^-23: the order k = 0, 1, 2 is visible."""
+    tiny = np.float32(2.0 ** -24)
+    e2p = np.array([0, 1, 2], np.int32)
+    y = np.array([[1.0], [tiny], [tiny]], np.float32)
+    assert oracle.combine_rows(y, e2p, 3)[0, 0] == np.float32(1.0)
+    y_rev = np.array([[tiny], [tiny], [1.0]], np.float32)
+    assert oracle.combine_rows(y_rev, e2p, 3)[0, 0] == np.float32(1.0) + np.float32(2.0 ** -23)
+
+
+def test_combine_bf16_rounding_matches_torch():
+    """K = 1: out = bf16(w * y).  Compared bit for bit with torch's CPU binary32 product and its
+    round-to-nearest-even conversion, over random values and hand-made ties, overflow and NaN."""
+    import torch
+    rng = np.random.default_rng(9)
+    n = 4096
+    yv = rng.standard_normal(n).astype(np.float32) * np.float32(3)
+    w = rng.standard_normal(n).astype(np.float32)
+    # ties at 1.0: 1 + 2^-8 rounds to 1 (even); 1 + 3*2^-8 rounds up to 1 + 2^-6
+    yv[:4] = [1.0, 1.0, 3.0e38, 1.0]
+    w[:4] = [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 4.0, np.nan]
+    y = _bf16_bits(yv)
+    out = oracle.combine_rows(y.reshape(n, 1), np.arange(n, dtype=np.int32), 1, w.reshape(n, 1))
+    ref = (torch.from_numpy(w) * torch.from_numpy(_bf16_to_f32(y))).to(torch.bfloat16)
+    ref = ref.view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(_bf16_to_f32(ref))
+    assert np.array_equal(out.reshape(-1)[~nan], ref[~nan])
+    assert np.all(np.isnan(_bf16_to_f32(out.reshape(-1)[nan])))
+    assert _bf16_to_f32(out[:2, 0]).tolist() == [1.0, 1.0 + 2.0 ** -6]

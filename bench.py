@@ -196,6 +196,46 @@ def tile_map_leg(B, torch, L, wl, steps: int, stream):
             "GB_per_s": nbytes / (us * 1e-6) / 1e9}
 
 
+HIDDEN = 7168   # DeepSeek-V3 hidden size, for the rows of the permute / combine leg
+
+
+def rows_leg(B, torch, L, w, wl, steps: int, stream):
+    """Local permute and weighted combine of bf16 hidden rows over the last step's layout, each
+    timed on its own (not part of the step): `steps` back-to-back calls between two events."""
+    N, E, K = wl.N, wl.E, wl.K
+    dev = L.cu_seqlens.device
+    T = int(L.cu_seqlens[E].item())
+    row = HIDDEN * 2
+    g = torch.Generator(device=dev).manual_seed(0)
+    x = torch.randn((N, HIDDEN), generator=g, device=dev).to(torch.bfloat16)
+    xp = torch.empty((T, HIDDEN), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((N, HIDDEN), dtype=torch.bfloat16, device=dev)
+    legs = {
+        "permute": (B.bound_permute_rows(x, L.expanded_to_permuted, K, L.zero_fill, xp, stream),
+                    N * row + T * row + N * K * 4 + E * 8),
+        "combine": (B.bound_combine_rows(xp, L.expanded_to_permuted, K, w, out, stream),
+                    N * K * row + N * row + N * K * 8),
+    }
+    res = {"hidden": HIDDEN, "dtype": "bf16", "T": T}
+    for name, (call, nbytes) in legs.items():
+        for _ in range(2):
+            call()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(steps):
+            call()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / steps
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = {"us_per_call": us, "algorithmic_bytes": nbytes, "GB_per_s": gbs,
+                     "frac_of_peak": gbs / HBM_PEAK_GBS}
+    del x, xp, out
+    return res
+
+
 def main():
     args = parse()
     if args.record_traffic:
@@ -315,7 +355,9 @@ def main():
                  "slots_per_s": N * K / (ms_step * 1e-3), "T": T, "dedup_groups": G,
                  "dedup_dups": D, "host_wall_s": wall},
     }
-    out["next_rows"] = {"tile_map": tile_map_leg(B, torch, L, wl, args.steps, stream)}
+    w_last = sets[(args.warmup + args.steps - 1) % nsets][2]
+    out["next_rows"] = {"tile_map": tile_map_leg(B, torch, L, wl, args.steps, stream),
+                        "rows": rows_leg(B, torch, L, w_last, wl, min(args.steps, 20), stream)}
     if args.copy_calibration > 0:
         nbytes = args.copy_calibration << 20
         src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)

@@ -46,7 +46,8 @@ class PlanOutputs(ctypes.Structure):
 
 
 EXPORTS = ("mep_route_topk", "mep_route_topk_timed", "mep_build_layout", "mep_layout_workspace_size", "mep_plan",
-           "mep_plan_workspace_size", "mep_layout_plan", "mep_tile_map", "mep_status_string")
+           "mep_plan_workspace_size", "mep_layout_plan", "mep_tile_map", "mep_permute_rows",
+           "mep_combine_rows", "mep_status_string")
 
 _lib = None
 _lock = threading.Lock()
@@ -81,6 +82,10 @@ def lib():
                 L.mep_layout_plan.restype = I
                 L.mep_tile_map.argtypes = [P, I, I64, I, P, P, I64, P, P, P]
                 L.mep_tile_map.restype = I
+                L.mep_permute_rows.argtypes = [P, I, I64, I64, I, P, P, I, P, I64, P]
+                L.mep_permute_rows.restype = I
+                L.mep_combine_rows.argtypes = [P, I, I64, I64, I, P, P, I64, P, P]
+                L.mep_combine_rows.restype = I
                 L.mep_status_string.argtypes = [I]
                 L.mep_status_string.restype = ctypes.c_char_p
                 _lib = L
@@ -174,6 +179,55 @@ def mep_tile_map(tokens_per_expert, num_slots, tile, cta_to_expert=None, cta_mn_
                             _ptr(cta_mn_limit), cap, _ptr(permuted_idx_size), _ptr(num_ctas),
                             _stream(stream))
     _check(rc, "mep_tile_map")
+
+
+def _row_dtype(t):
+    if t.dtype == torch.bfloat16:
+        return MEP_BF16
+    if t.dtype == torch.float32:
+        return MEP_F32
+    raise ValueError("rows must be float32 or bfloat16")
+
+
+def _permute_args(x, expanded_to_permuted, K, zero_fill, x_permuted, stream):
+    _require_cuda(x, expanded_to_permuted, zero_fill, x_permuted)
+    if x.dtype != x_permuted.dtype:
+        raise ValueError("x and x_permuted must have the same dtype")
+    N, H = x.shape
+    E = zero_fill.shape[0] if zero_fill is not None else 0
+    return (_ptr(x), _row_dtype(x), N, H, K, _ptr(expanded_to_permuted), _ptr(zero_fill), E,
+            _ptr(x_permuted), x_permuted.shape[0], _stream(stream))
+
+
+def _combine_args(y_permuted, expanded_to_permuted, K, topk_weights, out, stream):
+    _require_cuda(y_permuted, expanded_to_permuted, topk_weights, out)
+    if y_permuted.dtype != out.dtype:
+        raise ValueError("y_permuted and out must have the same dtype")
+    N, H = out.shape
+    return (_ptr(y_permuted), _row_dtype(out), N, H, K, _ptr(expanded_to_permuted),
+            _ptr(topk_weights), y_permuted.shape[0], _ptr(out), _stream(stream))
+
+
+def mep_permute_rows(x, expanded_to_permuted, K, zero_fill, x_permuted, stream=None):
+    _check(lib().mep_permute_rows(*_permute_args(x, expanded_to_permuted, K, zero_fill, x_permuted,
+                                                 stream)), "mep_permute_rows")
+
+
+def mep_combine_rows(y_permuted, expanded_to_permuted, K, topk_weights, out, stream=None):
+    _check(lib().mep_combine_rows(*_combine_args(y_permuted, expanded_to_permuted, K, topk_weights,
+                                                 out, stream)), "mep_combine_rows")
+
+
+def bound_permute_rows(x, expanded_to_permuted, K, zero_fill, x_permuted, stream=None):
+    return _bound("mep_permute_rows",
+                  _permute_args(x, expanded_to_permuted, K, zero_fill, x_permuted, stream),
+                  "mep_permute_rows")
+
+
+def bound_combine_rows(y_permuted, expanded_to_permuted, K, topk_weights, out, stream=None):
+    return _bound("mep_combine_rows",
+                  _combine_args(y_permuted, expanded_to_permuted, K, topk_weights, out, stream),
+                  "mep_combine_rows")
 
 
 def bound_tile_map(tokens_per_expert, num_slots, tile, cta_to_expert=None, cta_mn_limit=None,

@@ -15,6 +15,9 @@
  *                    four)
  *   mep_tile_map     per-expert counts -> grouped-GEMM tile maps (the expert
  *                    and the row limit of every padded tile)
+ *   mep_permute_rows, mep_combine_rows
+ *                    hidden-state rows into the permuted order (zero padding)
+ *                    and back, summed over a token's K slots
  *
  * Sources, cited by page title and section:
  *   [TRT]  TensorRT-LLM RoutingKernel.cuh (blockScaleMoe routing helpers,
@@ -306,6 +309,55 @@ int mep_layout_plan(const int32_t* topk_ids, int64_t N, int E, int K, int alignm
 int mep_tile_map(const int32_t* tokens_per_expert, int E, int64_t num_slots, int tile,
                  int32_t* cta_to_expert, int32_t* cta_mn_limit, int64_t cap_ctas,
                  int32_t* permuted_idx_size, int32_t* num_ctas, void* stream);
+
+/*
+ * mep_permute_rows -- one GPU's share of expert dispatch for hidden-state
+ * rows ([DEEP] intranode dispatch: a token's row is copied to the slot of
+ * every rank it is sent to; here the slots are the layout's permuted rows).
+ *   x_permuted[expanded_to_permuted[t*K+k]] = x[t]   for every t, k
+ *   x_permuted[start .. start+len) = 0 for every zero_fill[e] = (start, len)
+ * Rows of [0, permuted_rows) covered by neither are not written (with the
+ * layout's own zero_fill, every row of [0, cu_seqlens[E]) is covered).
+ *
+ * Arguments
+ *   x                  device [N, H] rows of `dtype` (MEP_F32 or MEP_BF16; the
+ *                      bytes are copied unchanged), 16-byte aligned
+ *   H                  elements per row; H * sizeof(element) % 16 == 0
+ *   K                  1 .. 32, N*K <= INT32_MAX
+ *   expanded_to_permuted device int32[N*K] (from mep_build_layout); an entry
+ *                      outside [0, permuted_rows) is skipped
+ *   zero_fill, E       device int32[E,2] padding ranges (nullable; from
+ *                      mep_build_layout), E >= 1 when given; a range that
+ *                      leaves [0, permuted_rows) is skipped
+ *   x_permuted         device [permuted_rows, H], 16-byte aligned
+ *   permuted_rows      rows of x_permuted, <= INT32_MAX
+ */
+int mep_permute_rows(const void* x, int dtype, int64_t N, int64_t H, int K,
+                     const int32_t* expanded_to_permuted, const int32_t* zero_fill, int E,
+                     void* x_permuted, int64_t permuted_rows, void* stream);
+
+/*
+ * mep_combine_rows -- one GPU's share of expert combine ([DEEP] intranode
+ * combine: a token's received rows are summed in fp32 and cast back to the
+ * row type), with optional routing weights.
+ *   acc = 0.0f; for k = 0 .. K-1 in order:
+ *     acc = acc + w[t*K+k] * y[expanded_to_permuted[t*K+k]]   (with weights)
+ *     acc = acc + y[expanded_to_permuted[t*K+k]]              (without)
+ *   each step one binary32 multiply and one binary32 add, no fused
+ *   multiply-add; out[t] = acc cast to the row type (bf16: round to nearest,
+ *   ties to even, NaN kept quiet).
+ *
+ * Arguments
+ *   y_permuted         device [permuted_rows, H] rows of `dtype`, 16-byte
+ *                      aligned
+ *   topk_weights       device float[N*K] (nullable: plain sum)
+ *   out                device [N, H] rows of `dtype`, 16-byte aligned
+ *   others             as mep_permute_rows; an index outside
+ *                      [0, permuted_rows) drops its term
+ */
+int mep_combine_rows(const void* y_permuted, int dtype, int64_t N, int64_t H, int K,
+                     const int32_t* expanded_to_permuted, const float* topk_weights,
+                     int64_t permuted_rows, void* out, void* stream);
 
 /* Static, NUL-terminated name of a return code. */
 const char* mep_status_string(int code);

@@ -163,3 +163,32 @@ def test_tile_map_validation():
     assert _tile(c2e=None, cap=(64 + 8 * 3) // 4 - 1) == B.MEP_ERR_CAPACITY  # either array
     # nothing to write: accepted without a launch
     assert _tile(c2e=None, lim=None, pis=None, nct=None, cap=0) == B.MEP_OK
+
+
+def test_rows_validation():
+    L = B.lib()
+    perm = lambda x=FAKE, dt=1, N=16, H=64, K=2, e2p=FAKE, zf=FAKE, E=4, out=FAKE, T=64: \
+        L.mep_permute_rows(x, dt, N, H, K, e2p, zf, E, out, T, None)
+    comb = lambda y=FAKE, dt=1, N=16, H=64, K=2, e2p=FAKE, w=FAKE, T=64, out=FAKE: \
+        L.mep_combine_rows(y, dt, N, H, K, e2p, w, T, out, None)
+    for f in (perm, comb):
+        assert f(dt=2) == B.MEP_ERR_INVALID_ARG
+        assert f(N=-1) == B.MEP_ERR_INVALID_ARG
+        assert f(H=0) == B.MEP_ERR_INVALID_ARG
+        assert f(K=0) == B.MEP_ERR_INVALID_ARG
+        assert f(e2p=None) == B.MEP_ERR_INVALID_ARG
+        assert f(e2p=FAKE + 2) == B.MEP_ERR_INVALID_ARG
+        assert f(H=12) == B.MEP_ERR_UNSUPPORTED           # 24-byte bf16 rows
+        assert f(dt=0, H=6) == B.MEP_ERR_UNSUPPORTED      # 24-byte fp32 rows
+        assert f(K=33) == B.MEP_ERR_UNSUPPORTED
+        assert f(T=2 ** 31) == B.MEP_ERR_UNSUPPORTED
+    assert perm(x=MIS) == B.MEP_ERR_INVALID_ARG
+    assert perm(out=MIS) == B.MEP_ERR_INVALID_ARG
+    assert perm(x=None) == B.MEP_ERR_INVALID_ARG
+    assert perm(E=0) == B.MEP_ERR_INVALID_ARG
+    assert perm(N=0, x=None, e2p=None, out=None) == B.MEP_ERR_INVALID_ARG  # zero_fill needs out
+    assert perm(N=0, x=None, e2p=None, zf=None, out=None) == B.MEP_OK       # nothing to do
+    assert comb(y=MIS) == B.MEP_ERR_INVALID_ARG
+    assert comb(out=None) == B.MEP_ERR_INVALID_ARG
+    assert comb(w=FAKE + 1) == B.MEP_ERR_INVALID_ARG
+    assert comb(N=0, y=None, e2p=None, out=None) == B.MEP_OK

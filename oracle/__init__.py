@@ -57,6 +57,9 @@ def load(path: str):
     L.oracle_permute_rows.restype = i32
     L.oracle_combine_rows.argtypes = [P, i32, i64, i64, i32, P, P, P, i64]
     L.oracle_combine_rows.restype = i32
+    L.oracle_plan_balanced.argtypes = ([P, P, P, P, i64, i32, i32, i32, i32, i32, i64, i64]
+                                       + [P] * 10)
+    L.oracle_plan_balanced.restype = i32
     return L
 
 
@@ -191,6 +194,43 @@ def combine_rows(y: np.ndarray, expanded_to_permuted: np.ndarray, K: int,
     rc = lib().oracle_combine_rows(_p(y), _row_dtype(y), N, H, K, _p(e2p), _p(w), _p(out), T)
     if rc != 0:
         raise ValueError("oracle_combine_rows failed (code %d)" % rc)
+    return out
+
+
+@dataclass
+class BalancedPlan:
+    group_tokens: np.ndarray     # [R]
+    z: np.ndarray                # [R, R] slots moved from rank s to rank d
+    alloc: np.ndarray            # [R, E] slots of expert e computed on rank r
+    alloc_cumsum: np.ndarray     # [E, R]
+    experts_to_copy: np.ndarray  # [R, B]
+    remote_stats: np.ndarray     # [R, 2]
+    cu_seqlens: np.ndarray       # [R, E+B] group ends
+    zero_fill: np.ndarray        # [R, E+B, 2]
+    expert_offsets: np.ndarray   # [R, E]
+    dst: np.ndarray              # [N*K]
+
+
+def plan_balanced(ids, tokens_per_expert, cu_seqlens, expanded_to_permuted, E, R, B, tp,
+                  capacity, NvS) -> BalancedPlan:
+    """MoonEP capacity rebalancing with redundant remote experts, for all R ranks."""
+    ids = np.ascontiguousarray(ids, np.int32)
+    N, K = ids.shape
+    G = E + B
+    out = BalancedPlan(np.empty(R, np.int32), np.empty((R, R), np.int32),
+                       np.empty((R, E), np.int32), np.empty((E, R), np.int32),
+                       np.empty((R, max(B, 0)), np.int32), np.empty((R, 2), np.int32),
+                       np.empty((R, G), np.int32), np.empty((R, G, 2), np.int32),
+                       np.empty((R, E), np.int32), np.empty(N * K, np.int32))
+    rc = lib().oracle_plan_balanced(
+        _p(ids), _p(np.ascontiguousarray(tokens_per_expert, np.int32)),
+        _p(np.ascontiguousarray(cu_seqlens, np.int32)),
+        _p(np.ascontiguousarray(expanded_to_permuted, np.int32)), N, E, K, R, B, tp, capacity,
+        NvS, *[_p(getattr(out, f)) for f in ("group_tokens", "z", "alloc", "alloc_cumsum",
+                                              "experts_to_copy", "remote_stats", "cu_seqlens",
+                                              "zero_fill", "expert_offsets", "dst")])
+    if rc != 0:
+        raise ValueError("oracle_plan_balanced failed (code %d)" % rc)
     return out
 
 

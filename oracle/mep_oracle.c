@@ -2,8 +2,9 @@
  * mep_oracle.c -- TEST INFRASTRUCTURE ONLY.
  *
  * A plain, slow, single-threaded CPU oracle for MoE routing, dispatch layout,
- * expert-parallel planning, grouped-GEMM tile maps and the local permute /
- * combine of hidden-state rows.  Only tests, the smoke check and the CPU
+ * expert-parallel planning (plain, and with capacity rebalancing),
+ * grouped-GEMM tile maps and the local permute / combine of hidden-state
+ * rows.  Only tests, the smoke check and the CPU
  * baseline leg of the benchmark may load it; the product path never does.
  * It shares no code, header, table or constant with the HIP library.
  *
@@ -21,7 +22,8 @@
  * that takes them.  Parity status: every function here is pinned by the
  * CPU tests (brute force, exact-arithmetic sigmoid, closed forms,
  * stable-sort equivalence, plan invariants, row-by-row tile enumeration,
- * exact permute/combine round trips and sums, bf16 rounding against torch);
+ * exact permute/combine round trips and sums, bf16 rounding against torch,
+ * hand-worked rebalancing cases and the no-move reduction to the plain plan);
  * none is "parity unpinned".
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math -shared -fPIC
@@ -641,4 +643,210 @@ int oracle_combine_rows(const void* y, int dtype, int64_t N, int64_t H, int K,
             else ((uint16_t*)out)[t * H + h] = bf16_round_nearest_even(acc);
         }
     return OR_OK;
+}
+
+/*
+ * Capacity rebalancing with redundant remote experts: [MOON] PlanningKernel
+ * phases after the gather of per-rank expert counts (the balancing loop,
+ * the per-owner quota allocation, the per-destination choice of experts to
+ * copy with its padded group scan, and the dst search), run for all R
+ * ranks at once.  The N*K slots of the batch play every source rank in
+ * turn: a slot's position among the slots of its expert (source-then-token
+ * order, i.e. global slot order) is expanded_to_permuted - cu_seqlens[e].
+ *
+ *   total[e] = tokens_per_expert[e]; group_tokens[r] = sum of total over
+ *     r's experts (owner(e) = e / epn).
+ *   balance[r] = group_tokens[r] - CAP.  Repeat: the largest balance
+ *     (lowest rank on ties) is the surplus, the smallest (lowest rank on
+ *     ties) the deficit; stop when surplus <= 0 or deficit >= 0; otherwise
+ *     move = -deficit (the deficit rank is refilled to CAP in one move even
+ *     if that takes the surplus rank below CAP), z[surplus][deficit] = move,
+ *     balance[surplus] -= move, balance[deficit] = 0.
+ *   For every owner o: remaining[j] = total of o's j-th expert,
+ *     quota[r] = z[o][r].  Repeat: the largest quota (lowest rank on ties);
+ *     stop if <= 0; the largest remaining (lowest index on ties); stop if
+ *     <= 0; take = min of the two; alloc[target][that expert] += take, both
+ *     are reduced by take.  What is left stays at o.
+ *   alloc_cumsum[e][r] = sum_{r' <= r} alloc[r'][e].
+ *   For every destination d: counts[e] = alloc[d][e]; the remote ones
+ *     (owner != d) with a count > 0 are counted in remote_stats[d][0]; B
+ *     times the largest remote count is picked (highest index on ties) and
+ *     cleared: experts_to_copy[d][slot] = that expert, or -1 when the
+ *     largest is 0; each pick adds one to remote_stats[owner][1].
+ *     E + B groups: group g < E holds expert g with counts[g] unless g was
+ *     picked (then 0); group E + slot holds the picked expert's count.
+ *     padded = round_up(count, tp) (tp <= 1: count).  An exclusive scan of
+ *     padded gives each group's start; cu_seqlens[d][g] = its end;
+ *     expert_offsets[d][expert] = its start when its count > 0 (else -1 here);
+ *     zero_fill[d][g] = (start + count, padded - count) when count > 0 and
+ *     padded > count, else (0, 0).
+ *   dst of slot i with expert e and global position q: lo = the first rank
+ *     with alloc_cumsum[e][lo] > q (binary search), pc = alloc_cumsum[e][lo-1]
+ *     (0 for lo = 0); dst = lo*NvS + expert_offsets[lo][e] + (q - pc).  Then
+ *     each token's later slots whose rank (dst / NvS) repeats an earlier
+ *     slot's store -dst - 1.
+ * Returns OR_ERR_ARG on bad sizes or a layout that does not match the
+ * counts.  All outputs are required.
+ */
+static int beats_max_low(int64_t a, int ia, int64_t b, int ib) { return a > b || (a == b && ia < ib); }
+static int beats_min_low(int64_t a, int ia, int64_t b, int ib) { return a < b || (a == b && ia < ib); }
+static int beats_max_high(int64_t a, int ia, int64_t b, int ib) { return a > b || (a == b && ia > ib); }
+
+int oracle_plan_balanced(const int32_t* ids, const int32_t* tokens_per_expert,
+                         const int32_t* cu_seqlens, const int32_t* expanded_to_permuted,
+                         int64_t N, int E, int K, int R, int B, int tp, int64_t CAP,
+                         int64_t NvS, int32_t* group_tokens, int32_t* z, int32_t* alloc,
+                         int32_t* alloc_cumsum, int32_t* experts_to_copy,
+                         int32_t* remote_stats, int32_t* cu_out, int32_t* zero_fill,
+                         int32_t* expert_offsets, int32_t* dst) {
+    if (N < 0 || E <= 0 || K <= 0 || R <= 0 || B < 0 || CAP < 0 || NvS <= 0) return OR_ERR_ARG;
+    if (E % R != 0) return OR_ERR_ARG;
+    int epn = E / R;
+    int G = E + B;
+    int64_t* bal = (int64_t*)calloc((size_t)R, sizeof(int64_t));
+    int64_t* counts = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    int64_t* remote = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    int* picked = (int*)calloc((size_t)E, sizeof(int));
+    int* slot_expert = (int*)calloc((size_t)(B > 0 ? B : 1), sizeof(int));
+
+    /* group totals */
+    for (int r = 0; r < R; ++r) {
+        int64_t s = 0;
+        for (int j = 0; j < epn; ++j) s += tokens_per_expert[r * epn + j];
+        group_tokens[r] = (int32_t)s;
+    }
+    /* balancing loop */
+    for (int i = 0; i < R * R; ++i) z[i] = 0;
+    for (int r = 0; r < R; ++r) bal[r] = (int64_t)group_tokens[r] - CAP;
+    for (;;) {
+        int sr = 0, dr = 0;
+        for (int r = 1; r < R; ++r) {
+            if (beats_max_low(bal[r], r, bal[sr], sr)) sr = r;
+            if (beats_min_low(bal[r], r, bal[dr], dr)) dr = r;
+        }
+        if (bal[sr] <= 0 || bal[dr] >= 0) break;
+        int64_t move = -bal[dr];
+        bal[sr] -= move;
+        bal[dr] = 0;
+        z[sr * R + dr] = (int32_t)move;
+    }
+    /* quota allocation per owner */
+    for (int i = 0; i < R * E; ++i) alloc[i] = 0;
+    for (int o = 0; o < R; ++o) {
+        int64_t* quota = (int64_t*)calloc((size_t)R, sizeof(int64_t));
+        int64_t* rem = (int64_t*)calloc((size_t)epn, sizeof(int64_t));
+        for (int r = 0; r < R; ++r) quota[r] = z[o * R + r];
+        for (int j = 0; j < epn; ++j) rem[j] = tokens_per_expert[o * epn + j];
+        for (;;) {
+            int tr = 0;
+            for (int r = 1; r < R; ++r)
+                if (beats_max_low(quota[r], r, quota[tr], tr)) tr = r;
+            if (quota[tr] <= 0) break;
+            int sj = 0;
+            for (int j = 1; j < epn; ++j)
+                if (beats_max_low(rem[j], j, rem[sj], sj)) sj = j;
+            if (rem[sj] <= 0) break;
+            int64_t take = rem[sj] < quota[tr] ? rem[sj] : quota[tr];
+            quota[tr] -= take;
+            rem[sj] -= take;
+            alloc[tr * E + o * epn + sj] += (int32_t)take;
+        }
+        for (int j = 0; j < epn; ++j) alloc[o * E + o * epn + j] += (int32_t)rem[j];
+        free(quota);
+        free(rem);
+    }
+    for (int e = 0; e < E; ++e) {
+        int64_t run = 0;
+        for (int r = 0; r < R; ++r) {
+            run += alloc[r * E + e];
+            alloc_cumsum[e * R + r] = (int32_t)run;
+        }
+    }
+    /* per destination: experts to copy, groups, offsets */
+    for (int i = 0; i < 2 * R; ++i) remote_stats[i] = 0;
+    for (int d = 0; d < R; ++d) {
+        int nremote = 0;
+        for (int e = 0; e < E; ++e) {
+            counts[e] = alloc[d * E + e];
+            remote[e] = (e / epn == d) ? 0 : counts[e];
+            picked[e] = 0;
+            if (remote[e] > 0) nremote += 1;
+        }
+        remote_stats[2 * d] = nremote;
+        for (int b = 0; b < B; ++b) {
+            int best = 0;
+            for (int e = 1; e < E; ++e)
+                if (beats_max_high(remote[e], e, remote[best], best)) best = e;
+            int chosen = remote[best] > 0 ? best : -1;
+            remote[best] = 0;
+            slot_expert[b] = chosen;
+            experts_to_copy[d * B + b] = chosen;
+            if (chosen >= 0) {
+                remote_stats[2 * (chosen / epn) + 1] += 1;
+                picked[chosen] = 1;
+            }
+        }
+        for (int e = 0; e < E; ++e) expert_offsets[d * E + e] = -1;
+        int64_t base = 0;
+        for (int g = 0; g < G; ++g) {
+            int64_t cnt = 0;
+            int ex = -1;
+            if (g < E) {
+                if (!picked[g]) { cnt = counts[g]; ex = g; }
+            } else if (slot_expert[g - E] >= 0) {
+                ex = slot_expert[g - E];
+                cnt = counts[ex];
+            }
+            int64_t padded = 0;
+            if (cnt > 0) padded = tp > 1 ? ((cnt + tp - 1) / tp) * tp : cnt;
+            if (cnt > 0) expert_offsets[d * E + ex] = (int32_t)base;
+            cu_out[(int64_t)d * G + g] = (int32_t)(base + padded);
+            if (cnt > 0 && padded > cnt) {
+                zero_fill[2 * ((int64_t)d * G + g)] = (int32_t)(base + cnt);
+                zero_fill[2 * ((int64_t)d * G + g) + 1] = (int32_t)(padded - cnt);
+            } else {
+                zero_fill[2 * ((int64_t)d * G + g)] = 0;
+                zero_fill[2 * ((int64_t)d * G + g) + 1] = 0;
+            }
+            base += padded;
+        }
+    }
+    /* dst: binary search over the expert's cumulative allocation */
+    int rc = OR_OK;
+    for (int64_t i = 0; i < N * K; ++i) {
+        int e = ids[i];
+        int64_t q = (int64_t)expanded_to_permuted[i] - cu_seqlens[e];
+        if (e < 0 || e >= E || q < 0 || q >= alloc_cumsum[e * R + R - 1]) {
+            rc = OR_ERR_ARG; /* the layout does not match the counts */
+            goto done;
+        }
+        int lo = 0, hi = R;
+        int64_t pc = 0;
+        while (lo < hi) {
+            int mid = (lo + hi) / 2;
+            int64_t ac = alloc_cumsum[e * R + mid];
+            if (ac > q) hi = mid;
+            else { lo = mid + 1; pc = ac; }
+        }
+        dst[i] = (int32_t)((int64_t)lo * NvS + expert_offsets[lo * E + e] + (q - pc));
+    }
+    /* duplicate canonicalisation per token */
+    for (int64_t t = 0; t < N; ++t)
+        for (int k = 0; k < K; ++k) {
+            int64_t rk = dst[t * K + k] / NvS;
+            int seen = 0;
+            for (int k2 = 0; k2 < k; ++k2) {
+                int64_t v = dst[t * K + k2];
+                int64_t raw = v < 0 ? -v - 1 : v;
+                if (raw / NvS == rk) seen = 1;
+            }
+            if (seen) dst[t * K + k] = -dst[t * K + k] - 1;
+        }
+done:
+    free(bal);
+    free(counts);
+    free(remote);
+    free(picked);
+    free(slot_expert);
+    return rc;
 }

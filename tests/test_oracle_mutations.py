@@ -71,6 +71,20 @@ MUTANTS = [
      "for (int k = K - 1; k >= 0; --k) {\n                int64_t p = expanded_to_permuted[t * K + k];\n                float v"),
     ("bf16_truncates_ties", "if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1;",
      "if (lower > 0x8000u) upper += 1;"),
+    ("balance_surplus_tie_high", "if (beats_max_low(bal[r], r, bal[sr], sr)) sr = r;",
+     "if (beats_max_high(bal[r], r, bal[sr], sr)) sr = r;"),
+    ("balance_move_capped_by_surplus", "int64_t move = -bal[dr];",
+     "int64_t move = -bal[dr] < bal[sr] ? -bal[dr] : bal[sr];"),
+    ("quota_remaining_tie_high", "if (beats_max_low(rem[j], j, rem[sj], sj)) sj = j;",
+     "if (beats_max_high(rem[j], j, rem[sj], sj)) sj = j;"),
+    ("copy_tie_low", "if (beats_max_high(remote[e], e, remote[best], best)) best = e;",
+     "if (beats_max_low(remote[e], e, remote[best], best)) best = e;"),
+    ("group_end_is_start", "cu_out[(int64_t)d * G + g] = (int32_t)(base + padded);",
+     "cu_out[(int64_t)d * G + g] = (int32_t)(base);"),
+    ("search_takes_equal", "if (ac > q) hi = mid;", "if (ac >= q) hi = mid;"),
+    ("balanced_no_dup_encoding", "if (seen) dst[t * K + k] = -dst[t * K + k] - 1;", "(void)seen;"),
+    ("unpicked_remote_dropped", "if (!picked[g]) { cnt = counts[g]; ex = g; }",
+     "if (!picked[g] && g / epn == d) { cnt = counts[g]; ex = g; }"),
 ]
 
 
@@ -101,6 +115,9 @@ def _battery():
         pins.test_combine_small_integers_exact(dtype)
     pins.test_combine_sums_in_slot_order()
     pins.test_combine_bf16_rounding_matches_torch()
+    pins.test_balanced_hand_examples()
+    pins.test_balanced_without_moves_is_the_plain_plan(64, 8, 2, 2, 1)
+    pins.test_balanced_invariants(0, 16, 4, 4, 2, 3)
 
 
 def test_real_oracle_passes_battery():

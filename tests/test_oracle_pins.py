@@ -571,3 +571,103 @@ def test_combine_bf16_rounding_matches_torch():
     assert np.array_equal(out.reshape(-1)[~nan], ref[~nan])
     assert np.all(np.isnan(_bf16_to_f32(out.reshape(-1)[nan])))
     assert _bf16_to_f32(out[:2, 0]).tolist() == [1.0, 1.0 + 2.0 ** -6]
+
+
+# ---------------------------------------------------------------------------------------------
+# Capacity rebalancing: hand-worked cases, the no-move case against the plain plan, invariants
+# ---------------------------------------------------------------------------------------------
+
+def _balanced_from_counts(counts, R, B, tp, capacity, NvS):
+    E = len(counts)
+    ids = np.repeat(np.arange(E), counts).astype(np.int32).reshape(-1, 1)
+    L = oracle.layout(ids, E, 1)
+    return oracle.plan_balanced(ids, L.tokens_per_expert, L.cu_seqlens, L.expanded_to_permuted,
+                                E, R, B, tp, capacity, NvS)
+
+
+def test_balanced_hand_examples():
+    for c in json.load(open(GOLDEN))["balanced_plan"]["cases"]:
+        P = _balanced_from_counts(c["counts"], c["R"], c["B"], c["tp"], c["capacity"], c["NvS"])
+        for k in ("group_tokens", "z", "alloc", "alloc_cumsum", "experts_to_copy", "remote_stats",
+                  "cu_seqlens", "expert_offsets", "dst"):
+            if k in c:
+                assert getattr(P, k).tolist() == c[k], k
+        if "zero_fill_nonzero" in c:
+            nz = [[r, g] + P.zero_fill[r, g].tolist() for r in range(c["R"])
+                  for g in range(P.zero_fill.shape[1]) if P.zero_fill[r, g, 1] != 0]
+            assert nz == c["zero_fill_nonzero"]
+
+
+@pytest.mark.parametrize("N,E,K,R,A", [(64, 8, 2, 2, 1), (200, 16, 4, 4, 3), (300, 32, 8, 8, 8)])
+def test_balanced_without_moves_is_the_plain_plan(N, E, K, R, A):
+    """A capacity above every rank's load moves nothing: every expert stays at its owner, the
+    groups of a rank are its own experts' padded segments, and dst equals the plain plan's."""
+    rng = np.random.default_rng(N + E)
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(N)]).astype(np.int32)
+    L = oracle.layout(ids, E, A)
+    epn = E // R
+    NvS = N * min(K, epn) + (E + 2) * (A - 1)
+    Pb = oracle.plan_balanced(ids, L.tokens_per_expert, L.cu_seqlens, L.expanded_to_permuted, E,
+                              R, 2, A, N * K, NvS)
+    Pp = oracle.plan(ids, L.cu_seqlens, L.expanded_to_permuted, E, R, 1, 1, NvS)
+    assert not Pb.z.any() and np.all(Pb.experts_to_copy == -1) and not Pb.remote_stats.any()
+    assert np.array_equal(Pb.dst, Pp.dst)
+    for r in range(R):
+        own = slice(r * epn, (r + 1) * epn)
+        assert np.array_equal(Pb.alloc[r, own], L.tokens_per_expert[own])
+        assert Pb.alloc[r].sum() == L.tokens_per_expert[own].sum()
+        assert np.array_equal(Pb.cu_seqlens[r, own], Pp.recv_cu_seqlens[r, 1:])
+        assert np.array_equal(Pb.zero_fill[r, own], Pp.recv_zero_fill[own])
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("E,K,R,B,tp", [(8, 2, 4, 1, 1), (16, 4, 4, 2, 3), (32, 6, 8, 3, 4),
+                                        (64, 8, 8, 4, 1)])
+def test_balanced_invariants(seed, E, K, R, B, tp):
+    rng = np.random.default_rng(seed * 101 + E)
+    N = 160
+    # skewed routing: low experts are hot, so some ranks sit far above the capacity
+    p = np.exp(-np.arange(E) / (E / 4))
+    ids = np.stack([rng.choice(E, K, replace=False, p=p / p.sum()) for _ in range(N)]).astype(np.int32)
+    L = oracle.layout(ids, E, 1)
+    epn = E // R
+    cap = N * K // R
+    NvS = max(N * min(K, epn), cap) + (E + B) * tp
+    P = oracle.plan_balanced(ids, L.tokens_per_expert, L.cu_seqlens, L.expanded_to_permuted, E,
+                             R, B, tp, cap, NvS)
+    tpe = L.tokens_per_expert.astype(np.int64)
+    assert np.array_equal(P.group_tokens, tpe.reshape(R, epn).sum(axis=1))
+    assert np.all(P.alloc >= 0) and np.array_equal(P.alloc.sum(axis=0), tpe)
+    assert np.array_equal(P.alloc_cumsum, np.cumsum(P.alloc, axis=0).T)
+    load = P.alloc.sum(axis=1)
+    recv, sent = P.z.sum(axis=0), P.z.sum(axis=1)
+    assert np.array_equal(load, P.group_tokens - sent + recv)       # every quota is handed out
+    assert np.all(load[recv > 0] == cap)                            # receivers end at capacity
+    assert not np.any((recv > 0) & (P.group_tokens > cap) & (sent == 0))
+    for d in range(R):
+        remote = [(int(P.alloc[d, e]), e) for e in range(E) if e // epn != d and P.alloc[d, e] > 0]
+        assert P.remote_stats[d, 0] == len(remote)
+        best = [e for _, e in sorted(remote, key=lambda ce: (-ce[0], -ce[1]))[:B]]
+        assert P.experts_to_copy[d].tolist() == best + [-1] * (B - len(best))
+    picks = P.experts_to_copy[P.experts_to_copy >= 0]
+    assert np.array_equal(P.remote_stats[:, 1], np.bincount(picks // epn, minlength=R))
+    # every slot decodes to a distinct row of its expert's group on the rank that computes it
+    flat = ids.reshape(-1)
+    raw = np.where(P.dst < 0, -P.dst - 1, P.dst)
+    rank, loff = raw // NvS, raw % NvS
+    q = L.expanded_to_permuted - L.cu_seqlens[flat]
+    for i in range(N * K):
+        e, r = flat[i], rank[i]
+        lo_cum = P.alloc_cumsum[e, r - 1] if r > 0 else 0
+        assert lo_cum <= q[i] < P.alloc_cumsum[e, r]
+        assert loff[i] == P.expert_offsets[r, e] + (q[i] - lo_cum)
+    assert len(set(raw.tolist())) == N * K
+    for t in range(N):
+        seen = set()
+        for k in range(K):
+            i = t * K + k
+            assert (P.dst[i] < 0) == (rank[i] in seen)
+            seen.add(rank[i])
+    for r in range(R):
+        ends = P.cu_seqlens[r]
+        assert np.all(np.diff(ends) >= 0) and ends[-1] <= NvS

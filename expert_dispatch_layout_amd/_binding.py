@@ -45,8 +45,16 @@ class PlanOutputs(ctypes.Structure):
                 ("cap_dups", ctypes.c_int64)]
 
 
+BALANCED_FIELDS = ("group_tokens", "z", "alloc", "alloc_cumsum", "experts_to_copy", "remote_stats",
+                   "cu_seqlens", "zero_fill", "expert_offsets", "dst")
+
+
+class BalancedOutputs(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in BALANCED_FIELDS]
+
+
 EXPORTS = ("mep_route_topk", "mep_route_topk_timed", "mep_build_layout", "mep_layout_workspace_size", "mep_plan",
-           "mep_plan_workspace_size", "mep_layout_plan", "mep_tile_map", "mep_permute_rows",
+           "mep_plan_workspace_size", "mep_layout_plan", "mep_tile_map", "mep_plan_balanced", "mep_permute_rows",
            "mep_combine_rows", "mep_status_string")
 
 _lib = None
@@ -82,6 +90,9 @@ def lib():
                 L.mep_layout_plan.restype = I
                 L.mep_tile_map.argtypes = [P, I, I64, I, P, P, I64, P, P, P]
                 L.mep_tile_map.restype = I
+                L.mep_plan_balanced.argtypes = [P, P, P, P, I64, I, I, I, I, I, I64, I64,
+                                                ctypes.POINTER(BalancedOutputs), P]
+                L.mep_plan_balanced.restype = I
                 L.mep_permute_rows.argtypes = [P, I, I64, I64, I, P, P, I, P, I64, P]
                 L.mep_permute_rows.restype = I
                 L.mep_combine_rows.argtypes = [P, I, I64, I64, I, P, P, I64, P, P]
@@ -453,6 +464,65 @@ class PlanTensors:
 
 def _addr(t):
     return None if t is None else t.data_ptr()
+
+
+@dataclass
+class BalancedTensors:
+    group_tokens: "torch.Tensor"
+    z: "torch.Tensor"
+    alloc: "torch.Tensor"
+    alloc_cumsum: "torch.Tensor"
+    experts_to_copy: "torch.Tensor"
+    remote_stats: "torch.Tensor"
+    cu_seqlens: "torch.Tensor"
+    zero_fill: "torch.Tensor"
+    expert_offsets: "torch.Tensor"
+    dst: "torch.Tensor"
+
+    def as_struct(self) -> BalancedOutputs:
+        return BalancedOutputs(*[getattr(self, f).data_ptr() if getattr(self, f).numel() else None
+                                 for f in BALANCED_FIELDS])
+
+
+def balanced_nvs(N, E, K, R, num_copies, token_padding, capacity) -> int:
+    """The smallest per-rank row stride mep_plan_balanced accepts."""
+    epn = E // R
+    return max(N * min(K, epn), capacity) + (E + num_copies) * (token_padding - 1)
+
+
+def alloc_balanced(N, E, K, R, num_copies, device="cuda") -> BalancedTensors:
+    i32 = dict(dtype=torch.int32, device=device)
+    G = E + num_copies
+    return BalancedTensors(torch.empty(R, **i32), torch.empty((R, R), **i32),
+                           torch.empty((R, E), **i32), torch.empty((E, R), **i32),
+                           torch.empty((R, num_copies), **i32), torch.empty((R, 2), **i32),
+                           torch.empty((R, G), **i32), torch.empty((R, G, 2), **i32),
+                           torch.empty((R, E), **i32), torch.empty(N * K, **i32))
+
+
+def _balanced_args(topk_ids, layout, E, R, num_copies, token_padding, capacity, NvS, out, stream):
+    _require_cuda(topk_ids, layout.tokens_per_expert, layout.cu_seqlens, layout.expanded_to_permuted)
+    N, K = topk_ids.shape
+    st = out.as_struct()
+    return ((_ptr(topk_ids), _ptr(layout.tokens_per_expert), _ptr(layout.cu_seqlens),
+             _ptr(layout.expanded_to_permuted), N, E, K, R, num_copies, token_padding, capacity, NvS,
+             ctypes.byref(st), _stream(stream)), st)
+
+
+def mep_plan_balanced(topk_ids, layout, E, R, num_copies, token_padding, capacity, NvS,
+                      out: BalancedTensors, stream=None):
+    args, _keep = _balanced_args(topk_ids, layout, E, R, num_copies, token_padding, capacity, NvS,
+                                 out, stream)
+    _check(lib().mep_plan_balanced(*args), "mep_plan_balanced")
+
+
+def bound_plan_balanced(topk_ids, layout, E, R, num_copies, token_padding, capacity, NvS,
+                        out: BalancedTensors, stream=None):
+    args, keep = _balanced_args(topk_ids, layout, E, R, num_copies, token_padding, capacity, NvS,
+                                out, stream)
+    call = _bound("mep_plan_balanced", args, "mep_plan_balanced")
+    call.keep = keep  # the output table must outlive the prepared call
+    return call
 
 
 def default_nvs(N, E, K, R, alignment) -> int:

@@ -15,6 +15,9 @@
  *                    four)
  *   mep_tile_map     per-expert counts -> grouped-GEMM tile maps (the expert
  *                    and the row limit of every padded tile)
+ *   mep_plan_balanced the plan with capacity rebalancing: token moves between
+ *                    ranks, their split over experts, experts to copy, and
+ *                    dst on the rank that computes each slot
  *   mep_permute_rows, mep_combine_rows
  *                    hidden-state rows into the permuted order (zero padding)
  *                    and back, summed over a token's K slots
@@ -309,6 +312,73 @@ int mep_layout_plan(const int32_t* topk_ids, int64_t N, int E, int K, int alignm
 int mep_tile_map(const int32_t* tokens_per_expert, int E, int64_t num_slots, int tile,
                  int32_t* cta_to_expert, int32_t* cta_mn_limit, int64_t cap_ctas,
                  int32_t* permuted_idx_size, int32_t* num_ctas, void* stream);
+
+/* Outputs of mep_plan_balanced; device buffers, all required except
+ * experts_to_copy when num_copies == 0 and dst when N == 0. */
+typedef struct mep_balanced_outputs {
+    int32_t* group_tokens;    /* [R]       slots owned by rank r before moves */
+    int32_t* z;               /* [R,R]     slots moved from rank s to rank d */
+    int32_t* alloc;           /* [R,E]     slots of expert e computed on rank r */
+    int32_t* alloc_cumsum;    /* [E,R]     sum over r' <= r of alloc[r'][e] */
+    int32_t* experts_to_copy; /* [R,B]     experts rank d receives a copy of, -1 = none */
+    int32_t* remote_stats;    /* [R,2]     (remote experts with slots on r,
+                                            copies of r's experts sent out) */
+    int32_t* cu_seqlens;      /* [R,E+B]   end row of each group on rank r */
+    int32_t* zero_fill;       /* [R,E+B,2] (start, length) padding of each group */
+    int32_t* expert_offsets;  /* [R,E]     first row of expert e on rank r, -1 = none */
+    int32_t* dst;             /* [N*K]     rank-tagged row, duplicates as -raw-1 */
+} mep_balanced_outputs;
+
+/*
+ * mep_plan_balanced -- expert-parallel plan with capacity rebalancing and
+ * redundant remote experts ([MOON] PlanningKernel: balancing loop, quota
+ * allocation, experts to copy, group scan, dst search), for all R ranks.
+ *
+ * owner(e) = e / epn, epn = E / R; c_e = tokens_per_expert[e].
+ *   group_tokens[r] = sum of c_e over r's experts; balance = that - capacity.
+ *   Balancing: while the largest balance (lowest rank on ties) is > 0 and
+ *     the smallest (lowest rank on ties) is < 0, the largest moves
+ *     -smallest slots to the smallest (z), which ends at 0 -- in one move,
+ *     even when that takes the giver below capacity.
+ *   Quotas: each owner o hands z[o][r] out, largest quota first (lowest rank
+ *     on ties), each time from its expert with the most slots left (lowest
+ *     index on ties), min of the two at once; what is left stays at o.
+ *     alloc[r][e] is the result, alloc_cumsum its prefix over r.
+ *   Copies: for each rank d, the remote experts (owner != d) with slots on d
+ *     are counted (remote_stats[d][0]); num_copies times the one with most
+ *     slots (highest index on ties) is taken: experts_to_copy[d][b], or -1
+ *     once none is left; each copy adds 1 to remote_stats[owner][1].
+ *   Groups of rank d: E + B of them; group g < E is expert g with
+ *     alloc[d][g] slots unless g was copied (then empty), group E + b the
+ *     b-th copied expert.  Each holds round_up(slots, token_padding) rows;
+ *     cu_seqlens[d][g] is the end of group g (inclusive prefix), zero_fill
+ *     its padding (start, length) when it has slots and padding, else (0,0);
+ *     expert_offsets[d][e] the start of e's group on d, -1 if e has no slots
+ *     there.
+ *   dst: slot i = t*K+k of expert e sits at q = expanded_to_permuted[i] -
+ *     cu_seqlens_layout[e] among e's slots; its rank lo is the first with
+ *     alloc_cumsum[e][lo] > q; dst = lo*NvS + expert_offsets[lo][e] + q -
+ *     alloc_cumsum[e][lo-1] (0 for lo = 0).  A later k of token t whose rank
+ *     repeats an earlier k's stores -dst-1.
+ * The page runs the same steps on every rank from gathered per-rank counts;
+ * on one GPU the layout's stable positions give q directly.
+ *
+ * Arguments
+ *   topk_ids, cu_seqlens, expanded_to_permuted, tokens_per_expert: device
+ *     inputs as produced by mep_build_layout (any alignment) for the same
+ *     ids; tokens_per_expert is required even when N == 0
+ *   R            divides E, R <= 128, E <= 1024, K <= min(E, 32)
+ *   num_copies   B, 0 .. 64
+ *   token_padding >= 1 (1 = no padding)
+ *   capacity     slots per rank, 0 .. INT32_MAX
+ *   NvS          per-rank row stride, >= max(N*min(K,epn), capacity) +
+ *                (E+B)*(token_padding-1); R*NvS <= INT32_MAX
+ * Three kernels; no workspace (the intermediate arrays are outputs).
+ */
+int mep_plan_balanced(const int32_t* topk_ids, const int32_t* tokens_per_expert,
+                      const int32_t* cu_seqlens, const int32_t* expanded_to_permuted, int64_t N,
+                      int E, int K, int R, int num_copies, int token_padding, int64_t capacity,
+                      int64_t NvS, const mep_balanced_outputs* out, void* stream);
 
 /*
  * mep_permute_rows -- one GPU's share of expert dispatch for hidden-state

@@ -192,3 +192,32 @@ def test_rows_validation():
     assert comb(out=None) == B.MEP_ERR_INVALID_ARG
     assert comb(w=FAKE + 1) == B.MEP_ERR_INVALID_ARG
     assert comb(N=0, y=None, e2p=None, out=None) == B.MEP_OK
+
+
+def test_balanced_validation():
+    def call(N=64, E=16, K=4, R=4, nb=2, tp=2, cap=100, NvS=None, ptrs=FAKE, **kw):
+        if NvS is None:
+            NvS = B.balanced_nvs(N, E, K, R, nb, tp, cap)
+        out = B.BalancedOutputs(*([FAKE] * len(B.BALANCED_FIELDS)))
+        for k, v in kw.items():
+            setattr(out, k, v)
+        return B.lib().mep_plan_balanced(ptrs, FAKE, ptrs, ptrs, N, E, K, R, nb, tp, cap, NvS,
+                                         ctypes.byref(out), None)
+    assert B.balanced_nvs(64, 16, 4, 4, 2, 2, 100) == max(64 * 4, 100) + 18
+    assert call(N=-1) == B.MEP_ERR_INVALID_ARG
+    assert call(tp=0) == B.MEP_ERR_INVALID_ARG
+    assert call(nb=-1) == B.MEP_ERR_INVALID_ARG
+    assert call(cap=-1) == B.MEP_ERR_INVALID_ARG
+    assert call(z=None) == B.MEP_ERR_INVALID_ARG
+    assert call(dst=None) == B.MEP_ERR_INVALID_ARG
+    assert call(experts_to_copy=None) == B.MEP_ERR_INVALID_ARG
+    assert call(alloc=FAKE + 2) == B.MEP_ERR_INVALID_ARG
+    assert call(ptrs=None) == B.MEP_ERR_INVALID_ARG
+    assert call(E=18, R=4) == B.MEP_ERR_UNSUPPORTED
+    assert call(R=256, E=512) == B.MEP_ERR_UNSUPPORTED
+    assert call(E=2048, R=4) == B.MEP_ERR_UNSUPPORTED
+    assert call(nb=65) == B.MEP_ERR_UNSUPPORTED
+    assert call(K=33, E=64) == B.MEP_ERR_UNSUPPORTED
+    assert call(cap=2 ** 31) == B.MEP_ERR_UNSUPPORTED
+    assert call(NvS=B.balanced_nvs(64, 16, 4, 4, 2, 2, 100) - 1) == B.MEP_ERR_CAPACITY
+    assert call(N=2 ** 20, NvS=2 ** 30) == B.MEP_ERR_CAPACITY          # R * NvS > INT32_MAX

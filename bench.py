@@ -236,6 +236,35 @@ def rows_leg(B, torch, L, w, wl, steps: int, stream):
     return res
 
 
+def balanced_leg(B, torch, ids, L, wl, steps: int, stream):
+    """The plan with capacity rebalancing over the last step's ids and layout (R ranks, 4 copied
+    experts per rank, groups padded to the layout alignment, capacity = the mean rank load),
+    timed on its own: `steps` back-to-back calls between two events."""
+    N, E, K, R, A = wl.N, wl.E, wl.K, wl.R, wl.alignment
+    nb, cap = 4, N * K // R
+    nvs = B.balanced_nvs(N, E, K, R, nb, A, cap)
+    out = B.alloc_balanced(N, E, K, R, nb, ids.device)
+    call = B.bound_plan_balanced(ids, L, E, R, nb, A, cap, nvs, out, stream)
+    for _ in range(3):
+        call()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(steps):
+        call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / steps
+    # ids, expanded_to_permuted read and dst written per slot; counts, offsets and the small
+    # per-rank tables on top
+    nbytes = 12 * N * K + 4 * (E + 1) + 4 * R * (R + 4 * E + 3 * (E + nb) + nb + 3)
+    return {"us_per_call": us, "ranks": R, "copies_per_rank": nb, "capacity": cap,
+            "moves": int((out.z > 0).sum().item()),
+            "experts_copied": int((out.experts_to_copy >= 0).sum().item()),
+            "algorithmic_bytes": nbytes, "GB_per_s": nbytes / (us * 1e-6) / 1e9}
+
+
 def main():
     args = parse()
     if args.record_traffic:
@@ -355,8 +384,9 @@ def main():
                  "slots_per_s": N * K / (ms_step * 1e-3), "T": T, "dedup_groups": G,
                  "dedup_dups": D, "host_wall_s": wall},
     }
-    w_last = sets[(args.warmup + args.steps - 1) % nsets][2]
+    ids_last, w_last = sets[(args.warmup + args.steps - 1) % nsets][1:3]
     out["next_rows"] = {"tile_map": tile_map_leg(B, torch, L, wl, args.steps, stream),
+                        "balanced_plan": balanced_leg(B, torch, ids_last, L, wl, args.steps, stream),
                         "rows": rows_leg(B, torch, L, w_last, wl, min(args.steps, 20), stream)}
     if args.copy_calibration > 0:
         nbytes = args.copy_calibration << 20

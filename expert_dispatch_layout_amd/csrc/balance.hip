@@ -19,9 +19,9 @@
 //           arg-max passes over the remote counts held in registers), then the E + B groups
 //           scanned across the workgroup; remote_stats[owner][1] is counted with one global
 //           atomic add per copy.
-//   dst     one thread per token: each slot's rank by binary search over its expert's
-//           cumulative allocation (L2-resident), its row from the group offsets, and the
-//           duplicate encoding from a 128-bit mask of the ranks seen so far.
+//   dst     one lane per slot, whole tokens per wave: each slot's rank by binary search over
+//           its expert's cumulative allocation (L2-resident), its row from the group offsets,
+//           and the duplicate encoding from the ranks of the token's earlier slots (shuffles).
 // The loops are the page's, so each stops: every balancing step zeroes one deficit for good
 // and a rank turns from surplus to deficit at most once (at most 2R steps); every quota step
 // zeroes a quota or an expert's remainder (at most R + epn steps).
@@ -56,28 +56,46 @@ struct BalArgs {
     int32_t* expert_offsets;   // [R,E]
 };
 
-__device__ __forceinline__ long long wave_max64(long long v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        const long long o = __shfl_xor(v, m, 64);
-        v = o > v ? o : v;
-    }
-    return v;
+// Wave-wide 64-bit max / min through DPP lane moves (no LDS round trips): two quad
+// permutations, the half-row and row mirrors leave every lane with its row's extremum, the two
+// row broadcasts carry it into the last row, and lane 63 holds the result.  Lanes a move does
+// not reach keep their own value, which leaves the extremum unchanged.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ long long dpp64(long long v) {
+    const int lo = (int)(unsigned long long)v, hi = (int)((unsigned long long)v >> 32);
+    const int l2 = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xf, false);
+    const int h2 = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xf, false);
+    return (long long)(((unsigned long long)(unsigned)h2 << 32) | (unsigned)l2);
 }
 
-__device__ __forceinline__ long long wave_min64(long long v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        const long long o = __shfl_xor(v, m, 64);
-        v = o < v ? o : v;
-    }
-    return v;
+template <bool MAX>
+__device__ __forceinline__ long long wave_ext64(long long v) {
+    auto pick = [](long long a, long long b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+    v = pick(v, dpp64<0xB1, 0xf>(v));   // quad_perm 1,0,3,2
+    v = pick(v, dpp64<0x4E, 0xf>(v));   // quad_perm 2,3,0,1
+    v = pick(v, dpp64<0x141, 0xf>(v));  // row_half_mirror
+    v = pick(v, dpp64<0x140, 0xf>(v));  // row_mirror
+    v = pick(v, dpp64<0x142, 0xa>(v));  // row_bcast:15 into rows 1 and 3
+    v = pick(v, dpp64<0x143, 0xc>(v));  // row_bcast:31 into rows 2 and 3
+    const int lo = __builtin_amdgcn_readlane((int)(unsigned long long)v, 63);
+    const int hi = __builtin_amdgcn_readlane((int)((unsigned long long)v >> 32), 63);
+    return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
 }
+
+__device__ __forceinline__ long long wave_max64(long long v) { return wave_ext64<true>(v); }
+__device__ __forceinline__ long long wave_min64(long long v) { return wave_ext64<false>(v); }
 
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
     return v;
+}
+
+// Barrier that orders LDS only: global stores issued before it are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Arg-extremum keys: the value in the high bits, the index tie-break in the low 11 bits.
@@ -95,35 +113,58 @@ __device__ __forceinline__ int key_index(long long k) { return (int)(k - key_val
 // ---------------------------------------------------------------------------------------------
 // owner kernel
 // ---------------------------------------------------------------------------------------------
+template <int CH>
 __global__ __launch_bounds__(kBalBlock) void balance_owner_kernel(BalArgs a) {
     __shared__ int s_zrow[kBalMaxRanks];          // moves from this owner to each rank
     __shared__ int s_alloc[kBalMaxExperts];       // [R][epn] of this owner's experts
+    __shared__ int s_group[kBalMaxRanks];         // slots per rank before moves
+    __shared__ int s_tot[kBalMaxExperts];         // slots per expert
+    __shared__ int s_moves[3 * (2 * kBalMaxRanks + 1)];  // (from, to, slots) of each move
+    __shared__ int s_nmoves;
     const int o = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int R = a.R, epn = a.epn, E = a.E;
+    constexpr int kPerT = kBalMaxExperts / kBalBlock;
 
-    for (int i = tid; i < R; i += kBalBlock) s_zrow[i] = 0;
+    int tot[kPerT];  // loads first, so their latency overlaps the clearing below
+#pragma unroll
+    for (int i = 0; i < kPerT; ++i) {
+        const int e = tid + i * kBalBlock;
+        tot[i] = e < E ? a.tpe[e] : 0;
+    }
+    for (int i = tid; i < R; i += kBalBlock) {
+        s_zrow[i] = 0;
+        s_group[i] = 0;
+    }
     for (int i = tid; i < R * epn; i += kBalBlock) s_alloc[i] = 0;
     if (o == 0) {
         for (int i = tid; i < R * R; i += kBalBlock) a.z[i] = 0;
         for (int i = tid; i < 2 * R; i += kBalBlock) a.remote_stats[i] = 0;
     }
-    __syncthreads();
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < kPerT; ++i) {
+        const int e = tid + i * kBalBlock;
+        if (e < E) {
+            s_tot[e] = tot[i];
+            atomicAdd(&s_group[e / epn], tot[i]);
+        }
+    }
+    lds_barrier();
 
     if (tid < 64) {
-        // group totals; lane holds ranks lane and lane + 64
+        // lane holds ranks lane and lane + 64
         long long bal[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int r = lane + 64 * c;
-            long long s = 0;
-            if (r < R)
-                for (int j = 0; j < epn; ++j) s += a.tpe[r * epn + j];
+            const long long s = r < R ? s_group[r] : 0;
             if (r < R && o == 0) a.group_tokens[r] = (int32_t)s;
             bal[c] = s - a.cap;
         }
         // balancing loop
+        int nmoves = 0;
         for (;;) {
             long long kmax = LLONG_MIN, kmin = LLONG_MAX;
 #pragma unroll
@@ -148,11 +189,14 @@ __global__ __launch_bounds__(kBalBlock) void balance_owner_kernel(BalArgs a) {
                 if (r == dr) bal[c] = 0;
             }
             if (lane == 0) {
-                if (o == 0) a.z[sr * R + dr] = (int32_t)move;
-                if (sr == o) s_zrow[dr] = (int32_t)move;
+                s_moves[3 * nmoves] = sr;
+                s_moves[3 * nmoves + 1] = dr;
+                s_moves[3 * nmoves + 2] = (int)move;
+                if (sr == o) s_zrow[dr] = (int)move;
             }
+            ++nmoves;
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (lane == 0) s_nmoves = nmoves;
         // quota allocation of this owner's moves over its experts
         long long quota[2];
 #pragma unroll
@@ -160,12 +204,12 @@ __global__ __launch_bounds__(kBalBlock) void balance_owner_kernel(BalArgs a) {
             const int r = lane + 64 * c;
             quota[c] = r < R ? s_zrow[r] : 0;
         }
-        constexpr int kCh = kBalMaxExperts / 64;
+        constexpr int kCh = CH;  // 64-wide chunks of the owner's experts
         long long rem[kCh];
 #pragma unroll
         for (int c = 0; c < kCh; ++c) {
             const int j = lane + 64 * c;
-            rem[c] = j < epn ? a.tpe[o * epn + j] : 0;
+            rem[c] = j < epn ? s_tot[o * epn + j] : 0;
         }
         for (;;) {
             long long kq = LLONG_MIN;
@@ -208,7 +252,7 @@ __global__ __launch_bounds__(kBalBlock) void balance_owner_kernel(BalArgs a) {
             if (j < epn) s_alloc[o * epn + j] = (int)rem[c];
         }
     }
-    __syncthreads();
+    lds_barrier();
     // this owner's columns of alloc, and its experts' rows of alloc_cumsum
     for (int i = tid; i < R * epn; i += kBalBlock) {
         const int r = i / epn, j = i - r * epn;
@@ -222,11 +266,18 @@ __global__ __launch_bounds__(kBalBlock) void balance_owner_kernel(BalArgs a) {
             row[r] = run;
         }
     }
+    if (o == 0) {
+        // the moves go over the zeros stored at the start: a full barrier orders the two
+        __syncthreads();
+        for (int m = tid; m < s_nmoves; m += kBalBlock)
+            a.z[s_moves[3 * m] * R + s_moves[3 * m + 1]] = s_moves[3 * m + 2];
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
 // destination kernel
 // ---------------------------------------------------------------------------------------------
+template <int CH>
 __global__ __launch_bounds__(kBalBlock) void balance_dest_kernel(BalArgs a) {
     __shared__ int s_cnt[kBalMaxExperts];
     __shared__ int s_eoff[kBalMaxExperts];
@@ -243,9 +294,9 @@ __global__ __launch_bounds__(kBalBlock) void balance_dest_kernel(BalArgs a) {
         s_eoff[e] = -1;
         s_picked[e] = 0;
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < 64) {
-        constexpr int kCh = kBalMaxExperts / 64;
+        constexpr int kCh = CH;  // 64-wide chunks of the experts
         long long remote[kCh];
         int n = 0;
 #pragma unroll
@@ -283,7 +334,7 @@ __global__ __launch_bounds__(kBalBlock) void balance_dest_kernel(BalArgs a) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     // E + B groups, a few consecutive per thread, scanned across the workgroup
     constexpr int kPer = (kBalMaxExperts + kBalMaxCopies + kBalBlock - 1) / kBalBlock;
     int cnt[kPer], pad[kPer], ex[kPer];
@@ -310,7 +361,7 @@ __global__ __launch_bounds__(kBalBlock) void balance_dest_kernel(BalArgs a) {
         if (lane >= s) incl += y;
     }
     if (lane == 63) s_wave[wv] = incl;
-    __syncthreads();
+    lds_barrier();
     int base = incl - mine;
     for (int w = 0; w < wv; ++w) base += s_wave[w];
 #pragma unroll
@@ -326,13 +377,16 @@ __global__ __launch_bounds__(kBalBlock) void balance_dest_kernel(BalArgs a) {
         }
         base += pad[i];
     }
-    __syncthreads();
+    lds_barrier();
     for (int e = tid; e < E; e += kBalBlock) a.expert_offsets[d * E + e] = s_eoff[e];
 }
 
 // ---------------------------------------------------------------------------------------------
 // dst kernel
 // ---------------------------------------------------------------------------------------------
+// A wave holds 64 / K whole tokens, one slot per lane (lanes past the last whole token idle), so
+// the dependent loads of the search run for every slot at once and a slot finds the ranks of
+// its token's earlier slots in the lanes just below it.
 __global__ __launch_bounds__(kBalTokBlock) void balance_dst_kernel(const int32_t* __restrict__ ids,
                                                                    const int32_t* __restrict__ cu_seqlens,
                                                                    const int32_t* __restrict__ e2p,
@@ -340,10 +394,15 @@ __global__ __launch_bounds__(kBalTokBlock) void balance_dst_kernel(const int32_t
                                                                    const int32_t* __restrict__ expert_offsets,
                                                                    int64_t N, int E, int K, int R, int64_t NvS,
                                                                    int32_t* __restrict__ dst) {
-    const int64_t t = (int64_t)blockIdx.x * kBalTokBlock + threadIdx.x;
-    if (t >= N) return;
-    unsigned long long seen_lo = 0, seen_hi = 0;
-    for (int k = 0; k < K; ++k) {
+    const int lane = threadIdx.x & 63;
+    const int tpw = 64 / K;
+    const int64_t wave = ((int64_t)blockIdx.x * kBalTokBlock + threadIdx.x) >> 6;
+    const int tl = lane / K, k = lane - tl * K;
+    const int64_t t = wave * tpw + tl;
+    const bool active = tl < tpw && t < N;
+    int rank = -1;
+    int64_t raw = 0;
+    if (active) {
         const int64_t i = t * K + k;
         const int e = ids[i];
         const int q = e2p[i] - cu_seqlens[e];
@@ -356,19 +415,22 @@ __global__ __launch_bounds__(kBalTokBlock) void balance_dst_kernel(const int32_t
             else { lo = mid + 1; pc = ac; }
         }
         if (lo >= R) lo = R - 1;  // only for inputs that break the layout's invariants
-        const int64_t raw = (int64_t)lo * NvS + expert_offsets[(int64_t)lo * E + e] + (q - pc);
-        bool dup;
-        if (lo < 64) {
-            const unsigned long long bit = 1ull << lo;
-            dup = (seen_lo & bit) != 0;
-            seen_lo |= bit;
-        } else {
-            const unsigned long long bit = 1ull << (lo - 64);
-            dup = (seen_hi & bit) != 0;
-            seen_hi |= bit;
-        }
-        dst[i] = (int32_t)(dup ? -raw - 1 : raw);
+        rank = lo;
+        raw = (int64_t)lo * NvS + expert_offsets[(int64_t)lo * E + e] + (q - pc);
     }
+    bool dup = false;
+    for (int k2 = 0; k2 + 1 < K; ++k2) {
+        const int src = lane - k + k2;
+        const int r2 = __shfl(rank, src < 0 ? 0 : src, 64);
+        if (k2 < k && r2 == rank) dup = true;
+    }
+    if (active) dst[t * K + k] = (int32_t)(dup ? -raw - 1 : raw);
+}
+
+// 64-wide chunks covering n entries, rounded up to a compiled count (1, 2, 4 or 16)
+int chunks64(int n) {
+    const int c = (n + 63) / 64;
+    return c <= 1 ? 1 : c <= 2 ? 2 : c <= 4 ? 4 : 16;
 }
 
 }  // namespace
@@ -425,11 +487,20 @@ extern "C" int mep_plan_balanced(const int32_t* topk_ids, const int32_t* tokens_
     a.zero_fill = out->zero_fill;
     a.expert_offsets = out->expert_offsets;
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(balance_owner_kernel, dim3(R), dim3(kBalBlock), 0, st, a);
-    hipLaunchKernelGGL(balance_dest_kernel, dim3(R), dim3(kBalBlock), 0, st, a);
-    if (N > 0)
-        hipLaunchKernelGGL(balance_dst_kernel, dim3((unsigned)ceil_div64(N, kBalTokBlock)), dim3(kBalTokBlock), 0, st,
-                           topk_ids, cu_seqlens, expanded_to_permuted, out->alloc_cumsum, out->expert_offsets, N,
-                           E, K, R, NvS, out->dst);
+    const int ch_o = chunks64(epn), ch_d = chunks64(E);
+    if (ch_o == 1) hipLaunchKernelGGL(balance_owner_kernel<1>, dim3(R), dim3(kBalBlock), 0, st, a);
+    else if (ch_o == 2) hipLaunchKernelGGL(balance_owner_kernel<2>, dim3(R), dim3(kBalBlock), 0, st, a);
+    else if (ch_o == 4) hipLaunchKernelGGL(balance_owner_kernel<4>, dim3(R), dim3(kBalBlock), 0, st, a);
+    else hipLaunchKernelGGL(balance_owner_kernel<16>, dim3(R), dim3(kBalBlock), 0, st, a);
+    if (ch_d == 1) hipLaunchKernelGGL(balance_dest_kernel<1>, dim3(R), dim3(kBalBlock), 0, st, a);
+    else if (ch_d == 2) hipLaunchKernelGGL(balance_dest_kernel<2>, dim3(R), dim3(kBalBlock), 0, st, a);
+    else if (ch_d == 4) hipLaunchKernelGGL(balance_dest_kernel<4>, dim3(R), dim3(kBalBlock), 0, st, a);
+    else hipLaunchKernelGGL(balance_dest_kernel<16>, dim3(R), dim3(kBalBlock), 0, st, a);
+    if (N > 0) {
+        const int64_t waves = ceil_div64(N, 64 / K);
+        hipLaunchKernelGGL(balance_dst_kernel, dim3((unsigned)ceil_div64(waves, kBalTokBlock / 64)),
+                           dim3(kBalTokBlock), 0, st, topk_ids, cu_seqlens, expanded_to_permuted, out->alloc_cumsum,
+                           out->expert_offsets, N, E, K, R, NvS, out->dst);
+    }
     return launch_status();
 }

@@ -47,7 +47,12 @@
 
 namespace mep {
 
-constexpr int kCandCap = 32;
+// Candidate list length per token: a token whose keys above the threshold do not fit is redone
+// on the slow exact path, which costs its wave far more than the rest of its set, so wide tokens
+// (32 experts per lane and at least 4 lanes) get 64 entries; with 2 lanes the list stays at 32
+// to keep the LDS of a workgroup's 128 tokens within budget.
+template <int LPT>
+constexpr int cand_cap() { return LPT >= 4 ? 64 : 32; }
 constexpr int kFastEPL = 32;    // experts per lane
 constexpr int kFastBlock = 256;  // four waves, each independent after the prologue
 constexpr int kFastWaves = kFastBlock / 64;
@@ -227,6 +232,7 @@ __global__ __launch_bounds__(kFastBlock, 3) void route_fast_kernel(RouteArgs a, 
     __shared__ float4 s_bias4[LPT * kFastEPL / 4];
     __shared__ float s_gscore[TPB][MAXG];
     __shared__ float s_gthr[TPB][MAXG];
+    constexpr int kCandCap = cand_cap<LPT>();
     __shared__ uint64_t s_cand[TPB][kCandCap];
     __shared__ int s_ccount[TPB];
     __shared__ int s_sel[TPB][KMAX];

@@ -392,3 +392,17 @@ def test_optional_outputs_may_be_null():
     B.mep_route_topk(t, 2, None, B.route_params(), ids_g, None)
     torch.cuda.synchronize()
     assert np.array_equal(_np(ids_g), ids_o)
+
+
+@pytest.mark.parametrize("E,K,dtype", [(128, 8, synth.BF16), (256, 8, synth.F32), (512, 4, synth.BF16)])
+def test_route_candidate_overflow_takes_exact_path(E, K, dtype):
+    """Rows with long runs of equal logits put every tied key above the threshold, so the
+    candidate list overflows and those tokens are redone exactly; ties go to the lower index."""
+    rng = np.random.default_rng(E + K)
+    N = 300
+    x = rng.standard_normal((N, E)).astype(np.float32)
+    x[::3] = 0.5                                  # whole rows tied
+    x[1::3, : E // 2] = 1.25                      # half rows tied at the top
+    if dtype == synth.BF16:
+        x = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    check_route(x, K, dtype)

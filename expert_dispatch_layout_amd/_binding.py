@@ -54,7 +54,7 @@ class BalancedOutputs(ctypes.Structure):
 
 
 EXPORTS = ("mep_route_topk", "mep_route_topk_timed", "mep_build_layout", "mep_layout_workspace_size", "mep_plan",
-           "mep_plan_workspace_size", "mep_layout_plan", "mep_tile_map", "mep_plan_balanced", "mep_permute_rows",
+           "mep_plan_workspace_size", "mep_layout_plan", "mep_route_layout_plan", "mep_tile_map", "mep_plan_balanced", "mep_permute_rows",
            "mep_combine_rows", "mep_status_string")
 
 _lib = None
@@ -90,6 +90,10 @@ def lib():
                 L.mep_layout_plan.restype = I
                 L.mep_tile_map.argtypes = [P, I, I64, I, P, P, I64, P, P, P]
                 L.mep_tile_map.restype = I
+                L.mep_route_layout_plan.argtypes = [P, I, I64, I, I, P, ctypes.POINTER(RouteParams), P, P,
+                                                    I, P, P, P, P, I64, P, I, I, I, I64,
+                                                    ctypes.POINTER(PlanOutputs), P, SZ, P]
+                L.mep_route_layout_plan.restype = I
                 L.mep_plan_balanced.argtypes = [P, P, P, P, I64, I, I, I, I, I, I64, I64,
                                                 ctypes.POINTER(BalancedOutputs), P]
                 L.mep_plan_balanced.restype = I
@@ -349,6 +353,43 @@ def _layout_plan_args(topk_ids, E, alignment, layout, R, num_src, num_channels, 
             _ptr(layout.expanded_to_permuted), _ptr(layout.permuted_to_expanded), cap,
             _ptr(layout.zero_fill), R, num_src, num_channels, NvS, ctypes.byref(po), _ptr(ws),
             ws.numel() * ws.element_size(), _stream(stream))
+
+
+def _route_layout_plan_args(logits, K, bias, params, topk_ids, topk_weights, alignment, layout, R,
+                            num_src, num_channels, NvS, po, ws, stream):
+    _require_cuda(logits, bias, topk_ids, topk_weights, ws)
+    if logits.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("logits must be float32 or bfloat16")
+    dtype = MEP_BF16 if logits.dtype == torch.bfloat16 else MEP_F32
+    N, E = logits.shape
+    cap = layout.permuted_to_expanded.numel() if layout.permuted_to_expanded is not None else 0
+    return (_ptr(logits), dtype, N, E, K, _ptr(bias), ctypes.byref(params), _ptr(topk_ids),
+            _ptr(topk_weights), alignment, _ptr(layout.tokens_per_expert), _ptr(layout.cu_seqlens),
+            _ptr(layout.expanded_to_permuted), _ptr(layout.permuted_to_expanded), cap,
+            _ptr(layout.zero_fill), R, num_src, num_channels, NvS, ctypes.byref(po), _ptr(ws),
+            ws.numel() * ws.element_size(), _stream(stream))
+
+
+def mep_route_layout_plan(logits, K, bias, params, topk_ids, topk_weights, alignment,
+                          layout: "LayoutTensors", R, num_src, num_channels, NvS,
+                          outputs: "PlanTensors", ws, stream=None):
+    """Routing, layout and plan in one call (one kernel for small batches)."""
+    po = outputs.as_struct()
+    rc = lib().mep_route_layout_plan(*_route_layout_plan_args(
+        logits, K, bias, params, topk_ids, topk_weights, alignment, layout, R, num_src,
+        num_channels, NvS, po, ws, stream))
+    _check(rc, "mep_route_layout_plan")
+
+
+def bound_route_layout_plan(logits, K, bias, params, topk_ids, topk_weights, alignment,
+                            layout: "LayoutTensors", R, num_src, num_channels, NvS,
+                            outputs: "PlanTensors", ws, stream=None):
+    po = outputs.as_struct()
+    call = _bound("mep_route_layout_plan", _route_layout_plan_args(
+        logits, K, bias, params, topk_ids, topk_weights, alignment, layout, R, num_src,
+        num_channels, NvS, po, ws, stream), "mep_route_layout_plan")
+    call.keep = po
+    return call
 
 
 def mep_layout_plan(topk_ids, E, alignment, layout: "LayoutTensors", R, num_src, num_channels, NvS,

@@ -14,49 +14,12 @@ namespace mep {
 
 template <int LPT, int NV, bool BF16, int KMAX>
 __global__ __launch_bounds__(kRouteBlock) void route_generic_kernel(RouteArgs a) {
-    constexpr int W = BF16 ? 8 : 4;
-    constexpr int NE = NV * W;
     constexpr int KPL = (KMAX + LPT - 1) / LPT;
     constexpr int TPB = kRouteBlock / LPT;
-
     const int lseg = threadIdx.x % LPT;
     const int64_t tok_raw = (int64_t)blockIdx.x * TPB + threadIdx.x / LPT;
-    const bool live = tok_raw < a.N;
-    const int64_t tok = live ? tok_raw : (a.N - 1);
-
-    float x[NE];
-    load_row<LPT, NV, BF16>(a, tok, lseg, x);
     int my_e[KPL];
-#pragma unroll
-    for (int m = 0; m < KPL; ++m) my_e[m] = 0;
-    float first_x;
-    exact_select_token<LPT, NV, BF16, KMAX>(a, a.bias, lseg, x, my_e, first_x);
-
-    const bool sig = a.score_fn == MEP_SIGMOID;
-    float my_v[KPL];
-#pragma unroll
-    for (int m = 0; m < KPL; ++m) {
-        const int j = m * LPT + lseg;
-        float v = 0.0f;
-        if (j < a.K) {
-            const float xe = load_logit(a, tok, my_e[m], BF16);
-            v = sig ? sigmoid_cr(xe) : xe;
-        }
-        my_v[m] = v;
-    }
-    double full_max = 0.0, full_den = 0.0;
-    if (!sig && !a.renormalize) {
-        float fm = -FLT_MAX;
-#pragma unroll
-        for (int q = 0; q < NE; ++q)
-            if (chunk_expert(q, W, LPT, lseg) < a.E) fm = fmaxf(fm, x[q]);
-        full_max = (double)order_key_inv(seg_max_u32<LPT>(order_key(fm)));
-#pragma unroll
-        for (int q = 0; q < NE; ++q)
-            if (chunk_expert(q, W, LPT, lseg) < a.E) full_den += exp_neg_f64((double)x[q] - full_max);
-        full_den = seg_sum_f64<LPT>(full_den);
-    }
-    write_weights<LPT, KPL>(a, tok, lseg, live, my_e, my_v, (double)first_x, full_max, full_den);
+    route_generic_token<LPT, NV, BF16, KMAX>(a, tok_raw, lseg, my_e);
 }
 
 template <int LPT, int NV, bool BF16>
@@ -92,9 +55,8 @@ static int dispatch_generic(const RouteArgs& a, const Launch& st) {
 
 namespace mep {
 
-static int route_topk(const void* logits, int dtype, int64_t N, int E, int K, const float* bias,
-                      const mep_route_params* p, int32_t* topk_ids, float* topk_weights,
-                      const Launch& st) {
+int route_prepare(const void* logits, int dtype, int64_t N, int E, int K, const float* bias,
+                  const mep_route_params* p, int32_t* topk_ids, float* topk_weights, RouteArgs& a) {
     if (!p) return MEP_ERR_INVALID_ARG;
     if (N > 0 && (!logits || !topk_ids)) return MEP_ERR_INVALID_ARG;  // N == 0 reads nothing
     if (dtype != MEP_F32 && dtype != MEP_BF16) return MEP_ERR_INVALID_ARG;
@@ -114,9 +76,9 @@ static int route_topk(const void* logits, int dtype, int64_t N, int E, int K, co
         if (p->group_topn < 1 || p->group_topn > 2 || p->group_topn > gsize) return MEP_ERR_UNSUPPORTED;
         if ((int64_t)p->topk_group * gsize < K) return MEP_ERR_UNSUPPORTED;
     }
+    a.N = 0;
     if (N == 0) return MEP_OK;
 
-    RouteArgs a;
     a.logits = logits;
     a.bias = bias;
     a.N = N;
@@ -133,6 +95,15 @@ static int route_topk(const void* logits, int dtype, int64_t N, int E, int K, co
     a.weights = topk_weights;
     const int W = dtype == MEP_BF16 ? 8 : 4;
     a.vec = (E % W) == 0;
+    return MEP_OK;
+}
+
+static int route_topk(const void* logits, int dtype, int64_t N, int E, int K, const float* bias,
+                      const mep_route_params* p, int32_t* topk_ids, float* topk_weights,
+                      const Launch& st) {
+    RouteArgs a;
+    const int rc = route_prepare(logits, dtype, N, E, K, bias, p, topk_ids, topk_weights, a);
+    if (rc != MEP_OK || a.N == 0) return rc;
     if (launch_route_sig(a, dtype, st)) return launch_status();
     if (launch_route_fast(a, dtype, st)) return launch_status();
     return dtype == MEP_BF16 ? dispatch_generic<true>(a, st) : dispatch_generic<false>(a, st);

@@ -310,6 +310,58 @@ __device__ __forceinline__ void write_weights(const RouteArgs& a, int64_t tok, i
 }
 
 // Fast-kernel launcher (route_fast.hip).  Returns false when the shape is not covered.
+// One token on LPT lanes, exactly: keys for every expert, K rounds of a segmented arg-max, and the
+// weights (the generic routing kernel's whole body; also the routing phase of the one-workgroup
+// small-batch kernel).  Token `tok_raw` past the batch computes on the last token and writes
+// nothing.  On return, lane lseg holds the experts of output slots k = m*LPT + lseg in my_e[m].
+template <int LPT, int NV, bool BF16, int KMAX>
+__device__ __forceinline__ void route_generic_token(const RouteArgs& a, int64_t tok_raw, int lseg,
+                                                    int (&my_e)[(KMAX + LPT - 1) / LPT]) {
+    constexpr int W = BF16 ? 8 : 4;
+    constexpr int NE = NV * W;
+    constexpr int KPL = (KMAX + LPT - 1) / LPT;
+    const bool live = tok_raw < a.N;
+    const int64_t tok = live ? tok_raw : (a.N - 1);
+
+    float x[NE];
+    load_row<LPT, NV, BF16>(a, tok, lseg, x);
+#pragma unroll
+    for (int m = 0; m < KPL; ++m) my_e[m] = 0;
+    float first_x;
+    exact_select_token<LPT, NV, BF16, KMAX>(a, a.bias, lseg, x, my_e, first_x);
+
+    const bool sig = a.score_fn == MEP_SIGMOID;
+    float my_v[KPL];
+#pragma unroll
+    for (int m = 0; m < KPL; ++m) {
+        const int j = m * LPT + lseg;
+        float v = 0.0f;
+        if (j < a.K) {
+            const float xe = load_logit(a, tok, my_e[m], BF16);
+            v = sig ? sigmoid_cr(xe) : xe;
+        }
+        my_v[m] = v;
+    }
+    double full_max = 0.0, full_den = 0.0;
+    if (!sig && !a.renormalize) {
+        float fm = -FLT_MAX;
+#pragma unroll
+        for (int q = 0; q < NE; ++q)
+            if (chunk_expert(q, W, LPT, lseg) < a.E) fm = fmaxf(fm, x[q]);
+        full_max = (double)order_key_inv(seg_max_u32<LPT>(order_key(fm)));
+#pragma unroll
+        for (int q = 0; q < NE; ++q)
+            if (chunk_expert(q, W, LPT, lseg) < a.E) full_den += exp_neg_f64((double)x[q] - full_max);
+        full_den = seg_sum_f64<LPT>(full_den);
+    }
+    write_weights<LPT, KPL>(a, tok, lseg, live, my_e, my_v, (double)first_x, full_max, full_den);
+}
+
+// Checks of mep_route_topk's arguments; on MEP_OK `a` holds the launch arguments (a.N == 0: nothing
+// to launch).
+int route_prepare(const void* logits, int dtype, int64_t N, int E, int K, const float* bias,
+                  const mep_route_params* p, int32_t* topk_ids, float* topk_weights, RouteArgs& a);
+
 bool launch_route_fast(const RouteArgs& a, int dtype, const Launch& st);
 
 // Sigmoid routing kernel launcher (route_sig.hip).  Returns false when the shape is not covered.

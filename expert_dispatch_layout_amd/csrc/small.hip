@@ -1,0 +1,371 @@
+// mep_route_layout_plan: routing, layout and plan of one batch in one call.  Small batches
+// (decode sizes) run as one kernel of one workgroup, in the spirit of TensorRT-LLM
+// RoutingKernel.cuh's routingPermutation (the whole routing permutation of a small batch inside
+// one cluster, without a second launch); larger batches take the three kernels of
+// mep_route_topk followed by mep_layout_plan.  Results are identical either way.
+//
+// The one-workgroup kernel (1024 threads) keeps every slot's expert and permuted position in
+// LDS and walks the phases with barriers in between:
+//   route    tokens on LPT lanes each, 1024 / LPT at a time, with the generic routing code
+//            (exact keys, K rounds of a segmented arg-max, binary64 weights); the experts also
+//            go to LDS
+//   layout   histogram by LDS atomics, padded exclusive scan, then the slots in order, 1024 at
+//            a time: a slot's rank among its wave's slots of the same expert from one ballot per
+//            id bit, per-(wave, expert) counts prefixed across the waves, plus the running
+//            count of the earlier chunks -- the stable order
+//   plan     per token: membership mask, per-shard counts and channel counts by LDS atomics,
+//            dst with the duplicate encoding; then the prefix matrices, the receive layout, and
+//            per rank two token-order scans (totals, then positions) for the dedup lists
+// Nothing crosses workgroups, so the kernel needs no workspace and has no look-back.
+#include <float.h>
+#include <limits.h>
+
+#include "calls.h"
+#include "host_common.h"
+#include "route_common.h"
+
+namespace mep {
+
+namespace {
+
+constexpr int kSmBlock = 1024;
+constexpr int kSmWaves = kSmBlock / 64;
+constexpr int kSmMaxSlots = 8192;
+constexpr int kSmMaxE = 256;
+constexpr int kSmMaxR = 8;
+constexpr int kSmMaxShardE = 4096;   // num_src * E
+constexpr int kSmMaxChan = 4096;     // num_src * R * num_channels
+constexpr int kSmKMax = 8;
+
+struct SmallArgs {
+    RouteArgs ra;
+    int A;
+    LayoutOut lo;
+    PlanGeom g;
+    PlanOutDev po;
+};
+
+template <int LPT, int NV, bool BF16>
+__global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
+    __shared__ int s_ids[kSmMaxSlots];
+    __shared__ int s_P[kSmMaxSlots];
+    __shared__ int s_cnt[kSmMaxE];
+    __shared__ int s_cu[kSmMaxE + 1];
+    __shared__ int s_run[kSmMaxE];
+    __shared__ int s_chunk[kSmMaxE];
+    __shared__ int s_wc[kSmWaves][kSmMaxE];
+    __shared__ int s_ntpe[kSmMaxShardE];
+    __shared__ int s_ntpr[kSmMaxShardE];
+    __shared__ int s_chan[kSmMaxChan];
+    __shared__ int s_tmp[kSmWaves];
+    __shared__ int s_dtot[2 * kSmMaxR];
+
+    const RouteArgs& a = sa.ra;
+    const PlanGeom& g = sa.g;
+    const int tid = threadIdx.x;
+    const int wv = tid >> 6;
+    const int N = (int)a.N, E = a.E, K = a.K, NK = N * K;
+    const int R = g.R, epn = g.epn, S = g.S, C = g.C, n = g.n;
+
+    // ---- route -----------------------------------------------------------------------------------
+    {
+        constexpr int KPL = (kSmKMax + LPT - 1) / LPT;
+        constexpr int TPI = kSmBlock / LPT;
+        const int lseg = tid % LPT;
+        for (int base = 0; base < N; base += TPI) {
+            const int tok = base + tid / LPT;
+            int my_e[KPL];
+            route_generic_token<LPT, NV, BF16, kSmKMax>(a, tok, lseg, my_e);
+            if (tok < N) {
+#pragma unroll
+                for (int m = 0; m < KPL; ++m) {
+                    const int j = m * LPT + lseg;
+                    if (j < K) s_ids[tok * K + j] = my_e[m];
+                }
+            }
+        }
+    }
+    for (int e = tid; e < E; e += kSmBlock) {
+        s_cnt[e] = 0;
+        s_run[e] = 0;
+    }
+    for (int i = tid; i < S * E; i += kSmBlock) s_ntpe[i] = 0;
+    for (int i = tid; i < S * R; i += kSmBlock) s_ntpr[i] = 0;
+    for (int i = tid; i < S * R * C; i += kSmBlock) s_chan[i] = 0;
+    __syncthreads();
+
+    // ---- layout: histogram, padded scan ----------------------------------------------------------
+    for (int i = tid; i < NK; i += kSmBlock) atomicAdd(&s_cnt[s_ids[i]], 1);
+    __syncthreads();
+    {
+        const int c = tid < E ? s_cnt[tid] : 0;
+        const int padded = c > 0 ? (c + sa.A - 1) / sa.A * sa.A : 0;
+        int total;
+        const int excl = block_exclusive_scan<kSmBlock>(padded, s_tmp, total);
+        if (tid < E) {
+            s_cu[tid] = excl;
+            if (sa.lo.tokens_per_expert) sa.lo.tokens_per_expert[tid] = c;
+            sa.lo.cu_seqlens[tid] = excl;
+            if (sa.lo.zero_fill) {
+                const bool zf = c > 0 && padded > c;
+                sa.lo.zero_fill[2 * tid] = zf ? excl + c : 0;
+                sa.lo.zero_fill[2 * tid + 1] = zf ? padded - c : 0;
+            }
+        }
+        if (tid == 0) {
+            s_cu[E] = total;
+            sa.lo.cu_seqlens[E] = total;
+        }
+    }
+    __syncthreads();
+
+    // ---- layout: stable positions, 1024 slots at a time ------------------------------------------
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    for (int c0 = 0; c0 < NK; c0 += kSmBlock) {
+        for (int i = tid; i < kSmWaves * E; i += kSmBlock) s_wc[i / E][i % E] = 0;
+        __syncthreads();
+        const int i = c0 + tid;
+        const bool valid = i < NK;
+        const int e = valid ? s_ids[i] : 0;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const uint64_t ones = __ballot(valid && ((e >> b) & 1));
+            peers &= ((e >> b) & 1) ? ones : ~ones;
+        }
+        const int rank = __popcll(peers & lanes_below());
+        if (valid && rank == 0) s_wc[wv][e] = __popcll(peers);
+        __syncthreads();
+        if (tid < E) {
+            int run = 0;
+            for (int w = 0; w < kSmWaves; ++w) {
+                const int t = s_wc[w][tid];
+                s_wc[w][tid] = run;
+                run += t;
+            }
+            s_chunk[tid] = run;
+        }
+        __syncthreads();
+        if (valid) {
+            const int P = s_cu[e] + s_run[e] + s_wc[wv][e] + rank;
+            s_P[i] = P;
+            sa.lo.e2p[i] = P;
+            if (sa.lo.p2e) sa.lo.p2e[P] = i;
+        }
+        __syncthreads();
+        if (tid < E) s_run[tid] += s_chunk[tid];  // the earlier chunks' slots of each expert
+        __syncthreads();
+    }
+    if (sa.lo.p2e) {
+        for (int e = 0; e < E; ++e) {
+            const int start = s_cu[e] + s_cnt[e], end = s_cu[e + 1];
+            for (int p = start + tid; p < end; p += kSmBlock) sa.lo.p2e[p] = -1;
+        }
+    }
+
+    // ---- plan: per token ---------------------------------------------------------------------------
+    const int q = (n + C - 1) / C;
+    for (int t = tid; t < N; t += kSmBlock) {
+        const int s = t / n;
+        const int ch = (t - s * n) / q;
+        uint32_t mask = 0;
+        for (int k = 0; k < K; ++k) {
+            const int e = s_ids[t * K + k];
+            const int r = e / epn;
+            atomicAdd(&s_ntpe[s * E + e], 1);
+            const int raw = (int)((int64_t)r * g.NvS + (s_P[t * K + k] - s_cu[r * epn]));
+            const bool dup = (mask >> r) & 1u;
+            if (sa.po.dst) sa.po.dst[t * K + k] = dup ? -raw - 1 : raw;
+            mask |= 1u << r;
+        }
+        for (int r = 0; r < R; ++r) {
+            const bool in = (mask >> r) & 1u;
+            if (sa.po.itr) sa.po.itr[(int64_t)t * R + r] = in ? 1 : 0;
+            if (in) {
+                atomicAdd(&s_ntpr[s * R + r], 1);
+                atomicAdd(&s_chan[(s * R + r) * C + ch], 1);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- plan: matrices and receive layout -----------------------------------------------------------
+    for (int i = tid; i < S * E; i += kSmBlock)
+        if (sa.po.ntpe) sa.po.ntpe[i] = s_ntpe[i];
+    for (int r = tid; r < R; r += kSmBlock) {
+        int run = 0;
+        for (int s = 0; s < S; ++s) {
+            const int v = s_ntpr[s * R + r];
+            run += v;
+            if (sa.po.ntpr) sa.po.ntpr[s * R + r] = v;
+            if (sa.po.rank_prefix) sa.po.rank_prefix[s * R + r] = run;
+        }
+        if (sa.po.recv_tokens) sa.po.recv_tokens[r] = run;
+    }
+    if (sa.po.chan) {
+        for (int sr = tid; sr < S * R; sr += kSmBlock) {
+            int run = 0;
+            for (int c = 0; c < C; ++c) {
+                run += s_chan[sr * C + c];
+                sa.po.chan[sr * C + c] = run;
+            }
+        }
+    }
+    if (sa.po.recv_cu) {
+        for (int i = tid; i < R * (epn + 1); i += kSmBlock) {
+            const int r = i / (epn + 1), j = i - r * (epn + 1);
+            sa.po.recv_cu[i] = s_cu[r * epn + j] - s_cu[r * epn];
+        }
+    }
+    if (sa.po.recv_zf) {
+        for (int e = tid; e < E; e += kSmBlock) {
+            const int c = s_cnt[e], padded = s_cu[e + 1] - s_cu[e], r = e / epn;
+            const bool zf = c > 0 && padded > c;
+            sa.po.recv_zf[2 * e] = zf ? s_cu[e] + c - s_cu[r * epn] : 0;
+            sa.po.recv_zf[2 * e + 1] = zf ? padded - c : 0;
+        }
+    }
+
+    // ---- plan: dedup lists, rank by rank in token order -----------------------------------------------
+    // pass 0 counts groups and duplicates per rank, pass 1 writes them at their offsets
+    for (int pass = 0; pass < 2; ++pass) {
+        int goff = 0, doff = 0;
+        if (pass == 1)
+            for (int r = 0; r < R; ++r) {
+                if (tid == 0) {
+                    if (sa.po.dup_counts) {
+                        sa.po.dup_counts[2 * r] = s_dtot[2 * r];
+                        sa.po.dup_counts[2 * r + 1] = s_dtot[2 * r + 1];
+                    }
+                    if (sa.po.dup_offsets) {
+                        sa.po.dup_offsets[2 * r] = goff;
+                        sa.po.dup_offsets[2 * r + 1] = doff;
+                    }
+                }
+                goff += s_dtot[2 * r];
+                doff += s_dtot[2 * r + 1];
+            }
+        if (pass == 1 && tid == 0 && sa.po.dup_offsets) {
+            sa.po.dup_offsets[2 * R] = goff;
+            sa.po.dup_offsets[2 * R + 1] = doff;
+        }
+        goff = 0;
+        doff = 0;
+        for (int r = 0; r < R; ++r) {
+            int gcarry = 0, dcarry = 0;
+            for (int t0 = 0; t0 < N; t0 += kSmBlock) {
+                const int t = t0 + tid;
+                int hits = 0;
+                if (t < N && epn > 1)
+                    for (int k = 0; k < K; ++k) hits += s_ids[t * K + k] / epn == r;
+                const int gflag = hits >= 2 ? 1 : 0;
+                const int dcnt = hits >= 2 ? hits - 1 : 0;
+                int tot;
+                const int ex = block_exclusive_scan<kSmBlock>((gflag << 16) | dcnt, s_tmp, tot);
+                const int gi = gcarry + (ex >> 16), di = dcarry + (ex & 0xFFFF);
+                if (pass == 1 && gflag) {
+                    int first = -1, j = 0;
+                    for (int k = 0; k < K; ++k) {
+                        const int e = s_ids[t * K + k];
+                        if (e / epn != r) continue;
+                        const int loff = s_P[t * K + k] - s_cu[r * epn];
+                        if (first < 0) {
+                            first = loff;
+                        } else {
+                            if (sa.po.dup_loffs) sa.po.dup_loffs[doff + di + j] = loff;
+                            ++j;
+                        }
+                    }
+                    if (sa.po.dup_groups) {
+                        int32_t* grp = sa.po.dup_groups + 3 * (int64_t)(goff + gi);
+                        grp[0] = first;
+                        grp[1] = di;
+                        grp[2] = dcnt;
+                    }
+                }
+                gcarry += tot >> 16;
+                dcarry += tot & 0xFFFF;
+            }
+            if (pass == 0 && tid == 0) {
+                s_dtot[2 * r] = gcarry;
+                s_dtot[2 * r + 1] = dcarry;
+            }
+            goff += gcarry;
+            doff += dcarry;
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+}  // namespace mep
+
+namespace mep {
+
+namespace {
+
+template <int LPT, int NV, bool BF16>
+void launch_small(const SmallArgs& sa, hipStream_t st) {
+    hipLaunchKernelGGL((small_path_kernel<LPT, NV, BF16>), dim3(1), dim3(kSmBlock), 0, st, sa);
+}
+
+template <bool BF16>
+bool dispatch_small(const SmallArgs& sa, hipStream_t st) {
+    constexpr int W = BF16 ? 8 : 4;
+    const int nchunks = (sa.ra.E + W - 1) / W;
+    if (nchunks <= 1) launch_small<1, 1, BF16>(sa, st);
+    else if (nchunks <= 2) launch_small<2, 1, BF16>(sa, st);
+    else if (nchunks <= 4) launch_small<4, 1, BF16>(sa, st);
+    else if (nchunks <= 8) launch_small<8, 1, BF16>(sa, st);
+    else if (nchunks <= 16) launch_small<16, 1, BF16>(sa, st);
+    else if (nchunks <= 32) launch_small<32, 1, BF16>(sa, st);
+    else if (nchunks <= 64) launch_small<64, 1, BF16>(sa, st);
+    else return false;
+    return true;
+}
+
+}  // namespace
+
+}  // namespace mep
+
+extern "C" int mep_route_layout_plan(const void* logits, int dtype, int64_t N, int E, int K, const float* bias,
+                                     const mep_route_params* p, int32_t* topk_ids, float* topk_weights,
+                                     int alignment, int32_t* tokens_per_expert, int32_t* cu_seqlens,
+                                     int32_t* expanded_to_permuted, int32_t* permuted_to_expanded,
+                                     int64_t permuted_cap, int32_t* zero_fill, int R, int num_src,
+                                     int num_channels, int64_t NvS, const mep_plan_outputs* out, void* ws,
+                                     size_t ws_bytes, void* stream) {
+    using namespace mep;
+    if (N > 0 && !topk_ids) return MEP_ERR_INVALID_ARG;
+    SmallArgs sa;
+    int rc = route_prepare(logits, dtype, N, E, K, bias, p, topk_ids, topk_weights, sa.ra);
+    if (rc != MEP_OK) return rc;
+    PlanCall pc;
+    rc = plan_prepare(topk_ids, cu_seqlens, expanded_to_permuted, N, E, K, alignment, R, num_src, num_channels,
+                      NvS, out, ws, ws_bytes, pc);
+    if (rc != MEP_OK) return rc;
+    LayoutCall lc;
+    rc = layout_prepare_outputs(topk_ids, N, E, K, alignment, tokens_per_expert, cu_seqlens, expanded_to_permuted,
+                                permuted_to_expanded, permuted_cap, zero_fill, lc);
+    if (rc != MEP_OK) return rc;
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const int64_t NK = N * (int64_t)K;
+    const bool small = N > 0 && NK <= kSmMaxSlots && E <= kSmMaxE && K <= kSmKMax && R <= kSmMaxR &&
+                       (int64_t)num_src * E <= kSmMaxShardE &&
+                       (int64_t)num_src * R * num_channels <= kSmMaxChan;
+    if (small) {
+        sa.A = alignment;
+        sa.lo = lc.out;
+        sa.g = pc.g;
+        sa.po = pc.o;
+        const bool ok = dtype == MEP_BF16 ? dispatch_small<true>(sa, st) : dispatch_small<false>(sa, st);
+        if (ok) return launch_status();
+    }
+    // larger batches: the routing kernel, then the layout and plan kernels
+    rc = mep_route_topk(logits, dtype, N, E, K, bias, p, topk_ids, topk_weights, stream);
+    if (rc != MEP_OK) return rc;
+    return mep_layout_plan(topk_ids, N, E, K, alignment, tokens_per_expert, cu_seqlens, expanded_to_permuted,
+                           permuted_to_expanded, permuted_cap, zero_fill, R, num_src, num_channels, NvS, out, ws,
+                           ws_bytes, stream);
+}

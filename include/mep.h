@@ -13,6 +13,8 @@
  *                    destinations with duplicate encoding, dedup lists)
  *   mep_layout_plan  the two calls above in one (two kernels instead of
  *                    four)
+ *   mep_route_layout_plan
+ *                    all three in one call; one kernel for small batches
  *   mep_tile_map     per-expert counts -> grouped-GEMM tile maps (the expert
  *                    and the row limit of every padded tile)
  *   mep_plan_balanced the plan with capacity rebalancing: token moves between
@@ -428,6 +430,29 @@ int mep_permute_rows(const void* x, int dtype, int64_t N, int64_t H, int K,
 int mep_combine_rows(const void* y_permuted, int dtype, int64_t N, int64_t H, int K,
                      const int32_t* expanded_to_permuted, const float* topk_weights,
                      int64_t permuted_rows, void* out, void* stream);
+
+/*
+ * mep_route_layout_plan -- mep_route_topk, then mep_layout_plan, in one call,
+ * with the arguments, checks and results of the two (topk_ids is the
+ * routing's output and the layout's input, so it is required).
+ *
+ * Small batches run as a single kernel of one workgroup ([TRT]
+ * routingPermutation: a small batch's whole routing permutation without a
+ * second launch): N*K <= 8192, E <= 256, K <= 8, R <= 8,
+ * num_src*E <= 4096 and num_src*R*num_channels <= 4096.  That kernel routes
+ * every token exactly (no fast-path certification to fail), keeps ids and
+ * permuted positions in LDS, and uses no workspace.  Other batches take the
+ * three kernels of the two calls.  Either way the outputs equal those of
+ * mep_route_topk followed by mep_layout_plan; `ws` must satisfy
+ * mep_layout_plan's rules in both cases.
+ */
+int mep_route_layout_plan(const void* logits, int dtype, int64_t N, int E, int K,
+                          const float* bias, const mep_route_params* p, int32_t* topk_ids,
+                          float* topk_weights, int alignment, int32_t* tokens_per_expert,
+                          int32_t* cu_seqlens, int32_t* expanded_to_permuted,
+                          int32_t* permuted_to_expanded, int64_t permuted_cap, int32_t* zero_fill,
+                          int R, int num_src, int num_channels, int64_t NvS,
+                          const mep_plan_outputs* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Static, NUL-terminated name of a return code. */
 const char* mep_status_string(int code);

@@ -265,6 +265,53 @@ def balanced_leg(B, torch, ids, L, wl, steps: int, stream):
             "algorithmic_bytes": nbytes, "GB_per_s": nbytes / (us * 1e-6) / 1e9}
 
 
+def small_batch_leg(B, torch, synth, steps: int, stream):
+    """Decode-size batches (the tiny and small workloads): mep_route_layout_plan (one kernel)
+    against mep_route_topk followed by mep_layout_plan (three kernels), each timed over `steps`
+    back-to-back calls between two events."""
+    import numpy as np
+
+    res = {}
+    for name in ("tiny", "small"):
+        wl = synth.WORKLOADS[name]
+        inp = synth.make_inputs(wl)
+        N, E, K, A, R, S, C = wl.N, wl.E, wl.K, wl.alignment, wl.R, wl.S, wl.num_channels
+        dev = torch.device("cuda:0")
+        x = torch.from_numpy(inp.logits.view(np.int16) if wl.dtype == synth.BF16 else inp.logits).to(dev)
+        if wl.dtype == synth.BF16:
+            x = x.view(torch.bfloat16)
+        bias = torch.from_numpy(inp.bias).to(dev) if inp.bias is not None else None
+        params = B.route_params(wl.score_fn, wl.renormalize, wl.n_group, wl.topk_group,
+                                wl.group_topn, wl.scale)
+        ids = torch.empty((N, K), dtype=torch.int32, device=dev)
+        w = torch.empty((N, K), dtype=torch.float32, device=dev)
+        L = B.alloc_layout(N, E, K, A, dev)
+        P = B.alloc_plan(N, E, K, R, S, C, dev)
+        ws = B.alloc_workspace(B.plan_workspace_size(N, E, K, R, S), dev)
+        nvs = B.default_nvs(N, E, K, R, A)
+        one = B.bound_route_layout_plan(x, K, bias, params, ids, w, A, L, R, S, C, nvs, P, ws, stream)
+        r1 = B.bound_route_topk(x, K, bias, params, ids, w, stream)
+        r2 = B.bound_layout_plan(ids, E, A, L, R, S, C, nvs, P, ws, stream)
+        out = {}
+        for label, fns in (("one_call_us", (one,)), ("three_kernels_us", (r1, r2))):
+            for _ in range(5):
+                for f in fns:
+                    f()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0.record(stream)
+            for _ in range(steps):
+                for f in fns:
+                    f()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            out[label] = t0.elapsed_time(t1) * 1e3 / steps
+        out["tokens"] = N
+        res[name] = out
+    return res
+
+
 def main():
     args = parse()
     if args.record_traffic:
@@ -387,7 +434,8 @@ def main():
     ids_last, w_last = sets[(args.warmup + args.steps - 1) % nsets][1:3]
     out["next_rows"] = {"tile_map": tile_map_leg(B, torch, L, wl, args.steps, stream),
                         "balanced_plan": balanced_leg(B, torch, ids_last, L, wl, args.steps, stream),
-                        "rows": rows_leg(B, torch, L, w_last, wl, min(args.steps, 20), stream)}
+                        "rows": rows_leg(B, torch, L, w_last, wl, min(args.steps, 20), stream),
+                        "small_batch": small_batch_leg(B, torch, synth, 200, stream)}
     if args.copy_calibration > 0:
         nbytes = args.copy_calibration << 20
         src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)

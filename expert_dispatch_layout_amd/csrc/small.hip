@@ -4,12 +4,12 @@
 // one cluster, without a second launch); larger batches take the three kernels of
 // mep_route_topk followed by mep_layout_plan.  Results are identical either way.
 //
-// The one-workgroup kernel (1024 threads) keeps every slot's expert and permuted position in
+// The one-workgroup kernel (512 threads) keeps every slot's expert and permuted position in
 // LDS and walks the phases with barriers in between:
-//   route    tokens on LPT lanes each, 1024 / LPT at a time, with the generic routing code
+//   route    tokens on LPT lanes each, 512 / LPT at a time, with the generic routing code
 //            (exact keys, K rounds of a segmented arg-max, binary64 weights); the experts also
 //            go to LDS
-//   layout   histogram by LDS atomics, padded exclusive scan, then the slots in order, 1024 at
+//   layout   histogram by LDS atomics, padded exclusive scan, then the slots in order, 512 at
 //            a time: a slot's rank among its wave's slots of the same expert from one ballot per
 //            id bit, per-(wave, expert) counts prefixed across the waves, plus the running
 //            count of the earlier chunks -- the stable order
@@ -28,9 +28,9 @@ namespace mep {
 
 namespace {
 
-constexpr int kSmBlock = 1024;
+constexpr int kSmBlock = 512;
 constexpr int kSmWaves = kSmBlock / 64;
-constexpr int kSmMaxSlots = 8192;
+constexpr int kSmMaxSlots = 2048;  // above this the three-kernel path is faster
 constexpr int kSmMaxE = 256;
 constexpr int kSmMaxR = 8;
 constexpr int kSmMaxShardE = 4096;   // num_src * E
@@ -59,6 +59,9 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
     __shared__ int s_chan[kSmMaxChan];
     __shared__ int s_tmp[kSmWaves];
     __shared__ int s_dtot[2 * kSmMaxR];
+    __shared__ int s_wsum[kSmWaves][kSmMaxR];
+    __shared__ int s_goff[kSmMaxR];
+    __shared__ int s_doff[kSmMaxR];
 
     const RouteArgs& a = sa.ra;
     const PlanGeom& g = sa.g;
@@ -119,7 +122,7 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
     }
     __syncthreads();
 
-    // ---- layout: stable positions, 1024 slots at a time ------------------------------------------
+    // ---- layout: stable positions, 512 slots at a time ------------------------------------------
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     for (int c0 = 0; c0 < NK; c0 += kSmBlock) {
@@ -226,72 +229,118 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
         }
     }
 
-    // ---- plan: dedup lists, rank by rank in token order -----------------------------------------------
-    // pass 0 counts groups and duplicates per rank, pass 1 writes them at their offsets
-    for (int pass = 0; pass < 2; ++pass) {
-        int goff = 0, doff = 0;
-        if (pass == 1)
-            for (int r = 0; r < R; ++r) {
-                if (tid == 0) {
-                    if (sa.po.dup_counts) {
-                        sa.po.dup_counts[2 * r] = s_dtot[2 * r];
-                        sa.po.dup_counts[2 * r + 1] = s_dtot[2 * r + 1];
-                    }
-                    if (sa.po.dup_offsets) {
-                        sa.po.dup_offsets[2 * r] = goff;
-                        sa.po.dup_offsets[2 * r + 1] = doff;
-                    }
-                }
-                goff += s_dtot[2 * r];
-                doff += s_dtot[2 * r + 1];
-            }
-        if (pass == 1 && tid == 0 && sa.po.dup_offsets) {
-            sa.po.dup_offsets[2 * R] = goff;
-            sa.po.dup_offsets[2 * R + 1] = doff;
+    // ---- plan: dedup lists in token order, all ranks at once ----------------------------------------
+    // Per rank r and token t: a group when t has >= 2 slots on r, with hits - 1 duplicates.  The
+    // totals come from LDS counters; the positions from wave scans of every rank's (group,
+    // duplicates) pair, packed 16:16 (at most 2048 of each in a batch), combined across the waves
+    // after one barrier per 512 tokens.
+    if (epn == 1) {
+        // distinct experts on distinct ranks: no token has two slots on one rank
+        for (int i = tid; i < 2 * R; i += kSmBlock)
+            if (sa.po.dup_counts) sa.po.dup_counts[i] = 0;
+        for (int i = tid; i < 2 * (R + 1); i += kSmBlock)
+            if (sa.po.dup_offsets) sa.po.dup_offsets[i] = 0;
+        return;
+    }
+    for (int i = tid; i < 2 * R; i += kSmBlock) s_dtot[i] = 0;
+    __syncthreads();
+    for (int t = tid; t < N; t += kSmBlock) {
+        int hits[kSmMaxR];
+#pragma unroll
+        for (int r = 0; r < kSmMaxR; ++r) hits[r] = 0;
+        for (int k = 0; k < K; ++k) {
+            const int r = s_ids[t * K + k] / epn;
+#pragma unroll
+            for (int rr = 0; rr < kSmMaxR; ++rr) hits[rr] += rr == r;
         }
-        goff = 0;
-        doff = 0;
+#pragma unroll
+        for (int r = 0; r < kSmMaxR; ++r)
+            if (r < R && hits[r] >= 2) {
+                atomicAdd(&s_dtot[2 * r], 1);
+                atomicAdd(&s_dtot[2 * r + 1], hits[r] - 1);
+            }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int gacc = 0, dacc = 0;
         for (int r = 0; r < R; ++r) {
-            int gcarry = 0, dcarry = 0;
-            for (int t0 = 0; t0 < N; t0 += kSmBlock) {
-                const int t = t0 + tid;
-                int hits = 0;
-                if (t < N && epn > 1)
-                    for (int k = 0; k < K; ++k) hits += s_ids[t * K + k] / epn == r;
-                const int gflag = hits >= 2 ? 1 : 0;
-                const int dcnt = hits >= 2 ? hits - 1 : 0;
-                int tot;
-                const int ex = block_exclusive_scan<kSmBlock>((gflag << 16) | dcnt, s_tmp, tot);
-                const int gi = gcarry + (ex >> 16), di = dcarry + (ex & 0xFFFF);
-                if (pass == 1 && gflag) {
-                    int first = -1, j = 0;
-                    for (int k = 0; k < K; ++k) {
-                        const int e = s_ids[t * K + k];
-                        if (e / epn != r) continue;
-                        const int loff = s_P[t * K + k] - s_cu[r * epn];
-                        if (first < 0) {
-                            first = loff;
-                        } else {
-                            if (sa.po.dup_loffs) sa.po.dup_loffs[doff + di + j] = loff;
-                            ++j;
-                        }
-                    }
-                    if (sa.po.dup_groups) {
-                        int32_t* grp = sa.po.dup_groups + 3 * (int64_t)(goff + gi);
-                        grp[0] = first;
-                        grp[1] = di;
-                        grp[2] = dcnt;
+            s_goff[r] = gacc;
+            s_doff[r] = dacc;
+            if (sa.po.dup_counts) {
+                sa.po.dup_counts[2 * r] = s_dtot[2 * r];
+                sa.po.dup_counts[2 * r + 1] = s_dtot[2 * r + 1];
+            }
+            if (sa.po.dup_offsets) {
+                sa.po.dup_offsets[2 * r] = gacc;
+                sa.po.dup_offsets[2 * r + 1] = dacc;
+            }
+            gacc += s_dtot[2 * r];
+            dacc += s_dtot[2 * r + 1];
+        }
+        if (sa.po.dup_offsets) {
+            sa.po.dup_offsets[2 * R] = gacc;
+            sa.po.dup_offsets[2 * R + 1] = dacc;
+        }
+    }
+    __syncthreads();
+    const int lane = tid & 63;
+    int carry[kSmMaxR];
+#pragma unroll
+    for (int r = 0; r < kSmMaxR; ++r) carry[r] = 0;
+    auto hits_on = [&](int t, int r) {
+        int h = 0;
+        for (int k = 0; k < K; ++k) h += s_ids[t * K + k] / epn == r;
+        return h;
+    };
+    for (int t0 = 0; t0 < N; t0 += kSmBlock) {
+        const int t = t0 + tid;
+        int incl[kSmMaxR];
+#pragma unroll
+        for (int r = 0; r < kSmMaxR; ++r) {
+            const int h = (r < R && t < N) ? hits_on(t, r) : 0;
+            int x = h >= 2 ? (1 << 16) | (h - 1) : 0;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(x, o);
+                if (lane >= o) x += y;
+            }
+            incl[r] = x;
+            if (lane == 63) s_wsum[wv][r] = x;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kSmMaxR; ++r) {
+            int before = 0, tot = 0;
+            for (int w = 0; w < kSmWaves; ++w) {
+                const int x = s_wsum[w][r];
+                before += w < wv ? x : 0;
+                tot += x;
+            }
+            const int h = (r < R && t < N) ? hits_on(t, r) : 0;
+            if (h >= 2) {
+                const int ex = carry[r] + before + incl[r] - ((1 << 16) | (h - 1));
+                const int gi = ex >> 16, di = ex & 0xFFFF;
+                const int dbase = s_doff[r] + di;
+                int first = -1, j = 0;
+                for (int k = 0; k < K; ++k) {
+                    const int e = s_ids[t * K + k];
+                    if (e / epn != r) continue;
+                    const int loff = s_P[t * K + k] - s_cu[r * epn];
+                    if (first < 0) {
+                        first = loff;
+                    } else {
+                        if (sa.po.dup_loffs) sa.po.dup_loffs[dbase + j] = loff;
+                        ++j;
                     }
                 }
-                gcarry += tot >> 16;
-                dcarry += tot & 0xFFFF;
+                if (sa.po.dup_groups) {
+                    int32_t* grp = sa.po.dup_groups + 3 * (int64_t)(s_goff[r] + gi);
+                    grp[0] = first;
+                    grp[1] = di;
+                    grp[2] = h - 1;
+                }
             }
-            if (pass == 0 && tid == 0) {
-                s_dtot[2 * r] = gcarry;
-                s_dtot[2 * r + 1] = dcarry;
-            }
-            goff += gcarry;
-            doff += dcarry;
+            carry[r] += tot;
         }
         __syncthreads();
     }

@@ -438,7 +438,7 @@ int mep_combine_rows(const void* y_permuted, int dtype, int64_t N, int64_t H, in
  *
  * Small batches run as a single kernel of one workgroup ([TRT]
  * routingPermutation: a small batch's whole routing permutation without a
- * second launch): N*K <= 8192, E <= 256, K <= 8, R <= 8,
+ * second launch): N*K <= 2048, E <= 256, K <= 8, R <= 8,
  * num_src*E <= 4096 and num_src*R*num_channels <= 4096.  That kernel routes
  * every token exactly (no fast-path certification to fail), keeps ids and
  * permuted positions in LDS, and uses no workspace.  Other batches take the

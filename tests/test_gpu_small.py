@@ -83,11 +83,14 @@ def _logits(rng, N, E, dtype, sd=1.0):
 
 CASES = [
     # N, E, K, A, R, S, C, dtype, routing
-    (1000, 64, 8, 16, 4, 4, 5, synth.F32, "sigmoid_group"),
+    (250, 64, 8, 16, 4, 5, 5, synth.F32, "sigmoid_group"),
+    (1000, 64, 8, 16, 4, 4, 5, synth.F32, "sigmoid_group"),   # three-kernel path
     (300, 32, 4, 3, 8, 3, 7, synth.BF16, "softmax_full"),
-    (1024, 16, 8, 1, 2, 1, 24, synth.F32, "softmax"),          # 8192 slots, many duplicates
+    (256, 16, 8, 1, 2, 1, 24, synth.F32, "softmax"),           # 2048 slots, many duplicates
+    (1024, 16, 8, 1, 2, 1, 24, synth.F32, "softmax"),          # three-kernel path, duplicates
     (1, 2, 1, 1, 1, 1, 1, synth.F32, "softmax"),
-    (1024, 256, 8, 128, 8, 1, 1, synth.F32, "sigmoid"),        # 8192 slots, E = 256
+    (256, 256, 8, 128, 8, 1, 1, synth.F32, "sigmoid"),         # 2048 slots, E = 256
+    (1500, 24, 1, 2, 4, 3, 4, synth.F32, "softmax"),           # K = 1, 1500 slots
     (777, 40, 3, 5, 4, 7, 9, synth.BF16, "sigmoid"),           # E not a multiple of 16 bytes of bf16
     (2000, 64, 8, 4, 4, 2, 3, synth.F32, "softmax"),           # above the one-kernel envelope
     (500, 512, 4, 2, 8, 5, 2, synth.BF16, "softmax"),          # E above the one-kernel envelope

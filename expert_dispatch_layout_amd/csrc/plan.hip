@@ -1,6 +1,6 @@
 // mep_plan: expert-parallel dispatch plan over R virtual ranks, computed on one GPU's batch.
 //
-// Tokens are cut into tiles that never cross a source shard (TT tokens, TT*K <= 4096 slots).
+// Tokens are cut into tiles that never cross a source shard (TT tokens, TT*K <= 2048 slots).
 // Per token, with owner(e) = e / epn:
 //   c0[r]  1 if the token sends anything to r       (is_token_in_rank; DeepEP intranode.cu
 //                                                     notify_dispatch counts and prefixes these)
@@ -36,7 +36,7 @@ namespace mep {
 
 constexpr int kPlanBlock = 512;
 constexpr int kPlanWaves = kPlanBlock / kWave;
-constexpr int kPlanSlots = 4096;  // slots per tile
+constexpr int kPlanSlots = 2048;  // slots per tile
 constexpr int kMaxRanks = 128;
 constexpr int kMaxE = 1024;
 constexpr int kMaxCols = 3 * kMaxRanks + kMaxE;
@@ -519,7 +519,7 @@ __device__ __forceinline__ void plan_write_tile(const Src& src, const PlanGeom& 
     __syncthreads();
 
     // ---- slot pass 1: stable ranks among same-rank heads / duplicates of this wave --------
-    constexpr int kIters = kPlanSlots / kWTWaves / kWave;  // 8
+    constexpr int kIters = kPlanSlots / kWTWaves / kWave;
     const int per_wave = (nslots + kWTWaves - 1) / kWTWaves;
     const int wbeg = w * per_wave;
     const int wend = min(nslots, wbeg + per_wave);

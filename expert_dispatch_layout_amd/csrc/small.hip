@@ -37,6 +37,36 @@ constexpr int kSmMaxShardE = 4096;   // num_src * E
 constexpr int kSmMaxChan = 4096;     // num_src * R * num_channels
 constexpr int kSmKMax = 8;
 
+// Barrier that orders LDS only.  Every phase below reads what other threads wrote in LDS, never
+// in global memory, so no barrier needs to wait for the global stores still in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Exclusive scan of one int per thread over the workgroup, with LDS-only barriers.
+__device__ __forceinline__ int lds_block_scan(int v, int* s_tmp, int& total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) s_tmp[w] = incl;
+    lds_barrier();
+    int off = 0;
+    total = 0;
+    for (int i = 0; i < kSmWaves; ++i) {
+        const int x = s_tmp[i];
+        off += i < w ? x : 0;
+        total += x;
+    }
+    lds_barrier();
+    return off + incl - v;
+}
+
 struct SmallArgs {
     RouteArgs ra;
     int A;
@@ -95,16 +125,16 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
     for (int i = tid; i < S * E; i += kSmBlock) s_ntpe[i] = 0;
     for (int i = tid; i < S * R; i += kSmBlock) s_ntpr[i] = 0;
     for (int i = tid; i < S * R * C; i += kSmBlock) s_chan[i] = 0;
-    __syncthreads();
+    lds_barrier();
 
     // ---- layout: histogram, padded scan ----------------------------------------------------------
     for (int i = tid; i < NK; i += kSmBlock) atomicAdd(&s_cnt[s_ids[i]], 1);
-    __syncthreads();
+    lds_barrier();
     {
         const int c = tid < E ? s_cnt[tid] : 0;
         const int padded = c > 0 ? (c + sa.A - 1) / sa.A * sa.A : 0;
         int total;
-        const int excl = block_exclusive_scan<kSmBlock>(padded, s_tmp, total);
+        const int excl = lds_block_scan(padded, s_tmp, total);
         if (tid < E) {
             s_cu[tid] = excl;
             if (sa.lo.tokens_per_expert) sa.lo.tokens_per_expert[tid] = c;
@@ -120,14 +150,14 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
             sa.lo.cu_seqlens[E] = total;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- layout: stable positions, 512 slots at a time ------------------------------------------
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     for (int c0 = 0; c0 < NK; c0 += kSmBlock) {
         for (int i = tid; i < kSmWaves * E; i += kSmBlock) s_wc[i / E][i % E] = 0;
-        __syncthreads();
+        lds_barrier();
         const int i = c0 + tid;
         const bool valid = i < NK;
         const int e = valid ? s_ids[i] : 0;
@@ -138,7 +168,7 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
         }
         const int rank = __popcll(peers & lanes_below());
         if (valid && rank == 0) s_wc[wv][e] = __popcll(peers);
-        __syncthreads();
+        lds_barrier();
         if (tid < E) {
             int run = 0;
             for (int w = 0; w < kSmWaves; ++w) {
@@ -148,16 +178,16 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
             }
             s_chunk[tid] = run;
         }
-        __syncthreads();
+        lds_barrier();
         if (valid) {
             const int P = s_cu[e] + s_run[e] + s_wc[wv][e] + rank;
             s_P[i] = P;
             sa.lo.e2p[i] = P;
             if (sa.lo.p2e) sa.lo.p2e[P] = i;
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < E) s_run[tid] += s_chunk[tid];  // the earlier chunks' slots of each expert
-        __syncthreads();
+        lds_barrier();
     }
     if (sa.lo.p2e) {
         for (int e = 0; e < E; ++e) {
@@ -190,7 +220,7 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- plan: matrices and receive layout -----------------------------------------------------------
     for (int i = tid; i < S * E; i += kSmBlock)
@@ -243,7 +273,7 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
         return;
     }
     for (int i = tid; i < 2 * R; i += kSmBlock) s_dtot[i] = 0;
-    __syncthreads();
+    lds_barrier();
     for (int t = tid; t < N; t += kSmBlock) {
         int hits[kSmMaxR];
 #pragma unroll
@@ -260,7 +290,7 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
                 atomicAdd(&s_dtot[2 * r + 1], hits[r] - 1);
             }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) {
         int gacc = 0, dacc = 0;
         for (int r = 0; r < R; ++r) {
@@ -282,7 +312,7 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
             sa.po.dup_offsets[2 * R + 1] = dacc;
         }
     }
-    __syncthreads();
+    lds_barrier();
     const int lane = tid & 63;
     int carry[kSmMaxR];
 #pragma unroll
@@ -297,7 +327,9 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
         int incl[kSmMaxR];
 #pragma unroll
         for (int r = 0; r < kSmMaxR; ++r) {
-            const int h = (r < R && t < N) ? hits_on(t, r) : 0;
+            incl[r] = 0;
+            if (r >= R) continue;  // uniform: ranks past R cost nothing
+            const int h = t < N ? hits_on(t, r) : 0;
             int x = h >= 2 ? (1 << 16) | (h - 1) : 0;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
@@ -307,9 +339,10 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
             incl[r] = x;
             if (lane == 63) s_wsum[wv][r] = x;
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int r = 0; r < kSmMaxR; ++r) {
+            if (r >= R) continue;
             int before = 0, tot = 0;
             for (int w = 0; w < kSmWaves; ++w) {
                 const int x = s_wsum[w][r];
@@ -342,7 +375,7 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
             }
             carry[r] += tot;
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 

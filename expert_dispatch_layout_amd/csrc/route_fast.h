@@ -316,8 +316,9 @@ __global__ __launch_bounds__(kFastBlock, 3) void route_fast_kernel(RouteArgs a, 
             const float dlt_g = exact ? 0.0f : delta_g;
             fail = false;
             if (lseg == 0) s_ccount[tloc] = 0;
+            static_assert(kCandCap % LPT == 0, "whole rounds of the token's lanes");
 #pragma unroll
-            for (int i = lseg; i < kCandCap; i += LPT) s_cand[tloc][i] = 0ull;
+            for (int j = 0; j < kCandCap / LPT; ++j) s_cand[tloc][j * LPT + lseg] = 0ull;
             wave_lds_sync();
 
             // ---- keys -----------------------------------------------------------------------------

@@ -1,6 +1,7 @@
 // mep_plan: expert-parallel dispatch plan over R virtual ranks, computed on one GPU's batch.
 //
-// Tokens are cut into tiles that never cross a source shard (TT tokens, TT*K <= 2048 slots).
+// Tokens are cut into tiles that never cross a source shard (TT tokens, TT*K <= 4096 slots;
+// 2048 when that still gives at most one tile per compute unit).
 // Per token, with owner(e) = e / epn:
 //   c0[r]  1 if the token sends anything to r       (is_token_in_rank; DeepEP intranode.cu
 //                                                     notify_dispatch counts and prefixes these)
@@ -36,7 +37,11 @@ namespace mep {
 
 constexpr int kPlanBlock = 512;
 constexpr int kPlanWaves = kPlanBlock / kWave;
-constexpr int kPlanSlots = 2048;  // slots per tile
+constexpr int kPlanSlots = 4096;  // slots per tile, at most (LDS arrays are sized for it)
+// Compute units of an MI355X: tiles are halved (to 2048 slots) while that still leaves at most
+// one tile per unit -- a fused scatter + write workgroup needs most of a unit's LDS, so tiles
+// beyond the unit count only add rounds, and below it half the units would sit idle.
+constexpr int kTileUnits = 256;
 constexpr int kMaxRanks = 128;
 constexpr int kMaxE = 1024;
 constexpr int kMaxCols = 3 * kMaxRanks + kMaxE;
@@ -763,6 +768,7 @@ static PlanGeom plan_geom(int64_t N, int E, int K, int R, int S, int C, int64_t 
     g.S = S;
     g.n = (int)(N / S);
     g.TT = plan_tile_tokens(K);
+    if (g.TT >= 2 && (int64_t)S * ceil_div64(g.n, g.TT / 2) <= kTileUnits) g.TT /= 2;
     g.tps = (int)ceil_div64(g.n, g.TT);
     g.ntiles = S * g.tps;
     g.ncols = 3 * R + E;

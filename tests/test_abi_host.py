@@ -43,16 +43,23 @@ def test_workspace_sizes():
     assert B.layout_workspace_size(0, 8, 2) == 256 + arrive
     assert B.layout_workspace_size(65536, 256, 8) == 256 + arrive + 32 * 256 * 8 + 128 * 256 * 8
     assert B.layout_workspace_size(1, 8, 2) == 256 + arrive + 256 + 256
-    # plan: write tiles of 4096 / K tokens that never cross a shard (128 here), grouped by 4
-    # into 32 count tiles; arrival counters (fixed region), look-back words for the 3R rank
-    # columns, tagged expert aggregates per count tile, and tagged 3R+E column histograms per
-    # write tile (each part 256-aligned)
+    # plan: write tiles of 4096 / K tokens that never cross a shard, halved to 2048 / K while
+    # that still gives at most 256 tiles (one per compute unit); tiles grouped into about 32
+    # count tiles; arrival counters (fixed region), look-back words for the 3R rank columns,
+    # tagged expert aggregates per count tile, and tagged 3R+E column histograms per write tile
+    # (each part 256-aligned)
     def a256(x):
         return (x + 255) // 256 * 256
 
-    want = 256 + 2048 * 4 + a256(32 * 24 * 8) + a256(32 * 256 * 8) + a256(128 * (24 + 256) * 8)
+    # 65536 tokens, K = 8: 256 tiles of 256 tokens (halved), 8 per count tile, 32 count tiles
+    want = 256 + 2048 * 4 + a256(32 * 24 * 8) + a256(32 * 256 * 8) + a256(256 * (24 + 256) * 8)
     assert B.plan_workspace_size(65536, 256, 8, 8, 8) == want
     assert B.plan_workspace_size(65536, 256, 8, 8, 1) == want
+    # 262144 tokens over 32 shards: halving would give 1024 tiles, so 512 tiles of 512 tokens
+    # stay, 16 per count tile (one per shard), 32 count tiles
+    want = (256 + 2048 * 4 + a256(32 * 96 * 8) + a256(32 * 256 * 8)
+            + a256(512 * (96 + 256) * 8))
+    assert B.plan_workspace_size(262144, 256, 8, 32, 32) == want
 
 FAKE = 0x10000          # aligned, never dereferenced
 MIS = 0x10004           # 4-aligned but not 16-aligned

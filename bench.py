@@ -1,7 +1,9 @@
 """Benchmark of the MoE routing + dispatch-layout hot path on one MI355X.
 
 A step is one pass of the whole path over one batch of router logits already resident in HBM:
-mep_route_topk, then mep_layout_plan (mep_build_layout + mep_plan in one call), on one stream.  The default workload
+mep_route_layout_plan (routing, layout and plan in one call) on one stream.  On the default
+workload that is two kernels: the sigmoid routing kernel, which also counts the plan tiles it
+routes and forms every prefix in its epilogue, then the plan-tile kernel.  The default workload
 is N=65536 tokens, E=256 experts, K=8, fp32 logits, sigmoid scoring with a per-expert bias,
 8 groups keep 4 by top-2 sum, weights renormalised x2.5, alignment 128, R=8 virtual ranks with
 one source shard per rank and 24 channels.
@@ -9,9 +11,13 @@ one source shard per rank and 24 channels.
 Input and output buffers rotate over several distinct sets (together larger than the 256 MB
 Infinity Cache) so every step reads logits from HBM, not from the last-level cache.
 
-Prints one JSON line.  `roofline` describes the dominant kernel (routing): algorithmic bytes per
-launch / its average duration, timed inside the timed region with HIP events that the kernel's
-launch on the bench stream stamps itself (mep_route_topk_timed).  `cpu_baseline` is the CPU oracle timed on this host on a bounded sample.
+Prints one JSON line.  `roofline` describes the dominant kernel (routing + counting):
+algorithmic bytes per launch / its average duration, timed inside the timed region with HIP
+events that the kernel's launch on the bench stream stamps itself (mep_route_layout_plan_timed);
+`roofline.path_frac` is the whole path's algorithmic bytes per step / the step time / peak.
+`three_calls` times mep_route_topk + mep_build_layout + mep_plan.  `cpu_baseline` is the CPU
+oracle timed on this host on a bounded sample (routing split over threads, layout and plan
+serial).
 """
 from __future__ import annotations
 
@@ -19,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -27,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 LLC_BYTES = 256 * 1024 * 1024  # MI355X Infinity Cache
+CPU_THREADS_MAX = 16           # the CPU share of one GPU on the benchmark hosts
 
 
 def parse():
@@ -35,6 +43,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--legs", choices=("all", "step"), default="all",
+                    help="'step': only the timed steps and the latency run (no three-call, "
+                         "widening-row or CPU legs), for profiler runs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time for the oracle baseline (0 disables it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -74,17 +85,22 @@ def route_kernel_name(wl) -> str:
     return "route_fast_kernel"
 
 
-# sources of the routing kernels; a counter profile is valid only while their text is unchanged
+# sources of the routing kernel (every file it includes, and the counting epilogue it runs) and
+# the compile flags; a counter profile is valid only while all of them are unchanged
 ROUTE_SOURCES = ["route.hip", "route_common.h", "route_sig.hip", "route_sig.h", "sigmoid_cr.h",
-                 "route_fast.h", "route_fast.hip", "route_fast_f32.hip", "route_fast_bf16.hip"]
+                 "route_fast.h", "route_fast.hip", "route_fast_f32.hip", "route_fast_bf16.hip",
+                 "device_common.h", "host_common.h", "calls.h", "path.h"]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "route_traffic.json")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
 def route_sources_sha256() -> str:
+    from expert_dispatch_layout_amd import build as hip_build
+
     h = hashlib.sha256()
     for name in ROUTE_SOURCES:
         h.update(open(os.path.join(ROOT, "expert_dispatch_layout_amd", "csrc", name), "rb").read())
+    h.update(" ".join(hip_build.CFLAGS).encode())
     return h.hexdigest()
 
 
@@ -147,26 +163,59 @@ def record_traffic(fetch_csv: str, write_csv: str, copy_mib: int, wl):
     print(json.dumps({k: rec[k] for k in rec if k != "kernels"}))
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, inp, seconds: float):
+    """The oracle on this host's cores, on the benchmark batch: one full pass (route, layout,
+    plan) with the routing split over T threads (tokens are independent; layout and plan stay
+    serial), and the same pass on one thread.  Each is the median of up to three passes,
+    bounded by `seconds` of CPU work in all."""
     import oracle
 
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
-        ids, _ = oracle.route(inp.logits, wl.K, bias=inp.bias, score_fn=wl.score_fn,
-                              renormalize=wl.renormalize, n_group=wl.n_group,
-                              topk_group=wl.topk_group, group_topn=wl.group_topn,
-                              scale=wl.scale, dtype=wl.dtype)
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    threads = max(1, min(avail or 1, CPU_THREADS_MAX))
+    kw = dict(bias=inp.bias, score_fn=wl.score_fn, renormalize=wl.renormalize,
+              n_group=wl.n_group, topk_group=wl.topk_group, group_topn=wl.group_topn,
+              scale=wl.scale, dtype=wl.dtype)
+
+    def one_pass(nthreads):
+        t0 = time.perf_counter()
+        if nthreads > 1:
+            ids, _ = oracle.route_threads(inp.logits, wl.K, nthreads, **kw)
+        else:
+            ids, _ = oracle.route(inp.logits, wl.K, **kw)
+        t1 = time.perf_counter()
         L = oracle.layout(ids, wl.E, wl.alignment)
         oracle.plan(ids, L.cu_seqlens, L.expanded_to_permuted, wl.E, wl.R, wl.S,
                     wl.num_channels, wl.NvS)
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or passes >= 1000:
-            break
-    return {"value": wl.N * passes / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "%d full passes (route+layout+plan) over the %d-token workload, one thread, "
-                      "%.1f s" % (passes, wl.N, el)}
+        t2 = time.perf_counter()
+        return t2 - t0, t1 - t0
+
+    t_start = time.perf_counter()
+    multi = [one_pass(threads)]
+    single = [one_pass(1)]
+    while len(single) < 3 and time.perf_counter() - t_start + multi[0][0] + single[0][0] < seconds:
+        multi.append(one_pass(threads))
+        single.append(one_pass(1))
+    m = statistics.median(p[0] for p in multi)
+    s1 = statistics.median(p[0] for p in single)
+    return {"value": wl.N / m, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "the whole %d-token batch, route + layout + plan; routing split over %d "
+                      "threads, layout and plan serial; median of %d passes"
+                      % (wl.N, threads, len(multi)),
+            "single_thread": {"value": wl.N / s1, "unit": "tokens/s", "cores": 1,
+                              "passes": len(single),
+                              "route_s": statistics.median(p[1] for p in single)},
+            "route_s": statistics.median(p[1] for p in multi),
+            "host_cores_visible": avail, "cpu_model": cpu_model()}
 
 
 def tile_map_leg(B, torch, L, wl, steps: int, stream):
@@ -312,6 +361,34 @@ def small_batch_leg(B, torch, synth, steps: int, stream):
     return res
 
 
+def three_calls_leg(B, torch, sets, bias, params, wl, ws_l, ws_p, steps: int, stream):
+    """mep_route_topk + mep_build_layout + mep_plan, back to back on one stream over the same
+    rotating buffer sets, `steps` steps between two events (µs per step)."""
+    N, E, K, A, R, S, C = wl.N, wl.E, wl.K, wl.alignment, wl.R, wl.S, wl.num_channels
+    calls = []
+    for x, ids, w, L, P in sets:
+        calls.append((B.bound_route_topk(x, K, bias, params, ids, w, stream),
+                      B.bound_build_layout(ids, E, A, L.tokens_per_expert, L.cu_seqlens,
+                                           L.expanded_to_permuted, L.permuted_to_expanded,
+                                           L.zero_fill, ws_l, stream),
+                      B.bound_plan(ids, L.cu_seqlens, L.expanded_to_permuted, E, A, R, S, C,
+                                   wl.NvS, P, ws_p, stream)))
+    for i in range(3):
+        for f in calls[i % len(calls)]:
+            f()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        for f in calls[i % len(calls)]:
+            f()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return {"us_per_step": t0.elapsed_time(t1) * 1e3 / steps, "steps": steps,
+            "kernels": "routing, layout count + scatter, plan count + write (5 launches)"}
+
+
 def main():
     args = parse()
     if args.record_traffic:
@@ -357,24 +434,20 @@ def main():
     NvS = wl.NvS
     stream = torch.cuda.current_stream()
 
-    # one prepared call per buffer set and entry point (arguments converted once): routing, then
-    # layout + plan in one call (mep_layout_plan: two kernels, the plan's counting pass also
-    # serving the layout).  Timed steps route through mep_route_topk_timed with a pair of
-    # events per step, which the routing kernel's launch itself stamps with its start and end.
-    calls = []
-    for x, ids, w, L, P in sets:
-        calls.append((B.bound_route_topk(x, K, bias, params, ids, w, stream),
-                      B.bound_layout_plan(ids, E, A, L, R, S, C, NvS, P, ws_p, stream)))
-    timers = [B.KernelTimer() for _ in range(args.steps)]
-    timed = []
-    for i in range(args.steps):
-        x, ids, w = sets[(args.warmup + i) % nsets][:3]
-        timed.append(B.bound_route_topk(x, K, bias, params, ids, w, stream, timer=timers[i]))
+    def step_call(i, rt=None, pt=None):
+        x, ids, w, L, P = sets[i % nsets]
+        return B.bound_route_layout_plan(x, K, bias, params, ids, w, A, L, R, S, C, NvS, P, ws_p,
+                                         stream, route_timer=rt, plan_timer=pt)
+
+    # one prepared call per step (arguments converted once); timed steps stamp two events per
+    # kernel through their own launches (mep_route_layout_plan_timed)
+    plain = [step_call(i) for i in range(nsets)]
+    rts = [B.KernelTimer() for _ in range(args.steps)]
+    pts = [B.KernelTimer() for _ in range(args.steps)]
+    timed = [step_call(args.warmup + i, rts[i], pts[i]) for i in range(args.steps)]
 
     for i in range(args.warmup):
-        route, layout_plan = calls[i % nsets]
-        route()
-        layout_plan()
+        plain[i % nsets]()
     torch.cuda.synchronize()
 
     # timed region: K steps bracketed by synchronisation
@@ -385,22 +458,41 @@ def main():
     t_start.record(stream)
     for i in range(args.steps):
         timed[i]()
-        calls[(args.warmup + i) % nsets][1]()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
-    route_ms = sum(t.elapsed_ms() for t in timers) / args.steps
+    route_us = [t.elapsed_ms() * 1e3 for t in rts]
+    plan_us = [t.elapsed_ms() * 1e3 for t in pts]
+    step_us = [B.event_elapsed_ms(r.start, p.stop) * 1e3 for r, p in zip(rts, pts)]
 
     # sizes of this batch's layout and dedup lists (for the whole-path byte count)
     L, P = sets[(args.warmup + args.steps - 1) % nsets][3:]
     T = int(L.cu_seqlens[E].item())
     G, D = [int(v) for v in P.dup_offsets[R].tolist()]
     rb = route_bytes(wl)
-    achieved = rb / (route_ms * 1e-3) / 1e9
+    route_mean = statistics.fmean(route_us)
+    achieved = rb / (route_mean * 1e-6) / 1e9
     pb = path_bytes(wl, T, G, D)
+    path_gbs = pb / (ms_step * 1e-3) / 1e9
     traffic = traffic_from_profile()
+
+    # per-step latency over at least 50 steps (launch-stamped events: routing start to plan end)
+    nlat = max(50, args.steps)
+    lrt = [B.KernelTimer() for _ in range(nlat)]
+    lpt = [B.KernelTimer() for _ in range(nlat)]
+    lat_calls = [step_call(i, lrt[i], lpt[i]) for i in range(nlat)]
+    torch.cuda.synchronize()
+    for c in lat_calls:
+        c()
+    torch.cuda.synchronize()
+    lat_us = sorted(B.event_elapsed_ms(r.start, p.stop) * 1e3 for r, p in zip(lrt, lpt))
+    lat_route = sorted(t.elapsed_ms() * 1e3 for t in lrt)
+    lat_plan = sorted(t.elapsed_ms() * 1e3 for t in lpt)
+
+    def pct(v, q):
+        return v[min(len(v) - 1, int(q * len(v)))]
 
     out = {
         "metric": "routed tokens/sec + achieved HBM GB/s (% of peak), N=65536 E=256 K=8",
@@ -421,21 +513,31 @@ def main():
                                                 "sigmoid+bias, 8 groups keep 4 (top-2 sum), "
                                                 "renorm x2.5" if wl.score_fn else "softmax top-K",
                                                 A, R, S, C),
-                   "buffer_sets": nsets},
+                   "buffer_sets": nsets, "call": "mep_route_layout_plan"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "kernel": route_kernel_name(wl), "bytes_per_launch": rb},
-        "path": {"route_ms": route_ms,
-                 "algorithmic_bytes": pb, "GB_per_s": pb / (ms_step * 1e-3) / 1e9,
-                 "frac_of_peak": pb / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": route_kernel_name(wl) + " (routing + plan-tile counting)",
+                     "bytes_per_launch": rb,
+                     "path_frac": path_gbs / HBM_PEAK_GBS},
+        "path": {"algorithmic_bytes": pb, "GB_per_s": path_gbs, "frac_of_peak": path_gbs / HBM_PEAK_GBS,
                  "slots_per_s": N * K / (ms_step * 1e-3), "T": T, "dedup_groups": G,
-                 "dedup_dups": D, "host_wall_s": wall},
+                 "dedup_dups": D, "host_wall_s": wall,
+                 "route_us_mean": route_mean, "plan_us_mean": statistics.fmean(plan_us),
+                 "step_us_mean_events": statistics.fmean(step_us),
+                 "latency": {"steps": nlat, "step_us_median": pct(lat_us, 0.5),
+                             "step_us_p10": pct(lat_us, 0.1), "step_us_p90": pct(lat_us, 0.9),
+                             "route_us_median": pct(lat_route, 0.5),
+                             "plan_us_median": pct(lat_plan, 0.5)}},
     }
-    ids_last, w_last = sets[(args.warmup + args.steps - 1) % nsets][1:3]
-    out["next_rows"] = {"tile_map": tile_map_leg(B, torch, L, wl, args.steps, stream),
-                        "balanced_plan": balanced_leg(B, torch, ids_last, L, wl, args.steps, stream),
-                        "rows": rows_leg(B, torch, L, w_last, wl, min(args.steps, 20), stream),
-                        "small_batch": small_batch_leg(B, torch, synth, 200, stream)}
+    if args.legs == "all":
+        ws_l = B.alloc_workspace(B.layout_workspace_size(N, E, K), dev)
+        out["three_calls"] = three_calls_leg(B, torch, sets, bias, params, wl, ws_l, ws_p,
+                                             max(50, args.steps), stream)
+        ids_last, w_last = sets[(args.warmup + args.steps - 1) % nsets][1:3]
+        out["next_rows"] = {"tile_map": tile_map_leg(B, torch, L, wl, args.steps, stream),
+                            "balanced_plan": balanced_leg(B, torch, ids_last, L, wl, args.steps, stream),
+                            "rows": rows_leg(B, torch, L, w_last, wl, min(args.steps, 20), stream),
+                            "small_batch": small_batch_leg(B, torch, synth, 200, stream)}
     if args.copy_calibration > 0:
         nbytes = args.copy_calibration << 20
         src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
@@ -444,7 +546,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and args.legs == "all":
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

@@ -54,7 +54,8 @@ class BalancedOutputs(ctypes.Structure):
 
 
 EXPORTS = ("mep_route_topk", "mep_route_topk_timed", "mep_build_layout", "mep_layout_workspace_size", "mep_plan",
-           "mep_plan_workspace_size", "mep_layout_plan", "mep_route_layout_plan", "mep_tile_map", "mep_plan_balanced", "mep_permute_rows",
+           "mep_plan_workspace_size", "mep_layout_plan", "mep_route_layout_plan",
+           "mep_route_layout_plan_timed", "mep_tile_map", "mep_plan_balanced", "mep_permute_rows",
            "mep_combine_rows", "mep_status_string")
 
 _lib = None
@@ -94,6 +95,8 @@ def lib():
                                                     I, P, P, P, P, I64, P, I, I, I, I64,
                                                     ctypes.POINTER(PlanOutputs), P, SZ, P]
                 L.mep_route_layout_plan.restype = I
+                L.mep_route_layout_plan_timed.argtypes = L.mep_route_layout_plan.argtypes + [P, P, P, P]
+                L.mep_route_layout_plan_timed.restype = I
                 L.mep_plan_balanced.argtypes = [P, P, P, P, I64, I, I, I, I, I, I64, I64,
                                                 ctypes.POINTER(BalancedOutputs), P]
                 L.mep_plan_balanced.restype = I
@@ -321,6 +324,17 @@ class KernelTimer:
                     h.hipEventDestroy(e)
 
 
+def event_elapsed_ms(start, stop) -> float:
+    """hipEventElapsedTime between two events (ctypes handles, e.g. of two KernelTimers)."""
+    if KernelTimer._hip is None:
+        KernelTimer(0)
+    ms = ctypes.c_float()
+    rc = KernelTimer._hip.hipEventElapsedTime(ctypes.byref(ms), start, stop)
+    if rc != 0:
+        raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+    return ms.value
+
+
 def bound_build_layout(topk_ids, E, alignment, tokens_per_expert, cu_seqlens, expanded_to_permuted,
                        permuted_to_expanded, zero_fill, ws, stream=None):
     _require_cuda(topk_ids, tokens_per_expert, cu_seqlens, expanded_to_permuted,
@@ -383,11 +397,19 @@ def mep_route_layout_plan(logits, K, bias, params, topk_ids, topk_weights, align
 
 def bound_route_layout_plan(logits, K, bias, params, topk_ids, topk_weights, alignment,
                             layout: "LayoutTensors", R, num_src, num_channels, NvS,
-                            outputs: "PlanTensors", ws, stream=None):
+                            outputs: "PlanTensors", ws, stream=None,
+                            route_timer: "KernelTimer" = None, plan_timer: "KernelTimer" = None):
+    """With a timer, the call is mep_route_layout_plan_timed: the routing kernel's launch stamps
+    route_timer's events, the plan-tile kernel's launch plan_timer's."""
     po = outputs.as_struct()
-    call = _bound("mep_route_layout_plan", _route_layout_plan_args(
-        logits, K, bias, params, topk_ids, topk_weights, alignment, layout, R, num_src,
-        num_channels, NvS, po, ws, stream), "mep_route_layout_plan")
+    args = _route_layout_plan_args(logits, K, bias, params, topk_ids, topk_weights, alignment,
+                                   layout, R, num_src, num_channels, NvS, po, ws, stream)
+    if route_timer is None and plan_timer is None:
+        call = _bound("mep_route_layout_plan", args, "mep_route_layout_plan")
+    else:
+        ev = (route_timer.start if route_timer else None, route_timer.stop if route_timer else None,
+              plan_timer.start if plan_timer else None, plan_timer.stop if plan_timer else None)
+        call = _bound("mep_route_layout_plan_timed", args + ev, "mep_route_layout_plan_timed")
     call.keep = po
     return call
 

@@ -143,4 +143,10 @@ void plan_launch_count(const PlanCall& c, hipStream_t st);
 void plan_launch_scatter_write(const LayoutCall& lc, const PlanCall& pc, hipStream_t st);
 void plan_launch_write(const PlanCall& c, hipStream_t st);
 
+// Optional events stamped by the launches of mep_route_layout_plan_timed: the routing kernel (or
+// the one small-batch kernel) and the plan-tile kernel.
+struct StepEvents {
+    hipEvent_t route_start = nullptr, route_stop = nullptr, plan_start = nullptr, plan_stop = nullptr;
+};
+
 }  // namespace mep

@@ -141,7 +141,11 @@ struct WsHeader {
     uint32_t epoch;    // epoch of the last completed call
     uint32_t ticket;   // tile ticket counter, reset to 0 by the consuming kernel
     uint32_t ct_done;  // count tiles whose totals are stored; reset to 0 by the last of them
-    uint32_t pad[61];
+    uint32_t err;      // sticky error bits (word 3): a bounded wait ran out, which only a misused
+                       // workspace (two calls on it at once) can cause
+    uint32_t pcall;    // calls of the fused path so far (its counting sums alternate between two
+                       // buffers by the parity); advanced by the plan-tile kernel
+    uint32_t pad[59];
 };
 static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 

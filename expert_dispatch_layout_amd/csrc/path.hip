@@ -1,0 +1,589 @@
+// The fused layout + plan path over plan tiles (path.h): the counting kernel (for ids given by
+// the caller; the routing kernel does the same counting in its epilogue when it runs in the
+// fused call), and the plan-tile kernel, which writes every per-slot and per-token output of the
+// layout and the plan for one tile from the prefixes the counting epilogue left.
+//
+// Plan-tile kernel, one workgroup of 512 threads per tile (at most 2048 slots):
+//   prologue   the tile's ids into LDS; the exclusive prefix of every column before the tile
+//              (three plain loads per column), cu_seqlens, the dedup segment starts;
+//   tokens     a thread per token: owner ranks of its K slots, first slot per rank, slots per
+//              rank -> a code per slot (expert, rank, head / duplicate / plain, slots on the rank);
+//              is_token_in_rank; per-wave ballots of each rank's tokens (channel prefixes);
+//   ranks      slots in slot order, 64 per wave step: a slot's rank among the same expert's
+//              slots of its wave from one ballot per id bit (a wave64 stand-in for a warp match),
+//              per-(wave, expert) counters in LDS; the same for dedup heads and duplicates per
+//              rank.  The order is MoonEP planning.py run_c1's stable order, so the result is
+//              deterministic;
+//   write      expanded_to_permuted = cu[e] + prefix before the tile + earlier waves + rank;
+//              permuted_to_expanded at that row; dst with the duplicate encoding (MoonEP
+//              planning.py dst computation and duplicate canonicalisation); dedup groups and
+//              duplicate offsets at their rank-major, token-ordered places;
+//   per tile   channel prefixes ending in the tile (DeepEP intranode.cu notify_dispatch channel
+//              part), the per-shard matrices from the shard's last tile, padding rows (-1) of
+//              a share of the experts.
+#include <limits.h>
+#include <math.h>
+
+#include "path.h"
+
+namespace mep {
+
+namespace {
+
+constexpr int kCountNT = 512;
+constexpr int kPlanNT = 512;
+constexpr int kPlanW = kPlanNT / 64;
+constexpr int kPlanIters = kPathSlots / kPlanNT;   // 64-slot steps per wave, at most
+enum : uint32_t { kSlotPlain = 0, kSlotHead = 1, kSlotDup = 2 };
+
+__device__ __forceinline__ uint32_t slot_code(int e, uint32_t type, int r, int h) {
+    return (uint32_t)e | (type << 10) | ((uint32_t)r << 12) | ((uint32_t)h << 17);
+}
+
+// Exclusive scan over the 64 lanes of a wave; `total` gets the sum.
+__device__ __forceinline__ int wave_excl_scan(int v, int& total) {
+    const int lane = threadIdx.x & 63;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    total = __shfl(incl, 63);
+    return incl - v;
+}
+
+}  // namespace
+
+// ---- counting kernel (ids given) ---------------------------------------------------------------
+
+// One counting workgroup per `sub` consecutive plan tiles: histogram rows in LDS, then the
+// epilogue of path.h.
+__global__ __launch_bounds__(kCountNT) void path_count_kernel(const int32_t* __restrict__ ids, PathGeom g,
+                                                              PathWs w, WsHeader* hdr) {
+    __shared__ int s_row[kPathMaxSub * kPathMaxNC];
+    __shared__ int64_t s_tb[kPathMaxSub + 1];
+    const int tid = threadIdx.x;
+    const int j0 = blockIdx.x * g.sub;
+    const int nsub = min(g.sub, g.ntiles - j0);
+    for (int i = tid; i < nsub * g.NC; i += kCountNT) s_row[i] = 0;
+    if (tid <= nsub) {
+        int64_t a, b;
+        path_tile_tokens(g, j0 + min(tid, nsub - 1), a, b);
+        s_tb[tid] = tid < nsub ? a : b;
+    }
+    const uint32_t pcall = path_count_begin(hdr);
+    __syncthreads();
+    const int64_t tb0 = s_tb[0], tb1 = s_tb[nsub];
+    const int K = g.K;
+    const bool vec8 = K == 8 && (((uintptr_t)ids) & 15u) == 0;
+    for (int64_t t = tb0 + tid; t < tb1; t += kCountNT) {
+        int i = 0;
+        while (i + 1 < nsub && t >= s_tb[i + 1]) ++i;
+        int* row = s_row + i * g.NC;
+        int id[kPathMaxK];
+        if (vec8) {
+            const MEP_GLOBAL u32x4* q = reinterpret_cast<const MEP_GLOBAL u32x4*>(gptr(ids) + t * 8);
+            const u32x4 a = q[0], b = q[1];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                id[k] = (int)a[k];
+                id[4 + k] = (int)b[k];
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kPathMaxK; ++k) id[k] = k < K ? gptr(ids)[t * K + k] : -1;
+        }
+        uint32_t m1 = 0u, m2 = 0u;
+#pragma unroll
+        for (int k = 0; k < kPathMaxK; ++k) {
+            if (k < K) {
+                atomicAdd(&row[id[k]], 1);
+                const uint32_t bit = 1u << (id[k] / g.epn);
+                m2 |= m1 & bit;
+                m1 |= bit;
+            }
+        }
+        path_count_ranks(g, row, m1, m2, 0, 1);
+    }
+    path_epilogue<kCountNT>(g, w, pcall, s_row);
+}
+
+// ---- totals -> cu_seqlens, dedup segment starts, small outputs --------------------------------
+
+// By wave 0: the padded exclusive scan of the expert totals (cu_seqlens, [MOON] Phase B2 padded
+// group scan) and the exclusive scans over the ranks of the dedup group and duplicate totals.
+__device__ __forceinline__ void path_scan_totals(const PathGeom& g, const int* s_tot, int* s_cu,
+                                                 int (*s_doff)[kPathMaxR + 1]) {
+    const int lane = threadIdx.x & 63;
+    const int E = g.E, R = g.R, A = g.A;
+    constexpr int PER = kPathMaxE / 64;
+    const int per = (E + 63) / 64;
+    int pad[PER];
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = lane * per + i;
+        int v = 0;
+        if (i < per && e < E) {
+            const int c = s_tot[e];
+            v = c > 0 ? ((c + A - 1) / A) * A : 0;
+        }
+        pad[i] = v;
+        s += v;
+    }
+    int total;
+    int run = wave_excl_scan(s, total);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = lane * per + i;
+        if (i < per && e < E) s_cu[e] = run;
+        run += pad[i];
+    }
+    if (lane == 0) s_cu[E] = total;
+    const int ng_r = lane < R ? s_tot[path_col_c1(g, lane)] : 0;
+    const int nd_r = lane < R ? s_tot[path_col_c2(g, lane)] : 0;
+    int tg, td;
+    const int eg = wave_excl_scan(ng_r, tg);
+    const int ed = wave_excl_scan(nd_r, td);
+    if (lane <= R) {
+        s_doff[0][lane] = lane < R ? eg : tg;
+        s_doff[1][lane] = lane < R ? ed : td;
+    }
+}
+
+// By one workgroup: cu_seqlens, tokens_per_expert, zero_fill ([MOON] zero-fill ranges), the
+// receive counts, offsets and zero-fill ranges ([DEEP] notify_dispatch), dedup counts and offsets.
+__device__ __forceinline__ void path_small_outputs(const PathGeom& g, const PathOut& o, const int* s_tot,
+                                                   const int* s_cu, const int (*s_doff)[kPathMaxR + 1]) {
+    const int tid = threadIdx.x;
+    const int E = g.E, R = g.R;
+    for (int e = tid; e <= E; e += kPlanNT) gptr(o.cu_seqlens)[e] = s_cu[e];
+    for (int e = tid; e < E; e += kPlanNT) {
+        const int c = s_tot[e];
+        const int cu0 = s_cu[e];
+        const int padded = s_cu[e + 1] - cu0;
+        const bool z = c > 0 && padded > c;
+        if (o.tokens_per_expert) gptr(o.tokens_per_expert)[e] = c;
+        if (o.zero_fill) {
+            gptr(o.zero_fill)[2 * e] = z ? cu0 + c : 0;
+            gptr(o.zero_fill)[2 * e + 1] = z ? padded - c : 0;
+        }
+        if (o.p.recv_zf) {
+            const int base = s_cu[(e / g.epn) * g.epn];
+            gptr(o.p.recv_zf)[2 * e] = z ? cu0 + c - base : 0;
+            gptr(o.p.recv_zf)[2 * e + 1] = z ? padded - c : 0;
+        }
+    }
+    for (int r = tid; r <= R; r += kPlanNT) {
+        if (o.p.dup_offsets) {
+            gptr(o.p.dup_offsets)[2 * r] = s_doff[0][r];
+            gptr(o.p.dup_offsets)[2 * r + 1] = s_doff[1][r];
+        }
+        if (r < R) {
+            if (o.p.dup_counts) {
+                gptr(o.p.dup_counts)[2 * r] = s_tot[path_col_c1(g, r)];
+                gptr(o.p.dup_counts)[2 * r + 1] = s_tot[path_col_c2(g, r)];
+            }
+            if (o.p.recv_tokens) gptr(o.p.recv_tokens)[r] = s_tot[path_col_c0(g, r)];
+        }
+    }
+    if (o.p.recv_cu)
+        for (int p = tid; p < R * (g.epn + 1); p += kPlanNT) {
+            const int r = p / (g.epn + 1);
+            const int jj = p - r * (g.epn + 1);
+            gptr(o.p.recv_cu)[p] = s_cu[r * g.epn + jj] - s_cu[r * g.epn];
+        }
+}
+
+// ---- plan-tile kernel --------------------------------------------------------------------------
+
+template <int NBE, int NBR>
+__global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __restrict__ ids, PathGeom g,
+                                                            PathWs w, PathOut o, WsHeader* hdr) {
+    __shared__ uint32_t s_code[kPathSlots + kPathSlots / 64];
+    __shared__ int s_ecnt[kPlanW][kPathMaxE];
+    __shared__ int s_rcnt[kPlanW][2][kPathMaxR];
+    __shared__ int s_cu[kPathMaxE + 1];
+    __shared__ int s_excl[kPathMaxNC];
+    __shared__ int s_shx[kPathMaxNC];
+    __shared__ int s_tot[kPathMaxNC];
+    __shared__ int s_doff[2][kPathMaxR + 1];
+    __shared__ int s_owner[kPathMaxE];
+    __shared__ uint64_t s_mask[kPathTokens / 64][kPathMaxR];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int j = blockIdx.x;
+    const int K = g.K, E = g.E, R = g.R, NC = g.NC;
+    int64_t t0, t1;
+    path_tile_tokens(g, j, t0, t1);
+    const int nt = (int)(t1 - t0);
+    const int ns = nt * K;
+    const int64_t s0 = t0 * K;
+    const int sh = j / g.tps;
+    const int l = j - sh * g.tps;
+    const bool shard_last = l == g.tps - 1;
+    const int jf = sh * g.tps;
+    const bool want_mask = o.p.chan || (shard_last && (o.p.rank_prefix || o.p.ntpr));
+    const bool want_shx = o.p.chan || (shard_last && (o.p.ntpr || o.p.ntpe));
+
+    // ---- prologue: every global load of the tile, issued together ----------------------------
+    {
+        const MEP_GLOBAL int32_t* gid = gptr(ids) + s0;
+        if (((s0 & 3) == 0) && ((((uintptr_t)ids) & 15u) == 0)) {
+            const int nq = ns >> 2;
+            for (int q = tid; q < nq; q += kPlanNT) {
+                const u32x4 v = reinterpret_cast<const MEP_GLOBAL u32x4*>(gid)[q];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s_code[slot_pad(4 * q + i)] = v[i];
+            }
+            for (int s = (nq << 2) + tid; s < ns; s += kPlanNT) s_code[slot_pad(s)] = (uint32_t)gid[s];
+        } else {
+            for (int s = tid; s < ns; s += kPlanNT) s_code[slot_pad(s)] = (uint32_t)gid[s];
+        }
+    }
+    // prefixes before this tile (and before the shard's first tile) and the totals, from the
+    // counting kernel's group sums, workgroup totals and within-workgroup prefixes
+    // (one of the two parity buffers holds this call's group sums, the other is zero)
+    {
+        const MEP_GLOBAL uint32_t* gs0 = gptr(w.gsum);
+        const MEP_GLOBAL uint32_t* gs1 = gs0 + kPathGsumWords;
+        const int wg = j / g.sub, grp = wg / g.GW;
+        const int wgf = jf / g.sub, grpf = wgf / g.GW;
+        const int wg0 = grp * g.GW, wgf0 = grpf * g.GW;
+        for (int c = tid; c < NC; c += kPlanNT) {
+            // every load of a batch first (16 rows at a time), then the sums
+            uint32_t tot = 0, pg = 0, pgf = 0;
+            for (int q0 = 0; q0 < g.ng; q0 += 16) {
+                uint32_t v[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const size_t at = (size_t)min(q0 + i, g.ng - 1) * NC + c;
+                    v[i] = gs0[at] + gs1[at];
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int q = q0 + i;
+                    const uint32_t x = q < g.ng ? v[i] : 0u;
+                    tot += x;
+                    pg += q < grp ? x : 0u;
+                    pgf += q < grpf ? x : 0u;
+                }
+            }
+            uint32_t ex = pg + gptr(w.tpre)[(size_t)j * NC + c];
+            for (int b0 = wg0; b0 < wg; b0 += 16) {
+                uint32_t v[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[i] = gptr(w.wrow)[(size_t)min(b0 + i, wg - 1) * NC + c];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) ex += b0 + i < wg ? v[i] : 0u;
+            }
+            s_excl[c] = (int)ex;
+            s_tot[c] = (int)tot;
+            if (want_shx) {
+                uint32_t sx = pgf + gptr(w.tpre)[(size_t)jf * NC + c];
+                for (int b0 = wgf0; b0 < wgf; b0 += 16) {
+                    uint32_t v[16];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) v[i] = gptr(w.wrow)[(size_t)min(b0 + i, wgf - 1) * NC + c];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sx += b0 + i < wgf ? v[i] : 0u;
+                }
+                s_shx[c] = (int)sx;
+            }
+        }
+    }
+    for (int e = tid; e < E; e += kPlanNT) s_owner[e] = e / g.epn;
+    for (int i = tid; i < kPlanW * E; i += kPlanNT) s_ecnt[i / E][i % E] = 0;
+    for (int i = tid; i < kPlanW * 2 * R; i += kPlanNT) s_rcnt[i / (2 * R)][(i / R) & 1][i % R] = 0;
+    __syncthreads();
+    if (wv == 0) path_scan_totals(g, s_tot, s_cu, s_doff);
+    __syncthreads();
+    if (j == 0) path_small_outputs(g, o, s_tot, s_cu, s_doff);
+    // ---- tokens: slot codes, is_token_in_rank, rank ballots ------------------------------------
+    for (int base = wv * 64; base < nt; base += kPlanNT) {
+        const int tk = base + lane;
+        const bool live = tk < nt;
+        uint32_t m = 0u;
+        if (live) {
+            int e[kPathMaxK], r[kPathMaxK];
+#pragma unroll
+            for (int k = 0; k < kPathMaxK; ++k) {
+                e[k] = k < K ? (int)s_code[slot_pad(tk * K + k)] : 0;
+                r[k] = k < K ? s_owner[e[k]] : -1 - k;
+            }
+#pragma unroll
+            for (int k = 0; k < kPathMaxK; ++k) {
+                if (k >= K) continue;
+                int h = 0;
+                bool first = true;
+#pragma unroll
+                for (int k2 = 0; k2 < kPathMaxK; ++k2) {
+                    const bool same = r[k2] == r[k];
+                    h += same ? 1 : 0;
+                    if (k2 < k && same) first = false;
+                }
+                const uint32_t type = first ? (h >= 2 ? kSlotHead : kSlotPlain) : kSlotDup;
+                s_code[slot_pad(tk * K + k)] = slot_code(e[k], type, r[k], h);
+                m |= 1u << r[k];
+            }
+            if (o.p.itr) {
+                MEP_GLOBAL uint8_t* row = gptr(o.p.itr) + (t0 + tk) * R;
+                if ((R & 3) == 0) {
+                    for (int bb = 0; bb < R; bb += 4) {
+                        const uint32_t wd = ((m >> bb) & 1u) | (((m >> (bb + 1)) & 1u) << 8) |
+                                            (((m >> (bb + 2)) & 1u) << 16) | (((m >> (bb + 3)) & 1u) << 24);
+                        *reinterpret_cast<MEP_GLOBAL uint32_t*>(row + bb) = wd;
+                    }
+                } else {
+                    for (int bb = 0; bb < R; ++bb) row[bb] = (uint8_t)((m >> bb) & 1u);
+                }
+            }
+        }
+        if (want_mask) {
+            const int tw = base >> 6;
+            for (int r = 0; r < R; ++r) {
+                const uint64_t bm = __ballot((m >> r) & 1u);
+                if (lane == 0) s_mask[tw][r] = bm;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- stable ranks within the waves ------------------------------------------------------------
+    const int spw = ((ns + kPlanNT - 1) / kPlanNT) * 64;  // slots per wave, a multiple of 64
+    const int sbeg = wv * spw;
+    int erank[kPlanIters], hrank[kPlanIters], drank[kPlanIters];
+#pragma unroll
+    for (int it = 0; it < kPlanIters; ++it) {
+        erank[it] = hrank[it] = drank[it] = 0;
+        if (it * 64 >= spw) continue;
+        const int si = sbeg + it * 64 + lane;
+        const bool valid = si < ns;
+        const uint32_t code = valid ? s_code[slot_pad(si)] : 0u;
+        const int e = (int)(code & 1023u);
+        const uint32_t type = (code >> 10) & 3u;
+        const int r = (int)((code >> 12) & 31u);
+        const uint64_t act = __ballot(valid);
+        if (act == 0ull) continue;
+        const uint64_t pe = match_peers<NBE>((uint32_t)e, act);
+        const int eb = valid ? s_ecnt[wv][e] : 0;
+        erank[it] = eb + popc64(pe & lanes_below());
+        if (valid && (pe >> lane) == 1ull) s_ecnt[wv][e] = eb + popc64(pe);
+        const uint64_t hm = __ballot(valid && type == kSlotHead);
+        const uint64_t dm = __ballot(valid && type == kSlotDup);
+        const uint64_t rel = hm | dm;
+        if (rel != 0ull) {
+            const bool inr = (rel >> lane) & 1ull;
+            const uint64_t pr = match_peers<NBR>((uint32_t)r, rel);
+            const uint64_t bl = pr & lanes_below();
+            const int hb = inr ? s_rcnt[wv][0][r] : 0;
+            const int db = inr ? s_rcnt[wv][1][r] : 0;
+            hrank[it] = hb + popc64(bl & hm);
+            drank[it] = db + popc64(bl & dm);
+            if (inr && (pr >> lane) == 1ull) {
+                s_rcnt[wv][0][r] = hb + popc64(pr & hm);
+                s_rcnt[wv][1][r] = db + popc64(pr & dm);
+            }
+        }
+    }
+    __syncthreads();
+    // per-(wave, column) counts -> exclusive prefixes over the waves; the tile's own expert counts
+    for (int e = tid; e < E; e += kPlanNT) {
+        int run = 0;
+#pragma unroll
+        for (int ww = 0; ww < kPlanW; ++ww) {
+            const int x = s_ecnt[ww][e];
+            s_ecnt[ww][e] = run;
+            run += x;
+        }
+        if (shard_last && o.p.ntpe) gptr(o.p.ntpe)[(int64_t)sh * E + e] = s_excl[e] + run - s_shx[e];
+    }
+    for (int p = tid; p < 2 * R; p += kPlanNT) {
+        const int q = p / R, r = p - (p / R) * R;
+        int run = 0;
+#pragma unroll
+        for (int ww = 0; ww < kPlanW; ++ww) {
+            const int x = s_rcnt[ww][q][r];
+            s_rcnt[ww][q][r] = run;
+            run += x;
+        }
+    }
+    __syncthreads();
+
+    // ---- per-slot outputs ----------------------------------------------------------------------
+    const int epn = g.epn;
+    const int NvS = (int)g.NvS;
+#pragma unroll
+    for (int it = 0; it < kPlanIters; ++it) {
+        if (it * 64 >= spw) continue;
+        const int si = sbeg + it * 64 + lane;
+        if (si >= ns) continue;
+        const uint32_t code = s_code[slot_pad(si)];
+        const int e = (int)(code & 1023u);
+        const uint32_t type = (code >> 10) & 3u;
+        const int r = (int)((code >> 12) & 31u);
+        const int h = (int)(code >> 17);
+        const int P = s_cu[e] + s_excl[e] + s_ecnt[wv][e] + erank[it];
+        const int64_t gs = s0 + si;
+        gptr(o.e2p)[gs] = P;
+        if (o.p2e) gptr(o.p2e)[P] = (int32_t)gs;
+        const int loff = P - s_cu[r * epn];
+        const int raw = r * NvS + loff;
+        if (o.p.dst) gptr(o.p.dst)[gs] = type == kSlotDup ? -raw - 1 : raw;
+        const int dloc = s_excl[path_col_c2(g, r)] + s_rcnt[wv][1][r] + drank[it];
+        if (type == kSlotHead) {
+            if (o.p.dup_groups) {
+                const int64_t gpos = (int64_t)s_doff[0][r] + s_excl[path_col_c1(g, r)] + s_rcnt[wv][0][r] + hrank[it];
+                if (gpos < o.p.cap_g) {
+                    gptr(o.p.dup_groups)[3 * gpos + 0] = loff;
+                    gptr(o.p.dup_groups)[3 * gpos + 1] = dloc;
+                    gptr(o.p.dup_groups)[3 * gpos + 2] = h - 1;
+                }
+            }
+        } else if (type == kSlotDup) {
+            const int64_t dpos = (int64_t)s_doff[1][r] + dloc;
+            if (o.p.dup_loffs && dpos < o.p.cap_d) gptr(o.p.dup_loffs)[dpos] = loff;
+        }
+    }
+
+    // ---- channel prefixes ending in this tile --------------------------------------------------
+    if (o.p.chan) {
+        const int64_t q = ((int64_t)g.n + g.C - 1) / g.C;
+        const int64_t tl0 = (int64_t)l * g.T, tl1 = tl0 + nt;
+        const int c_lo = (int)(tl0 / q);
+        int c_hi = c_lo;
+        while (c_hi < g.C && ((int64_t)(c_hi + 1) * q < g.n ? (int64_t)(c_hi + 1) * q : (int64_t)g.n) <= tl1) ++c_hi;
+        const int npairs = (c_hi - c_lo) * R;
+        for (int p = tid; p < npairs; p += kPlanNT) {
+            const int c = c_lo + p / R;
+            const int r = p - (p / R) * R;
+            const int64_t end = (int64_t)(c + 1) * q < g.n ? (int64_t)(c + 1) * q : (int64_t)g.n;
+            const int L = (int)(end - tl0);  // tokens of the tile before the channel's end
+            int cnt = 0;
+            const int wf = L >> 6;
+            for (int tw = 0; tw < wf; ++tw) cnt += popc64(s_mask[tw][r]);
+            if (L & 63) cnt += popc64(s_mask[wf][r] & ((1ull << (L & 63)) - 1ull));
+            const int c0 = path_col_c0(g, r);
+            gptr(o.p.chan)[((int64_t)sh * R + r) * g.C + c] = s_excl[c0] - s_shx[c0] + cnt;
+        }
+    }
+
+    // ---- per-shard matrices from the shard's last tile ----------------------------------------
+    if (shard_last && (o.p.rank_prefix || o.p.ntpr)) {
+        for (int r = tid; r < R; r += kPlanNT) {
+            int own = 0;
+            for (int tw = 0; tw * 64 < nt; ++tw) own += popc64(s_mask[tw][r]);
+            const int c0 = path_col_c0(g, r);
+            if (o.p.rank_prefix) gptr(o.p.rank_prefix)[(int64_t)sh * R + r] = s_excl[c0] + own;
+            if (o.p.ntpr) gptr(o.p.ntpr)[(int64_t)sh * R + r] = s_excl[c0] + own - s_shx[c0];
+        }
+    }
+
+    // ---- padding rows of a share of the experts -------------------------------------------------
+    if (o.p2e) {
+        for (int e = j; e < E; e += g.ntiles) {
+            const int beg = s_cu[e] + s_tot[e];
+            const int end = s_cu[e + 1];
+            for (int row = beg + tid; row < end; row += kPlanNT) gptr(o.p2e)[row] = -1;
+        }
+    }
+    if (j == 0 && tid == 0) __hip_atomic_fetch_add(&gptr(hdr)->pcall, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- host ----------------------------------------------------------------------------------------
+
+PathGeom path_geom(int64_t N, int E, int K, int R, int S, int C, int A, int64_t NvS) {
+    PathGeom g{};
+    g.N = (int)N;
+    g.E = E;
+    g.K = K;
+    g.R = R;
+    g.epn = E / R;
+    g.S = S;
+    g.n = (int)(N / S);
+    g.C = C;
+    g.A = A;
+    g.NvS = NvS;
+    int kp = 1;
+    while (kp < K) kp <<= 1;
+    g.T = kPathSlots / kp;
+    if (g.T > kPathTokens) g.T = kPathTokens;
+    if (g.T > g.n) g.T = g.n > 0 ? g.n : 1;
+    g.tps = (int)ceil_div64(g.n, g.T);
+    g.ntiles = S * g.tps;
+    g.NC = E + 3 * R;
+    int sub = (int)ceil_div64(g.ntiles, kPathUnits);
+    if (sub < 1) sub = 1;
+    if (sub > kPathMaxSub) sub = kPathMaxSub;
+    g.sub = sub;
+    g.nwg = (int)ceil_div64(g.ntiles, sub);
+    int gw = (int)ceil(sqrt((double)g.nwg));
+    const int gw_min = (int)ceil_div64(g.nwg, kPathMaxGroups);
+    if (gw < gw_min) gw = gw_min;
+    if (gw < 1) gw = 1;
+    g.GW = gw;
+    g.ng = (int)ceil_div64(g.nwg, gw);
+    return g;
+}
+
+// The counters of mep_plan's count-tile kernels follow the group sums (8 KiB, always left at
+// zero by those kernels); the rows of this path follow them, overlapping only parts of the
+// workspace that every call of either kernel set rewrites before reading.
+constexpr size_t kPlanArriveBytes = 8192;
+
+PathWsLayout path_ws_layout(const PathGeom& g) {
+    PathWsLayout L;
+    L.gsum = sizeof(WsHeader);
+    size_t off = L.gsum + kPathGsumBytes + kPlanArriveBytes;
+    L.wrow = off;
+    off += align256((size_t)g.nwg * g.NC * 4);
+    L.tpre = off;
+    off += align256((size_t)g.ntiles * g.NC * 4);
+    L.bytes = off;
+    return L;
+}
+
+PathWs path_ws_views(void* ws, const PathGeom& g) {
+    const PathWsLayout L = path_ws_layout(g);
+    char* b = reinterpret_cast<char*>(ws);
+    return PathWs{reinterpret_cast<uint32_t*>(b + L.gsum), reinterpret_cast<uint32_t*>(b + L.wrow),
+                  reinterpret_cast<uint32_t*>(b + L.tpre)};
+}
+
+bool path_supported(int64_t N, int E, int K, int R) {
+    return N > 0 && E <= kPathMaxE && K <= kPathMaxK && R <= kPathMaxR;
+}
+
+size_t path_workspace_bytes(int64_t N, int E, int K, int R, int S) {
+    if (!path_supported(N, E, K, R) || S < 1 || N % S != 0) return 0;
+    return path_ws_layout(path_geom(N, E, K, R, S, 1, 1, 0)).bytes;
+}
+
+PathCall path_call(const LayoutCall& lc, const PlanCall& pc, void* ws) {
+    PathCall c;
+    c.g = path_geom(pc.g.N, pc.g.E, pc.g.K, pc.g.R, pc.g.S, pc.g.C, lc.A, pc.g.NvS);
+    c.w = path_ws_views(ws, c.g);
+    c.hdr = reinterpret_cast<WsHeader*>(ws);
+    c.o = PathOut{lc.out.tokens_per_expert, lc.out.cu_seqlens, lc.out.e2p, lc.out.p2e, lc.out.zero_fill, pc.o};
+    c.ids = pc.ids;
+    return c;
+}
+
+void path_launch_count(const PathCall& c, hipStream_t st) {
+    hipLaunchKernelGGL(path_count_kernel, dim3(c.g.nwg), dim3(kCountNT), 0, st, c.ids, c.g, c.w, c.hdr);
+}
+
+void path_launch_plan(const PathCall& c, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+    auto launch = [&](auto kernel) {
+        hipExtLaunchKernelGGL(kernel, dim3(c.g.ntiles), dim3(kPlanNT), 0, st, start, stop, 0, c.ids, c.g, c.w, c.o,
+                              c.hdr);
+    };
+    const bool wideE = c.g.E > 256;
+    if (c.g.R <= 8) wideE ? launch(path_plan_kernel<9, 3>) : launch(path_plan_kernel<8, 3>);
+    else wideE ? launch(path_plan_kernel<9, 5>) : launch(path_plan_kernel<8, 5>);
+}
+
+}  // namespace mep

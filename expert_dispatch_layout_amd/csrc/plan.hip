@@ -32,6 +32,7 @@
 #include "host_common.h"
 #include "calls.h"
 #include "layout_scatter.h"
+#include "path.h"
 
 namespace mep {
 
@@ -798,7 +799,8 @@ struct PlanWsLayout {
 static PlanWsLayout plan_ws_layout(const PlanGeom& g) {
     PlanWsLayout L;
     const size_t n3 = 3 * (size_t)g.R;
-    L.arrive = sizeof(WsHeader);
+    // after the fused path's group sums, which only its kernels ever write
+    L.arrive = sizeof(WsHeader) + kPathGsumBytes;
     L.status3 = L.arrive + kMaxCountTiles * sizeof(uint32_t);
     L.statusE = L.status3 + align256((size_t)g.nct * n3 * sizeof(uint64_t));
     L.tilehist = L.statusE + align256((size_t)g.nct * g.E * sizeof(uint64_t));
@@ -812,7 +814,10 @@ extern "C" size_t mep_plan_workspace_size(int64_t N, int E, int K, int R, int nu
     using namespace mep;
     if (N < 0 || E < 1 || K < 1 || R < 1 || num_src < 1 || R > kMaxRanks || E > kMaxE)
         return sizeof(WsHeader);
-    return plan_ws_layout(plan_geom(N, E, K, R, num_src, 1, 0)).bytes;
+    // large enough for both the count-tile kernels of mep_plan and the fused path's plan tiles
+    const size_t a = plan_ws_layout(plan_geom(N, E, K, R, num_src, 1, 0)).bytes;
+    const size_t b = path_workspace_bytes(N, E, K, R, num_src);
+    return a > b ? a : b;
 }
 
 namespace mep {

@@ -48,7 +48,7 @@ static int dispatch_generic(const RouteArgs& a, const Launch& st) {
     else if (nchunks <= 128) launch_generic<64, 2, BF16>(a, st);
     else if (nchunks <= 256) launch_generic<64, 4, BF16>(a, st);
     else return MEP_ERR_UNSUPPORTED;
-    return launch_status();
+    return MEP_OK;
 }
 
 }  // namespace mep
@@ -98,15 +98,20 @@ int route_prepare(const void* logits, int dtype, int64_t N, int E, int K, const 
     return MEP_OK;
 }
 
+int route_launch(const RouteArgs& a, int dtype, const Launch& st) {
+    if (launch_route_sig(a, dtype, st)) return MEP_OK;
+    if (launch_route_fast(a, dtype, st)) return MEP_OK;
+    return dtype == MEP_BF16 ? dispatch_generic<true>(a, st) : dispatch_generic<false>(a, st);
+}
+
 static int route_topk(const void* logits, int dtype, int64_t N, int E, int K, const float* bias,
                       const mep_route_params* p, int32_t* topk_ids, float* topk_weights,
                       const Launch& st) {
     RouteArgs a;
     const int rc = route_prepare(logits, dtype, N, E, K, bias, p, topk_ids, topk_weights, a);
     if (rc != MEP_OK || a.N == 0) return rc;
-    if (launch_route_sig(a, dtype, st)) return launch_status();
-    if (launch_route_fast(a, dtype, st)) return launch_status();
-    return dtype == MEP_BF16 ? dispatch_generic<true>(a, st) : dispatch_generic<false>(a, st);
+    const int lr = route_launch(a, dtype, st);
+    return lr != MEP_OK ? lr : launch_status();
 }
 
 }  // namespace mep

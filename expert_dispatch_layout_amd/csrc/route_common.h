@@ -364,7 +364,15 @@ int route_prepare(const void* logits, int dtype, int64_t N, int E, int K, const 
 
 bool launch_route_fast(const RouteArgs& a, int dtype, const Launch& st);
 
+// Enqueue the routing kernel that covers the shape (sigmoid, fast, or generic); MEP_OK or
+// MEP_ERR_UNSUPPORTED.
+int route_launch(const RouteArgs& a, int dtype, const Launch& st);
+
 // Sigmoid routing kernel launcher (route_sig.hip).  Returns false when the shape is not covered.
 bool launch_route_sig(const RouteArgs& a, int dtype, const Launch& st);
+// The same kernel also counting the plan tiles of the fused path (path.h) it owns, with the
+// counting epilogue; false when the shape is not covered (nothing is launched then).
+struct PathCall;
+bool launch_route_sig_counting(const RouteArgs& a, int dtype, const Launch& st, const PathCall& pc);
 
 }  // namespace mep

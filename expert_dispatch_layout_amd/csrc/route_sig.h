@@ -49,12 +49,12 @@
 // the test itself.
 #pragma once
 
+#include "path.h"
 #include "route_fast.h"
 
 namespace mep {
 
 constexpr int kSigT = 6;                          // list depth per lane
-constexpr int kSigMaxSetsPerGroup = 4096;         // sets per workgroup at most (16 KB of LDS)
 constexpr int kSigEmpty = (int)0xFF800000u;       // -inf: below every key as float and as integer
 
 // LDS row layout: lane group g of a token (its CPL chunks) starts at chunk g * (CPL + 1).
@@ -79,8 +79,8 @@ __device__ __forceinline__ float lds_volatile_load(const float* p) {
 }
 
 struct SigCfg {
-    int64_t nsets;  // token sets of 64 / LPT tokens
-    int tg;         // groups kept (MODE 1)
+    int64_t tokens_per_group;  // tokens of a workgroup when it does not count (a multiple of TPW)
+    int tg;                    // groups kept (MODE 1)
 };
 
 // Value held by lane (lane ^ O) of the aligned segment (O < 16), through DPP: quad permutes for
@@ -178,7 +178,7 @@ template <int LPT, bool BF16, int MODE>
 __device__ __forceinline__ void exact_token_sig(const void* logits, const float* bias, int32_t* ids,
                                              float* weights, int K, int group_topn, int renormalize,
                                              float scale, int64_t tok, int tg, int wl,
-                                             const u32x4* lds_row) {
+                                             const u32x4* lds_row, int (&sel)[1]) {
     constexpr int E = kFastEPL * LPT;
     constexpr int NPL = E / 64;    // 1, 2, 4 or 8 experts per lane
     constexpr int S = 32 / NPL;    // lanes per group of 32 experts
@@ -277,6 +277,7 @@ __device__ __forceinline__ void exact_token_sig(const void* logits, const float*
     }
     const double v = wl < K ? (double)s_sel : 0.0;
     const double den = seg_allreduce<8>(v, 8, PartnerF64{}, [](double x, double y) { return x + y; });
+    sel[0] = my_e;
     if (wl < K) {
         const double inv = renormalize ? (den > 0.0 ? recip_f64(den) : 0.0) : 1.0;
         gptr(ids)[tok * K + wl] = my_e;
@@ -286,12 +287,60 @@ __device__ __forceinline__ void exact_token_sig(const void* logits, const float*
 
 // ---- the kernel -----------------------------------------------------------------------------------
 
+// Counting of a routed token set into the histogram rows of the fused layout + plan path
+// (path.h): the segment's lanes hold the token's slots (KPL per lane, -1 where there is none).
+template <int LPT, int KPL>
+__device__ __forceinline__ void sig_count_token(const PathGeom& g, int eshift, int* row, const int (&e)[KPL],
+                                                int lseg) {
+    uint32_t m1 = 0u, m2 = 0u;
+#pragma unroll
+    for (int q = 0; q < KPL; ++q) {
+        if (e[q] >= 0) {
+            const uint32_t bit = 1u << (e[q] >> eshift);
+            m2 |= m1 & bit;
+            m1 |= bit;
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < KPL; ++q)
+        if (e[q] >= 0) atomicAdd(&row[e[q]], 1);
+    if constexpr (LPT >= 2) {
+        auto step = [&](auto partner) {
+            const uint32_t b1 = partner(m1), b2 = partner(m2);
+            path_mask_merge(m1, m2, b1, b2);
+        };
+        step([](uint32_t u) { return seg_partner_u32<1>(u); });
+        if constexpr (LPT >= 4) step([](uint32_t u) { return seg_partner_u32<2>(u); });
+        if constexpr (LPT >= 8) step([](uint32_t u) { return seg_partner_u32<4>(u); });
+        if constexpr (LPT >= 16) step([](uint32_t u) { return seg_partner_u32<8>(u); });
+    }
+    path_count_ranks(g, row, m1, m2, lseg, LPT);
+}
+
+// Where the routing kernel counts: off (mep_route_topk), or into the rows of the plan tiles it
+// owns, followed by the counting epilogue (the routing phase of the fused path).
+struct SigEpi {
+    int on;
+    int eshift;  // log2(E / R): E = 32 * LPT is a power of two, hence so is every E / R
+    PathGeom g;
+    PathWs w;
+    WsHeader* hdr;
+};
+
+// Dynamic LDS of the kernel: uncertified-token bits per set, then (counting) the tile rows.
+__host__ __device__ constexpr size_t sig_dyn_lds(int64_t sets_per_group, int sub, int nc) {
+    return (size_t)sets_per_group * 4 + (size_t)sub * nc * 4;
+}
+
 // MODE 0: no group limit; MODE 1: lane lseg of a segment is group lseg (n_group == LPT).
-// NW waves per workgroup, each independent after the prologue.  A workgroup owns a contiguous
-// range of sets and its waves take them one at a time from an LDS counter, so a wave that spends
-// time on an uncertified token takes fewer sets and the workgroup still finishes with its peers.
+// NW waves per workgroup.  A workgroup owns the contiguous tokens [t0, t1) -- with counting on,
+// the plan tiles [blockIdx * sub, ...) -- cut into sets of TPW tokens, and its waves take sets one
+// at a time from an LDS counter: every wave requests its first set at once, and a wave whose data
+// arrives early takes more sets, so the workgroup ends when its last set is routed rather than
+// when its slowest wave is.  Uncertified tokens are redone after the loop, spread over all the
+// waves.
 template <int LPT, bool BF16, int MODE, int NW>
-__global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_kernel(RouteArgs a, SigCfg cfg) {
+__global__ __launch_bounds__(64 * NW) void route_sig_kernel(RouteArgs a, SigCfg cfg, SigEpi ep) {
     using G = SigGeom<LPT, BF16>;
     constexpr int W = G::W;
     constexpr int CPL = G::CPL;
@@ -308,6 +357,9 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
     __shared__ u32x4 s_rows[NW][TPW * RS];
     __shared__ float4 s_bsh4[LPT * kFastEPL / 4];  // b - c
     __shared__ float s_bconst[2];                   // constant terms of the two margins
+    __shared__ int s_next;                          // next unclaimed set of this workgroup
+    __shared__ int s_tb[kPathMaxSub + 1];           // token boundaries of the owned plan tiles
+    extern __shared__ uint32_t s_dyn[];
 
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the set loop is not divergent
@@ -315,23 +367,38 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
     const int tw = wl / LPT;
     const int lseg = wl % LPT;
     const int K = a.K;
-    // this workgroup's sets [set_lo, set_hi); wave wv starts with set_lo + wv
-    const int64_t spb = (cfg.nsets + gridDim.x - 1) / gridDim.x;
-    const int64_t set_lo = (int64_t)blockIdx.x * spb;
-    const int64_t set_hi = min(set_lo + spb, cfg.nsets);
-    const int64_t first_set = set_lo + wv;
-    __shared__ int s_next;  // next unclaimed set of this workgroup, relative to set_lo
+    const bool epi = ep.on != 0;
+
+    // ---- this workgroup's tokens (N * K < 2^31, so token indices fit 32 bits) --------------------
+    int t0, t1;
+    int nsub = 0;
+    if (epi) {
+        const int j0 = blockIdx.x * ep.g.sub;
+        nsub = min(ep.g.sub, ep.g.ntiles - j0);
+        int64_t a0, a1, b0, b1;
+        path_tile_tokens(ep.g, j0, a0, a1);
+        path_tile_tokens(ep.g, j0 + nsub - 1, b0, b1);
+        t0 = (int)a0;
+        t1 = (int)b1;
+        if (tid <= nsub) {
+            int64_t c0, c1;
+            path_tile_tokens(ep.g, j0 + min(tid, nsub - 1), c0, c1);
+            s_tb[tid] = (int)(tid < nsub ? c0 : c1);
+        }
+    } else {
+        t0 = blockIdx.x * (int)cfg.tokens_per_group;
+        t1 = (int)min((int64_t)t0 + cfg.tokens_per_group, a.N);
+    }
+    t0 = __builtin_amdgcn_readfirstlane(t0);
+    t1 = __builtin_amdgcn_readfirstlane(t1);
+    const int nsets = (t1 - t0 + TPW - 1) / TPW;
+    uint32_t* s_fail = s_dyn;          // per set: tokens the filter could not certify (bit t)
+    int* s_row = reinterpret_cast<int*>(s_dyn + nsets);  // counting: the tile rows
+    for (int i = tid; i < nsets; i += NT) s_fail[i] = 0u;
+    if (epi)
+        for (int i = tid; i < nsub * ep.g.NC; i += NT) s_row[i] = 0;
     if (tid == 0) s_next = NW;
-    // a copy of the first uncertified token's row (when the LDS budget of four workgroups per CU
-    // leaves room), so the exact pass usually reads no row from global memory
-    constexpr bool kStash = (NW * TPW * RS + LPT * kFastEPL / 4 + CPR) * 16 + 1024 <= 40 * 1024;
-    __shared__ u32x4 s_xrow[kStash ? CPR : 1];
-    __shared__ int s_xtok;  // its token, or -1
-    if (tid == 0) s_xtok = -1;
-    // per set of this workgroup: its tokens that the filter could not certify (bit t = token t);
-    // they are redone exactly after the streaming loop, so the loop holds no call
-    extern __shared__ uint32_t s_fail[];
-    for (int i = tid; i < (int)(set_hi - set_lo); i += NT) s_fail[i] = 0u;
+    const uint32_t pcall = epi ? path_count_begin(ep.hdr) : 0u;
 
     // the bias first (so that waiting for it does not also wait for the logits), then the first set
     constexpr int BPL = LPT * NE / 64;  // bias entries per lane
@@ -340,10 +407,22 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
 #pragma unroll
     for (int i = 0; i < BPL; ++i) bv[i] = gb[i * 64 + wl];
     __builtin_amdgcn_sched_barrier(0);  // keep the bias loads ahead of the logits loads
+    const MEP_GLOBAL u32x4* lbase = gptr(reinterpret_cast<const u32x4*>(a.logits));
+    // the CPL coalesced 16-byte loads of the set starting at token ts (rows past t1 re-read row
+    // t1 - 1); a wave without a set of its own loads set 0 again, unused, so that the loads in
+    // flight are the same on every path into the loop
+    auto load_set = [&](int set, u32x4 (&b)[CPL]) {
+        const int ts = t0 + set * TPW;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int q = c * 64 + wl;
+            const int r = q / CPR;
+            const int t = min(ts + r, t1 - 1);
+            b[c] = lbase[(int64_t)t * CPR + (q - r * CPR)];
+        }
+    };
     u32x4 buf[CPL];
-    // (a wave without a set of its own loads the workgroup's last one, unused, so that the loads
-    // in flight are the same on every path into the loop)
-    fast_load_set<LPT, BF16>(a, min(first_set, max(set_hi - 1, (int64_t)0)), wl, buf);
+    load_set(wv < nsets ? wv : 0, buf);
 
     // ---- shift c, the error-bound constants, and the shifted biases --------------------------------
     float mb = 0.0f;
@@ -406,8 +485,8 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
         }
     };
 
-    int64_t next_set = first_set;
-    for (int64_t set = first_set; set < set_hi; set = next_set) {
+    int next_set = wv;
+    for (int set = wv; set < nsets; set = next_set) {
         // ---- registers -> this wave's LDS rows; refill with the next set --------------------------
         wave_lds_sync();
 #pragma unroll
@@ -419,14 +498,14 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
         {
             int claimed = 0;
             if (wl == 0) claimed = atomicAdd(&s_next, 1);
-            next_set = set_lo + __builtin_amdgcn_readfirstlane(claimed);
+            next_set = __builtin_amdgcn_readfirstlane(claimed);
         }
-        if (next_set < set_hi) fast_load_set<LPT, BF16>(a, next_set, wl, buf);
+        if (next_set < nsets) load_set(next_set, buf);
         wave_lds_sync();
 
-        const int tok_raw = (int)set * TPW + tw;  // N * K < 2^31
-        const bool live = tok_raw < (int)a.N;
-        const int tok = live ? tok_raw : (int)a.N - 1;
+        const int tok_raw = t0 + set * TPW + tw;
+        const bool live = tok_raw < t1;
+        const int tok = live ? tok_raw : t1 - 1;
         const float b_gap = lds_volatile_load(&s_bconst[0]);
         const float b_grp = lds_volatile_load(&s_bconst[1]);
 
@@ -469,7 +548,7 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
         // so no round depends on a run-time condition.  `slot_bits` marks this lane's output slots;
         // it is derived from the set index (the shift is always 0) so that the compiler forms the
         // per-round lane tests inside the loop instead of hoisting them all into scalar registers.
-        const uint32_t slot_bits = (1u << lseg) << (uint32_t)(set >> 40);
+        const uint32_t slot_bits = (1u << lseg) << (uint32_t)(set >> 30);
         uint32_t wm = 0;      // rounds this lane won
         uint32_t gapbad = 0;  // rounds whose value is too close to the previous one
         int myM[KPL];         // value extracted in round lseg + q * LPT
@@ -539,45 +618,51 @@ __global__ __launch_bounds__(64 * NW, (LPT == 2 ? 12 : 16) / NW) void route_sig_
                 }
             }
         }
+        // ---- counting (fused path): certified live tokens now, the others after the exact pass ----
+        if (epi) {
+            int ce[KPL];
+#pragma unroll
+            for (int q = 0; q < KPL; ++q) ce[q] = (live && !fail && lseg + q * LPT < K) ? my_e[q] : -1;
+            int ri = 0;
+            while (ri + 1 < nsub && tok >= s_tb[ri + 1]) ++ri;
+            sig_count_token<LPT, KPL>(ep.g, ep.eshift, s_row + ri * ep.g.NC, ce, lseg);
+        }
 
         // ---- uncertified tokens: recorded for the exact pass after the loop ------------------------
         const uint64_t fm = __ballot(fail && live && lseg == 0);
-        if (fm != 0ull) {
-            if (wl == 0) {
-                uint32_t m = 0u;
+        if (fm != 0ull && wl == 0) {
+            uint32_t m = 0u;
 #pragma unroll
-                for (int t = 0; t < TPW; ++t) m |= (uint32_t)((fm >> (t * LPT)) & 1ull) << t;
-                s_fail[set - set_lo] = m;
-            }
-            if constexpr (kStash) {
-                const int t0 = __builtin_ctzll(fm) / LPT;
-                int won = 0;
-                if (wl == 0) won = atomicCAS(&s_xtok, -1, (int)(set * TPW + t0)) == -1;
-                if (__builtin_amdgcn_readfirstlane(won)) {
-                    for (int ch = wl; ch < CPR; ch += 64) s_xrow[ch] = my_rows[t0 * RS + G::pos(ch)];
-                }
-            }
+            for (int t = 0; t < TPW; ++t) m |= (uint32_t)((fm >> (t * LPT)) & 1ull) << t;
+            s_fail[set] = m;
         }
     }
 
     // ---- uncertified tokens of this workgroup's sets: exact, one token per wave in turn ----------
     __syncthreads();
     int idx = 0;
-    for (int i = 0; i < (int)(set_hi - set_lo); ++i) {
+    for (int i = 0; i < nsets; ++i) {
         uint32_t m = s_fail[i];
         while (m) {
             const int t = __builtin_ctz(m);
             m &= m - 1u;
             if (idx % NW == wv) {
-                const int64_t tok = (set_lo + i) * TPW + t;
-                const bool stashed = kStash && tok == (int64_t)s_xtok;
+                const int tok = t0 + i * TPW + t;
+                int sel[1];
                 exact_token_sig<LPT, BF16, MODE>(a.logits, a.bias, a.ids, a.weights, K, a.group_topn,
-                                                 a.renormalize, a.scale, tok, cfg.tg, wl,
-                                                 stashed ? s_xrow : nullptr);
+                                                 a.renormalize, a.scale, tok, cfg.tg, wl, nullptr, sel);
+                if (epi) {
+                    int ri = 0;
+                    while (ri + 1 < nsub && tok >= s_tb[ri + 1]) ++ri;
+                    int ce[1] = {wl < K ? sel[0] : -1};
+                    // the token's slots are on lanes 0..K-1 (K <= 8): an 8-lane segment
+                    if (wl < 8) sig_count_token<8, 1>(ep.g, ep.eshift, s_row + ri * ep.g.NC, ce, wl);
+                }
             }
             ++idx;
         }
     }
+    if (epi) path_epilogue<NT>(ep.g, ep.w, pcall, s_row);
 }
 
 }  // namespace mep

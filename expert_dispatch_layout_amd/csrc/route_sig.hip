@@ -1,37 +1,85 @@
-// Shape dispatch of the sigmoid routing kernel (route_sig.h).
+// Shape dispatch of the sigmoid routing kernel (route_sig.h): plain routing (mep_route_topk) and
+// routing that also counts the plan tiles it owns (the routing phase of the fused path).
+#include <mutex>
+
 #include "route_sig.h"
 
 namespace mep {
 
+namespace {
+
+constexpr int kSigWaves = 16;        // one workgroup of 16 waves per compute unit
+constexpr size_t kLdsLimit = 160 * 1024;
+
+int device_units() {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// Static LDS of a kernel (bytes).
+size_t static_lds(const void* kernel) {
+    hipFuncAttributes attr;
+    if (hipFuncGetAttributes(&attr, kernel) != hipSuccess) return kLdsLimit;
+    return attr.sharedSizeBytes;
+}
+
 template <int LPT, bool BF16, int MODE>
-static void launch_sig(const RouteArgs& a, const Launch& st) {
+bool launch_sig(const RouteArgs& a, const Launch& st, const PathCall* pc) {
+    constexpr int TPW = SigGeom<LPT, BF16>::TPW;
+    auto kernel = route_sig_kernel<LPT, BF16, MODE, kSigWaves>;
     SigCfg cfg;
-    cfg.nsets = ceil_div64(a.N, FastGeom<LPT, BF16>::TPW);
     cfg.tg = MODE == 1 ? a.topk_group : LPT;
-    constexpr int NW = 2;  // waves per workgroup: 2 measured ahead of 4 and 8 at the dsv3 batch
-    auto kernel = route_sig_kernel<LPT, BF16, MODE, NW>;
-    const int64_t need = ceil_div64(cfg.nsets, NW);
-    int64_t grid = resident_blocks(reinterpret_cast<const void*>(kernel), 64 * NW);
-    // more workgroups than fit at once when a workgroup would own more sets than its LDS list of
-    // uncertified tokens holds
-    if (grid < ceil_div64(cfg.nsets, kSigMaxSetsPerGroup)) grid = ceil_div64(cfg.nsets, kSigMaxSetsPerGroup);
-    if (grid > need) grid = need;
-    if (grid < 1) grid = 1;
-    const int64_t spb = ceil_div64(cfg.nsets, grid);  // sets per workgroup (as the kernel computes)
-    launch_kernel(kernel, dim3((unsigned)grid), dim3(64 * NW), (uint32_t)(spb * sizeof(uint32_t)), st, a, cfg);
+    SigEpi ep{};
+    int64_t grid;
+    size_t dyn;
+    if (pc) {
+        const PathGeom& g = pc->g;
+        // sets of the largest workgroup: sub tiles of at most T tokens each
+        const int64_t sets = ceil_div64((int64_t)g.sub * g.T, TPW);
+        dyn = sig_dyn_lds(sets, g.sub, g.NC);
+        grid = g.nwg;
+        ep.on = 1;
+        ep.eshift = 0;
+        while ((1 << ep.eshift) < g.epn) ++ep.eshift;
+        ep.g = g;
+        ep.w = pc->w;
+        ep.hdr = pc->hdr;
+        cfg.tokens_per_group = 0;
+    } else {
+        const int64_t nsets = ceil_div64(a.N, TPW);
+        grid = device_units();
+        if (grid > nsets) grid = nsets;
+        const int64_t sets = ceil_div64(nsets, grid);
+        cfg.tokens_per_group = sets * TPW;
+        grid = ceil_div64(a.N, cfg.tokens_per_group);
+        dyn = sig_dyn_lds(sets, 0, 0);
+        ep.on = 0;
+    }
+    if (static_lds(reinterpret_cast<const void*>(kernel)) + dyn > kLdsLimit) return false;
+    launch_kernel(kernel, dim3((unsigned)grid), dim3(64 * kSigWaves), (uint32_t)dyn, st, a, cfg, ep);
+    return true;
 }
 
 template <bool BF16, int MODE>
-static void launch_sig_lpt(int LPT, const RouteArgs& a, const Launch& st) {
+bool launch_sig_lpt(int LPT, const RouteArgs& a, const Launch& st, const PathCall* pc) {
     switch (LPT) {
-        case 2: launch_sig<2, BF16, MODE>(a, st); break;
-        case 4: launch_sig<4, BF16, MODE>(a, st); break;
-        case 8: launch_sig<8, BF16, MODE>(a, st); break;
-        default: launch_sig<16, BF16, MODE>(a, st); break;
+        case 2: return launch_sig<2, BF16, MODE>(a, st, pc);
+        case 4: return launch_sig<4, BF16, MODE>(a, st, pc);
+        case 8: return launch_sig<8, BF16, MODE>(a, st, pc);
+        default: return launch_sig<16, BF16, MODE>(a, st, pc);
     }
 }
 
-bool launch_route_sig(const RouteArgs& a, int dtype, const Launch& st) {
+bool route_sig_dispatch(const RouteArgs& a, int dtype, const Launch& st, const PathCall* pc) {
     if (a.score_fn != MEP_SIGMOID || !a.vec || a.K > 8 || a.E % kFastEPL != 0) return false;
     const int LPT = a.E / kFastEPL;
     if (LPT != 2 && LPT != 4 && LPT != 8 && LPT != 16) return false;
@@ -40,14 +88,18 @@ bool launch_route_sig(const RouteArgs& a, int dtype, const Launch& st) {
     else if (a.n_group == LPT) mode = 1;
     else return false;
     const bool bf16 = dtype == MEP_BF16;
-    if (bf16) {
-        if (mode == 0) launch_sig_lpt<true, 0>(LPT, a, st);
-        else launch_sig_lpt<true, 1>(LPT, a, st);
-    } else {
-        if (mode == 0) launch_sig_lpt<false, 0>(LPT, a, st);
-        else launch_sig_lpt<false, 1>(LPT, a, st);
-    }
-    return true;
+    if (bf16) return mode == 0 ? launch_sig_lpt<true, 0>(LPT, a, st, pc) : launch_sig_lpt<true, 1>(LPT, a, st, pc);
+    return mode == 0 ? launch_sig_lpt<false, 0>(LPT, a, st, pc) : launch_sig_lpt<false, 1>(LPT, a, st, pc);
+}
+
+}  // namespace
+
+bool launch_route_sig(const RouteArgs& a, int dtype, const Launch& st) {
+    return route_sig_dispatch(a, dtype, st, nullptr);
+}
+
+bool launch_route_sig_counting(const RouteArgs& a, int dtype, const Launch& st, const PathCall& pc) {
+    return route_sig_dispatch(a, dtype, st, &pc);
 }
 
 }  // namespace mep

@@ -22,6 +22,7 @@
 
 #include "calls.h"
 #include "host_common.h"
+#include "path.h"
 #include "route_common.h"
 
 namespace mep {
@@ -388,12 +389,12 @@ namespace mep {
 namespace {
 
 template <int LPT, int NV, bool BF16>
-void launch_small(const SmallArgs& sa, hipStream_t st) {
-    hipLaunchKernelGGL((small_path_kernel<LPT, NV, BF16>), dim3(1), dim3(kSmBlock), 0, st, sa);
+void launch_small(const SmallArgs& sa, const Launch& st) {
+    launch_kernel(small_path_kernel<LPT, NV, BF16>, dim3(1), dim3(kSmBlock), 0, st, sa);
 }
 
 template <bool BF16>
-bool dispatch_small(const SmallArgs& sa, hipStream_t st) {
+bool dispatch_small(const SmallArgs& sa, const Launch& st) {
     constexpr int W = BF16 ? 8 : 4;
     const int nchunks = (sa.ra.E + W - 1) / W;
     if (nchunks <= 1) launch_small<1, 1, BF16>(sa, st);
@@ -411,14 +412,19 @@ bool dispatch_small(const SmallArgs& sa, hipStream_t st) {
 
 }  // namespace mep
 
-extern "C" int mep_route_layout_plan(const void* logits, int dtype, int64_t N, int E, int K, const float* bias,
-                                     const mep_route_params* p, int32_t* topk_ids, float* topk_weights,
-                                     int alignment, int32_t* tokens_per_expert, int32_t* cu_seqlens,
-                                     int32_t* expanded_to_permuted, int32_t* permuted_to_expanded,
-                                     int64_t permuted_cap, int32_t* zero_fill, int R, int num_src,
-                                     int num_channels, int64_t NvS, const mep_plan_outputs* out, void* ws,
-                                     size_t ws_bytes, void* stream) {
-    using namespace mep;
+namespace mep {
+
+// The whole path in one call: the one-workgroup kernel for small batches, else the routing kernel
+// (counting the plan tiles itself where it can), then the plan-tile kernel of the fused path; or
+// the routing kernel followed by mep_layout_plan's kernels where the fused path does not cover
+// the shape.  `ev` optionally stamps the routing kernel (or the single small kernel) and the
+// plan-tile kernel with their start and end times.
+int route_layout_plan(const void* logits, int dtype, int64_t N, int E, int K, const float* bias,
+                      const mep_route_params* p, int32_t* topk_ids, float* topk_weights, int alignment,
+                      int32_t* tokens_per_expert, int32_t* cu_seqlens, int32_t* expanded_to_permuted,
+                      int32_t* permuted_to_expanded, int64_t permuted_cap, int32_t* zero_fill, int R, int num_src,
+                      int num_channels, int64_t NvS, const mep_plan_outputs* out, void* ws, size_t ws_bytes,
+                      void* stream, const StepEvents& ev) {
     if (N > 0 && !topk_ids) return MEP_ERR_INVALID_ARG;
     SmallArgs sa;
     int rc = route_prepare(logits, dtype, N, E, K, bias, p, topk_ids, topk_weights, sa.ra);
@@ -441,13 +447,59 @@ extern "C" int mep_route_layout_plan(const void* logits, int dtype, int64_t N, i
         sa.lo = lc.out;
         sa.g = pc.g;
         sa.po = pc.o;
-        const bool ok = dtype == MEP_BF16 ? dispatch_small<true>(sa, st) : dispatch_small<false>(sa, st);
+        const Launch sl{st, ev.route_start, ev.route_stop};
+        const bool ok = dtype == MEP_BF16 ? dispatch_small<true>(sa, sl) : dispatch_small<false>(sa, sl);
         if (ok) return launch_status();
     }
-    // larger batches: the routing kernel, then the layout and plan kernels
-    rc = mep_route_topk(logits, dtype, N, E, K, bias, p, topk_ids, topk_weights, stream);
-    if (rc != MEP_OK) return rc;
-    return mep_layout_plan(topk_ids, N, E, K, alignment, tokens_per_expert, cu_seqlens, expanded_to_permuted,
-                           permuted_to_expanded, permuted_cap, zero_fill, R, num_src, num_channels, NvS, out, ws,
-                           ws_bytes, stream);
+    const Launch rl{st, ev.route_start, ev.route_stop};
+    if (path_supported(N, E, K, R)) {
+        const PathCall c = path_call(lc, pc, ws);
+        if (!launch_route_sig_counting(sa.ra, dtype, rl, c)) {
+            rc = route_launch(sa.ra, dtype, rl);
+            if (rc != MEP_OK) return rc;
+            path_launch_count(c, st);
+        }
+        path_launch_plan(c, st, ev.plan_start, ev.plan_stop);
+        return launch_status();
+    }
+    // shapes outside the fused path: the routing kernel, then the layout and plan kernels
+    if (N > 0) {
+        rc = route_launch(sa.ra, dtype, rl);
+        if (rc != MEP_OK) return rc;
+    }
+    plan_launch_count(pc, st);
+    plan_launch_scatter_write(lc, pc, st);
+    return launch_status();
+}
+
+}  // namespace mep
+
+extern "C" int mep_route_layout_plan(const void* logits, int dtype, int64_t N, int E, int K, const float* bias,
+                                     const mep_route_params* p, int32_t* topk_ids, float* topk_weights,
+                                     int alignment, int32_t* tokens_per_expert, int32_t* cu_seqlens,
+                                     int32_t* expanded_to_permuted, int32_t* permuted_to_expanded,
+                                     int64_t permuted_cap, int32_t* zero_fill, int R, int num_src,
+                                     int num_channels, int64_t NvS, const mep_plan_outputs* out, void* ws,
+                                     size_t ws_bytes, void* stream) {
+    return mep::route_layout_plan(logits, dtype, N, E, K, bias, p, topk_ids, topk_weights, alignment,
+                                  tokens_per_expert, cu_seqlens, expanded_to_permuted, permuted_to_expanded,
+                                  permuted_cap, zero_fill, R, num_src, num_channels, NvS, out, ws, ws_bytes, stream,
+                                  mep::StepEvents{});
+}
+
+extern "C" int mep_route_layout_plan_timed(const void* logits, int dtype, int64_t N, int E, int K,
+                                           const float* bias, const mep_route_params* p, int32_t* topk_ids,
+                                           float* topk_weights, int alignment, int32_t* tokens_per_expert,
+                                           int32_t* cu_seqlens, int32_t* expanded_to_permuted,
+                                           int32_t* permuted_to_expanded, int64_t permuted_cap, int32_t* zero_fill,
+                                           int R, int num_src, int num_channels, int64_t NvS,
+                                           const mep_plan_outputs* out, void* ws, size_t ws_bytes, void* stream,
+                                           void* route_start, void* route_stop, void* plan_start,
+                                           void* plan_stop) {
+    const mep::StepEvents ev{reinterpret_cast<hipEvent_t>(route_start), reinterpret_cast<hipEvent_t>(route_stop),
+                             reinterpret_cast<hipEvent_t>(plan_start), reinterpret_cast<hipEvent_t>(plan_stop)};
+    return mep::route_layout_plan(logits, dtype, N, E, K, bias, p, topk_ids, topk_weights, alignment,
+                                  tokens_per_expert, cu_seqlens, expanded_to_permuted, permuted_to_expanded,
+                                  permuted_cap, zero_fill, R, num_src, num_channels, NvS, out, ws, ws_bytes, stream,
+                                  ev);
 }

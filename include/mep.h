@@ -14,7 +14,8 @@
  *   mep_layout_plan  the two calls above in one (two kernels instead of
  *                    four)
  *   mep_route_layout_plan
- *                    all three in one call; one kernel for small batches
+ *                    all three in one call; one kernel for small batches,
+ *                    two for large ones (the routing kernel also counts)
  *   mep_tile_map     per-expert counts -> grouped-GEMM tile maps (the expert
  *                    and the row limit of every padded tile)
  *   mep_plan_balanced the plan with capacity rebalancing: token moves between
@@ -260,16 +261,26 @@ size_t mep_plan_workspace_size(int64_t N, int E, int K, int R, int num_src);
  * mep_layout_plan -- mep_build_layout followed by mep_plan in one call, with
  * the results of the two calls and the checks of both (the layout's
  * cu_seqlens and expanded_to_permuted are outputs of the first part and inputs
- * of the second, so both are required).  Two kernels instead of four: the
- * plan's counting pass also produces the per-expert totals and prefixes the
- * layout needs, so the layout's own counting pass is not run, and one kernel
- * both scatters the layout and writes the plan.
+ * of the second, so both are required).
+ *
+ * Two kernels.  With K <= 8, R <= 32 and E <= 512 (and N > 0): a counting
+ * kernel takes each plan tile's histogram of experts and rank columns
+ * ([TRT] routingIndicesHistogramKernel; [DEEP] notify_dispatch counts) and
+ * leaves per-tile, per-workgroup and per-group partial sums, without any
+ * workgroup waiting for another; a plan-tile kernel then forms every prefix it
+ * needs from those sums, writes the padded offsets ([MOON] Phase B2) and
+ * scatters its tile stably ([MOON] run_c1 passA) while writing that tile's
+ * part of the plan.  Other shapes: the plan's count-tile kernels, with one
+ * kernel scattering the layout and writing the plan.
  *
  * Arguments as mep_build_layout (without its workspace) and mep_plan; `ws` is
  * a workspace of mep_plan_workspace_size(N, E, K, R, num_src) bytes, the only
  * scratch of the call, with the rules of every workspace (zero-filled before
- * first use, calls sharing it ordered).  It may be shared with mep_plan calls
- * but not with mep_build_layout calls.
+ * first use, calls sharing it ordered).  It may be shared with mep_plan and
+ * mep_route_layout_plan calls of any size, not with mep_build_layout calls.
+ * Word 3 of the workspace (uint32 at byte 12) holds sticky error bits: it
+ * stays 0 unless a bounded wait of the count-tile kernels ran out, which only
+ * overlapping calls on one workspace can cause.
  */
 int mep_layout_plan(const int32_t* topk_ids, int64_t N, int E, int K, int alignment,
                     int32_t* tokens_per_expert, int32_t* cu_seqlens,
@@ -441,10 +452,14 @@ int mep_combine_rows(const void* y_permuted, int dtype, int64_t N, int64_t H, in
  * second launch): N*K <= 2048, E <= 256, K <= 8, R <= 8,
  * num_src*E <= 4096 and num_src*R*num_channels <= 4096.  That kernel routes
  * every token exactly (no fast-path certification to fail), keeps ids and
- * permuted positions in LDS, and uses no workspace.  Other batches take the
- * three kernels of the two calls.  Either way the outputs equal those of
- * mep_route_topk followed by mep_layout_plan; `ws` must satisfy
- * mep_layout_plan's rules in both cases.
+ * permuted positions in LDS, and uses no workspace.  Larger batches: where
+ * mep_layout_plan takes two kernels (K <= 8, R <= 32, E <= 512) and the
+ * sigmoid routing kernel covers the shape (E = 64, 128, 256 or 512, one
+ * group of 32 experts per lane or no group limit), the routing kernel also
+ * counts the plan tiles it routes, so the whole path is two kernels; else the
+ * routing kernel is followed by mep_layout_plan's kernels.  Either way the
+ * outputs equal those of mep_route_topk followed by mep_layout_plan; `ws` must
+ * satisfy mep_layout_plan's rules in both cases.
  */
 int mep_route_layout_plan(const void* logits, int dtype, int64_t N, int E, int K,
                           const float* bias, const mep_route_params* p, int32_t* topk_ids,
@@ -453,6 +468,27 @@ int mep_route_layout_plan(const void* logits, int dtype, int64_t N, int E, int K
                           int32_t* permuted_to_expanded, int64_t permuted_cap, int32_t* zero_fill,
                           int R, int num_src, int num_channels, int64_t NvS,
                           const mep_plan_outputs* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mep_route_layout_plan_timed -- mep_route_layout_plan with kernel timing.
+ *
+ * Computes exactly what mep_route_layout_plan computes (same arguments, checks
+ * and errors).  The four events (hipEvent_t created by the caller, each may be
+ * NULL) are updated by kernel launches themselves (hipExtLaunchKernel), with no
+ * marker packet on the stream: route_start / route_stop with the start and end
+ * of the routing kernel (of the single kernel of a small batch), plan_start /
+ * plan_stop with those of the plan-tile kernel of the fused path (left
+ * untouched by small batches and by shapes outside the fused path).  For
+ * measuring the kernels in place inside a stream of work.
+ */
+int mep_route_layout_plan_timed(const void* logits, int dtype, int64_t N, int E, int K,
+                                const float* bias, const mep_route_params* p, int32_t* topk_ids,
+                                float* topk_weights, int alignment, int32_t* tokens_per_expert,
+                                int32_t* cu_seqlens, int32_t* expanded_to_permuted,
+                                int32_t* permuted_to_expanded, int64_t permuted_cap, int32_t* zero_fill,
+                                int R, int num_src, int num_channels, int64_t NvS,
+                                const mep_plan_outputs* out, void* ws, size_t ws_bytes, void* stream,
+                                void* route_start, void* route_stop, void* plan_start, void* plan_stop);
 
 /* Static, NUL-terminated name of a return code. */
 const char* mep_status_string(int code);

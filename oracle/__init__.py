@@ -114,6 +114,39 @@ class Layout:
     zero_fill: np.ndarray
 
 
+def route_threads(logits: np.ndarray, K: int, nthreads: int, **kw):
+    """route() with the tokens split into `nthreads` contiguous ranges, each routed by the same
+    C routine on its own thread (ctypes releases the GIL during the call).  Tokens are
+    independent, so the result equals route()'s."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    dtype = kw.get("dtype", F32)
+    logits = np.ascontiguousarray(logits)
+    assert logits.dtype == (np.float32 if dtype == F32 else np.uint16)
+    N, E = logits.shape
+    ids = np.empty((N, K), dtype=np.int32)
+    w = np.empty((N, K), dtype=np.float32)
+    bias = kw.get("bias")
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    bounds = [N * i // nthreads for i in range(nthreads + 1)]
+
+    def one(i):
+        lo, hi = bounds[i], bounds[i + 1]
+        if hi <= lo:
+            return 0
+        return lib().oracle_route(_p(logits[lo:hi]), dtype, hi - lo, E, K, _p(b),
+                                  kw.get("score_fn", SOFTMAX), int(kw.get("renormalize", True)),
+                                  kw.get("n_group", 1), kw.get("topk_group", 1),
+                                  kw.get("group_topn", 2), float(kw.get("scale", 1.0)),
+                                  _p(ids[lo:hi]), _p(w[lo:hi]))
+
+    with ThreadPoolExecutor(max_workers=nthreads) as ex:
+        rcs = list(ex.map(one, range(nthreads)))
+    if any(rc != 0 for rc in rcs):
+        raise ValueError("oracle_route rejected the arguments (codes %s)" % rcs)
+    return ids, w
+
+
 def layout(ids: np.ndarray, E: int, alignment: int) -> Layout:
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     N, K = ids.shape

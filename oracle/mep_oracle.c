@@ -58,8 +58,9 @@ static float logit_at(const void* logits, int dtype, int64_t i) {
     return bf16_to_float(((const uint16_t*)logits)[i]);
 }
 
-/* Which path decided the last sigmoid: 1 = double, 2 = quad. For tests. */
-static int g_sigmoid_path = 0;
+/* Which path decided the last sigmoid on this thread: 1 = double, 2 = quad.  For tests.
+ * Thread-local, so routing calls on separate token ranges may run in parallel threads. */
+static _Thread_local int g_sigmoid_path = 0;
 
 /*
  * Logistic sigmoid 1/(1+exp(-x)), correctly rounded to binary32.

@@ -51,15 +51,32 @@ def test_workspace_sizes():
     def a256(x):
         return (x + 255) // 256 * 256
 
+    # every plan workspace first reserves the fused path's two buffers of group sums (64 groups
+    # x (512 + 3 * 32) columns of u32 each) right after the header
+    gsum = 2 * 64 * (512 + 96) * 4
+
     # 65536 tokens, K = 8: 256 tiles of 256 tokens (halved), 8 per count tile, 32 count tiles
-    want = 256 + 2048 * 4 + a256(32 * 24 * 8) + a256(32 * 256 * 8) + a256(256 * (24 + 256) * 8)
+    old = (256 + gsum + 2048 * 4 + a256(32 * 24 * 8) + a256(32 * 256 * 8)
+           + a256(256 * (24 + 256) * 8))
+
+    # the fused path's plan tiles (2048 slots: 256 tokens at K = 8, never crossing a shard),
+    # counting workgroups of `sub` tiles (about 256 of them): header, group sums, the count-tile
+    # counters of mep_plan, then the workgroup totals and the within-workgroup tile prefixes
+    # (E + 3R columns, 256-aligned parts)
+    def path(ntiles, sub, nc):
+        nwg = -(-ntiles // sub)
+        return 256 + gsum + 8192 + a256(nwg * nc * 4) + a256(ntiles * nc * 4)
+
+    want = max(old, path(256, 1, 256 + 24))
     assert B.plan_workspace_size(65536, 256, 8, 8, 8) == want
     assert B.plan_workspace_size(65536, 256, 8, 8, 1) == want
     # 262144 tokens over 32 shards: halving would give 1024 tiles, so 512 tiles of 512 tokens
-    # stay, 16 per count tile (one per shard), 32 count tiles
-    want = (256 + 2048 * 4 + a256(32 * 96 * 8) + a256(32 * 256 * 8)
-            + a256(512 * (96 + 256) * 8))
-    assert B.plan_workspace_size(262144, 256, 8, 32, 32) == want
+    # stay, 16 per count tile (one per shard), 32 count tiles; the fused path has 1024 tiles of
+    # 256 tokens, 4 per counting workgroup
+    old = (256 + gsum + 2048 * 4 + a256(32 * 96 * 8) + a256(32 * 256 * 8)
+           + a256(512 * (96 + 256) * 8))
+    assert B.plan_workspace_size(262144, 256, 8, 32, 32) == max(old, path(1024, 4, 256 + 96))
+
 
 FAKE = 0x10000          # aligned, never dereferenced
 MIS = 0x10004           # 4-aligned but not 16-aligned

@@ -55,7 +55,8 @@ class BalancedOutputs(ctypes.Structure):
 
 EXPORTS = ("mep_route_topk", "mep_route_topk_timed", "mep_build_layout", "mep_layout_workspace_size", "mep_plan",
            "mep_plan_workspace_size", "mep_layout_plan", "mep_route_layout_plan",
-           "mep_route_layout_plan_timed", "mep_tile_map", "mep_plan_balanced", "mep_permute_rows",
+           "mep_route_layout_plan_timed", "mep_route_layout_plan_noalloc", "mep_tile_map",
+           "mep_plan_balanced", "mep_permute_rows",
            "mep_combine_rows", "mep_status_string")
 
 _lib = None
@@ -97,6 +98,8 @@ def lib():
                 L.mep_route_layout_plan.restype = I
                 L.mep_route_layout_plan_timed.argtypes = L.mep_route_layout_plan.argtypes + [P, P, P, P]
                 L.mep_route_layout_plan_timed.restype = I
+                L.mep_route_layout_plan_noalloc.argtypes = L.mep_route_layout_plan.argtypes[:21] + [P]
+                L.mep_route_layout_plan_noalloc.restype = I
                 L.mep_plan_balanced.argtypes = [P, P, P, P, I64, I, I, I, I, I, I64, I64,
                                                 ctypes.POINTER(BalancedOutputs), P]
                 L.mep_plan_balanced.restype = I
@@ -372,6 +375,7 @@ def _layout_plan_args(topk_ids, E, alignment, layout, R, num_src, num_channels, 
 def _route_layout_plan_args(logits, K, bias, params, topk_ids, topk_weights, alignment, layout, R,
                             num_src, num_channels, NvS, po, ws, stream):
     _require_cuda(logits, bias, topk_ids, topk_weights, ws)
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     if logits.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("logits must be float32 or bfloat16")
     dtype = MEP_BF16 if logits.dtype == torch.bfloat16 else MEP_F32
@@ -381,7 +385,7 @@ def _route_layout_plan_args(logits, K, bias, params, topk_ids, topk_weights, ali
             _ptr(topk_weights), alignment, _ptr(layout.tokens_per_expert), _ptr(layout.cu_seqlens),
             _ptr(layout.expanded_to_permuted), _ptr(layout.permuted_to_expanded), cap,
             _ptr(layout.zero_fill), R, num_src, num_channels, NvS, ctypes.byref(po), _ptr(ws),
-            ws.numel() * ws.element_size(), _stream(stream))
+            ws_bytes, _stream(stream))
 
 
 def mep_route_layout_plan(logits, K, bias, params, topk_ids, topk_weights, alignment,
@@ -393,6 +397,17 @@ def mep_route_layout_plan(logits, K, bias, params, topk_ids, topk_weights, align
         logits, K, bias, params, topk_ids, topk_weights, alignment, layout, R, num_src,
         num_channels, NvS, po, ws, stream))
     _check(rc, "mep_route_layout_plan")
+
+
+def mep_route_layout_plan_noalloc(logits, K, bias, params, topk_ids, topk_weights, alignment,
+                                  layout: "LayoutTensors", R, num_src, num_channels, NvS,
+                                  outputs: "PlanTensors", stream=None):
+    """mep_route_layout_plan with the library's own per-GPU workspace (allocates nothing)."""
+    po = outputs.as_struct()
+    args = _route_layout_plan_args(logits, K, bias, params, topk_ids, topk_weights, alignment,
+                                   layout, R, num_src, num_channels, NvS, po, None, stream)
+    rc = lib().mep_route_layout_plan_noalloc(*(args[:21] + args[23:]))
+    _check(rc, "mep_route_layout_plan_noalloc")
 
 
 def bound_route_layout_plan(logits, K, bias, params, topk_ids, topk_weights, alignment,

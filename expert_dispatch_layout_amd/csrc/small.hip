@@ -418,13 +418,14 @@ namespace mep {
 // (counting the plan tiles itself where it can), then the plan-tile kernel of the fused path; or
 // the routing kernel followed by mep_layout_plan's kernels where the fused path does not cover
 // the shape.  `ev` optionally stamps the routing kernel (or the single small kernel) and the
-// plan-tile kernel with their start and end times.
+// plan-tile kernel with their start and end times.  With `validate_only` every check runs and
+// nothing is enqueued (the workspace pointer is checked, never dereferenced).
 int route_layout_plan(const void* logits, int dtype, int64_t N, int E, int K, const float* bias,
                       const mep_route_params* p, int32_t* topk_ids, float* topk_weights, int alignment,
                       int32_t* tokens_per_expert, int32_t* cu_seqlens, int32_t* expanded_to_permuted,
                       int32_t* permuted_to_expanded, int64_t permuted_cap, int32_t* zero_fill, int R, int num_src,
                       int num_channels, int64_t NvS, const mep_plan_outputs* out, void* ws, size_t ws_bytes,
-                      void* stream, const StepEvents& ev) {
+                      void* stream, const StepEvents& ev, bool validate_only) {
     if (N > 0 && !topk_ids) return MEP_ERR_INVALID_ARG;
     SmallArgs sa;
     int rc = route_prepare(logits, dtype, N, E, K, bias, p, topk_ids, topk_weights, sa.ra);
@@ -436,7 +437,7 @@ int route_layout_plan(const void* logits, int dtype, int64_t N, int E, int K, co
     LayoutCall lc;
     rc = layout_prepare_outputs(topk_ids, N, E, K, alignment, tokens_per_expert, cu_seqlens, expanded_to_permuted,
                                 permuted_to_expanded, permuted_cap, zero_fill, lc);
-    if (rc != MEP_OK) return rc;
+    if (rc != MEP_OK || validate_only) return rc;
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const int64_t NK = N * (int64_t)K;
     const bool small = N > 0 && NK <= kSmMaxSlots && E <= kSmMaxE && K <= kSmKMax && R <= kSmMaxR &&
@@ -484,7 +485,7 @@ extern "C" int mep_route_layout_plan(const void* logits, int dtype, int64_t N, i
     return mep::route_layout_plan(logits, dtype, N, E, K, bias, p, topk_ids, topk_weights, alignment,
                                   tokens_per_expert, cu_seqlens, expanded_to_permuted, permuted_to_expanded,
                                   permuted_cap, zero_fill, R, num_src, num_channels, NvS, out, ws, ws_bytes, stream,
-                                  mep::StepEvents{});
+                                  mep::StepEvents{}, false);
 }
 
 extern "C" int mep_route_layout_plan_timed(const void* logits, int dtype, int64_t N, int E, int K,
@@ -501,5 +502,5 @@ extern "C" int mep_route_layout_plan_timed(const void* logits, int dtype, int64_
     return mep::route_layout_plan(logits, dtype, N, E, K, bias, p, topk_ids, topk_weights, alignment,
                                   tokens_per_expert, cu_seqlens, expanded_to_permuted, permuted_to_expanded,
                                   permuted_cap, zero_fill, R, num_src, num_channels, NvS, out, ws, ws_bytes, stream,
-                                  ev);
+                                  ev, false);
 }

@@ -490,6 +490,30 @@ int mep_route_layout_plan_timed(const void* logits, int dtype, int64_t N, int E,
                                 const mep_plan_outputs* out, void* ws, size_t ws_bytes, void* stream,
                                 void* route_start, void* route_stop, void* plan_start, void* plan_stop);
 
+/*
+ * mep_route_layout_plan_noalloc -- mep_route_layout_plan without a caller
+ * workspace and without any allocation, for callers that cannot allocate:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.
+ *
+ * Same arguments (less ws / ws_bytes), checks, results and kernels as
+ * mep_route_layout_plan.  The workspace is a device array of 8 MiB per GPU
+ * inside the library (held by each GPU the library runs on until the process
+ * ends); the first call on a device clears it with a small kernel on `stream`
+ * and every call leaves it ready for the next.  Returns MEP_ERR_CAPACITY when
+ * mep_plan_workspace_size(N, E, K, R, num_src) exceeds 8 MiB (nothing is
+ * enqueued then), MEP_ERR_DEVICE when the array's address cannot be obtained.
+ * Calls on one GPU share the array: calls that overlap on one GPU (two streams,
+ * two host threads) race and must be ordered by the caller.
+ */
+int mep_route_layout_plan_noalloc(const void* logits, int dtype, int64_t N, int E, int K,
+                                  const float* bias, const mep_route_params* p, int32_t* topk_ids,
+                                  float* topk_weights, int alignment, int32_t* tokens_per_expert,
+                                  int32_t* cu_seqlens, int32_t* expanded_to_permuted,
+                                  int32_t* permuted_to_expanded, int64_t permuted_cap,
+                                  int32_t* zero_fill, int R, int num_src, int num_channels,
+                                  int64_t NvS, const mep_plan_outputs* out, void* stream);
+
 /* Static, NUL-terminated name of a return code. */
 const char* mep_status_string(int code);
 

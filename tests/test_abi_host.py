@@ -245,3 +245,21 @@ def test_balanced_validation():
     assert call(cap=2 ** 31) == B.MEP_ERR_UNSUPPORTED
     assert call(NvS=B.balanced_nvs(64, 16, 4, 4, 2, 2, 100) - 1) == B.MEP_ERR_CAPACITY
     assert call(N=2 ** 20, NvS=2 ** 30) == B.MEP_ERR_CAPACITY          # R * NvS > INT32_MAX
+
+
+def test_noalloc_rejects_sizes_beyond_its_array():
+    """mep_route_layout_plan_noalloc returns MEP_ERR_CAPACITY, before touching anything, when the
+    call's plan workspace would exceed the library's 8 MiB per-GPU array."""
+    N, E, K, A, R, S, C = 1 << 22, 256, 8, 128, 8, 8, 24
+    assert B.plan_workspace_size(N, E, K, R, S) > 8 << 20
+    params = B.RouteParams(1, 1, 8, 4, 2, 2.5)
+    po = B.PlanOutputs(*([FAKE] * 12), N * 4, FAKE, N * 7)
+    rc = B.lib().mep_route_layout_plan_noalloc(
+        FAKE, 0, N, E, K, FAKE, ctypes.byref(params), FAKE, FAKE, A, FAKE, FAKE, FAKE, FAKE,
+        N * K + E * (A - 1), FAKE, R, S, C, B.default_nvs(N, E, K, R, A), ctypes.byref(po), None)
+    assert rc == B.MEP_ERR_CAPACITY
+    # a bad argument is reported the same way as by mep_route_layout_plan, nothing enqueued
+    rc = B.lib().mep_route_layout_plan_noalloc(
+        FAKE, 0, 64, E, K, FAKE, ctypes.byref(params), FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE,
+        64 * K, FAKE, R, S, C, B.default_nvs(64, E, K, R, 1), ctypes.byref(po), None)
+    assert rc == B.MEP_ERR_INVALID_ARG

@@ -62,6 +62,7 @@ struct PathGeom {
     int tps;     // plan tiles per shard
     int ntiles;  // plan tiles
     int NC;      // histogram columns
+    int NCs;     // row stride of the histogram rows in the workspace (NC rounded up to 4 words)
     int sub;     // plan tiles per counting workgroup
     int nwg;     // counting workgroups
     int GW;      // counting workgroups per group
@@ -84,9 +85,9 @@ __host__ __device__ __forceinline__ void path_tile_tokens(const PathGeom& g, int
 
 // Workspace views.
 struct PathWs {
-    uint32_t* gsum;  // [2][kPathGsumWords]: group sum rows [ng][NC] of the two parities
-    uint32_t* wrow;  // [nwg][NC] counting-workgroup totals
-    uint32_t* tpre;  // [ntiles][NC] exclusive prefix within the counting workgroup
+    uint32_t* gsum;  // [2][kPathGsumWords]: group sum rows [ng][NCs] of the two parities
+    uint32_t* wrow;  // [nwg][NCs] counting-workgroup totals
+    uint32_t* tpre;  // [ntiles][NCs] exclusive prefix within the counting workgroup
 };
 
 // Outputs of the layout and the plan (device pointers; NULL skips an optional one).
@@ -113,7 +114,7 @@ __device__ __forceinline__ void path_epilogue(const PathGeom& g, const PathWs& w
     const int b = blockIdx.x;
     const int j0 = b * g.sub;
     const int nsub = min(g.sub, g.ntiles - j0);
-    const int NC = g.NC, R = g.R;
+    const int NC = g.NC, NCs = g.NCs, R = g.R;
     __syncthreads();
     // duplicates per rank = slots on the rank (its experts' counts) - tokens on the rank
     for (int p = tid; p < nsub * R; p += NT) {
@@ -132,14 +133,14 @@ __device__ __forceinline__ void path_epilogue(const PathGeom& g, const PathWs& w
         const size_t hi = lo + per < kPathGsumWords ? lo + per : kPathGsumWords;
         for (size_t i = lo + tid; i < hi; i += NT) other[i] = 0u;
     }
-    MEP_GLOBAL uint32_t* gs = gptr(w.gsum) + (pcall & 1u) * kPathGsumWords + (size_t)(b / g.GW) * NC;
+    MEP_GLOBAL uint32_t* gs = gptr(w.gsum) + (pcall & 1u) * kPathGsumWords + (size_t)(b / g.GW) * NCs;
     for (int c = tid; c < NC; c += NT) {
         uint32_t run = 0;
         for (int i = 0; i < nsub; ++i) {
-            gptr(w.tpre)[(size_t)(j0 + i) * NC + c] = run;
+            gptr(w.tpre)[(size_t)(j0 + i) * NCs + c] = run;
             run += (uint32_t)s_row[i * NC + c];
         }
-        gptr(w.wrow)[(size_t)b * NC + c] = run;
+        gptr(w.wrow)[(size_t)b * NCs + c] = run;
         if (run != 0u) __hip_atomic_fetch_add(gs + c, run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }

@@ -5,7 +5,8 @@
 //
 // Plan-tile kernel, one workgroup of 512 threads per tile (at most 2048 slots):
 //   prologue   the tile's ids into LDS; the exclusive prefix of every column before the tile
-//              (three plain loads per column), cu_seqlens, the dedup segment starts;
+//              (a sum of the rows the counting epilogue left, 16-byte loads spread over every
+//              thread), cu_seqlens, the dedup segment starts;
 //   tokens     a thread per token: owner ranks of its K slots, first slot per rank, slots per
 //              rank -> a code per slot (expert, rank, head / duplicate / plain, slots on the rank);
 //              is_token_in_rank; per-wave ballots of each rank's tokens (channel prefixes);
@@ -40,17 +41,19 @@ __device__ __forceinline__ uint32_t slot_code(int e, uint32_t type, int r, int h
     return (uint32_t)e | (type << 10) | ((uint32_t)r << 12) | ((uint32_t)h << 17);
 }
 
-// Exclusive scan over the 64 lanes of a wave; `total` gets the sum.
+// Exclusive scan over the 64 lanes of a wave; `total` gets the sum.  DPP row shifts by 1, 2, 4
+// and 8 give the inclusive scan within each row of 16 lanes; the row broadcasts of lane 15 (into
+// rows 1 and 3) and of lane 31 (into rows 2 and 3) carry it across rows.
 __device__ __forceinline__ int wave_excl_scan(int v, int& total) {
-    const int lane = threadIdx.x & 63;
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-    }
-    total = __shfl(incl, 63);
-    return incl - v;
+    int x = v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    total = __builtin_amdgcn_readlane(x, 63);
+    return x - v;
 }
 
 }  // namespace
@@ -201,7 +204,7 @@ __device__ __forceinline__ void path_small_outputs(const PathGeom& g, const Path
 template <int NBE, int NBR>
 __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __restrict__ ids, PathGeom g,
                                                             PathWs w, PathOut o, WsHeader* hdr) {
-    __shared__ uint32_t s_code[kPathSlots + kPathSlots / 64];
+    __shared__ __align__(16) uint32_t s_code[kPathSlots];
     __shared__ int s_ecnt[kPlanW][kPathMaxE];
     __shared__ int s_rcnt[kPlanW][2][kPathMaxR];
     __shared__ int s_cu[kPathMaxE + 1];
@@ -211,6 +214,7 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
     __shared__ int s_doff[2][kPathMaxR + 1];
     __shared__ int s_owner[kPathMaxE];
     __shared__ uint64_t s_mask[kPathTokens / 64][kPathMaxR];
+    __shared__ u32x4 s_pq[3][kPlanNT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -237,62 +241,87 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
             for (int q = tid; q < nq; q += kPlanNT) {
                 const u32x4 v = reinterpret_cast<const MEP_GLOBAL u32x4*>(gid)[q];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s_code[slot_pad(4 * q + i)] = v[i];
+                for (int i = 0; i < 4; ++i) s_code[4 * q + i] = v[i];
             }
-            for (int s = (nq << 2) + tid; s < ns; s += kPlanNT) s_code[slot_pad(s)] = (uint32_t)gid[s];
+            for (int s = (nq << 2) + tid; s < ns; s += kPlanNT) s_code[s] = (uint32_t)gid[s];
         } else {
-            for (int s = tid; s < ns; s += kPlanNT) s_code[slot_pad(s)] = (uint32_t)gid[s];
+            for (int s = tid; s < ns; s += kPlanNT) s_code[s] = (uint32_t)gid[s];
         }
     }
-    // prefixes before this tile (and before the shard's first tile) and the totals, from the
-    // counting kernel's group sums, workgroup totals and within-workgroup prefixes
-    // (one of the two parity buffers holds this call's group sums, the other is zero)
+    // prefixes before this tile (and before the shard's first tile) and the totals: sums of rows
+    // the counting epilogue left -- the group sum rows of both parities (one holds this call's
+    // sums, the other is zero), the total rows of the earlier workgroups of the tile's group, the
+    // tile's within-workgroup prefix row, and for the shard start the same two kinds of rows.
+    // Each thread owns a column quad and a slice of the rows: 16-byte loads, all in flight at
+    // once, summed in registers, then the slices summed through LDS.
     {
-        const MEP_GLOBAL uint32_t* gs0 = gptr(w.gsum);
-        const MEP_GLOBAL uint32_t* gs1 = gs0 + kPathGsumWords;
-        const int wg = j / g.sub, grp = wg / g.GW;
-        const int wgf = jf / g.sub, grpf = wgf / g.GW;
-        const int wg0 = grp * g.GW, wgf0 = grpf * g.GW;
+        const int NCs = g.NCs;
+        const int NQ = NCs >> 2;
+        const int nsl = kPlanNT / NQ;
+        const int q = tid % NQ, sl = tid / NQ;
+        const int ng = g.ng;
+        const int wg = j / g.sub, grp = wg / g.GW, wg0 = grp * g.GW;
+        const int wgf = jf / g.sub, grpf = wgf / g.GW, wgf0 = grpf * g.GW;
+        // the shard start's prefix: every column for the shard's last tile (per-shard expert
+        // counts), the rank token columns for the channel prefixes, none otherwise
+        const bool shx_all = shard_last && o.p.ntpe;
+        const bool shx_rank = o.p.chan || (shard_last && (o.p.ntpr || o.p.ntpe));
+        const bool need_f = shx_all || (shx_rank && 4 * q < E + R && 4 * q + 4 > E);
+        const int r_w = 2 * ng;                 // first workgroup row of the tile's group
+        const int r_t = r_w + (wg - wg0);       // the tile's prefix row
+        const int r_f = r_t + 1;                // first workgroup row of the shard start's group
+        const int nf = (shx_all || shx_rank) ? (wgf - wgf0) + 1 : 0;
+        const int nrows = r_f + nf;
+        // every row as a word offset from the first group sum row (rows past the list, and the
+        // shard start's rows of columns that do not need them, read group row 0 and count nowhere)
+        const MEP_GLOBAL uint32_t* base = gptr(w.gsum);
+        const int64_t ow = w.wrow - w.gsum, ot = w.tpre - w.gsum;
+        u32x4 tot = {0u, 0u, 0u, 0u}, ex = tot, sx = tot;
+        if (sl < nsl) {
+            for (int r0 = sl; r0 < nrows; r0 += 8 * nsl) {
+                u32x4 v[8];
+                uint32_t use[8];  // bit 0: totals, bit 1: prefix of the tile, bit 2: of the shard start
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int r = r0 + i * nsl;
+                    const bool in_g = r < r_w, par1 = r >= ng;
+                    const int gi = par1 ? r - ng : r;
+                    const bool in_w = r >= r_w && r < r_t, in_t = r == r_t;
+                    const bool in_wf = need_f && r >= r_f && r < nrows - 1, in_tf = need_f && r == nrows - 1;
+                    const int64_t off = in_g    ? (par1 ? (int64_t)kPathGsumWords : 0) + (int64_t)gi * NCs
+                                        : in_w  ? ow + (int64_t)(wg0 + (r - r_w)) * NCs
+                                        : in_t  ? ot + (int64_t)j * NCs
+                                        : in_wf ? ow + (int64_t)(wgf0 + (r - r_f)) * NCs
+                                        : in_tf ? ot + (int64_t)jf * NCs
+                                                : 0;
+                    use[i] = in_g ? 1u | (gi < grp ? 2u : 0u) | (gi < grpf ? 4u : 0u)
+                                  : (in_w || in_t) ? 2u : (in_wf || in_tf) ? 4u : 0u;
+                    v[i] = reinterpret_cast<const MEP_GLOBAL u32x4*>(base + off)[q];
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const u32x4 z = {0u, 0u, 0u, 0u};
+                    tot += (use[i] & 1u) ? v[i] : z;
+                    ex += (use[i] & 2u) ? v[i] : z;
+                    sx += (use[i] & 4u) ? v[i] : z;
+                }
+            }
+        }
+        s_pq[0][tid] = tot;
+        s_pq[1][tid] = ex;
+        s_pq[2][tid] = sx;
+        __syncthreads();
         for (int c = tid; c < NC; c += kPlanNT) {
-            // every load of a batch first (16 rows at a time), then the sums
-            uint32_t tot = 0, pg = 0, pgf = 0;
-            for (int q0 = 0; q0 < g.ng; q0 += 16) {
-                uint32_t v[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const size_t at = (size_t)min(q0 + i, g.ng - 1) * NC + c;
-                    v[i] = gs0[at] + gs1[at];
-                }
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int q = q0 + i;
-                    const uint32_t x = q < g.ng ? v[i] : 0u;
-                    tot += x;
-                    pg += q < grp ? x : 0u;
-                    pgf += q < grpf ? x : 0u;
-                }
+            const int qc = c >> 2, ic = c & 3;
+            uint32_t a = 0u, b = 0u, f = 0u;
+            for (int s2 = 0; s2 < nsl; ++s2) {
+                a += s_pq[0][s2 * NQ + qc][ic];
+                b += s_pq[1][s2 * NQ + qc][ic];
+                f += s_pq[2][s2 * NQ + qc][ic];
             }
-            uint32_t ex = pg + gptr(w.tpre)[(size_t)j * NC + c];
-            for (int b0 = wg0; b0 < wg; b0 += 16) {
-                uint32_t v[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) v[i] = gptr(w.wrow)[(size_t)min(b0 + i, wg - 1) * NC + c];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) ex += b0 + i < wg ? v[i] : 0u;
-            }
-            s_excl[c] = (int)ex;
-            s_tot[c] = (int)tot;
-            if (want_shx) {
-                uint32_t sx = pgf + gptr(w.tpre)[(size_t)jf * NC + c];
-                for (int b0 = wgf0; b0 < wgf; b0 += 16) {
-                    uint32_t v[16];
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) v[i] = gptr(w.wrow)[(size_t)min(b0 + i, wgf - 1) * NC + c];
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) sx += b0 + i < wgf ? v[i] : 0u;
-                }
-                s_shx[c] = (int)sx;
-            }
+            s_tot[c] = (int)a;
+            s_excl[c] = (int)b;
+            s_shx[c] = (int)f;
         }
     }
     for (int e = tid; e < E; e += kPlanNT) s_owner[e] = e / g.epn;
@@ -309,11 +338,25 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
         uint32_t m = 0u;
         if (live) {
             int e[kPathMaxK], r[kPathMaxK];
+            uint32_t cd[kPathMaxK];
+            if (K == 8) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(&s_code[tk * 8]);
+                const u32x4 b = *reinterpret_cast<const u32x4*>(&s_code[tk * 8 + 4]);
 #pragma unroll
-            for (int k = 0; k < kPathMaxK; ++k) {
-                e[k] = k < K ? (int)s_code[slot_pad(tk * K + k)] : 0;
-                r[k] = k < K ? s_owner[e[k]] : -1 - k;
+                for (int k = 0; k < 4; ++k) {
+                    e[k] = (int)a[k];
+                    e[4 + k] = (int)b[k];
+                }
+            } else if (K == 4) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(&s_code[tk * 4]);
+#pragma unroll
+                for (int k = 0; k < kPathMaxK; ++k) e[k] = k < 4 ? (int)a[k & 3] : 0;
+            } else {
+#pragma unroll
+                for (int k = 0; k < kPathMaxK; ++k) e[k] = k < K ? (int)s_code[tk * K + k] : 0;
             }
+#pragma unroll
+            for (int k = 0; k < kPathMaxK; ++k) r[k] = k < K ? s_owner[e[k]] : -1 - k;
 #pragma unroll
             for (int k = 0; k < kPathMaxK; ++k) {
                 if (k >= K) continue;
@@ -326,8 +369,18 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
                     if (k2 < k && same) first = false;
                 }
                 const uint32_t type = first ? (h >= 2 ? kSlotHead : kSlotPlain) : kSlotDup;
-                s_code[slot_pad(tk * K + k)] = slot_code(e[k], type, r[k], h);
+                cd[k] = slot_code(e[k], type, r[k], h);
                 m |= 1u << r[k];
+            }
+            if (K == 8) {
+                *reinterpret_cast<u32x4*>(&s_code[tk * 8]) = u32x4{cd[0], cd[1], cd[2], cd[3]};
+                *reinterpret_cast<u32x4*>(&s_code[tk * 8 + 4]) = u32x4{cd[4], cd[5], cd[6], cd[7]};
+            } else if (K == 4) {
+                *reinterpret_cast<u32x4*>(&s_code[tk * 4]) = u32x4{cd[0], cd[1], cd[2], cd[3]};
+            } else {
+#pragma unroll
+                for (int k = 0; k < kPathMaxK; ++k)
+                    if (k < K) s_code[tk * K + k] = cd[k];
             }
             if (o.p.itr) {
                 MEP_GLOBAL uint8_t* row = gptr(o.p.itr) + (t0 + tk) * R;
@@ -362,7 +415,7 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
         if (it * 64 >= spw) continue;
         const int si = sbeg + it * 64 + lane;
         const bool valid = si < ns;
-        const uint32_t code = valid ? s_code[slot_pad(si)] : 0u;
+        const uint32_t code = valid ? s_code[si] : 0u;
         const int e = (int)(code & 1023u);
         const uint32_t type = (code >> 10) & 3u;
         const int r = (int)((code >> 12) & 31u);
@@ -421,7 +474,7 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
         if (it * 64 >= spw) continue;
         const int si = sbeg + it * 64 + lane;
         if (si >= ns) continue;
-        const uint32_t code = s_code[slot_pad(si)];
+        const uint32_t code = s_code[si];
         const int e = (int)(code & 1023u);
         const uint32_t type = (code >> 10) & 3u;
         const int r = (int)((code >> 12) & 31u);
@@ -515,6 +568,7 @@ PathGeom path_geom(int64_t N, int E, int K, int R, int S, int C, int A, int64_t 
     g.tps = (int)ceil_div64(g.n, g.T);
     g.ntiles = S * g.tps;
     g.NC = E + 3 * R;
+    g.NCs = (g.NC + 3) & ~3;
     int sub = (int)ceil_div64(g.ntiles, kPathUnits);
     if (sub < 1) sub = 1;
     if (sub > kPathMaxSub) sub = kPathMaxSub;
@@ -539,9 +593,9 @@ PathWsLayout path_ws_layout(const PathGeom& g) {
     L.gsum = sizeof(WsHeader);
     size_t off = L.gsum + kPathGsumBytes + kPlanArriveBytes;
     L.wrow = off;
-    off += align256((size_t)g.nwg * g.NC * 4);
+    off += align256((size_t)g.nwg * g.NCs * 4);
     L.tpre = off;
-    off += align256((size_t)g.ntiles * g.NC * 4);
+    off += align256((size_t)g.ntiles * g.NCs * 4);
     L.bytes = off;
     return L;
 }

@@ -57,7 +57,7 @@ EXPORTS = ("mep_route_topk", "mep_route_topk_timed", "mep_build_layout", "mep_la
            "mep_plan_workspace_size", "mep_layout_plan", "mep_route_layout_plan",
            "mep_route_layout_plan_timed", "mep_route_layout_plan_noalloc", "mep_tile_map",
            "mep_plan_balanced", "mep_permute_rows",
-           "mep_combine_rows", "mep_status_string")
+           "mep_combine_rows", "mep_sigmoid_eval", "mep_status_string")
 
 _lib = None
 _lock = threading.Lock()
@@ -107,6 +107,8 @@ def lib():
                 L.mep_permute_rows.restype = I
                 L.mep_combine_rows.argtypes = [P, I, I64, I64, I, P, P, I64, P, P]
                 L.mep_combine_rows.restype = I
+                L.mep_sigmoid_eval.argtypes = [P, I64, P, P, P, P]
+                L.mep_sigmoid_eval.restype = I
                 L.mep_status_string.argtypes = [I]
                 L.mep_status_string.restype = ctypes.c_char_p
                 _lib = L
@@ -152,6 +154,20 @@ def mep_route_topk(logits, K, bias, params: RouteParams, topk_ids, topk_weights=
     rc = lib().mep_route_topk(_ptr(logits), dtype, N, E, K, _ptr(bias), ctypes.byref(params),
                               _ptr(topk_ids), _ptr(topk_weights), _stream(stream))
     _check(rc, "mep_route_topk")
+
+
+def mep_sigmoid_eval(x, cr_out=None, filter_out=None, weight_out=None, stream=None):
+    """The routing kernels' sigmoid evaluations of float32 device tensor `x` into the given
+    outputs (float32, float32, float64; any may be None)."""
+    _require_cuda(x, cr_out, filter_out, weight_out)
+    if x.dtype != torch.float32 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 tensor")
+    for t, dt in ((cr_out, torch.float32), (filter_out, torch.float32), (weight_out, torch.float64)):
+        if t is not None and (t.dtype != dt or t.numel() < x.numel() or not t.is_contiguous()):
+            raise ValueError("outputs must be contiguous, of the input's size and of their dtype")
+    rc = lib().mep_sigmoid_eval(_ptr(x), x.numel(), _ptr(cr_out), _ptr(filter_out), _ptr(weight_out),
+                                _stream(stream))
+    _check(rc, "mep_sigmoid_eval")
 
 
 def mep_build_layout(topk_ids, E, alignment, tokens_per_expert, cu_seqlens, expanded_to_permuted,

@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmep.so")
-SOURCES = ["route.hip", "route_sig.hip", "route_fast.hip", "route_fast_f32.hip", "route_fast_bf16.hip", "layout.hip", "plan.hip", "layout_plan.hip", "path.hip", "tile_map.hip", "rows.hip", "balance.hip", "small.hip", "noalloc.hip", "api.hip"]
+SOURCES = ["route.hip", "route_sig.hip", "route_fast.hip", "route_fast_f32.hip", "route_fast_bf16.hip", "layout.hip", "plan.hip", "layout_plan.hip", "path.hip", "tile_map.hip", "rows.hip", "balance.hip", "small.hip", "noalloc.hip", "sigmoid_eval.hip", "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -514,6 +514,27 @@ int mep_route_layout_plan_noalloc(const void* logits, int dtype, int64_t N, int 
                                   int32_t* zero_fill, int R, int num_src, int num_channels,
                                   int64_t NvS, const mep_plan_outputs* out, void* stream);
 
+/*
+ * mep_sigmoid_eval -- the sigmoid evaluations the routing kernels use, applied
+ * element-wise, for verifying them over every binary32 input (not a step of
+ * the path).  The real function is the logistic sigmoid 1/(1+exp(-x)) of
+ * [TRT] RoutingKernel.cuh (sigmoid_accurate), the scoring function of
+ * sigmoid routing.
+ *
+ * x:          device, n binary32 inputs (4-byte aligned).
+ * cr_out:     device, n binary32 (or NULL): sigma(x) correctly rounded to
+ *             binary32 (round to nearest even, subnormals kept) -- the value
+ *             every exact selection key is formed from.
+ * filter_out: device, n binary32 (or NULL): the binary32 filter value
+ *             rcp(1 + exp2(-x * log2 e)) of the certified fast selection.
+ * weight_out: device, n binary64 (or NULL, 8-byte aligned): the binary64
+ *             sigmoid the routing weights are computed from.
+ * Returns MEP_ERR_INVALID_ARG for n < 0, a NULL x with n > 0, or a misaligned
+ * pointer; MEP_OK with nothing enqueued for n == 0 or no output.
+ */
+int mep_sigmoid_eval(const float* x, int64_t n, float* cr_out, float* filter_out, double* weight_out,
+                     void* stream);
+
 /* Static, NUL-terminated name of a return code. */
 const char* mep_status_string(int code);
 

@@ -263,3 +263,14 @@ def test_noalloc_rejects_sizes_beyond_its_array():
         FAKE, 0, 64, E, K, FAKE, ctypes.byref(params), FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE,
         64 * K, FAKE, R, S, C, B.default_nvs(64, E, K, R, 1), ctypes.byref(po), None)
     assert rc == B.MEP_ERR_INVALID_ARG
+
+
+def test_sigmoid_eval_validation():
+    L = B.lib()
+    assert L.mep_sigmoid_eval(FAKE, -1, FAKE, None, None, None) == B.MEP_ERR_INVALID_ARG
+    assert L.mep_sigmoid_eval(None, 16, FAKE, None, None, None) == B.MEP_ERR_INVALID_ARG
+    assert L.mep_sigmoid_eval(FAKE, 16, FAKE + 2, None, None, None) == B.MEP_ERR_INVALID_ARG
+    assert L.mep_sigmoid_eval(FAKE, 16, None, None, FAKE + 4, None) == B.MEP_ERR_INVALID_ARG
+    # nothing to do: no launch
+    assert L.mep_sigmoid_eval(FAKE, 0, FAKE, FAKE, FAKE, None) == B.MEP_OK
+    assert L.mep_sigmoid_eval(FAKE, 16, None, None, None, None) == B.MEP_OK

@@ -116,13 +116,19 @@ __device__ __forceinline__ void path_epilogue(const PathGeom& g, const PathWs& w
     const int nsub = min(g.sub, g.ntiles - j0);
     const int NC = g.NC, NCs = g.NCs, R = g.R;
     __syncthreads();
-    // duplicates per rank = slots on the rank (its experts' counts) - tokens on the rank
-    for (int p = tid; p < nsub * R; p += NT) {
-        const int i = p / R, r = p - (p / R) * R;
-        int* row = s_row + i * NC;
-        int s = 0;
-        for (int e = r * g.epn; e < (r + 1) * g.epn; ++e) s += row[e];
-        row[path_col_c2(g, r)] = s - row[path_col_c0(g, r)];
+    // duplicates per rank = slots on the rank (its experts' counts) - tokens on the rank: a wave
+    // per (tile, rank), a lane per expert, then a sum over the wave
+    {
+        const int wv = tid >> 6, lane = tid & 63;
+        for (int p = wv; p < nsub * R; p += NT / 64) {
+            const int i = p / R, r = p - (p / R) * R;
+            int* row = s_row + i * NC;
+            int s = 0;
+            for (int e = r * g.epn + lane; e < (r + 1) * g.epn; e += 64) s += row[e];
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+            if (lane == 0) row[path_col_c2(g, r)] = s - row[path_col_c0(g, r)];
+        }
     }
     __syncthreads();
     // this workgroup's share of clearing the other parity's buffer (the previous call's sums)

@@ -639,27 +639,36 @@ __global__ __launch_bounds__(64 * NW) void route_sig_kernel(RouteArgs a, SigCfg 
     }
 
     // ---- uncertified tokens of this workgroup's sets: exact, one token per wave in turn ----------
+    // The sets' failure words are read 64 at a time, one per lane, and only the non-zero ones are
+    // visited (a serial scan of the words would be a chain of LDS round trips).
     __syncthreads();
     int idx = 0;
-    for (int i = 0; i < nsets; ++i) {
-        uint32_t m = s_fail[i];
-        while (m) {
-            const int t = __builtin_ctz(m);
-            m &= m - 1u;
-            if (idx % NW == wv) {
-                const int tok = t0 + i * TPW + t;
-                int sel[1];
-                exact_token_sig<LPT, BF16, MODE>(a.logits, a.bias, a.ids, a.weights, K, a.group_topn,
-                                                 a.renormalize, a.scale, tok, cfg.tg, wl, nullptr, sel);
-                if (epi) {
-                    int ri = 0;
-                    while (ri + 1 < nsub && tok >= s_tb[ri + 1]) ++ri;
-                    int ce[1] = {wl < K ? sel[0] : -1};
-                    // the token's slots are on lanes 0..K-1 (K <= 8): an 8-lane segment
-                    if (wl < 8) sig_count_token<8, 1>(ep.g, ep.eshift, s_row + ri * ep.g.NC, ce, wl);
+    for (int i0 = 0; i0 < nsets; i0 += 64) {
+        const uint32_t mine = i0 + wl < nsets ? s_fail[i0 + wl] : 0u;
+        uint64_t any = __ballot(mine != 0u);
+        while (any) {
+            const int l = __builtin_ctzll(any);
+            any &= any - 1ull;
+            uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)mine, l);
+            const int i = i0 + l;
+            while (m) {
+                const int t = __builtin_ctz(m);
+                m &= m - 1u;
+                if (idx % NW == wv) {
+                    const int tok = t0 + i * TPW + t;
+                    int sel[1];
+                    exact_token_sig<LPT, BF16, MODE>(a.logits, a.bias, a.ids, a.weights, K, a.group_topn,
+                                                     a.renormalize, a.scale, tok, cfg.tg, wl, nullptr, sel);
+                    if (epi) {
+                        int ri = 0;
+                        while (ri + 1 < nsub && tok >= s_tb[ri + 1]) ++ri;
+                        int ce[1] = {wl < K ? sel[0] : -1};
+                        // the token's slots are on lanes 0..K-1 (K <= 8): an 8-lane segment
+                        if (wl < 8) sig_count_token<8, 1>(ep.g, ep.eshift, s_row + ri * ep.g.NC, ce, wl);
+                    }
                 }
+                ++idx;
             }
-            ++idx;
         }
     }
     if (epi) path_epilogue<NT>(ep.g, ep.w, pcall, s_row);

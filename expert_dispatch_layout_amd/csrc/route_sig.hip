@@ -8,7 +8,7 @@ namespace mep {
 
 namespace {
 
-constexpr int kSigWaves = 16;        // one workgroup of 16 waves per compute unit
+constexpr int kSigWaves = 8;         // one workgroup of 8 waves per compute unit
 constexpr size_t kLdsLimit = 160 * 1024;
 
 int device_units() {

@@ -58,6 +58,8 @@ constexpr size_t kPathGsumBytes = 2 * kPathGsumWords * sizeof(uint32_t);
 
 struct PathGeom {
     int N, E, K, R, epn, S, n, C, A;
+    int eshift;  // log2(epn) when epn is a power of two, else -1
+    int ashift;  // log2(A) when A is a power of two, else -1
     int T;       // tokens per plan tile
     int tps;     // plan tiles per shard
     int ntiles;  // plan tiles

@@ -130,7 +130,7 @@ __device__ __forceinline__ void path_scan_totals(const PathGeom& g, const int* s
         int v = 0;
         if (i < per && e < E) {
             const int c = s_tot[e];
-            v = c > 0 ? ((c + A - 1) / A) * A : 0;
+            v = c <= 0 ? 0 : g.ashift >= 0 ? ((c + A - 1) >> g.ashift) << g.ashift : ((c + A - 1) / A) * A;
         }
         pad[i] = v;
         s += v;
@@ -328,15 +328,37 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
     for (int i = tid; i < kPlanW * E; i += kPlanNT) s_ecnt[i / E][i % E] = 0;
     for (int i = tid; i < kPlanW * 2 * R; i += kPlanNT) s_rcnt[i / (2 * R)][(i / R) & 1][i % R] = 0;
     __syncthreads();
-    if (wv == 0) path_scan_totals(g, s_tot, s_cu, s_doff);
-    __syncthreads();
-    if (j == 0) path_small_outputs(g, o, s_tot, s_cu, s_doff);
-    // ---- tokens: slot codes, is_token_in_rank, rank ballots ------------------------------------
-    for (int base = wv * 64; base < nt; base += kPlanNT) {
+    // ---- tokens (waves 0 .. kPlanW - 2): slot codes, is_token_in_rank, rank ballots; the last
+    // wave meanwhile forms cu_seqlens and the dedup segment starts ---------------------------------
+    if (wv == kPlanW - 1) path_scan_totals(g, s_tot, s_cu, s_doff);
+    for (int base = wv * 64; wv < kPlanW - 1 && base < nt; base += (kPlanW - 1) * 64) {
         const int tk = base + lane;
         const bool live = tk < nt;
         uint32_t m = 0u;
-        if (live) {
+        if (live && K == 8 && R <= 8) {
+            // eight slots, at most eight ranks: per-rank slot counts as 4-bit fields of one word
+            const u32x4 a = *reinterpret_cast<const u32x4*>(&s_code[tk * 8]);
+            const u32x4 b = *reinterpret_cast<const u32x4*>(&s_code[tk * 8 + 4]);
+            const int e[8] = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+            int r[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) r[k] = g.eshift >= 0 ? e[k] >> g.eshift : s_owner[e[k]];
+            uint32_t cnt = 0u;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) cnt += 1u << (4 * r[k]);
+            uint32_t cd[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t bit = 1u << r[k];
+                const bool first = (m & bit) == 0u;
+                m |= bit;
+                const int h = (int)((cnt >> (4 * r[k])) & 15u);
+                const uint32_t type = first ? (h >= 2 ? kSlotHead : kSlotPlain) : kSlotDup;
+                cd[k] = slot_code(e[k], type, r[k], h);
+            }
+            *reinterpret_cast<u32x4*>(&s_code[tk * 8]) = u32x4{cd[0], cd[1], cd[2], cd[3]};
+            *reinterpret_cast<u32x4*>(&s_code[tk * 8 + 4]) = u32x4{cd[4], cd[5], cd[6], cd[7]};
+        } else if (live) {
             int e[kPathMaxK], r[kPathMaxK];
             uint32_t cd[kPathMaxK];
             if (K == 8) {
@@ -382,6 +404,8 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
                 for (int k = 0; k < kPathMaxK; ++k)
                     if (k < K) s_code[tk * K + k] = cd[k];
             }
+        }
+        if (live) {
             if (o.p.itr) {
                 MEP_GLOBAL uint8_t* row = gptr(o.p.itr) + (t0 + tk) * R;
                 if ((R & 3) == 0) {
@@ -404,6 +428,7 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
         }
     }
     __syncthreads();
+    if (j == 0) path_small_outputs(g, o, s_tot, s_cu, s_doff);
 
     // ---- stable ranks within the waves ------------------------------------------------------------
     const int spw = ((ns + kPlanNT - 1) / kPlanNT) * 64;  // slots per wave, a multiple of 64
@@ -560,6 +585,13 @@ PathGeom path_geom(int64_t N, int E, int K, int R, int S, int C, int A, int64_t 
     g.C = C;
     g.A = A;
     g.NvS = NvS;
+    auto log2_exact = [](int v) {
+        int k = 0;
+        while (k < 30 && (1 << k) < v) ++k;
+        return v > 0 && (1 << k) == v ? k : -1;
+    };
+    g.eshift = log2_exact(g.epn);
+    g.ashift = log2_exact(A);
     int kp = 1;
     while (kp < K) kp <<= 1;
     g.T = kPathSlots / kp;

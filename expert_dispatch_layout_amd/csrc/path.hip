@@ -3,7 +3,7 @@
 // fused call), and the plan-tile kernel, which writes every per-slot and per-token output of the
 // layout and the plan for one tile from the prefixes the counting epilogue left.
 //
-// Plan-tile kernel, one workgroup of 512 threads per tile (at most 2048 slots):
+// Plan-tile kernel, one workgroup of 1024 threads per tile (at most 2048 slots):
 //   prologue   the tile's ids into LDS; the exclusive prefix of every column before the tile
 //              (a sum of the rows the counting epilogue left, 16-byte loads spread over every
 //              thread), cu_seqlens, the dedup segment starts;
@@ -32,7 +32,8 @@ namespace mep {
 namespace {
 
 constexpr int kCountNT = 512;
-constexpr int kPlanNT = 512;
+constexpr int kPlanNT = 1024;
+constexpr int kPlanRowNT = 512;  // threads that load the prefix rows (at most 7 row slices to sum)
 constexpr int kPlanW = kPlanNT / 64;
 constexpr int kPlanIters = kPathSlots / kPlanNT;   // 64-slot steps per wave, at most
 enum : uint32_t { kSlotPlain = 0, kSlotHead = 1, kSlotDup = 2 };
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
     __shared__ int s_doff[2][kPathMaxR + 1];
     __shared__ int s_owner[kPathMaxE];
     __shared__ uint64_t s_mask[kPathTokens / 64][kPathMaxR];
-    __shared__ u32x4 s_pq[3][kPlanNT];
+    __shared__ u32x4 s_pq[3][kPlanRowNT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
     {
         const int NCs = g.NCs;
         const int NQ = NCs >> 2;
-        const int nsl = kPlanNT / NQ;
+        const int nsl = kPlanRowNT / NQ;
         const int q = tid % NQ, sl = tid / NQ;
         const int ng = g.ng;
         const int wg = j / g.sub, grp = wg / g.GW, wg0 = grp * g.GW;
@@ -307,9 +308,11 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
                 }
             }
         }
-        s_pq[0][tid] = tot;
-        s_pq[1][tid] = ex;
-        s_pq[2][tid] = sx;
+        if (tid < kPlanRowNT) {
+            s_pq[0][tid] = tot;
+            s_pq[1][tid] = ex;
+            s_pq[2][tid] = sx;
+        }
         __syncthreads();
         for (int c = tid; c < NC; c += kPlanNT) {
             const int qc = c >> 2, ic = c & 3;

@@ -11,6 +11,12 @@ one source shard per rank and 24 channels.
 Input and output buffers rotate over several distinct sets (together larger than the 256 MB
 Infinity Cache) so every step reads logits from HBM, not from the last-level cache.
 
+The K timed steps are captured once into a HIP graph and the graph is replayed between two
+events (`ms_per_step`, `value`): the path launches kernels only, so a replay does the work of the
+eager calls without the host's per-launch cost.  `eager_ms_per_step` is the same K steps issued
+call by call, and `path.latency` the per-step time from the routing kernel's start to the plan
+kernel's end over at least 50 eager steps.
+
 Prints one JSON line.  `roofline` describes the dominant kernel (routing + counting):
 algorithmic bytes per launch / its average duration, timed inside the timed region with HIP
 events that the kernel's launch on the bench stream stamps itself (mep_route_layout_plan_timed);
@@ -434,10 +440,10 @@ def main():
     NvS = wl.NvS
     stream = torch.cuda.current_stream()
 
-    def step_call(i, rt=None, pt=None):
+    def step_call(i, rt=None, pt=None, on=None):
         x, ids, w, L, P = sets[i % nsets]
         return B.bound_route_layout_plan(x, K, bias, params, ids, w, A, L, R, S, C, NvS, P, ws_p,
-                                         stream, route_timer=rt, plan_timer=pt)
+                                         on if on is not None else stream, route_timer=rt, plan_timer=pt)
 
     # one prepared call per step (arguments converted once); timed steps stamp two events per
     # kernel through their own launches (mep_route_layout_plan_timed)
@@ -463,6 +469,31 @@ def main():
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
+    ms_eager = ms_step
+
+    # The same K steps captured once into a HIP graph and replayed: the host's per-launch cost
+    # leaves the timed region (the path records kernels only, so a replay writes what the eager
+    # calls write).  The graph's replay time is the headline; the eager loop is reported beside it.
+    gstream = torch.cuda.Stream()
+    gcalls = [step_call(args.warmup + i, on=gstream) for i in range(args.steps)]
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=gstream):
+        for c in gcalls:
+            c()
+    with torch.cuda.stream(gstream):
+        graph.replay()
+    torch.cuda.synchronize()
+    g_start = torch.cuda.Event(enable_timing=True)
+    g_end = torch.cuda.Event(enable_timing=True)
+    g_start.record(gstream)
+    with torch.cuda.stream(gstream):
+        graph.replay()
+    g_end.record(gstream)
+    torch.cuda.synchronize()
+    ms_step = g_start.elapsed_time(g_end) / args.steps
+    del graph
+
     route_us = [t.elapsed_ms() * 1e3 for t in rts]
     plan_us = [t.elapsed_ms() * 1e3 for t in pts]
     step_us = [B.event_elapsed_ms(r.start, p.stop) * 1e3 for r, p in zip(rts, pts)]
@@ -513,7 +544,9 @@ def main():
                                                 "sigmoid+bias, 8 groups keep 4 (top-2 sum), "
                                                 "renorm x2.5" if wl.score_fn else "softmax top-K",
                                                 A, R, S, C),
-                   "buffer_sets": nsets, "call": "mep_route_layout_plan"},
+                   "buffer_sets": nsets, "call": "mep_route_layout_plan",
+                   "timed": "HIP graph of the K steps, replayed"},
+        "eager_ms_per_step": ms_eager,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": route_kernel_name(wl) + " (routing + plan-tile counting)",

@@ -213,3 +213,68 @@ def test_fused_run_twice_identical():
     G, D = [int(v) for v in a[3].dup_offsets[wl.R].tolist()]
     assert torch.equal(a[3].dup_groups[:G], b[3].dup_groups[:G])
     assert torch.equal(a[3].dup_loffs[:D], b[3].dup_loffs[:D])
+
+
+def test_fused_graph_replay_matches_eager():
+    """Three fused steps (different batches, one workspace) captured into a HIP graph and replayed
+    three times, with eager calls and synchronisations between the replays: every replay writes
+    the same bytes as the eager calls (the path records no memset node; the workspace's call
+    counter advances on the device)."""
+    wl = synth.WORKLOADS["dsv3"]
+    inp = synth.make_inputs(wl)
+    N, E, K, A, R, S, C = wl.N, wl.E, wl.K, wl.alignment, wl.R, wl.S, wl.num_channels
+    params = B.route_params(wl.score_fn, wl.renormalize, wl.n_group, wl.topk_group, wl.group_topn, wl.scale)
+    bias = torch.from_numpy(inp.bias).to(DEV)
+    nvs = B.default_nvs(N, E, K, R, A)
+    ws = B.alloc_workspace(B.plan_workspace_size(N, E, K, R, S), DEV)
+    xs = [_dev_logits(np.roll(inp.logits, 97 * i, axis=0), wl.dtype) for i in range(3)]
+
+    def outputs():
+        ids = torch.full((N, K), -9, dtype=torch.int32, device=DEV)
+        w = torch.full((N, K), -9.0, dtype=torch.float32, device=DEV)
+        return ids, w, B.alloc_layout(N, E, K, A, DEV), B.alloc_plan(N, E, K, R, S, C, DEV)
+
+    def snapshot(o):
+        ids, w, L, P = o
+        G, D = [int(v) for v in P.dup_offsets[R].tolist()]
+        return [ids.clone(), w.clone(), L.expanded_to_permuted.clone(), L.permuted_to_expanded.clone(),
+                L.cu_seqlens.clone(), L.zero_fill.clone(), P.dst.clone(), P.channel_prefix_matrix.clone(),
+                P.is_token_in_rank.clone(), P.dup_offsets.clone(), P.dup_groups[:G].clone(),
+                P.dup_loffs[:D].clone()]
+
+    eager = []
+    for x in xs:
+        o = outputs()
+        B.mep_route_layout_plan(x, K, bias, params, o[0], o[1], A, o[2], R, S, C, nvs, o[3], ws)
+        torch.cuda.synchronize()
+        eager.append(snapshot(o))
+
+    gs = torch.cuda.Stream()
+    gouts = [outputs() for _ in xs]
+    calls = [B.bound_route_layout_plan(x, K, bias, params, o[0], o[1], A, o[2], R, S, C, nvs, o[3], ws, gs)
+             for x, o in zip(xs, gouts)]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=gs):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in gouts:
+            o[0].fill_(-9)
+            o[2].expanded_to_permuted.fill_(-9)
+            o[3].dst.fill_(-9)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(gs):
+            g.replay()
+        gs.synchronize()
+        for i, o in enumerate(gouts):
+            got = snapshot(o)
+            for k, (a, b) in enumerate(zip(eager[i], got)):
+                assert torch.equal(a, b), "replay %d, batch %d, output %d" % (rep, i, k)
+        # eager work on the same workspace between replays
+        o = outputs()
+        B.mep_route_layout_plan(xs[rep], K, bias, params, o[0], o[1], A, o[2], R, S, C, nvs, o[3], ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o[0], eager[rep][0])
+    assert ws_error(ws) == 0

@@ -208,16 +208,19 @@ __device__ __forceinline__ int slot_pad(int i) { return i + (i >> 6); }
 // Lanes of this wave (restricted to `active`) holding the same key as the calling lane: one wave
 // ballot per key bit (a wave64 stand-in for a warp match).  NB = key bits, fixed at compile time
 // so the loop unrolls.
+// Per bit, the lanes that agree with the calling lane are ~(ballot ^ m) with m the lane's bit
+// spread over a word, taken on the two 32-bit halves (one three-input bit operation each).
 template <int NB>
 __device__ __forceinline__ uint64_t match_peers(uint32_t key, uint64_t active) {
-    uint64_t peers = active;
+    uint32_t lo = (uint32_t)active, hi = (uint32_t)(active >> 32);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        const bool bit = (key >> b) & 1u;
-        const uint64_t ones = __ballot(bit);
-        peers &= bit ? ones : ~ones;
+        const uint32_t m = 0u - ((key >> b) & 1u);
+        const uint64_t ones = __ballot(m != 0u);
+        lo &= ~((uint32_t)ones ^ m);
+        hi &= ~((uint32_t)(ones >> 32) ^ m);
     }
-    return peers;
+    return ((uint64_t)hi << 32) | lo;
 }
 
 }  // namespace mep

@@ -237,7 +237,8 @@ def test_fused_graph_replay_matches_eager():
     def snapshot(o):
         ids, w, L, P = o
         G, D = [int(v) for v in P.dup_offsets[R].tolist()]
-        return [ids.clone(), w.clone(), L.expanded_to_permuted.clone(), L.permuted_to_expanded.clone(),
+        T = int(L.cu_seqlens[E].item())   # rows past T of permuted_to_expanded are not written
+        return [ids.clone(), w.clone(), L.expanded_to_permuted.clone(), L.permuted_to_expanded[:T].clone(),
                 L.cu_seqlens.clone(), L.zero_fill.clone(), P.dst.clone(), P.channel_prefix_matrix.clone(),
                 P.is_token_in_rank.clone(), P.dup_offsets.clone(), P.dup_groups[:G].clone(),
                 P.dup_loffs[:D].clone()]

@@ -442,6 +442,7 @@ extern "C" int mep_plan_balanced(const int32_t* topk_ids, const int32_t* tokens_
                                  int64_t N, int E, int K, int R, int num_copies, int token_padding,
                                  int64_t capacity, int64_t NvS, const mep_balanced_outputs* out,
                                  void* stream) {
+    mep::launch_begin();
     using namespace mep;
     if (!out || !tokens_per_expert) return MEP_ERR_INVALID_ARG;
     if (N < 0 || E < 1 || K < 1 || R < 1 || num_copies < 0 || token_padding < 1 || capacity < 0 ||
@@ -488,17 +489,17 @@ extern "C" int mep_plan_balanced(const int32_t* topk_ids, const int32_t* tokens_
     a.expert_offsets = out->expert_offsets;
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const int ch_o = chunks64(epn), ch_d = chunks64(E);
-    if (ch_o == 1) hipLaunchKernelGGL(balance_owner_kernel<1>, dim3(R), dim3(kBalBlock), 0, st, a);
-    else if (ch_o == 2) hipLaunchKernelGGL(balance_owner_kernel<2>, dim3(R), dim3(kBalBlock), 0, st, a);
-    else if (ch_o == 4) hipLaunchKernelGGL(balance_owner_kernel<4>, dim3(R), dim3(kBalBlock), 0, st, a);
-    else hipLaunchKernelGGL(balance_owner_kernel<16>, dim3(R), dim3(kBalBlock), 0, st, a);
-    if (ch_d == 1) hipLaunchKernelGGL(balance_dest_kernel<1>, dim3(R), dim3(kBalBlock), 0, st, a);
-    else if (ch_d == 2) hipLaunchKernelGGL(balance_dest_kernel<2>, dim3(R), dim3(kBalBlock), 0, st, a);
-    else if (ch_d == 4) hipLaunchKernelGGL(balance_dest_kernel<4>, dim3(R), dim3(kBalBlock), 0, st, a);
-    else hipLaunchKernelGGL(balance_dest_kernel<16>, dim3(R), dim3(kBalBlock), 0, st, a);
+    if (ch_o == 1) launch_ggl(balance_owner_kernel<1>, dim3(R), dim3(kBalBlock), 0, st, a);
+    else if (ch_o == 2) launch_ggl(balance_owner_kernel<2>, dim3(R), dim3(kBalBlock), 0, st, a);
+    else if (ch_o == 4) launch_ggl(balance_owner_kernel<4>, dim3(R), dim3(kBalBlock), 0, st, a);
+    else launch_ggl(balance_owner_kernel<16>, dim3(R), dim3(kBalBlock), 0, st, a);
+    if (ch_d == 1) launch_ggl(balance_dest_kernel<1>, dim3(R), dim3(kBalBlock), 0, st, a);
+    else if (ch_d == 2) launch_ggl(balance_dest_kernel<2>, dim3(R), dim3(kBalBlock), 0, st, a);
+    else if (ch_d == 4) launch_ggl(balance_dest_kernel<4>, dim3(R), dim3(kBalBlock), 0, st, a);
+    else launch_ggl(balance_dest_kernel<16>, dim3(R), dim3(kBalBlock), 0, st, a);
     if (N > 0) {
         const int64_t waves = ceil_div64(N, 64 / K);
-        hipLaunchKernelGGL(balance_dst_kernel, dim3((unsigned)ceil_div64(waves, kBalTokBlock / 64)),
+        launch_ggl(balance_dst_kernel, dim3((unsigned)ceil_div64(waves, kBalTokBlock / 64)),
                            dim3(kBalTokBlock), 0, st, topk_ids, cu_seqlens, expanded_to_permuted, out->alloc_cumsum,
                            out->expert_offsets, N, E, K, R, NvS, out->dst);
     }

@@ -57,6 +57,14 @@ __device__ __forceinline__ uint64_t status_load(const uint64_t* p) {
 
 constexpr uint32_t kLookbackSpinLimit = 1u << 22;
 
+// Sticky error bit of the workspace header's word 3: a bounded wait ran out (only a misused
+// workspace -- two calls on it at once -- can cause it; the values of that call are then wrong).
+constexpr uint32_t kErrWaitLimit = 1u;
+
+__device__ __forceinline__ void ws_raise(uint32_t* err, uint32_t bits) {
+    if (err) __hip_atomic_fetch_or(gptr(err), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Status word: high 32 bits = tag | inclusive_flag, low 32 bits = value.  The tag has bit 31 set
 // and carries the low 30 bits of the call's epoch, so neither a zero-filled workspace nor the
 // 32-bit counts that other calls with a different geometry store in the same bytes (always below
@@ -78,7 +86,7 @@ __device__ __forceinline__ uint64_t status_make(uint32_t epoch, bool inclusive, 
 constexpr int kLbWin = 32;
 
 __device__ __forceinline__ uint32_t lookback_column(uint64_t* status, int tile, int ncols, int col,
-                                                    uint32_t epoch, uint32_t aggregate) {
+                                                    uint32_t epoch, uint32_t aggregate, uint32_t* err) {
     uint64_t* mine = status + (size_t)tile * ncols + col;
     if (tile == 0) {
         status_store(mine, status_make(epoch, true, aggregate));
@@ -114,7 +122,10 @@ __device__ __forceinline__ uint32_t lookback_column(uint64_t* status, int tile, 
         if (stall) {
             // A predecessor always publishes; the bound only guarantees that a misused workspace
             // (two calls sharing it at once) ends in wrong values, never in a hang.
-            if (++spins > kLookbackSpinLimit) break;
+            if (++spins > kLookbackSpinLimit) {
+                ws_raise(err, kErrWaitLimit);
+                break;
+            }
             __builtin_amdgcn_s_sleep(1);
         }
     }
@@ -126,10 +137,15 @@ __device__ __forceinline__ uint32_t status_value(const uint64_t* status, int til
     return (uint32_t)(status[(size_t)tile * ncols + col]);
 }
 
-// Value of a tagged word written in this call, re-read until its tag is current (bounded).
-__device__ __forceinline__ uint32_t tagged_value(const uint64_t* p, uint64_t v, uint32_t want) {
+// Value of a tagged word written in this call, re-read until its tag is current (bounded: when
+// the bound runs out, the error bit is raised in *err and the stale value is returned).
+__device__ __forceinline__ uint32_t tagged_value(const uint64_t* p, uint64_t v, uint32_t want, uint32_t* err) {
     uint32_t spins = 0;
-    while (((uint32_t)(v >> 32) & ~1u) != want && ++spins < kLookbackSpinLimit) {
+    while (((uint32_t)(v >> 32) & ~1u) != want) {
+        if (++spins >= kLookbackSpinLimit) {
+            ws_raise(err, kErrWaitLimit);
+            break;
+        }
         __builtin_amdgcn_s_sleep(1);
         v = status_load(p);
     }
@@ -167,7 +183,7 @@ constexpr int kDirectCountTiles = 64;
 // Inclusive scan in place of one column over count tiles 0..nct-1 whose words hold tagged totals
 // of this call (re-read until current: their stores may still be in flight from other dies).
 __device__ __forceinline__ void scan_count_column(uint64_t* status, int nct, int ncols, int col,
-                                                  uint32_t epoch) {
+                                                  uint32_t epoch, uint32_t* err) {
     const uint32_t want = status_tag(epoch);
     uint32_t run = 0;
     for (int j0 = 0; j0 < nct; j0 += 32) {  // 32 loads in flight (one round trip at <= 32 count tiles)
@@ -179,7 +195,7 @@ __device__ __forceinline__ void scan_count_column(uint64_t* status, int nct, int
         for (int j = 0; j < 32; ++j) {
             if (j0 + j >= nct) break;
             uint64_t* p = status + (size_t)(j0 + j) * ncols + col;
-            run += tagged_value(p, v[j], want);
+            run += tagged_value(p, v[j], want, err);
             status_store(p, status_make(epoch, true, run));
         }
     }

@@ -1,8 +1,12 @@
 // Host-side helpers shared by the entry points of libmep.so.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <tuple>
+#include <type_traits>
 
 #include "../../include/mep.h"
 
@@ -10,9 +14,41 @@ namespace mep {
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Launch status of an entry point: the first failing return code of its own launches
+// (hipExtLaunchKernel reports each launch's result), never an error that an earlier, unrelated
+// call left in the runtime.  Kept per host thread: launch_begin() at the start of an entry
+// point, launch_status() at its end (which also clears it).
+inline thread_local hipError_t t_launch_error = hipSuccess;
+
+inline void launch_begin() { t_launch_error = hipSuccess; }
+
 inline int launch_status() {
-    hipError_t e = hipGetLastError();
+    const hipError_t e = t_launch_error;
+    t_launch_error = hipSuccess;
     return e == hipSuccess ? MEP_OK : MEP_ERR_DEVICE;
+}
+
+// Launches `kernel` with its arguments converted to the kernel's parameter types; start / stop
+// (may be null) are events the launch itself records around the kernel.
+template <typename... KArgs, typename... Args>
+inline void launch_ext(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t st,
+                       hipEvent_t start, hipEvent_t stop, uint32_t flags, Args&&... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    std::tuple<std::decay_t<KArgs>...> t{static_cast<std::decay_t<KArgs>>(args)...};
+    const hipError_t e = std::apply(
+        [&](auto&... v) {
+            void* p[] = {static_cast<void*>(&v)...};
+            return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, p, shmem, st, start, stop,
+                                      (int)flags);
+        },
+        t);
+    if (e != hipSuccess && t_launch_error == hipSuccess) t_launch_error = e;
+}
+
+template <typename... KArgs, typename... Args>
+inline void launch_ggl(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t st,
+                       Args&&... args) {
+    launch_ext(kernel, grid, block, shmem, st, nullptr, nullptr, 0u, std::forward<Args>(args)...);
 }
 
 inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }

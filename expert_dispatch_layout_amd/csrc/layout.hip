@@ -94,12 +94,12 @@ __global__ __launch_bounds__(kCountBlock) void layout_count_kernel(const int32_t
                 x[b] = b0 + b < nsub_here ? status_load(w.tilehist + (size_t)(t0 + b0 + b) * E + e) : 0;
 #pragma unroll
             for (int b = 0; b < 8; ++b)
-                if (b0 + b < nsub_here) agg += tagged_value(w.tilehist + (size_t)(t0 + b0 + b) * E + e, x[b], want);
+                if (b0 + b < nsub_here) agg += tagged_value(w.tilehist + (size_t)(t0 + b0 + b) * E + e, x[b], want, &hdr->err);
         }
         status_store(w.status + (size_t)ct * E + e, status_make(epoch, false, agg));
     }
     if (last_count_tile(hdr, g.nct, &s_arrived))
-        for (int e = tid; e < E; e += kCountBlock) scan_count_column(w.status, g.nct, E, e, epoch);
+        for (int e = tid; e < E; e += kCountBlock) scan_count_column(w.status, g.nct, E, e, epoch, &hdr->err);
 }
 
 
@@ -196,19 +196,19 @@ static void launch_scatter(const LayoutCall& c, const ScatterSrc& src, int ntile
     const dim3 sgrid(ntiles > 0 ? ntiles : 1), sblock(kScatBlock);
     const int E = c.g.E;
     if (E <= 16)
-        hipLaunchKernelGGL(layout_scatter_kernel<4>, sgrid, sblock, 0, st, c.ids, E, c.A, src, hdr, c.out);
+        launch_ggl(layout_scatter_kernel<4>, sgrid, sblock, 0, st, c.ids, E, c.A, src, hdr, c.out);
     else if (E <= 64)
-        hipLaunchKernelGGL(layout_scatter_kernel<6>, sgrid, sblock, 0, st, c.ids, E, c.A, src, hdr, c.out);
+        launch_ggl(layout_scatter_kernel<6>, sgrid, sblock, 0, st, c.ids, E, c.A, src, hdr, c.out);
     else if (E <= 256)
-        hipLaunchKernelGGL(layout_scatter_kernel<8>, sgrid, sblock, 0, st, c.ids, E, c.A, src, hdr, c.out);
+        launch_ggl(layout_scatter_kernel<8>, sgrid, sblock, 0, st, c.ids, E, c.A, src, hdr, c.out);
     else
-        hipLaunchKernelGGL(layout_scatter_kernel<10>, sgrid, sblock, 0, st, c.ids, E, c.A, src, hdr, c.out);
+        launch_ggl(layout_scatter_kernel<10>, sgrid, sblock, 0, st, c.ids, E, c.A, src, hdr, c.out);
 }
 
 void layout_launch(const LayoutCall& c, hipStream_t st) {
     const LayGeom& g = c.g;
     if (g.nsub > 0)
-        hipLaunchKernelGGL(layout_count_kernel, dim3(g.nsub), dim3(kCountBlock), 0, st, c.ids, g, c.lw, c.hdr);
+        launch_ggl(layout_count_kernel, dim3(g.nsub), dim3(kCountBlock), 0, st, c.ids, g, c.lw, c.hdr);
     ScatterSrc src{};
     src.plan = 0;
     src.lg = g;
@@ -231,6 +231,7 @@ extern "C" int mep_build_layout(const int32_t* topk_ids, int64_t N, int E, int K
                                 int32_t* expanded_to_permuted, int32_t* permuted_to_expanded,
                                 int64_t permuted_cap, int32_t* zero_fill, void* ws, size_t ws_bytes,
                                 void* stream) {
+    mep::launch_begin();
     using namespace mep;
     LayoutCall c;
     const int rc = layout_prepare(topk_ids, N, E, K, alignment, tokens_per_expert, cu_seqlens,

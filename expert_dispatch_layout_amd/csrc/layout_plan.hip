@@ -14,6 +14,7 @@ extern "C" int mep_layout_plan(const int32_t* topk_ids, int64_t N, int E, int K,
                                int32_t* permuted_to_expanded, int64_t permuted_cap, int32_t* zero_fill, int R,
                                int num_src, int num_channels, int64_t NvS, const mep_plan_outputs* out, void* ws,
                                size_t ws_bytes, void* stream) {
+    mep::launch_begin();
     using namespace mep;
     PlanCall pc;
     int rc = plan_prepare(topk_ids, cu_seqlens, expanded_to_permuted, N, E, K, alignment, R, num_src, num_channels,

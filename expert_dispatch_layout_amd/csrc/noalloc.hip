@@ -46,9 +46,9 @@ int scratch_for_current_device(hipStream_t st, void** out) {
     if (!g_ptr[dev]) {
         void* p = nullptr;
         if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MEP_ERR_DEVICE;
-        hipLaunchKernelGGL(scratch_clear_kernel, dim3(256), dim3(256), 0, st, reinterpret_cast<u32x4*>(p),
+        launch_ggl(scratch_clear_kernel, dim3(256), dim3(256), 0, st, reinterpret_cast<u32x4*>(p),
                            kScratchBytes / 16);
-        if (hipGetLastError() != hipSuccess) return MEP_ERR_DEVICE;
+        if (launch_status() != MEP_OK) return MEP_ERR_DEVICE;
         g_ptr[dev] = p;
     }
     *out = g_ptr[dev];
@@ -66,6 +66,7 @@ extern "C" int mep_route_layout_plan_noalloc(const void* logits, int dtype, int6
                                              int32_t* permuted_to_expanded, int64_t permuted_cap,
                                              int32_t* zero_fill, int R, int num_src, int num_channels, int64_t NvS,
                                              const mep_plan_outputs* out, void* stream) {
+    mep::launch_begin();
     using namespace mep;
     // every check first (sizes beyond the array included); nothing is enqueued on an error
     if (N < 0 || E < 1 || K < 1 || R < 1 || num_src < 1) return MEP_ERR_INVALID_ARG;

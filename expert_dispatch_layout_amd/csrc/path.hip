@@ -662,12 +662,12 @@ PathCall path_call(const LayoutCall& lc, const PlanCall& pc, void* ws) {
 }
 
 void path_launch_count(const PathCall& c, hipStream_t st) {
-    hipLaunchKernelGGL(path_count_kernel, dim3(c.g.nwg), dim3(kCountNT), 0, st, c.ids, c.g, c.w, c.hdr);
+    launch_ggl(path_count_kernel, dim3(c.g.nwg), dim3(kCountNT), 0, st, c.ids, c.g, c.w, c.hdr);
 }
 
 void path_launch_plan(const PathCall& c, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
     auto launch = [&](auto kernel) {
-        hipExtLaunchKernelGGL(kernel, dim3(c.g.ntiles), dim3(kPlanNT), 0, st, start, stop, 0, c.ids, c.g, c.w, c.o,
+        launch_ext(kernel, dim3(c.g.ntiles), dim3(kPlanNT), 0, st, start, stop, 0, c.ids, c.g, c.w, c.o,
                               c.hdr);
     };
     const bool wideE = c.g.E > 256;

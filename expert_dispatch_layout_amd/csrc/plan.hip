@@ -280,21 +280,21 @@ __global__ __launch_bounds__(kPlanBlock) void plan_count_kernel(const int32_t* _
                 v[b] = b0 + b < nsub_here ? status_load(w.tilehist + (size_t)(wt0 + b0 + b) * nc + c) : 0;
 #pragma unroll
             for (int b = 0; b < 8; ++b)
-                if (b0 + b < nsub_here) agg += tagged_value(w.tilehist + (size_t)(wt0 + b0 + b) * nc + c, v[b], want);
+                if (b0 + b < nsub_here) agg += tagged_value(w.tilehist + (size_t)(wt0 + b0 + b) * nc + c, v[b], want, &hdr->err);
         }
         if (g.direct) {
             uint64_t* word = c < n3 ? w.status3 + (size_t)ct * n3 + c : w.statusE + (size_t)ct * E + (c - n3);
             status_store(word, status_make(epoch, false, agg));
         } else if (c < n3) {
-            lookback_column(w.status3, ct, n3, c, epoch, agg);
+            lookback_column(w.status3, ct, n3, c, epoch, agg, &hdr->err);
         } else {
-            lookback_column(w.statusE, ct, E, c - n3, epoch, agg);
+            lookback_column(w.statusE, ct, E, c - n3, epoch, agg, &hdr->err);
         }
     }
     if (g.direct && last_count_tile(hdr, g.nct, &s_arrived)) {
         for (int c = tid; c < nc; c += kPlanBlock) {
-            if (c < n3) scan_count_column(w.status3, g.nct, n3, c, epoch);
-            else scan_count_column(w.statusE, g.nct, E, c - n3, epoch);
+            if (c < n3) scan_count_column(w.status3, g.nct, n3, c, epoch, &hdr->err);
+            else scan_count_column(w.statusE, g.nct, E, c - n3, epoch, &hdr->err);
         }
     }
 }
@@ -878,7 +878,7 @@ void plan_launch_count(const PlanCall& c, hipStream_t st) {
     const PlanGeom& g = c.g;
     if (g.ntiles == 0) return;
     auto launch = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, dim3(g.ntiles), dim3(kPlanBlock), 0, st, c.ids, g, c.pw, c.hdr, c.o.itr);
+        launch_ggl(kernel, dim3(g.ntiles), dim3(kPlanBlock), 0, st, c.ids, g, c.pw, c.hdr, c.o.itr);
     };
     if (g.K <= 8) {
         if (g.R <= 32) launch(plan_count_kernel<8, 1>);
@@ -902,7 +902,7 @@ void plan_launch_scatter_write(const LayoutCall& lc, const PlanCall& c, hipStrea
     src.pw = c.pw;
     const int grid = g.ntiles > 0 ? g.ntiles : 1;
     auto launch = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kScatBlock), 0, st, c.ids, lc.A, src, c.hdr, lc.out, c.o);
+        launch_ggl(kernel, dim3(grid), dim3(kScatBlock), 0, st, c.ids, lc.A, src, c.hdr, lc.out, c.o);
     };
     const bool wideE = g.E > 256;  // expert ids need 10 bits for the scatter's wave matching
     if (g.R <= 8) wideE ? launch(plan_scatter_write_kernel<10, 8, 3>) : launch(plan_scatter_write_kernel<8, 8, 3>);
@@ -914,7 +914,7 @@ void plan_launch_write(const PlanCall& c, hipStream_t st) {
     const PlanGeom& g = c.g;
     const int grid = g.ntiles > 0 ? g.ntiles : 1;
     auto launch = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kPlanBlock), 0, st, c.ids, c.cu, c.e2p, g, c.pw, c.hdr, c.o);
+        launch_ggl(kernel, dim3(grid), dim3(kPlanBlock), 0, st, c.ids, c.cu, c.e2p, g, c.pw, c.hdr, c.o);
     };
     if (g.K <= 8) {
         if (g.R <= 8) launch(plan_write_kernel<8, 3>);
@@ -933,6 +933,7 @@ extern "C" int mep_plan(const int32_t* topk_ids, const int32_t* cu_seqlens,
                         const int32_t* expanded_to_permuted, int64_t N, int E, int K, int alignment,
                         int R, int num_src, int num_channels, int64_t NvS, const mep_plan_outputs* out,
                         void* ws, size_t ws_bytes, void* stream) {
+    mep::launch_begin();
     using namespace mep;
     PlanCall c;
     const int rc = plan_prepare(topk_ids, cu_seqlens, expanded_to_permuted, N, E, K, alignment, R, num_src,

@@ -119,6 +119,7 @@ static int route_topk(const void* logits, int dtype, int64_t N, int E, int K, co
 extern "C" int mep_route_topk(const void* logits, int dtype, int64_t N, int E, int K,
                               const float* bias, const mep_route_params* p, int32_t* topk_ids,
                               float* topk_weights, void* stream) {
+    mep::launch_begin();
     const mep::Launch l{reinterpret_cast<hipStream_t>(stream), nullptr, nullptr};
     return mep::route_topk(logits, dtype, N, E, K, bias, p, topk_ids, topk_weights, l);
 }
@@ -127,6 +128,7 @@ extern "C" int mep_route_topk_timed(const void* logits, int dtype, int64_t N, in
                                     const float* bias, const mep_route_params* p,
                                     int32_t* topk_ids, float* topk_weights, void* stream,
                                     void* start_event, void* stop_event) {
+    mep::launch_begin();
     const mep::Launch l{reinterpret_cast<hipStream_t>(stream),
                         reinterpret_cast<hipEvent_t>(start_event),
                         reinterpret_cast<hipEvent_t>(stop_event)};

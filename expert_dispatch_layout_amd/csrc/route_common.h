@@ -52,7 +52,7 @@ struct Launch {
 template <typename F, typename... Args>
 inline void launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t shmem, const Launch& l,
                           Args... args) {
-    hipExtLaunchKernelGGL(kernel, grid, block, shmem, l.st, l.start, l.stop, 0, args...);
+    launch_ext(kernel, grid, block, shmem, l.st, l.start, l.stop, 0, args...);
 }
 
 constexpr int kRouteBlock = 256;

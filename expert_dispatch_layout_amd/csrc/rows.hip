@@ -192,6 +192,7 @@ int rows_check(const void* a, int dtype, int64_t N, int64_t H, int K, const int3
 extern "C" int mep_permute_rows(const void* x, int dtype, int64_t N, int64_t H, int K,
                                 const int32_t* expanded_to_permuted, const int32_t* zero_fill, int E,
                                 void* x_permuted, int64_t permuted_rows, void* stream) {
+    mep::launch_begin();
     using namespace mep;
     int64_t vpr = 0;
     int rc = rows_check(x, dtype, N, H, K, expanded_to_permuted, permuted_rows, x_permuted, vpr);
@@ -203,7 +204,7 @@ extern "C" int mep_permute_rows(const void* x, int dtype, int64_t N, int64_t H, 
     const int64_t grid = tok_blocks + zb;
     if (grid == 0) return MEP_OK;
     if (grid > INT32_MAX) return MEP_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(permute_rows_kernel, dim3((unsigned)grid), dim3(kRowBlock), 0,
+    launch_ggl(permute_rows_kernel, dim3((unsigned)grid), dim3(kRowBlock), 0,
                        reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const u32x4*>(x), N, vpr,
                        K, expanded_to_permuted, zero_fill, zb, permuted_rows,
                        reinterpret_cast<u32x4*>(x_permuted));
@@ -213,6 +214,7 @@ extern "C" int mep_permute_rows(const void* x, int dtype, int64_t N, int64_t H, 
 extern "C" int mep_combine_rows(const void* y_permuted, int dtype, int64_t N, int64_t H, int K,
                                 const int32_t* expanded_to_permuted, const float* topk_weights,
                                 int64_t permuted_rows, void* out, void* stream) {
+    mep::launch_begin();
     using namespace mep;
     int64_t vpr = 0;
     int rc = rows_check(y_permuted, dtype, N, H, K, expanded_to_permuted, permuted_rows, out, vpr);
@@ -225,16 +227,16 @@ extern "C" int mep_combine_rows(const void* y_permuted, int dtype, int64_t N, in
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const bool bf = dtype == MEP_BF16;
     if (bf && topk_weights)
-        hipLaunchKernelGGL((combine_rows_kernel<true, true>), dim3((unsigned)grid), dim3(kRowBlock), 0, st, yy,
+        launch_ggl((combine_rows_kernel<true, true>), dim3((unsigned)grid), dim3(kRowBlock), 0, st, yy,
                            N, vpr, K, expanded_to_permuted, topk_weights, permuted_rows, oo);
     else if (bf)
-        hipLaunchKernelGGL((combine_rows_kernel<true, false>), dim3((unsigned)grid), dim3(kRowBlock), 0, st, yy,
+        launch_ggl((combine_rows_kernel<true, false>), dim3((unsigned)grid), dim3(kRowBlock), 0, st, yy,
                            N, vpr, K, expanded_to_permuted, topk_weights, permuted_rows, oo);
     else if (topk_weights)
-        hipLaunchKernelGGL((combine_rows_kernel<false, true>), dim3((unsigned)grid), dim3(kRowBlock), 0, st,
+        launch_ggl((combine_rows_kernel<false, true>), dim3((unsigned)grid), dim3(kRowBlock), 0, st,
                            yy, N, vpr, K, expanded_to_permuted, topk_weights, permuted_rows, oo);
     else
-        hipLaunchKernelGGL((combine_rows_kernel<false, false>), dim3((unsigned)grid), dim3(kRowBlock), 0, st,
+        launch_ggl((combine_rows_kernel<false, false>), dim3((unsigned)grid), dim3(kRowBlock), 0, st,
                            yy, N, vpr, K, expanded_to_permuted, topk_weights, permuted_rows, oo);
     return launch_status();
 }

@@ -34,6 +34,7 @@ __global__ __launch_bounds__(kEvalBlock) void sigmoid_eval_kernel(const float* _
 
 extern "C" int mep_sigmoid_eval(const float* x, int64_t n, float* cr_out, float* filter_out, double* weight_out,
                                 void* stream) {
+    mep::launch_begin();
     using namespace mep;
     if (n < 0 || (n > 0 && !x)) return MEP_ERR_INVALID_ARG;
     if (!mep::aligned(x, 4) || !mep::aligned(cr_out, 4) || !mep::aligned(filter_out, 4) ||
@@ -42,7 +43,7 @@ extern "C" int mep_sigmoid_eval(const float* x, int64_t n, float* cr_out, float*
     if (n == 0 || (!cr_out && !filter_out && !weight_out)) return MEP_OK;
     int64_t grid = ceil_div64(n, kEvalBlock);
     if (grid > kEvalMaxGrid) grid = kEvalMaxGrid;
-    hipLaunchKernelGGL(sigmoid_eval_kernel, dim3((unsigned)grid), dim3(kEvalBlock), 0,
+    launch_ggl(sigmoid_eval_kernel, dim3((unsigned)grid), dim3(kEvalBlock), 0,
                        reinterpret_cast<hipStream_t>(stream), x, n, cr_out, filter_out, weight_out);
     return launch_status();
 }

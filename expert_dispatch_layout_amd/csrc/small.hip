@@ -482,6 +482,7 @@ extern "C" int mep_route_layout_plan(const void* logits, int dtype, int64_t N, i
                                      int64_t permuted_cap, int32_t* zero_fill, int R, int num_src,
                                      int num_channels, int64_t NvS, const mep_plan_outputs* out, void* ws,
                                      size_t ws_bytes, void* stream) {
+    mep::launch_begin();
     return mep::route_layout_plan(logits, dtype, N, E, K, bias, p, topk_ids, topk_weights, alignment,
                                   tokens_per_expert, cu_seqlens, expanded_to_permuted, permuted_to_expanded,
                                   permuted_cap, zero_fill, R, num_src, num_channels, NvS, out, ws, ws_bytes, stream,
@@ -497,6 +498,7 @@ extern "C" int mep_route_layout_plan_timed(const void* logits, int dtype, int64_
                                            const mep_plan_outputs* out, void* ws, size_t ws_bytes, void* stream,
                                            void* route_start, void* route_stop, void* plan_start,
                                            void* plan_stop) {
+    mep::launch_begin();
     const mep::StepEvents ev{reinterpret_cast<hipEvent_t>(route_start), reinterpret_cast<hipEvent_t>(route_stop),
                              reinterpret_cast<hipEvent_t>(plan_start), reinterpret_cast<hipEvent_t>(plan_stop)};
     return mep::route_layout_plan(logits, dtype, N, E, K, bias, p, topk_ids, topk_weights, alignment,

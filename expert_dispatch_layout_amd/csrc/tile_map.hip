@@ -103,6 +103,7 @@ __global__ __launch_bounds__(kTmBlock) void tile_map_kernel(const int32_t* __res
 extern "C" int mep_tile_map(const int32_t* tokens_per_expert, int E, int64_t num_slots, int tile,
                             int32_t* cta_to_expert, int32_t* cta_mn_limit, int64_t cap_ctas,
                             int32_t* permuted_idx_size, int32_t* num_ctas, void* stream) {
+    mep::launch_begin();
     using namespace mep;
     if (!tokens_per_expert || E < 1 || tile < 1 || num_slots < 0 || cap_ctas < 0)
         return MEP_ERR_INVALID_ARG;
@@ -120,7 +121,7 @@ extern "C" int mep_tile_map(const int32_t* tokens_per_expert, int E, int64_t num
     int64_t grid = ceil_div64(cap, kTmBlock);
     if (grid > kTmMaxGrid) grid = kTmMaxGrid;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(tile_map_kernel, dim3((unsigned)grid), dim3(kTmBlock), 0,
+    launch_ggl(tile_map_kernel, dim3((unsigned)grid), dim3(kTmBlock), 0,
                        reinterpret_cast<hipStream_t>(stream), tokens_per_expert, E, tile, cta_to_expert,
                        cta_mn_limit, (int)cap, permuted_idx_size, num_ctas);
     return launch_status();

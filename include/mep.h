@@ -52,6 +52,11 @@
  *   - Optional outputs are marked "nullable"; NULL skips them.  With N == 0 the per-slot
  *     inputs and outputs (logits, ids, weights, permutation maps, dst) may be NULL.
  *   - No exceptions cross the ABI; mep_status_string names a return code.
+ *   - Word 3 of every layout / plan workspace (uint32 at byte 12) holds sticky
+ *     error bits: bit 0 is set when a bounded wait of a kernel ran out, which
+ *     only overlapping calls on one workspace can cause (the results of such a
+ *     call are wrong).  The library never clears it; zero-filling the
+ *     workspace does.
  */
 #ifndef MEP_H_
 #define MEP_H_
@@ -68,7 +73,9 @@ extern "C" {
 #define MEP_ERR_INVALID_ARG 1 /* NULL required pointer, bad enum, bad size, misalignment */
 #define MEP_ERR_UNSUPPORTED 2 /* outside the supported envelope (see each call) */
 #define MEP_ERR_CAPACITY 3    /* caller capacity or workspace below the bound */
-#define MEP_ERR_DEVICE 4      /* the HIP runtime reported an error on launch */
+#define MEP_ERR_DEVICE 4      /* a kernel launch of this call failed (its own return
+                                 code; errors earlier calls left in the runtime are not
+                                 reported) */
 
 /* Logit element types. */
 #define MEP_F32 0  /* IEEE binary32 */
@@ -278,9 +285,7 @@ size_t mep_plan_workspace_size(int64_t N, int E, int K, int R, int num_src);
  * scratch of the call, with the rules of every workspace (zero-filled before
  * first use, calls sharing it ordered).  It may be shared with mep_plan and
  * mep_route_layout_plan calls of any size, not with mep_build_layout calls.
- * Word 3 of the workspace (uint32 at byte 12) holds sticky error bits: it
- * stays 0 unless a bounded wait of the count-tile kernels ran out, which only
- * overlapping calls on one workspace can cause.
+ * Word 3 of the workspace holds the sticky error bits described above.
  */
 int mep_layout_plan(const int32_t* topk_ids, int64_t N, int E, int K, int alignment,
                     int32_t* tokens_per_expert, int32_t* cu_seqlens,

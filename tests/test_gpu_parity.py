@@ -406,3 +406,19 @@ def test_route_candidate_overflow_takes_exact_path(E, K, dtype):
     if dtype == synth.BF16:
         x = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     check_route(x, K, dtype)
+
+
+def test_earlier_runtime_error_is_not_reported_as_this_calls():
+    """An error that an unrelated HIP call left in the runtime's last-error slot is not returned
+    as the status of a later, successful entry-point call: each call reports the return codes of
+    its own launches."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipGetDeviceCount.argtypes = [ctypes.c_void_p]
+    assert hip.hipGetDeviceCount(None) != 0          # invalid argument: leaves a last error
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((512, 64)).astype(np.float32)
+    ids, w = gpu_route(x, 4, synth.F32)              # raises MepError if the call reports failure
+    ids_o, _ = oracle.route(x, 4)
+    assert np.array_equal(ids, ids_o)
+    hip.hipGetLastError()

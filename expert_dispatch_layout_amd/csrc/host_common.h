@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <tuple>
 #include <type_traits>
 
@@ -52,6 +53,21 @@ inline void launch_ggl(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t
 }
 
 inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Compute units of the current device (cached per device; 256 if the query fails).
+inline int device_units() {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 

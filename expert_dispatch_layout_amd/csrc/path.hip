@@ -32,10 +32,11 @@ namespace mep {
 namespace {
 
 constexpr int kCountNT = 512;
-constexpr int kPlanNT = 1024;
+// Plan-tile workgroups: 1024 threads when every tile has a compute unit of its own, else 512
+// (two tiles per compute unit at once, whose dependent chains then overlap).
+constexpr int kPlanNTBig = 1024;
+constexpr int kPlanNTSmall = 512;
 constexpr int kPlanRowNT = 512;  // threads that load the prefix rows (at most 7 row slices to sum)
-constexpr int kPlanW = kPlanNT / 64;
-constexpr int kPlanIters = kPathSlots / kPlanNT;   // 64-slot steps per wave, at most
 enum : uint32_t { kSlotPlain = 0, kSlotHead = 1, kSlotDup = 2 };
 
 __device__ __forceinline__ uint32_t slot_code(int e, uint32_t type, int r, int h) {
@@ -158,12 +159,13 @@ __device__ __forceinline__ void path_scan_totals(const PathGeom& g, const int* s
 
 // By one workgroup: cu_seqlens, tokens_per_expert, zero_fill ([MOON] zero-fill ranges), the
 // receive counts, offsets and zero-fill ranges ([DEEP] notify_dispatch), dedup counts and offsets.
+template <int NT>
 __device__ __forceinline__ void path_small_outputs(const PathGeom& g, const PathOut& o, const int* s_tot,
                                                    const int* s_cu, const int (*s_doff)[kPathMaxR + 1]) {
     const int tid = threadIdx.x;
     const int E = g.E, R = g.R;
-    for (int e = tid; e <= E; e += kPlanNT) gptr(o.cu_seqlens)[e] = s_cu[e];
-    for (int e = tid; e < E; e += kPlanNT) {
+    for (int e = tid; e <= E; e += NT) gptr(o.cu_seqlens)[e] = s_cu[e];
+    for (int e = tid; e < E; e += NT) {
         const int c = s_tot[e];
         const int cu0 = s_cu[e];
         const int padded = s_cu[e + 1] - cu0;
@@ -179,7 +181,7 @@ __device__ __forceinline__ void path_small_outputs(const PathGeom& g, const Path
             gptr(o.p.recv_zf)[2 * e + 1] = z ? padded - c : 0;
         }
     }
-    for (int r = tid; r <= R; r += kPlanNT) {
+    for (int r = tid; r <= R; r += NT) {
         if (o.p.dup_offsets) {
             gptr(o.p.dup_offsets)[2 * r] = s_doff[0][r];
             gptr(o.p.dup_offsets)[2 * r + 1] = s_doff[1][r];
@@ -193,7 +195,7 @@ __device__ __forceinline__ void path_small_outputs(const PathGeom& g, const Path
         }
     }
     if (o.p.recv_cu)
-        for (int p = tid; p < R * (g.epn + 1); p += kPlanNT) {
+        for (int p = tid; p < R * (g.epn + 1); p += NT) {
             const int r = p / (g.epn + 1);
             const int jj = p - r * (g.epn + 1);
             gptr(o.p.recv_cu)[p] = s_cu[r * g.epn + jj] - s_cu[r * g.epn];
@@ -202,9 +204,11 @@ __device__ __forceinline__ void path_small_outputs(const PathGeom& g, const Path
 
 // ---- plan-tile kernel --------------------------------------------------------------------------
 
-template <int NBE, int NBR>
+template <int NBE, int NBR, int kPlanNT>
 __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __restrict__ ids, PathGeom g,
                                                             PathWs w, PathOut o, WsHeader* hdr) {
+    constexpr int kPlanW = kPlanNT / 64;
+    constexpr int kPlanIters = kPathSlots / kPlanNT;  // 64-slot steps per wave, at most
     __shared__ __align__(16) uint32_t s_code[kPathSlots];
     __shared__ int s_ecnt[kPlanW][kPathMaxE];
     __shared__ int s_rcnt[kPlanW][2][kPathMaxR];
@@ -431,7 +435,7 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
         }
     }
     __syncthreads();
-    if (j == 0) path_small_outputs(g, o, s_tot, s_cu, s_doff);
+    if (j == 0) path_small_outputs<kPlanNT>(g, o, s_tot, s_cu, s_doff);
 
     // ---- stable ranks within the waves ------------------------------------------------------------
     const int spw = ((ns + kPlanNT - 1) / kPlanNT) * 64;  // slots per wave, a multiple of 64
@@ -666,13 +670,19 @@ void path_launch_count(const PathCall& c, hipStream_t st) {
 }
 
 void path_launch_plan(const PathCall& c, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-    auto launch = [&](auto kernel) {
-        launch_ext(kernel, dim3(c.g.ntiles), dim3(kPlanNT), 0, st, start, stop, 0, c.ids, c.g, c.w, c.o,
-                              c.hdr);
+    auto launch = [&](auto kernel, int nt) {
+        launch_ext(kernel, dim3(c.g.ntiles), dim3(nt), 0, st, start, stop, 0, c.ids, c.g, c.w, c.o, c.hdr);
     };
-    const bool wideE = c.g.E > 256;
-    if (c.g.R <= 8) wideE ? launch(path_plan_kernel<9, 3>) : launch(path_plan_kernel<8, 3>);
-    else wideE ? launch(path_plan_kernel<9, 5>) : launch(path_plan_kernel<8, 5>);
+    const bool wideE = c.g.E > 256, wideR = c.g.R > 8;
+    if (c.g.ntiles <= device_units()) {
+        constexpr int NT = kPlanNTBig;
+        if (!wideR) wideE ? launch(path_plan_kernel<9, 3, NT>, NT) : launch(path_plan_kernel<8, 3, NT>, NT);
+        else wideE ? launch(path_plan_kernel<9, 5, NT>, NT) : launch(path_plan_kernel<8, 5, NT>, NT);
+    } else {
+        constexpr int NT = kPlanNTSmall;
+        if (!wideR) wideE ? launch(path_plan_kernel<9, 3, NT>, NT) : launch(path_plan_kernel<8, 3, NT>, NT);
+        else wideE ? launch(path_plan_kernel<9, 5, NT>, NT) : launch(path_plan_kernel<8, 5, NT>, NT);
+    }
 }
 
 }  // namespace mep

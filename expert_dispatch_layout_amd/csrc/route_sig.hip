@@ -1,7 +1,5 @@
 // Shape dispatch of the sigmoid routing kernel (route_sig.h): plain routing (mep_route_topk) and
 // routing that also counts the plan tiles it owns (the routing phase of the fused path).
-#include <mutex>
-
 #include "route_sig.h"
 
 namespace mep {
@@ -10,20 +8,6 @@ namespace {
 
 constexpr int kSigWaves = 8;         // one workgroup of 8 waves per compute unit
 constexpr size_t kLdsLimit = 160 * 1024;
-
-int device_units() {
-    static std::mutex mu;
-    static int cache[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    std::lock_guard<std::mutex> lock(mu);
-    if (cache[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
-        cache[dev] = n;
-    }
-    return cache[dev];
-}
 
 // Static LDS of a kernel (bytes).
 size_t static_lds(const void* kernel) {

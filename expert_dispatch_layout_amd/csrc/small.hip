@@ -1,8 +1,10 @@
 // mep_route_layout_plan: routing, layout and plan of one batch in one call.  Small batches
 // (decode sizes) run as one kernel of one workgroup, in the spirit of TensorRT-LLM
 // RoutingKernel.cuh's routingPermutation (the whole routing permutation of a small batch inside
-// one cluster, without a second launch); larger batches take the three kernels of
-// mep_route_topk followed by mep_layout_plan.  Results are identical either way.
+// one cluster, without a second launch); larger batches take the plan-tile path (path.h): the
+// routing kernel, which for sigmoid routing also counts the plan tiles it routes (else the
+// counting kernel does, after routing), then the plan-tile kernel.  Results are identical to
+// mep_route_topk followed by mep_build_layout and mep_plan either way.
 //
 // The one-workgroup kernel (512 threads) keeps every slot's expert and permuted position in
 // LDS and walks the phases with barriers in between:

@@ -160,6 +160,27 @@ def test_group_limit_with_all_groups_kept_is_plain_topk():
 # Weights: closed forms
 # ---------------------------------------------------------------------------------------------
 
+@pytest.mark.parametrize("nthreads", [1, 3, 16])
+def test_threaded_routing_equals_serial(nthreads):
+    """The CPU baseline's threaded routing (contiguous token ranges on threads) returns the serial
+    oracle's ids and weights bit for bit, for softmax and for group-limited sigmoid routing, with
+    more threads than tokens too."""
+    rng = np.random.default_rng(nthreads)
+    x = rng.standard_normal((37, 64)).astype(np.float32)
+    a = oracle.route(x, 4)
+    b = oracle.route_threads(x, 4, nthreads)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    bias = rng.uniform(-0.1, 0.1, 64).astype(np.float32)
+    kw = dict(bias=bias, score_fn=oracle.SIGMOID, n_group=2, topk_group=1, group_topn=2, scale=2.5)
+    a = oracle.route(x, 4, **kw)
+    b = oracle.route_threads(x, 4, nthreads, **kw)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    xs = x[:2]
+    a = oracle.route(xs, 4, **kw)
+    b = oracle.route_threads(xs, 4, 16, **kw)
+    assert np.array_equal(a[0], b[0])
+
+
 def test_weights_k1_equal_scale():
     rng = np.random.default_rng(5)
     x = rng.standard_normal((50, 16)).astype(np.float32)

@@ -10,21 +10,21 @@
 // source-then-token order is global slot order.  So only the E totals enter the planning
 // steps, and no per-source counts are formed.
 //
-// Three kernels:
-//   owner   one workgroup per owner rank.  Wave 0 runs the balancing loop itself (every
-//           workgroup gets the same moves; workgroup 0 stores z, the group totals and clears
-//           remote_stats) and then hands the owner's moves out to its experts; the owner's
-//           columns of alloc and the rows of alloc_cumsum of its experts are written from LDS.
-//   dest    one workgroup per destination rank: the B experts to copy (wave 0, B wave-wide
-//           arg-max passes over the remote counts held in registers), then the E + B groups
-//           scanned across the workgroup; remote_stats[owner][1] is counted with one global
-//           atomic add per copy.
+// Two kernels:
+//   plan    one workgroup per destination rank d.  Wave 0 runs the balancing loop (every
+//           workgroup gets the same moves; workgroup 0 stores z and the group totals); then
+//           the waves run the owners' quota loops, owner o on wave o mod 4, each appending its
+//           (destination, expert, slots) allocations to an LDS list and leaving each expert's
+//           remainder with its owner; the owners' loops are short and run in every workgroup,
+//           which is cheaper than a second launch.  From the list the workgroup forms row d of
+//           alloc, the alloc_cumsum rows of d's own experts, and then, as destination: the B
+//           experts to copy (B wave-wide arg-max passes over the remote counts held in
+//           registers) and the E + B groups scanned across the workgroup.
 //   dst     one lane per slot, whole tokens per wave: each slot's rank by binary search over
 //           its expert's cumulative allocation (L2-resident), its row from the group offsets,
-//           and the duplicate encoding from the ranks of the token's earlier slots (shuffles).
-// The loops are the page's, so each stops: every balancing step zeroes one deficit for good
-// and a rank turns from surplus to deficit at most once (at most 2R steps); every quota step
-// zeroes a quota or an expert's remainder (at most R + epn steps).
+//           and the duplicate encoding from the ranks of the token's earlier slots (shuffles);
+//           workgroup 0 also counts each owner's copies (remote_stats[o][1]) from
+//           experts_to_copy.
 #include <hip/hip_runtime.h>
 #include <limits.h>
 
@@ -111,21 +111,35 @@ __device__ __forceinline__ int key_index_low(long long k) { return (int)(kIdxSpa
 __device__ __forceinline__ int key_index(long long k) { return (int)(k - key_value(k) * kIdxSpan); }
 
 // ---------------------------------------------------------------------------------------------
-// owner kernel
+// plan kernel (balancing, owners' quotas, destination groups)
 // ---------------------------------------------------------------------------------------------
+constexpr int kBalWaves = kBalBlock / 64;
+// allocation entries: each quota step zeroes a quota or an expert's remainder, and the nonzero
+// quotas are the moves (at most 2R + 1 of them), so all owners together make at most
+// moves + E entries
+constexpr int kBalMaxEntries = 2 * kBalMaxRanks + 1 + kBalMaxExperts;
+
 template <int CH>
-__global__ __launch_bounds__(kBalBlock) void balance_owner_kernel(BalArgs a) {
-    __shared__ int s_zrow[kBalMaxRanks];          // moves from this owner to each rank
-    __shared__ int s_alloc[kBalMaxExperts];       // [R][epn] of this owner's experts
+__global__ __launch_bounds__(kBalBlock) void balance_plan_kernel(BalArgs a) {
     __shared__ int s_group[kBalMaxRanks];         // slots per rank before moves
     __shared__ int s_tot[kBalMaxExperts];         // slots per expert
     __shared__ int s_moves[3 * (2 * kBalMaxRanks + 1)];  // (from, to, slots) of each move
     __shared__ int s_nmoves;
-    const int o = blockIdx.x;
+    __shared__ int s_ent[kBalMaxEntries][3];      // (destination, expert, slots) allocations
+    __shared__ int s_nent;
+    __shared__ int s_rem[kBalMaxExperts];         // each expert's slots left with its owner
+    __shared__ int s_acol[kBalMaxExperts];        // [R][epn]: d's experts' slots per rank
+    __shared__ int s_cnt[kBalMaxExperts];         // row d of alloc
+    __shared__ int s_eoff[kBalMaxExperts];
+    __shared__ unsigned char s_picked[kBalMaxExperts];
+    __shared__ int s_slot[kBalMaxCopies];
+    __shared__ int s_wave[kBalWaves];
+    const int d = blockIdx.x;
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int R = a.R, epn = a.epn, E = a.E;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int R = a.R, epn = a.epn, E = a.E, B = a.B, G = E + B;
     constexpr int kPerT = kBalMaxExperts / kBalBlock;
+    constexpr int kCh = CH;  // 64-wide chunks covering the experts
 
     int tot[kPerT];  // loads first, so their latency overlaps the clearing below
 #pragma unroll
@@ -133,15 +147,15 @@ __global__ __launch_bounds__(kBalBlock) void balance_owner_kernel(BalArgs a) {
         const int e = tid + i * kBalBlock;
         tot[i] = e < E ? a.tpe[e] : 0;
     }
-    for (int i = tid; i < R; i += kBalBlock) {
-        s_zrow[i] = 0;
-        s_group[i] = 0;
+    for (int i = tid; i < R; i += kBalBlock) s_group[i] = 0;
+    for (int i = tid; i < E; i += kBalBlock) {
+        s_acol[i] = 0;
+        s_eoff[i] = -1;
+        s_picked[i] = 0;
     }
-    for (int i = tid; i < R * epn; i += kBalBlock) s_alloc[i] = 0;
-    if (o == 0) {
+    if (tid == 0) s_nent = 0;
+    if (d == 0)
         for (int i = tid; i < R * R; i += kBalBlock) a.z[i] = 0;
-        for (int i = tid; i < 2 * R; i += kBalBlock) a.remote_stats[i] = 0;
-    }
     lds_barrier();
 #pragma unroll
     for (int i = 0; i < kPerT; ++i) {
@@ -153,17 +167,17 @@ __global__ __launch_bounds__(kBalBlock) void balance_owner_kernel(BalArgs a) {
     }
     lds_barrier();
 
-    if (tid < 64) {
+    // ---- balancing loop (wave 0) ----------------------------------------------------------------
+    if (wv == 0) {
         // lane holds ranks lane and lane + 64
         long long bal[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int r = lane + 64 * c;
-            const long long s = r < R ? s_group[r] : 0;
-            if (r < R && o == 0) a.group_tokens[r] = (int32_t)s;
-            bal[c] = s - a.cap;
+            const long long s2 = r < R ? s_group[r] : 0;
+            if (r < R && d == 0) a.group_tokens[r] = (int32_t)s2;
+            bal[c] = s2 - a.cap;
         }
-        // balancing loop
         int nmoves = 0;
         for (;;) {
             long long kmax = LLONG_MIN, kmin = LLONG_MAX;
@@ -192,24 +206,31 @@ __global__ __launch_bounds__(kBalBlock) void balance_owner_kernel(BalArgs a) {
                 s_moves[3 * nmoves] = sr;
                 s_moves[3 * nmoves + 1] = dr;
                 s_moves[3 * nmoves + 2] = (int)move;
-                if (sr == o) s_zrow[dr] = (int)move;
             }
             ++nmoves;
         }
         if (lane == 0) s_nmoves = nmoves;
-        // quota allocation of this owner's moves over its experts
+    }
+    lds_barrier();
+
+    // ---- quota allocation of every owner's moves over its experts (owner o on wave o mod 4) ----
+    const int nmoves = s_nmoves;
+    for (int o = wv; o < R; o += kBalWaves) {
         long long quota[2];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int r = lane + 64 * c;
-            quota[c] = r < R ? s_zrow[r] : 0;
+        for (int c = 0; c < 2; ++c) quota[c] = 0;
+        for (int m = 0; m < nmoves; ++m) {  // a (from, to) pair occurs at most once
+            if (s_moves[3 * m] != o) continue;
+            const int to = s_moves[3 * m + 1];
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                if (lane + 64 * c == to) quota[c] = s_moves[3 * m + 2];
         }
-        constexpr int kCh = CH;  // 64-wide chunks of the owner's experts
         long long rem[kCh];
 #pragma unroll
         for (int c = 0; c < kCh; ++c) {
-            const int j = lane + 64 * c;
-            rem[c] = j < epn ? s_tot[o * epn + j] : 0;
+            const int jj = lane + 64 * c;
+            rem[c] = jj < epn ? s_tot[o * epn + jj] : 0;
         }
         for (;;) {
             long long kq = LLONG_MIN;
@@ -227,9 +248,9 @@ __global__ __launch_bounds__(kBalBlock) void balance_owner_kernel(BalArgs a) {
             long long kr = LLONG_MIN;
 #pragma unroll
             for (int c = 0; c < kCh; ++c) {
-                const int j = lane + 64 * c;
-                if (j < epn) {
-                    const long long k = key_max_low(rem[c], j);
+                const int jj = lane + 64 * c;
+                if (jj < epn) {
+                    const long long k = key_max_low(rem[c], jj);
                     kr = k > kr ? k : kr;
                 }
             }
@@ -244,59 +265,50 @@ __global__ __launch_bounds__(kBalBlock) void balance_owner_kernel(BalArgs a) {
 #pragma unroll
             for (int c = 0; c < kCh; ++c)
                 if (lane + 64 * c == sj) rem[c] -= take;
-            if (lane == 0) s_alloc[tr * epn + sj] = (int)take;
+            if (lane == 0) {
+                const int at = atomicAdd(&s_nent, 1);
+                s_ent[at][0] = tr;
+                s_ent[at][1] = o * epn + sj;
+                s_ent[at][2] = (int)take;
+            }
         }
 #pragma unroll
         for (int c = 0; c < kCh; ++c) {
-            const int j = lane + 64 * c;
-            if (j < epn) s_alloc[o * epn + j] = (int)rem[c];
+            const int jj = lane + 64 * c;
+            if (jj < epn) s_rem[o * epn + jj] = (int)rem[c];
         }
     }
     lds_barrier();
-    // this owner's columns of alloc, and its experts' rows of alloc_cumsum
-    for (int i = tid; i < R * epn; i += kBalBlock) {
-        const int r = i / epn, j = i - r * epn;
-        a.alloc[r * E + o * epn + j] = s_alloc[i];
+
+    // ---- row d of alloc, and the alloc_cumsum rows of d's own experts ----------------------------
+    for (int e = tid; e < E; e += kBalBlock) s_cnt[e] = e / epn == d ? s_rem[e] : 0;
+    for (int j = tid; j < epn; j += kBalBlock) s_acol[d * epn + j] = s_rem[d * epn + j];
+    lds_barrier();
+    const int nent = s_nent;
+    for (int i = tid; i < nent; i += kBalBlock) {
+        const int to = s_ent[i][0], e = s_ent[i][1], take = s_ent[i][2];
+        if (to == d) s_cnt[e] = take;                       // e's owner is not d (moves leave d)
+        if (e / epn == d) s_acol[to * epn + (e - d * epn)] = take;
     }
+    lds_barrier();
+    for (int e = tid; e < E; e += kBalBlock) a.alloc[d * E + e] = s_cnt[e];
     for (int j = tid; j < epn; j += kBalBlock) {
         int run = 0;
-        int32_t* row = a.alloc_cumsum + (int64_t)(o * epn + j) * R;
+        int32_t* row = a.alloc_cumsum + (int64_t)(d * epn + j) * R;
         for (int r = 0; r < R; ++r) {
-            run += s_alloc[r * epn + j];
+            run += s_acol[r * epn + j];
             row[r] = run;
         }
     }
-    if (o == 0) {
+    if (d == 0) {
         // the moves go over the zeros stored at the start: a full barrier orders the two
         __syncthreads();
-        for (int m = tid; m < s_nmoves; m += kBalBlock)
+        for (int m = tid; m < nmoves; m += kBalBlock)
             a.z[s_moves[3 * m] * R + s_moves[3 * m + 1]] = s_moves[3 * m + 2];
     }
-}
 
-// ---------------------------------------------------------------------------------------------
-// destination kernel
-// ---------------------------------------------------------------------------------------------
-template <int CH>
-__global__ __launch_bounds__(kBalBlock) void balance_dest_kernel(BalArgs a) {
-    __shared__ int s_cnt[kBalMaxExperts];
-    __shared__ int s_eoff[kBalMaxExperts];
-    __shared__ unsigned char s_picked[kBalMaxExperts];
-    __shared__ int s_slot[kBalMaxCopies];
-    __shared__ int s_wave[kBalBlock / 64];
-    const int d = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wv = tid >> 6;
-    const int E = a.E, B = a.B, epn = a.epn, G = E + B;
-
-    for (int e = tid; e < E; e += kBalBlock) {
-        s_cnt[e] = a.alloc[d * E + e];
-        s_eoff[e] = -1;
-        s_picked[e] = 0;
-    }
-    lds_barrier();
-    if (tid < 64) {
-        constexpr int kCh = CH;  // 64-wide chunks of the experts
+    // ---- destination d: experts to copy, then the E + B groups ----------------------------------
+    if (wv == 0) {
         long long remote[kCh];
         int n = 0;
 #pragma unroll
@@ -327,10 +339,7 @@ __global__ __launch_bounds__(kBalBlock) void balance_dest_kernel(BalArgs a) {
             if (lane == 0) {
                 s_slot[b] = chosen;
                 a.experts_to_copy[d * B + b] = chosen;
-                if (chosen >= 0) {
-                    s_picked[chosen] = 1;
-                    atomicAdd(a.remote_stats + 2 * (chosen / epn) + 1, 1);
-                }
+                if (chosen >= 0) s_picked[chosen] = 1;
             }
         }
     }
@@ -341,12 +350,12 @@ __global__ __launch_bounds__(kBalBlock) void balance_dest_kernel(BalArgs a) {
     int mine = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-        const int g = tid * kPer + i;
+        const int gi = tid * kPer + i;
         int c = 0, x = -1;
-        if (g < E) {
-            if (!s_picked[g]) { c = s_cnt[g]; x = g; }
-        } else if (g < G) {
-            x = s_slot[g - E];
+        if (gi < E) {
+            if (!s_picked[gi]) { c = s_cnt[gi]; x = gi; }
+        } else if (gi < G) {
+            x = s_slot[gi - E];
             c = x >= 0 ? s_cnt[x] : 0;
         }
         cnt[i] = c;
@@ -356,9 +365,9 @@ __global__ __launch_bounds__(kBalBlock) void balance_dest_kernel(BalArgs a) {
     }
     int incl = mine;
 #pragma unroll
-    for (int s = 1; s < 64; s <<= 1) {
-        const int y = __shfl_up(incl, s, 64);
-        if (lane >= s) incl += y;
+    for (int st = 1; st < 64; st <<= 1) {
+        const int y = __shfl_up(incl, st, 64);
+        if (lane >= st) incl += y;
     }
     if (lane == 63) s_wave[wv] = incl;
     lds_barrier();
@@ -366,9 +375,9 @@ __global__ __launch_bounds__(kBalBlock) void balance_dest_kernel(BalArgs a) {
     for (int w = 0; w < wv; ++w) base += s_wave[w];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-        const int g = tid * kPer + i;
-        if (g < G) {
-            const int64_t at = (int64_t)d * G + g;
+        const int gi = tid * kPer + i;
+        if (gi < G) {
+            const int64_t at = (int64_t)d * G + gi;
             a.cu[at] = base + pad[i];
             const bool zf = cnt[i] > 0 && pad[i] > cnt[i];
             a.zero_fill[2 * at] = zf ? base + cnt[i] : 0;
@@ -392,8 +401,24 @@ __global__ __launch_bounds__(kBalTokBlock) void balance_dst_kernel(const int32_t
                                                                    const int32_t* __restrict__ e2p,
                                                                    const int32_t* __restrict__ alloc_cumsum,
                                                                    const int32_t* __restrict__ expert_offsets,
-                                                                   int64_t N, int E, int K, int R, int64_t NvS,
-                                                                   int32_t* __restrict__ dst) {
+                                                                   const int32_t* __restrict__ experts_to_copy,
+                                                                   int64_t N, int E, int K, int R, int B, int64_t NvS,
+                                                                   int32_t* __restrict__ dst,
+                                                                   int32_t* __restrict__ remote_stats) {
+    __shared__ int s_copies[kBalMaxRanks];
+    if (blockIdx.x == 0) {
+        // copies of each owner's experts over all destinations (remote_stats[o][1])
+        const int epn = E / R;
+        for (int o = threadIdx.x; o < R; o += kBalTokBlock) s_copies[o] = 0;
+        __syncthreads();
+        if (experts_to_copy)
+            for (int i = threadIdx.x; i < R * B; i += kBalTokBlock) {
+                const int x = experts_to_copy[i];
+                if (x >= 0) atomicAdd(&s_copies[x / epn], 1);
+            }
+        __syncthreads();
+        for (int o = threadIdx.x; o < R; o += kBalTokBlock) remote_stats[2 * o + 1] = s_copies[o];
+    }
     const int lane = threadIdx.x & 63;
     const int tpw = 64 / K;
     const int64_t wave = ((int64_t)blockIdx.x * kBalTokBlock + threadIdx.x) >> 6;
@@ -488,20 +513,16 @@ extern "C" int mep_plan_balanced(const int32_t* topk_ids, const int32_t* tokens_
     a.zero_fill = out->zero_fill;
     a.expert_offsets = out->expert_offsets;
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const int ch_o = chunks64(epn), ch_d = chunks64(E);
-    if (ch_o == 1) launch_ggl(balance_owner_kernel<1>, dim3(R), dim3(kBalBlock), 0, st, a);
-    else if (ch_o == 2) launch_ggl(balance_owner_kernel<2>, dim3(R), dim3(kBalBlock), 0, st, a);
-    else if (ch_o == 4) launch_ggl(balance_owner_kernel<4>, dim3(R), dim3(kBalBlock), 0, st, a);
-    else launch_ggl(balance_owner_kernel<16>, dim3(R), dim3(kBalBlock), 0, st, a);
-    if (ch_d == 1) launch_ggl(balance_dest_kernel<1>, dim3(R), dim3(kBalBlock), 0, st, a);
-    else if (ch_d == 2) launch_ggl(balance_dest_kernel<2>, dim3(R), dim3(kBalBlock), 0, st, a);
-    else if (ch_d == 4) launch_ggl(balance_dest_kernel<4>, dim3(R), dim3(kBalBlock), 0, st, a);
-    else launch_ggl(balance_dest_kernel<16>, dim3(R), dim3(kBalBlock), 0, st, a);
-    if (N > 0) {
-        const int64_t waves = ceil_div64(N, 64 / K);
-        launch_ggl(balance_dst_kernel, dim3((unsigned)ceil_div64(waves, kBalTokBlock / 64)),
-                           dim3(kBalTokBlock), 0, st, topk_ids, cu_seqlens, expanded_to_permuted, out->alloc_cumsum,
-                           out->expert_offsets, N, E, K, R, NvS, out->dst);
-    }
+    const int ch = chunks64(E);  // covers the owners' epn experts too
+    if (ch == 1) launch_ggl(balance_plan_kernel<1>, dim3(R), dim3(kBalBlock), 0, st, a);
+    else if (ch == 2) launch_ggl(balance_plan_kernel<2>, dim3(R), dim3(kBalBlock), 0, st, a);
+    else if (ch == 4) launch_ggl(balance_plan_kernel<4>, dim3(R), dim3(kBalBlock), 0, st, a);
+    else launch_ggl(balance_plan_kernel<16>, dim3(R), dim3(kBalBlock), 0, st, a);
+    // at least one workgroup: workgroup 0 also counts the copies per owner
+    const int64_t waves = N > 0 ? ceil_div64(N, 64 / K) : 1;
+    launch_ggl(balance_dst_kernel, dim3((unsigned)ceil_div64(waves, kBalTokBlock / 64)), dim3(kBalTokBlock), 0,
+               st, topk_ids, cu_seqlens, expanded_to_permuted, out->alloc_cumsum, out->expert_offsets,
+               num_copies > 0 ? out->experts_to_copy : nullptr, N, E, K, R, num_copies, NvS, out->dst,
+               out->remote_stats);
     return launch_status();
 }

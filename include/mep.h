@@ -391,7 +391,7 @@ typedef struct mep_balanced_outputs {
  *   capacity     slots per rank, 0 .. INT32_MAX
  *   NvS          per-rank row stride, >= max(N*min(K,epn), capacity) +
  *                (E+B)*(token_padding-1); R*NvS <= INT32_MAX
- * Three kernels; no workspace (the intermediate arrays are outputs).
+ * Two kernels; no workspace (the intermediate arrays are outputs).
  */
 int mep_plan_balanced(const int32_t* topk_ids, const int32_t* tokens_per_expert,
                       const int32_t* cu_seqlens, const int32_t* expanded_to_permuted, int64_t N,

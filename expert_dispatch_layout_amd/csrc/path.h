@@ -48,6 +48,7 @@ constexpr int kPathMaxK = 8;
 constexpr int kPathMaxNC = kPathMaxE + 3 * kPathMaxR;
 constexpr int kPathSlots = 2048;    // slots of a plan tile, at most
 constexpr int kPathTokens = 1024;   // tokens of a plan tile, at most
+constexpr int kPathMinTileTokens = 64;  // tokens of a plan tile, at least (unless a shard is smaller)
 constexpr int kPathMaxSub = 8;      // plan tiles per counting workgroup, at most
 constexpr int kPathUnits = 256;     // compute units of an MI355X: counting workgroups aimed at
 constexpr int kPathMaxGroups = 64;  // groups of counting workgroups, at most
@@ -168,6 +169,36 @@ __device__ __forceinline__ void path_count_ranks(const PathGeom& g, int* row, ui
         atomicAdd(&row[path_col_c0(g, r)], 1);
         if ((m2 >> r) & 1u) atomicAdd(&row[path_col_c1(g, r)], 1);
     }
+}
+
+// Counts one routed token into histogram row `row` (LDS): the token's slots are held by its
+// segment of LPT lanes, KPL per lane (-1 where there is none); expert columns by LDS atomics,
+// then the rank columns from the rank masks combined over the segment.
+template <int LPT, int KPL>
+__device__ __forceinline__ void path_count_token(const PathGeom& g, int* row, const int (&e)[KPL], int lseg) {
+    uint32_t m1 = 0u, m2 = 0u;
+#pragma unroll
+    for (int q = 0; q < KPL; ++q) {
+        if (e[q] >= 0) {
+            atomicAdd(&row[e[q]], 1);
+            const int r = g.eshift >= 0 ? e[q] >> g.eshift : e[q] / g.epn;
+            const uint32_t bit = 1u << r;
+            m2 |= m1 & bit;
+            m1 |= bit;
+        }
+    }
+    auto step = [&](auto partner) {
+        const uint32_t b1 = partner(m1), b2 = partner(m2);
+        m2 = m2 | b2 | (m1 & b1);
+        m1 = m1 | b1;
+    };
+    if constexpr (LPT >= 2) step([](uint32_t u) { return seg_partner_u32<1>(u); });
+    if constexpr (LPT >= 4) step([](uint32_t u) { return seg_partner_u32<2>(u); });
+    if constexpr (LPT >= 8) step([](uint32_t u) { return seg_partner_u32<4>(u); });
+    if constexpr (LPT >= 16) step([](uint32_t u) { return seg_partner_u32<8>(u); });
+    if constexpr (LPT >= 32) step([](uint32_t u) { return seg_partner_u32<16>(u); });
+    if constexpr (LPT >= 64) step([](uint32_t u) { return seg_partner_u32<32>(u); });
+    path_count_ranks(g, row, m1, m2, lseg, LPT);
 }
 
 // (m1, m2) of two lane shares combined: ranks reached, and ranks reached twice or more.

@@ -262,8 +262,6 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
     {
         const int NCs = g.NCs;
         const int NQ = NCs >> 2;
-        const int nsl = kPlanRowNT / NQ;
-        const int q = tid % NQ, sl = tid / NQ;
         const int ng = g.ng;
         const int wg = j / g.sub, grp = wg / g.GW, wg0 = grp * g.GW;
         const int wgf = jf / g.sub, grpf = wgf / g.GW, wgf0 = grpf * g.GW;
@@ -271,12 +269,16 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
         // counts), the rank token columns for the channel prefixes, none otherwise
         const bool shx_all = shard_last && o.p.ntpe;
         const bool shx_rank = o.p.chan || (shard_last && (o.p.ntpr || o.p.ntpe));
-        const bool need_f = shx_all || (shx_rank && 4 * q < E + R && 4 * q + 4 > E);
         const int r_w = 2 * ng;                 // first workgroup row of the tile's group
         const int r_t = r_w + (wg - wg0);       // the tile's prefix row
         const int r_f = r_t + 1;                // first workgroup row of the shard start's group
         const int nf = (shx_all || shx_rank) ? (wgf - wgf0) + 1 : 0;
         const int nrows = r_f + nf;
+        // row slices: as many as the loader threads allow, but no more than eight rows per slice
+        // need (each slice is summed again through LDS)
+        const int nsl = min(kPlanRowNT / NQ, max(1, (nrows + 7) / 8));
+        const int q = tid % NQ, sl = tid / NQ;
+        const bool need_f = shx_all || (shx_rank && 4 * q < E + R && 4 * q + 4 > E);
         // every row as a word offset from the first group sum row (rows past the list, and the
         // shard start's rows of columns that do not need them, read group row 0 and count nowhere)
         const MEP_GLOBAL uint32_t* base = gptr(w.gsum);
@@ -365,6 +367,27 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
             }
             *reinterpret_cast<u32x4*>(&s_code[tk * 8]) = u32x4{cd[0], cd[1], cd[2], cd[3]};
             *reinterpret_cast<u32x4*>(&s_code[tk * 8 + 4]) = u32x4{cd[4], cd[5], cd[6], cd[7]};
+        } else if (live && R <= 8) {
+            // fewer than eight slots, at most eight ranks: the same 4-bit per-rank counts
+            int e[kPathMaxK], r[kPathMaxK];
+            uint32_t cnt = 0u;
+#pragma unroll
+            for (int k = 0; k < kPathMaxK; ++k) {
+                e[k] = k < K ? (int)s_code[tk * K + k] : 0;
+                r[k] = g.eshift >= 0 ? e[k] >> g.eshift : s_owner[e[k]];
+                cnt += k < K ? 1u << (4 * r[k]) : 0u;
+            }
+#pragma unroll
+            for (int k = 0; k < kPathMaxK; ++k) {
+                if (k < K) {
+                    const uint32_t bit = 1u << r[k];
+                    const bool first = (m & bit) == 0u;
+                    m |= bit;
+                    const int h = (int)((cnt >> (4 * r[k])) & 15u);
+                    const uint32_t type = first ? (h >= 2 ? kSlotHead : kSlotPlain) : kSlotDup;
+                    s_code[tk * K + k] = slot_code(e[k], type, r[k], h);
+                }
+            }
         } else if (live) {
             int e[kPathMaxK], r[kPathMaxK];
             uint32_t cd[kPathMaxK];
@@ -603,6 +626,11 @@ PathGeom path_geom(int64_t N, int E, int K, int R, int S, int C, int A, int64_t 
     while (kp < K) kp <<= 1;
     g.T = kPathSlots / kp;
     if (g.T > kPathTokens) g.T = kPathTokens;
+    // small batches: tiles of fewer tokens, so that the batch spreads over about kPathUnits
+    // workgroups (each tile's latency-bound phases shrink with it), but not below 64 tokens
+    const int64_t t_spread = ceil_div64(N, kPathUnits);
+    const int t_fill = (int)(t_spread < kPathMinTileTokens ? kPathMinTileTokens : ceil_div64(t_spread, 64) * 64);
+    if (g.T > t_fill) g.T = t_fill;
     if (g.T > g.n) g.T = g.n > 0 ? g.n : 1;
     g.tps = (int)ceil_div64(g.n, g.T);
     g.ntiles = S * g.tps;

@@ -8,6 +8,7 @@
 //                         the chunk layout).
 //   route_generic_kernel  (this file) exact keys for every expert and K rounds of a segmented
 //                         arg-max; covers every shape the ABI accepts.
+#include "path.h"
 #include "route_common.h"
 
 namespace mep {
@@ -32,6 +33,84 @@ static void launch_generic(const RouteArgs& a, const Launch& st) {
     else
         launch_kernel((route_generic_kernel<LPT, NV, BF16, 32>), dim3((unsigned)blocks),
                            dim3(kRouteBlock), 0, st, a);
+}
+
+// The generic kernel as the routing phase of the fused layout + plan path (path.h), for
+// workgroups whose tokens fit one pass (small batches): workgroup b routes the tokens of plan
+// tiles [b * sub, b * sub + nsub), keeping their experts in LDS, then counts each token into its
+// tile's histogram row (LDS) and ends with the counting epilogue.  Routing first and counting
+// after keeps the plan geometry out of the routing code's registers; a loop over several passes
+// would make the routing code's live values spill, so larger batches take the routing kernel
+// and then the counting kernel instead.
+constexpr int kRouteCountBlock = 512;
+
+template <int LPT, int NV, bool BF16>
+__global__ __launch_bounds__(kRouteCountBlock) void route_generic_count_kernel(RouteArgs a, PathGeom g, PathWs w,
+                                                                               WsHeader* hdr) {
+    constexpr int NT = kRouteCountBlock;
+    constexpr int KMAX = kPathMaxK;
+    constexpr int KPL = (KMAX + LPT - 1) / LPT;
+    constexpr int TPB = NT / LPT;
+    __shared__ int s_e[TPB * kPathMaxK];  // experts of the workgroup's slots
+    __shared__ int s_row[kPathMaxSub * kPathMaxNC];
+    __shared__ int s_tb[kPathMaxSub + 1];
+    const int tid = threadIdx.x;
+    const int lseg = tid % LPT;
+    const int j0 = blockIdx.x * g.sub;
+    const int nsub = min(g.sub, g.ntiles - j0);
+    for (int i = tid; i < nsub * g.NC; i += NT) s_row[i] = 0;
+    if (tid <= nsub) {
+        int64_t c0, c1;
+        path_tile_tokens(g, j0 + min(tid, nsub - 1), c0, c1);
+        s_tb[tid] = (int)(tid < nsub ? c0 : c1);
+    }
+    const uint32_t pcall = path_count_begin(hdr);
+    __syncthreads();
+    const int t0 = s_tb[0], t1 = s_tb[nsub];  // t1 - t0 <= TPB
+    const int K = a.K;
+    // ---- routing (a wave whose tokens all lie past the tiles skips it; a token past the tiles
+    // computes on the batch's last token and writes nothing)
+    if (t0 + __builtin_amdgcn_readfirstlane((tid & ~63) / LPT) < t1) {
+        const int tok = t0 + tid / LPT;
+        const bool mine = tok < t1;
+        int my_e[KPL];
+        route_generic_token<LPT, NV, BF16, KMAX>(a, mine ? (int64_t)tok : a.N, lseg, my_e);
+#pragma unroll
+        for (int m = 0; m < KPL; ++m) {
+            const int j = m * LPT + lseg;
+            if (mine && j < K) s_e[(tok - t0) * K + j] = my_e[m];
+        }
+    }
+    __syncthreads();
+    // ---- counting: one token per thread
+    for (int t = t0 + tid; t < t1; t += NT) {
+        int i = 0;
+        while (i + 1 < nsub && t >= s_tb[i + 1]) ++i;
+        int e[kPathMaxK];
+#pragma unroll
+        for (int k = 0; k < kPathMaxK; ++k) e[k] = k < K ? s_e[(t - t0) * K + k] : -1;
+        path_count_token<1, kPathMaxK>(g, s_row + i * g.NC, e, 0);
+    }
+    path_epilogue<NT>(g, w, pcall, s_row);
+}
+
+template <int LPT, int NV, bool BF16>
+static bool launch_generic_count(const RouteArgs& a, const Launch& st, const PathCall& pc) {
+    if ((int64_t)pc.g.sub * pc.g.T > kRouteCountBlock / LPT) return false;  // more than one pass
+    launch_kernel((route_generic_count_kernel<LPT, NV, BF16>), dim3((unsigned)pc.g.nwg), dim3(kRouteCountBlock), 0,
+                  st, a, pc.g, pc.w, pc.hdr);
+    return true;
+}
+
+template <bool BF16>
+static bool dispatch_generic_count(const RouteArgs& a, const Launch& st, const PathCall& pc) {
+    constexpr int W = BF16 ? 8 : 4;
+    const int nchunks = (a.E + W - 1) / W;
+    if (nchunks <= 1) return launch_generic_count<1, 1, BF16>(a, st, pc);
+    if (nchunks <= 2) return launch_generic_count<2, 1, BF16>(a, st, pc);
+    if (nchunks <= 4) return launch_generic_count<4, 1, BF16>(a, st, pc);
+    if (nchunks <= 8) return launch_generic_count<8, 1, BF16>(a, st, pc);
+    return false;  // 16 or more lanes per token: fewer than the 64 tokens of a tile per pass
 }
 
 template <bool BF16>
@@ -96,6 +175,11 @@ int route_prepare(const void* logits, int dtype, int64_t N, int E, int K, const 
     const int W = dtype == MEP_BF16 ? 8 : 4;
     a.vec = (E % W) == 0;
     return MEP_OK;
+}
+
+bool launch_route_generic_counting(const RouteArgs& a, int dtype, const Launch& st, const PathCall& pc) {
+    if (a.K > kPathMaxK || route_sig_covers(a) || route_fast_covers(a)) return false;
+    return dtype == MEP_BF16 ? dispatch_generic_count<true>(a, st, pc) : dispatch_generic_count<false>(a, st, pc);
 }
 
 int route_launch(const RouteArgs& a, int dtype, const Launch& st) {

@@ -363,6 +363,9 @@ int route_prepare(const void* logits, int dtype, int64_t N, int E, int K, const 
                   const mep_route_params* p, int32_t* topk_ids, float* topk_weights, RouteArgs& a);
 
 bool launch_route_fast(const RouteArgs& a, int dtype, const Launch& st);
+// Whether the fast kernel, or the sigmoid kernel, covers a routing call (route_launch then takes it).
+bool route_fast_covers(const RouteArgs& a);
+bool route_sig_covers(const RouteArgs& a);
 
 // Enqueue the routing kernel that covers the shape (sigmoid, fast, or generic); MEP_OK or
 // MEP_ERR_UNSUPPORTED.
@@ -374,5 +377,8 @@ bool launch_route_sig(const RouteArgs& a, int dtype, const Launch& st);
 // counting epilogue; false when the shape is not covered (nothing is launched then).
 struct PathCall;
 bool launch_route_sig_counting(const RouteArgs& a, int dtype, const Launch& st, const PathCall& pc);
+// The generic kernel counting the plan tiles it owns, for calls neither the sigmoid nor the fast
+// kernel covers; false (nothing launched) otherwise or when K > 8.
+bool launch_route_generic_counting(const RouteArgs& a, int dtype, const Launch& st, const PathCall& pc);
 
 }  // namespace mep

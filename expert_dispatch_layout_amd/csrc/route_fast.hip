@@ -38,12 +38,12 @@ static int ilog2(int v) {
     return l;
 }
 
-bool launch_route_fast(const RouteArgs& a, int dtype, const Launch& st) {
-    const bool bf16 = dtype == MEP_BF16;
+// The fast kernel's configuration for a routing call; false when the kernel does not cover it.
+static bool fast_plan(const RouteArgs& a, int& LPT, FastCfg& cfg, int& M) {
     if (a.E % kFastEPL != 0 || !a.vec) return false;
-    const int LPT = a.E / kFastEPL;
+    LPT = a.E / kFastEPL;
     if (LPT != 2 && LPT != 4 && LPT != 8 && LPT != 16) return false;
-    FastCfg cfg{};
+    cfg = FastCfg{};
     int units;
     if (a.n_group <= 1) {
         cfg.mode = 0;
@@ -61,9 +61,21 @@ bool launch_route_fast(const RouteArgs& a, int dtype, const Launch& st) {
         units = a.topk_group;
     }
     cfg.mt = (a.K + units - 1) / units;
-    const int M = (cfg.mode != 0 && cfg.mt < 2) ? 2 : cfg.mt;  // group scores need the top two
-    if (M > 4) return false;
-    if (bf16)
+    M = (cfg.mode != 0 && cfg.mt < 2) ? 2 : cfg.mt;  // group scores need the top two
+    return M <= 4;
+}
+
+bool route_fast_covers(const RouteArgs& a) {
+    int LPT, M;
+    FastCfg cfg;
+    return fast_plan(a, LPT, cfg, M);
+}
+
+bool launch_route_fast(const RouteArgs& a, int dtype, const Launch& st) {
+    int LPT, M;
+    FastCfg cfg;
+    if (!fast_plan(a, LPT, cfg, M)) return false;
+    if (dtype == MEP_BF16)
         launch_fast_bf16(LPT, a, cfg, M, st);
     else
         launch_fast_f32(LPT, a, cfg, M, st);

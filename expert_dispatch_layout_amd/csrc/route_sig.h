@@ -613,8 +613,10 @@ __global__ __launch_bounds__(64 * NW) void route_sig_kernel(RouteArgs a, SigCfg 
             for (int q = 0; q < KPL; ++q) {
                 const int j = lseg + q * LPT;
                 if (j < K) {
-                    gptr(a.ids)[tok * K + j] = my_e[q];
-                    if (a.weights) gptr(a.weights)[tok * K + j] = (float)((my_v[q] * inv) * (double)a.scale);
+                    // streaming stores: nothing in this kernel reads them back
+                    __builtin_nontemporal_store(my_e[q], gptr(a.ids) + tok * K + j);
+                    if (a.weights)
+                        __builtin_nontemporal_store((float)((my_v[q] * inv) * (double)a.scale), gptr(a.weights) + tok * K + j);
                 }
             }
         }

@@ -63,20 +63,31 @@ bool launch_sig_lpt(int LPT, const RouteArgs& a, const Launch& st, const PathCal
     }
 }
 
-bool route_sig_dispatch(const RouteArgs& a, int dtype, const Launch& st, const PathCall* pc) {
+// The kernel's lanes per token and group mode for a routing call; false when it does not cover it.
+bool sig_plan(const RouteArgs& a, int& LPT, int& mode) {
     if (a.score_fn != MEP_SIGMOID || !a.vec || a.K > 8 || a.E % kFastEPL != 0) return false;
-    const int LPT = a.E / kFastEPL;
+    LPT = a.E / kFastEPL;
     if (LPT != 2 && LPT != 4 && LPT != 8 && LPT != 16) return false;
-    int mode;
     if (a.n_group <= 1) mode = 0;
     else if (a.n_group == LPT) mode = 1;
     else return false;
+    return true;
+}
+
+bool route_sig_dispatch(const RouteArgs& a, int dtype, const Launch& st, const PathCall* pc) {
+    int LPT, mode;
+    if (!sig_plan(a, LPT, mode)) return false;
     const bool bf16 = dtype == MEP_BF16;
     if (bf16) return mode == 0 ? launch_sig_lpt<true, 0>(LPT, a, st, pc) : launch_sig_lpt<true, 1>(LPT, a, st, pc);
     return mode == 0 ? launch_sig_lpt<false, 0>(LPT, a, st, pc) : launch_sig_lpt<false, 1>(LPT, a, st, pc);
 }
 
 }  // namespace
+
+bool route_sig_covers(const RouteArgs& a) {
+    int LPT, mode;
+    return sig_plan(a, LPT, mode);
+}
 
 bool launch_route_sig(const RouteArgs& a, int dtype, const Launch& st) {
     return route_sig_dispatch(a, dtype, st, nullptr);

@@ -2,8 +2,9 @@
 // (decode sizes) run as one kernel of one workgroup, in the spirit of TensorRT-LLM
 // RoutingKernel.cuh's routingPermutation (the whole routing permutation of a small batch inside
 // one cluster, without a second launch); larger batches take the plan-tile path (path.h): the
-// routing kernel, which for sigmoid routing also counts the plan tiles it routes (else the
-// counting kernel does, after routing), then the plan-tile kernel.  Results are identical to
+// routing kernel, which also counts the plan tiles it routes (the sigmoid kernel, and the
+// generic kernel for the shapes neither specialised kernel covers; after the fast kernel the
+// counting kernel does), then the plan-tile kernel.  Results are identical to
 // mep_route_topk followed by mep_build_layout and mep_plan either way.
 //
 // The one-workgroup kernel (512 threads) keeps every slot's expert and permuted position in
@@ -457,7 +458,7 @@ int route_layout_plan(const void* logits, int dtype, int64_t N, int E, int K, co
     const Launch rl{st, ev.route_start, ev.route_stop};
     if (path_supported(N, E, K, R)) {
         const PathCall c = path_call(lc, pc, ws);
-        if (!launch_route_sig_counting(sa.ra, dtype, rl, c)) {
+        if (!launch_route_sig_counting(sa.ra, dtype, rl, c) && !launch_route_generic_counting(sa.ra, dtype, rl, c)) {
             rc = route_launch(sa.ra, dtype, rl);
             if (rc != MEP_OK) return rc;
             path_launch_count(c, st);

@@ -148,6 +148,16 @@ FUSED_CASES = [
     (3333, 100, 7, synth.F32, "softmax", 5, 10, 3, 9),
     (6000, 8, 2, synth.BF16, "softmax_full", 128, 8, 8, 24),
     (40000, 256, 8, synth.F32, "sigmoid_group", 128, 8, 8, 24),
+    # shapes of the generic routing kernel: with counting (2 to 8 lanes per token, tiles of 64
+    # tokens with a ragged last one, experts per rank not a power of two) and, for 16 or more
+    # lanes per token, followed by the counting kernel (sigmoid outside the sigmoid kernel's lane
+    # layout, 64 lanes per token with two chunks each)
+    (3000, 24, 5, synth.F32, "softmax", 16, 8, 3, 24),
+    (1800, 16, 3, synth.BF16, "sigmoid", 4, 4, 2, 5),
+    (700, 12, 8, synth.F32, "softmax_full", 2, 3, 1, 7),
+    (2500, 96, 4, synth.F32, "sigmoid", 8, 6, 2, 11),
+    (1500, 500, 8, synth.F32, "softmax", 4, 20, 2, 6),
+    (3099, 300, 6, synth.BF16, "softmax_full", 16, 12, 3, 24),
 ]
 
 

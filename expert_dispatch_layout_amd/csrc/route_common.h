@@ -68,38 +68,38 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
 }
 
+// Reductions over a token's segment of LPT lanes (all of them active): DPP lane moves for the
+// partners within 16 lanes, ds_bpermute beyond (seg_partner_u32); every lane gets the result.
 template <int LPT>
 __device__ __forceinline__ uint32_t seg_max_u32(uint32_t v) {
-#pragma unroll
-    for (int o = LPT / 2; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, LPT));
-    return v;
+    return seg_allreduce<LPT>(v, LPT, PartnerU32{}, [](uint32_t p, uint32_t q) { return max(p, q); });
 }
 
 template <int LPT>
 __device__ __forceinline__ uint32_t seg_min_u32(uint32_t v) {
-#pragma unroll
-    for (int o = LPT / 2; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, LPT));
-    return v;
+    return seg_allreduce<LPT>(v, LPT, PartnerU32{}, [](uint32_t p, uint32_t q) { return min(p, q); });
 }
 
 template <int LPT>
 __device__ __forceinline__ double seg_sum_f64(double v) {
-#pragma unroll
-    for (int o = LPT / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, LPT);
-    return v;
+    return seg_allreduce<LPT>(v, LPT, PartnerF64{}, [](double p, double q) { return p + q; });
 }
 
 // keep the two largest of (t1 >= t2) and the partner lane's pair
 template <int LPT>
 __device__ __forceinline__ void seg_top2_u32(uint32_t& t1, uint32_t& t2) {
-#pragma unroll
-    for (int o = LPT / 2; o >= 1; o >>= 1) {
-        uint32_t b1 = (uint32_t)__shfl_xor((int)t1, o, LPT);
-        uint32_t b2 = (uint32_t)__shfl_xor((int)t2, o, LPT);
-        uint32_t n2 = max(min(t1, b1), max(t2, b2));
+    auto step = [&](auto partner) {
+        const uint32_t b1 = partner(t1), b2 = partner(t2);
+        const uint32_t n2 = max(min(t1, b1), max(t2, b2));
         t1 = max(t1, b1);
         t2 = n2;
-    }
+    };
+    if constexpr (LPT >= 2) step([](uint32_t u) { return seg_partner_u32<1>(u); });
+    if constexpr (LPT >= 4) step([](uint32_t u) { return seg_partner_u32<2>(u); });
+    if constexpr (LPT >= 8) step([](uint32_t u) { return seg_partner_u32<4>(u); });
+    if constexpr (LPT >= 16) step([](uint32_t u) { return seg_partner_u32<8>(u); });
+    if constexpr (LPT >= 32) step([](uint32_t u) { return seg_partner_u32<16>(u); });
+    if constexpr (LPT >= 64) step([](uint32_t u) { return seg_partner_u32<32>(u); });
 }
 
 __device__ __forceinline__ int chunk_expert(int q, int W, int LPT, int lseg) {
@@ -161,13 +161,15 @@ __device__ __forceinline__ float load_logit(const RouteArgs& a, int64_t tok, int
 // Exact selection for one token by the LPT lanes of its segment: exact keys (logit, or
 // correctly rounded sigmoid + bias), exact group limit, then K rounds of a segmented arg-max
 // (max of the order-preserving key, then min expert index among the maxima).  On return the
-// lane owning output slot k (k % LPT == lseg) holds its expert in my_e[k / LPT]; every lane
-// holds the first selected logit in first_x (used by the softmax weights).
+// lane owning output slot k (k % LPT == lseg) holds its expert in my_e[k / LPT] and the slot's
+// key in my_key[k / LPT] (for softmax the selected logit itself: the order key maps back to the
+// value, a -0 logit coming back as +0, which no softmax weight tells apart); every lane holds the
+// first selected logit in first_x (used by the softmax weights).
 template <int LPT, int NV, bool BF16, int KMAX>
 __device__ __forceinline__ void exact_select_token(const RouteArgs& a, const float* bias, int lseg,
                                                    const float (&x)[NV * (BF16 ? 8 : 4)],
                                                    int (&my_e)[(KMAX + LPT - 1) / LPT],
-                                                   float& first_x) {
+                                                   float (&my_key)[(KMAX + LPT - 1) / LPT], float& first_x) {
     constexpr int W = BF16 ? 8 : 4;
     constexpr int NE = NV * W;
     const int E = a.E;
@@ -248,7 +250,10 @@ __device__ __forceinline__ void exact_select_token(const RouteArgs& a, const flo
         const int e_sel = (int)seg_min_u32<LPT>(cand);
         if (best_q >= 0 && best_e == e_sel) taken |= 1u << best_q;
         if (k == 0) first_x = order_key_inv(m);  // softmax: the first selected logit
-        if ((k % LPT) == lseg) my_e[k / LPT] = e_sel;
+        if ((k % LPT) == lseg) {
+            my_e[k / LPT] = e_sel;
+            my_key[k / LPT] = order_key_inv(m);
+        }
     });
 }
 
@@ -325,21 +330,24 @@ __device__ __forceinline__ void route_generic_token(const RouteArgs& a, int64_t 
 
     float x[NE];
     load_row<LPT, NV, BF16>(a, tok, lseg, x);
+    float key[KPL];
 #pragma unroll
-    for (int m = 0; m < KPL; ++m) my_e[m] = 0;
+    for (int m = 0; m < KPL; ++m) {
+        my_e[m] = 0;
+        key[m] = 0.0f;
+    }
     float first_x;
-    exact_select_token<LPT, NV, BF16, KMAX>(a, a.bias, lseg, x, my_e, first_x);
+    exact_select_token<LPT, NV, BF16, KMAX>(a, a.bias, lseg, x, my_e, key, first_x);
 
+    // the weights' values: for softmax the selected logits (the keys), for sigmoid the correctly
+    // rounded sigmoid of the selected logit, read again from the row
     const bool sig = a.score_fn == MEP_SIGMOID;
     float my_v[KPL];
 #pragma unroll
     for (int m = 0; m < KPL; ++m) {
         const int j = m * LPT + lseg;
         float v = 0.0f;
-        if (j < a.K) {
-            const float xe = load_logit(a, tok, my_e[m], BF16);
-            v = sig ? sigmoid_cr(xe) : xe;
-        }
+        if (j < a.K) v = sig ? sigmoid_cr(load_logit(a, tok, my_e[m], BF16)) : key[m];
         my_v[m] = v;
     }
     double full_max = 0.0, full_den = 0.0;

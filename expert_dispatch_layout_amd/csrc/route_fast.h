@@ -182,17 +182,21 @@ __device__ __noinline__ void exact_token_full(const RouteArgs a, const float* s_
     float x[NE64];
     load_row<64, NV64, BF16>(a, tok, wl, x);
     int e64[KPL64];
+    float key[KPL64];
+#pragma unroll
+    for (int m = 0; m < KPL64; ++m) {
+        e64[m] = 0;
+        key[m] = 0.0f;
+    }
     float fx;
-    exact_select_token<64, NV64, BF16, KMAX>(a, s_bias, wl, x, e64, fx);
+    exact_select_token<64, NV64, BF16, KMAX>(a, s_bias, wl, x, e64, key, fx);
+    // softmax: the selected logits are the keys; sigmoid: the row is read again
     float v[KPL64];
 #pragma unroll
     for (int m = 0; m < KPL64; ++m) {
         const int j = m * 64 + wl;
         float vv = 0.0f;
-        if (j < a.K) {
-            const float xe = load_logit(a, tok, e64[m], BF16);
-            vv = SCORE == 2 ? sigmoid_cr(xe) : xe;
-        }
+        if (j < a.K) vv = SCORE == 2 ? sigmoid_cr(load_logit(a, tok, e64[m], BF16)) : key[m];
         v[m] = vv;
     }
     double full_max = 0.0, full_den = 0.0;

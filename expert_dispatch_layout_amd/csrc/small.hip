@@ -49,6 +49,20 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Exclusive scan over the 64 lanes of a wave (all active); `total` gets the sum.  DPP row
+// shifts give the inclusive scan within rows of 16 lanes, the row broadcasts carry it across.
+__device__ __forceinline__ int sm_wave_excl_scan(int v, int& total) {
+    int x = v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    total = __builtin_amdgcn_readlane(x, 63);
+    return x - v;
+}
+
 // Exclusive scan of one int per thread over the workgroup, with LDS-only barriers.
 __device__ __forceinline__ int lds_block_scan(int v, int* s_tmp, int& total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -93,9 +107,10 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
     __shared__ int s_chan[kSmMaxChan];
     __shared__ int s_tmp[kSmWaves];
     __shared__ int s_dtot[2 * kSmMaxR];
-    __shared__ int s_wsum[kSmWaves][kSmMaxR];
+    __shared__ int s_wsum[kSmMaxSlots / kSmBlock][kSmWaves][kSmMaxR];
     __shared__ int s_goff[kSmMaxR];
     __shared__ int s_doff[kSmMaxR];
+    __shared__ uint32_t s_hc[kSmMaxSlots];  // per token: slots on each rank, 4-bit fields
 
     const RouteArgs& a = sa.ra;
     const PlanGeom& g = sa.g;
@@ -103,6 +118,9 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
     const int wv = tid >> 6;
     const int N = (int)a.N, E = a.E, K = a.K, NK = N * K;
     const int R = g.R, epn = g.epn, S = g.S, C = g.C, n = g.n;
+    // owner rank of an expert: a shift when epn is a power of two
+    const int esh = (epn & (epn - 1)) == 0 ? __builtin_ctz((unsigned)epn) : -1;
+    auto owner = [&](int e) { return esh >= 0 ? e >> esh : e / epn; };
 
     // ---- route -----------------------------------------------------------------------------------
     {
@@ -205,16 +223,18 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
     for (int t = tid; t < N; t += kSmBlock) {
         const int s = t / n;
         const int ch = (t - s * n) / q;
-        uint32_t mask = 0;
+        uint32_t mask = 0, hc = 0;
         for (int k = 0; k < K; ++k) {
             const int e = s_ids[t * K + k];
-            const int r = e / epn;
+            const int r = owner(e);
             atomicAdd(&s_ntpe[s * E + e], 1);
             const int raw = (int)((int64_t)r * g.NvS + (s_P[t * K + k] - s_cu[r * epn]));
             const bool dup = (mask >> r) & 1u;
             if (sa.po.dst) sa.po.dst[t * K + k] = dup ? -raw - 1 : raw;
             mask |= 1u << r;
+            hc += 1u << (4 * r);  // R <= 8 ranks, at most K <= 8 slots on one
         }
+        s_hc[t] = hc;
         for (int r = 0; r < R; ++r) {
             const bool in = (mask >> r) & 1u;
             if (sa.po.itr) sa.po.itr[(int64_t)t * R + r] = in ? 1 : 0;
@@ -264,10 +284,11 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
     }
 
     // ---- plan: dedup lists in token order, all ranks at once ----------------------------------------
-    // Per rank r and token t: a group when t has >= 2 slots on r, with hits - 1 duplicates.  The
-    // totals come from LDS counters; the positions from wave scans of every rank's (group,
-    // duplicates) pair, packed 16:16 (at most 2048 of each in a batch), combined across the waves
-    // after one barrier per 512 tokens.
+    // Per rank r and token t: a group when t has >= 2 slots on r, with hits - 1 duplicates (the
+    // slots per rank come from the plan pass as 4-bit fields).  Every rank's (group, duplicates)
+    // pair, packed 16:16 (at most 2048 of each in a batch), is scanned per wave with DPP; the wave
+    // totals, prefixed over chunks and waves per rank, give the totals and the rank offsets, and
+    // a second round of the same scans places every record.  Three barriers in all.
     if (epn == 1) {
         // distinct experts on distinct ranks: no token has two slots on one rank
         for (int i = tid; i < 2 * R; i += kSmBlock)
@@ -276,92 +297,82 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
             if (sa.po.dup_offsets) sa.po.dup_offsets[i] = 0;
         return;
     }
-    for (int i = tid; i < 2 * R; i += kSmBlock) s_dtot[i] = 0;
-    lds_barrier();
-    for (int t = tid; t < N; t += kSmBlock) {
-        int hits[kSmMaxR];
-#pragma unroll
-        for (int r = 0; r < kSmMaxR; ++r) hits[r] = 0;
-        for (int k = 0; k < K; ++k) {
-            const int r = s_ids[t * K + k] / epn;
-#pragma unroll
-            for (int rr = 0; rr < kSmMaxR; ++rr) hits[rr] += rr == r;
-        }
-#pragma unroll
-        for (int r = 0; r < kSmMaxR; ++r)
-            if (r < R && hits[r] >= 2) {
-                atomicAdd(&s_dtot[2 * r], 1);
-                atomicAdd(&s_dtot[2 * r + 1], hits[r] - 1);
-            }
-    }
-    lds_barrier();
-    if (tid == 0) {
-        int gacc = 0, dacc = 0;
-        for (int r = 0; r < R; ++r) {
-            s_goff[r] = gacc;
-            s_doff[r] = dacc;
-            if (sa.po.dup_counts) {
-                sa.po.dup_counts[2 * r] = s_dtot[2 * r];
-                sa.po.dup_counts[2 * r + 1] = s_dtot[2 * r + 1];
-            }
-            if (sa.po.dup_offsets) {
-                sa.po.dup_offsets[2 * r] = gacc;
-                sa.po.dup_offsets[2 * r + 1] = dacc;
-            }
-            gacc += s_dtot[2 * r];
-            dacc += s_dtot[2 * r + 1];
-        }
-        if (sa.po.dup_offsets) {
-            sa.po.dup_offsets[2 * R] = gacc;
-            sa.po.dup_offsets[2 * R + 1] = dacc;
-        }
-    }
-    lds_barrier();
     const int lane = tid & 63;
-    int carry[kSmMaxR];
-#pragma unroll
-    for (int r = 0; r < kSmMaxR; ++r) carry[r] = 0;
-    auto hits_on = [&](int t, int r) {
-        int h = 0;
-        for (int k = 0; k < K; ++k) h += s_ids[t * K + k] / epn == r;
-        return h;
+    const int nch = (N + kSmBlock - 1) / kSmBlock;  // chunks of 512 tokens, at most 4
+    // the packed pair of token t on rank r: (1 group, h - 1 duplicates) when it has h >= 2 slots
+    auto pair_of = [&](uint32_t hc, int r) {
+        const int h = (int)((hc >> (4 * r)) & 15u);
+        return h >= 2 ? (1 << 16) | (h - 1) : 0;
     };
-    for (int t0 = 0; t0 < N; t0 += kSmBlock) {
-        const int t = t0 + tid;
-        int incl[kSmMaxR];
+    // pass 1: every rank's wave totals of the pairs, per chunk
+    for (int c = 0; c < nch; ++c) {
+        const int t = c * kSmBlock + tid;
+        const uint32_t hc = t < N ? s_hc[t] : 0u;
 #pragma unroll
         for (int r = 0; r < kSmMaxR; ++r) {
-            incl[r] = 0;
             if (r >= R) continue;  // uniform: ranks past R cost nothing
-            const int h = t < N ? hits_on(t, r) : 0;
-            int x = h >= 2 ? (1 << 16) | (h - 1) : 0;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_up(x, o);
-                if (lane >= o) x += y;
-            }
-            incl[r] = x;
-            if (lane == 63) s_wsum[wv][r] = x;
+            int wt;
+            sm_wave_excl_scan(pair_of(hc, r), wt);
+            if (lane == 0) s_wsum[c][wv][r] = wt;
         }
-        lds_barrier();
+    }
+    lds_barrier();
+    // per rank (one thread each): the wave totals become exclusive prefixes over chunks and
+    // waves; the rank's total
+    if (tid < R) {
+        int run = 0;
+        for (int c = 0; c < nch; ++c)
+            for (int w = 0; w < kSmWaves; ++w) {
+                const int x = s_wsum[c][w][tid];
+                s_wsum[c][w][tid] = run;
+                run += x;
+            }
+        s_dtot[tid] = run;
+    }
+    lds_barrier();
+    // rank offsets (exclusive scans over the ranks of the group and duplicate totals), counts
+    if (wv == 0) {
+        const int packed = lane < R ? s_dtot[lane] : 0;
+        const int gt = packed >> 16, dt = packed & 0xFFFF;
+        int gall, dall;
+        const int go = sm_wave_excl_scan(gt, gall), dof = sm_wave_excl_scan(dt, dall);
+        if (lane < R) {
+            s_goff[lane] = go;
+            s_doff[lane] = dof;
+            if (sa.po.dup_counts) {
+                sa.po.dup_counts[2 * lane] = gt;
+                sa.po.dup_counts[2 * lane + 1] = dt;
+            }
+            if (sa.po.dup_offsets) {
+                sa.po.dup_offsets[2 * lane] = go;
+                sa.po.dup_offsets[2 * lane + 1] = dof;
+            }
+        }
+        if (lane == 0 && sa.po.dup_offsets) {
+            sa.po.dup_offsets[2 * R] = gall;
+            sa.po.dup_offsets[2 * R + 1] = dall;
+        }
+    }
+    lds_barrier();
+    // pass 2: the same wave scans again plus the prefixes give each token's group and duplicate
+    // indices on each rank; the records
+    for (int c = 0; c < nch; ++c) {
+        const int t = c * kSmBlock + tid;
+        const uint32_t hc = t < N ? s_hc[t] : 0u;
 #pragma unroll
         for (int r = 0; r < kSmMaxR; ++r) {
             if (r >= R) continue;
-            int before = 0, tot = 0;
-            for (int w = 0; w < kSmWaves; ++w) {
-                const int x = s_wsum[w][r];
-                before += w < wv ? x : 0;
-                tot += x;
-            }
-            const int h = (r < R && t < N) ? hits_on(t, r) : 0;
-            if (h >= 2) {
-                const int ex = carry[r] + before + incl[r] - ((1 << 16) | (h - 1));
+            int wt;
+            const int x = pair_of(hc, r);
+            const int ex = sm_wave_excl_scan(x, wt) + s_wsum[c][wv][r];
+            if (x != 0) {
+                const int h = (x & 0xFFFF) + 1;
                 const int gi = ex >> 16, di = ex & 0xFFFF;
                 const int dbase = s_doff[r] + di;
                 int first = -1, j = 0;
                 for (int k = 0; k < K; ++k) {
                     const int e = s_ids[t * K + k];
-                    if (e / epn != r) continue;
+                    if (owner(e) != r) continue;
                     const int loff = s_P[t * K + k] - s_cu[r * epn];
                     if (first < 0) {
                         first = loff;
@@ -377,9 +388,7 @@ __global__ __launch_bounds__(kSmBlock) void small_path_kernel(SmallArgs sa) {
                     grp[2] = h - 1;
                 }
             }
-            carry[r] += tot;
         }
-        lds_barrier();
     }
 }
 

@@ -93,6 +93,8 @@ CASES = [
     (1500, 24, 1, 2, 4, 3, 4, synth.F32, "softmax"),           # K = 1, 1500 slots
     (777, 40, 3, 5, 4, 7, 9, synth.BF16, "sigmoid"),           # E not a multiple of 16 bytes of bf16
     (2000, 64, 8, 4, 4, 2, 3, synth.F32, "softmax"),           # above the one-kernel envelope
+    (1000, 16, 2, 1, 2, 1, 24, synth.F32, "softmax"),          # duplicates over two 512-token chunks
+    (700, 30, 2, 3, 3, 7, 5, synth.BF16, "softmax"),           # two chunks, 10 experts per rank
     (500, 512, 4, 2, 8, 5, 2, synth.BF16, "softmax"),          # E above the one-kernel envelope
 ]
 

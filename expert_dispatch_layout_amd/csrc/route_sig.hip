@@ -6,7 +6,9 @@ namespace mep {
 
 namespace {
 
-constexpr int kSigWaves = 8;         // one workgroup of 8 waves per compute unit
+constexpr int kSigWaves = 8;          // one workgroup per compute unit: two waves per SIMD
+constexpr int kSigWavesBig = 12;      // three per SIMD, where a workgroup has many sets
+constexpr int64_t kSigBigSets = 96;   // sets per workgroup from which the third wave pays
 constexpr size_t kLdsLimit = 160 * 1024;
 
 // Static LDS of a kernel (bytes).
@@ -19,16 +21,15 @@ size_t static_lds(const void* kernel) {
 template <int LPT, bool BF16, int MODE>
 bool launch_sig(const RouteArgs& a, const Launch& st, const PathCall* pc) {
     constexpr int TPW = SigGeom<LPT, BF16>::TPW;
-    auto kernel = route_sig_kernel<LPT, BF16, MODE, kSigWaves>;
     SigCfg cfg;
     cfg.tg = MODE == 1 ? a.topk_group : LPT;
     SigEpi ep{};
-    int64_t grid;
+    int64_t grid, sets;
     size_t dyn;
     if (pc) {
         const PathGeom& g = pc->g;
         // sets of the largest workgroup: sub tiles of at most T tokens each
-        const int64_t sets = ceil_div64((int64_t)g.sub * g.T, TPW);
+        sets = ceil_div64((int64_t)g.sub * g.T, TPW);
         dyn = sig_dyn_lds(sets, g.sub, g.NC);
         grid = g.nwg;
         ep.on = 1;
@@ -42,14 +43,23 @@ bool launch_sig(const RouteArgs& a, const Launch& st, const PathCall* pc) {
         const int64_t nsets = ceil_div64(a.N, TPW);
         grid = device_units();
         if (grid > nsets) grid = nsets;
-        const int64_t sets = ceil_div64(nsets, grid);
+        sets = ceil_div64(nsets, grid);
         cfg.tokens_per_group = sets * TPW;
         grid = ceil_div64(a.N, cfg.tokens_per_group);
         dyn = sig_dyn_lds(sets, 0, 0);
         ep.on = 0;
     }
-    if (static_lds(reinterpret_cast<const void*>(kernel)) + dyn > kLdsLimit) return false;
-    launch_kernel(kernel, dim3((unsigned)grid), dim3(64 * kSigWaves), (uint32_t)dyn, st, a, cfg, ep);
+    // long streams (a decode-size workgroup has few sets) take a third wave per SIMD to hide
+    // more of the loop's latencies, if its LDS fits
+    auto fits = [&](const void* kernel) { return static_lds(kernel) + dyn <= kLdsLimit; };
+    auto big = route_sig_kernel<LPT, BF16, MODE, kSigWavesBig>;
+    auto base = route_sig_kernel<LPT, BF16, MODE, kSigWaves>;
+    if (sets >= kSigBigSets && fits(reinterpret_cast<const void*>(big))) {
+        launch_kernel(big, dim3((unsigned)grid), dim3(64 * kSigWavesBig), (uint32_t)dyn, st, a, cfg, ep);
+        return true;
+    }
+    if (!fits(reinterpret_cast<const void*>(base))) return false;
+    launch_kernel(base, dim3((unsigned)grid), dim3(64 * kSigWaves), (uint32_t)dyn, st, a, cfg, ep);
     return true;
 }
 

@@ -213,6 +213,38 @@ def test_route_sigmoid_lane_groups(G, K, dtype):
         check_route(logits, K, dtype, score_fn=1, bias=bias, scale=1.0, renormalize=False)
 
 
+# long streams: workgroups of 96 sets or more take the sigmoid kernel with three waves per SIMD
+# (every lane layout, with and without group limits, fp32 and bf16, a ragged last set); the oracle
+# runs threaded (oracle.route_threads, pinned to oracle.route by the CPU tests)
+LONG_CASES = [
+    (100003, 512, 8, synth.F32, 0),    # 16 lanes per token, no group limit
+    (400001, 128, 6, synth.BF16, 1),   # 4 lanes per token, groups of 32
+    (800003, 64, 4, synth.F32, 1),     # 2 lanes per token
+]
+
+
+@pytest.mark.parametrize("N,E,K,dtype,grouped", LONG_CASES)
+def test_route_sigmoid_long_streams(N, E, K, dtype, grouped):
+    import os
+    rng = np.random.default_rng(N + E)
+    x = rng.standard_normal((N, E)).astype(np.float32)
+    x[::97, 1::3] = x[::97, 0:1]       # equal logits: the exact path
+    logits = synth.f32_to_bf16_bits(x) if dtype == synth.BF16 else x
+    del x
+    bias = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    kw = dict(score_fn=1, bias=bias, scale=2.5)
+    if grouped:
+        G = E // 32
+        kw.update(n_group=G, topk_group=max(1, G // 2), group_topn=2)
+    ids_g, w_g = gpu_route(logits, K, dtype, **kw)
+    ids_o, w_o = oracle.route_threads(logits, K, max(1, min(16, os.cpu_count() or 1)), dtype=dtype, **kw)
+    bad = np.nonzero((ids_g != ids_o).any(axis=1))[0]
+    assert bad.size == 0, "ids differ on %d tokens, first %s" % (bad.size, bad[:3])
+    tol = 2e-3 if dtype == synth.BF16 else 1e-6
+    err = np.abs(w_g.astype(np.float64) - w_o) / np.maximum(np.abs(w_o.astype(np.float64)), 1e-30)
+    assert float(err.max()) <= tol, err.max()
+
+
 def test_route_tiny_batches():
     rng = np.random.default_rng(9)
     for N in (1, 2, 3, 63, 65, 257):

@@ -46,7 +46,7 @@ constexpr int kPathMaxE = 512;
 constexpr int kPathMaxR = 32;
 constexpr int kPathMaxK = 8;
 constexpr int kPathMaxNC = kPathMaxE + 3 * kPathMaxR;
-constexpr int kPathSlots = 2048;    // slots of a plan tile, at most
+constexpr int kPathSlots = 4096;    // slots of a plan tile, at most
 constexpr int kPathTokens = 1024;   // tokens of a plan tile, at most
 constexpr int kPathMinTileTokens = 64;  // tokens of a plan tile, at least (unless a shard is smaller)
 constexpr int kPathMaxSub = 8;      // plan tiles per counting workgroup, at most

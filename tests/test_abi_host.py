@@ -59,8 +59,9 @@ def test_workspace_sizes():
     old = (256 + gsum + 2048 * 4 + a256(32 * 24 * 8) + a256(32 * 256 * 8)
            + a256(256 * (24 + 256) * 8))
 
-    # the fused path's plan tiles (2048 slots: 256 tokens at K = 8, never crossing a shard),
-    # counting workgroups of `sub` tiles (about 256 of them): header, group sums, the count-tile
+    # the fused path's plan tiles (at most 4096 slots, at most ceil(N / 256) tokens rounded up
+    # to a multiple of 64 but no fewer than 64, never crossing a shard), counting workgroups of
+    # `sub` tiles (about 256 of them): header, group sums, the count-tile
     # counters of mep_plan, then the workgroup totals and the within-workgroup tile prefixes
     # (E + 3R columns, 256-aligned parts)
     def path(ntiles, sub, nc):
@@ -71,11 +72,11 @@ def test_workspace_sizes():
     assert B.plan_workspace_size(65536, 256, 8, 8, 8) == want
     assert B.plan_workspace_size(65536, 256, 8, 8, 1) == want
     # 262144 tokens over 32 shards: halving would give 1024 tiles, so 512 tiles of 512 tokens
-    # stay, 16 per count tile (one per shard), 32 count tiles; the fused path has 1024 tiles of
-    # 256 tokens, 4 per counting workgroup
+    # stay, 16 per count tile (one per shard), 32 count tiles; the fused path has 512 tiles of
+    # 512 tokens (4096 slots), 2 per counting workgroup
     old = (256 + gsum + 2048 * 4 + a256(32 * 96 * 8) + a256(32 * 256 * 8)
            + a256(512 * (96 + 256) * 8))
-    assert B.plan_workspace_size(262144, 256, 8, 32, 32) == max(old, path(1024, 4, 256 + 96))
+    assert B.plan_workspace_size(262144, 256, 8, 32, 32) == max(old, path(512, 2, 256 + 96))
 
 
 FAKE = 0x10000          # aligned, never dereferenced

@@ -407,22 +407,28 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
 #pragma unroll
                 for (int k = 0; k < kPathMaxK; ++k) e[k] = k < K ? (int)s_code[tk * K + k] : 0;
             }
+            // up to 32 ranks: per-rank slot counts as 4-bit fields of four words (ranks 8q .. 8q + 7
+            // in word q)
 #pragma unroll
-            for (int k = 0; k < kPathMaxK; ++k) r[k] = k < K ? s_owner[e[k]] : -1 - k;
+            for (int k = 0; k < kPathMaxK; ++k) r[k] = k < K ? (g.eshift >= 0 ? e[k] >> g.eshift : s_owner[e[k]]) : 0;
+            uint32_t c4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int k = 0; k < kPathMaxK; ++k) {
+                const uint32_t inc = k < K ? 1u << (4 * (r[k] & 7)) : 0u;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) c4[q] += (r[k] >> 3) == q ? inc : 0u;
+            }
 #pragma unroll
             for (int k = 0; k < kPathMaxK; ++k) {
                 if (k >= K) continue;
-                int h = 0;
-                bool first = true;
-#pragma unroll
-                for (int k2 = 0; k2 < kPathMaxK; ++k2) {
-                    const bool same = r[k2] == r[k];
-                    h += same ? 1 : 0;
-                    if (k2 < k && same) first = false;
-                }
+                const int q = r[k] >> 3;
+                const uint32_t wq = q == 0 ? c4[0] : q == 1 ? c4[1] : q == 2 ? c4[2] : c4[3];
+                const int h = (int)((wq >> (4 * (r[k] & 7))) & 15u);
+                const uint32_t bit = 1u << r[k];
+                const bool first = (m & bit) == 0u;
+                m |= bit;
                 const uint32_t type = first ? (h >= 2 ? kSlotHead : kSlotPlain) : kSlotDup;
                 cd[k] = slot_code(e[k], type, r[k], h);
-                m |= 1u << r[k];
             }
             if (K == 8) {
                 *reinterpret_cast<u32x4*>(&s_code[tk * 8]) = u32x4{cd[0], cd[1], cd[2], cd[3]};

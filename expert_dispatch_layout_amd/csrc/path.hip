@@ -456,11 +456,16 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
             }
         }
         if (want_mask) {
+            // the wave's tokens on rank r as one 64-bit ballot, kept by lane r, then one store
+            // per lane (no branch or LDS store inside the loop)
             const int tw = base >> 6;
+            uint64_t mine = 0ull;
+#pragma unroll 8
             for (int r = 0; r < R; ++r) {
                 const uint64_t bm = __ballot((m >> r) & 1u);
-                if (lane == 0) s_mask[tw][r] = bm;
+                mine = lane == r ? bm : mine;
             }
+            if (lane < R) s_mask[tw][lane] = mine;
         }
     }
     __syncthreads();

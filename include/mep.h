@@ -126,8 +126,8 @@ typedef struct mep_route_params {
  *   p            host pointer to the parameters above
  *   topk_ids     device, int32[N,K] (output)
  *   topk_weights device, float[N,K] (output, nullable)
- * Returns MEP_ERR_UNSUPPORTED for E > 1024, K > min(E, 32), group_topn not
- * in {1,2}, E % n_group != 0, or topk_group*(E/n_group) < K.
+ * Returns MEP_ERR_UNSUPPORTED for E > 1024, K > min(E, 32), n_group > 32,
+ * group_topn not in {1,2}, E % n_group != 0, or topk_group*(E/n_group) < K.
  * Non-finite logits give unspecified (but memory-safe) results.
  */
 int mep_route_topk(const void* logits, int dtype, int64_t N, int E, int K,

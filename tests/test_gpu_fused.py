@@ -148,6 +148,7 @@ FUSED_CASES = [
     (3333, 100, 7, synth.F32, "softmax", 5, 10, 3, 9),
     (6000, 8, 2, synth.BF16, "softmax_full", 128, 8, 8, 24),
     (40000, 256, 8, synth.F32, "sigmoid_group", 128, 8, 8, 24),
+    (65536, 256, 8, synth.F32, "sigmoid_group", 128, 8, 1024, 4),  # 1024 tiles, 4 per counting workgroup
     # shapes of the generic routing kernel: with counting (2 to 8 lanes per token, tiles of 64
     # tokens with a ragged last one, experts per rank not a power of two) and, for 16 or more
     # lanes per token, followed by the counting kernel (sigmoid outside the sigmoid kernel's lane

@@ -392,7 +392,7 @@ def three_calls_leg(B, torch, sets, bias, params, wl, ws_l, ws_p, steps: int, st
     t1.record(stream)
     torch.cuda.synchronize()
     return {"us_per_step": t0.elapsed_time(t1) * 1e3 / steps, "steps": steps,
-            "kernels": "routing, layout count + scatter, plan count + write (5 launches)"}
+            "kernels": "routing, layout count + scatter, plan-tile counting + plan-tile kernel (5 launches)"}
 
 
 def main():

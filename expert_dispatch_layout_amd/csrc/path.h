@@ -93,7 +93,10 @@ struct PathWs {
     uint32_t* tpre;  // [ntiles][NCs] exclusive prefix within the counting workgroup
 };
 
-// Outputs of the layout and the plan (device pointers; NULL skips an optional one).
+// Outputs of the layout and the plan (device pointers; NULL skips an optional one).  For
+// mep_plan, whose layout is an input, the layout outputs are NULL and cu_in / p_in point to
+// the given cu_seqlens and expanded_to_permuted, which the plan then uses (NULL otherwise: the
+// plan-tile kernel forms them itself).
 struct PathOut {
     int32_t* tokens_per_expert;
     int32_t* cu_seqlens;
@@ -101,6 +104,8 @@ struct PathOut {
     int32_t* p2e;
     int32_t* zero_fill;
     PlanOutDev p;
+    const int32_t* cu_in;
+    const int32_t* p_in;
 };
 
 // The counting kernel's view of the call counter: its parity names the buffer the group sums go
@@ -231,6 +236,9 @@ struct PathCall {
     const int32_t* ids;
 };
 PathCall path_call(const LayoutCall& lc, const PlanCall& pc, void* ws);
+// mep_plan on the plan-tile path: the layout comes in (cu_seqlens, expanded_to_permuted of
+// alignment A), only the plan goes out.
+PathCall path_call_plan(const PlanCall& pc, const int32_t* cu_seqlens, const int32_t* e2p, int A, void* ws);
 // The counting kernel over the ids (when the routing kernel did not count), then the plan-tile
 // kernel (optionally stamped with start / stop events by its launch).
 void path_launch_count(const PathCall& c, hipStream_t st);

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kCountNT) void path_count_kernel(const int32_t* __r
 // By wave 0: the padded exclusive scan of the expert totals (cu_seqlens, [MOON] Phase B2 padded
 // group scan) and the exclusive scans over the ranks of the dedup group and duplicate totals.
 __device__ __forceinline__ void path_scan_totals(const PathGeom& g, const int* s_tot, int* s_cu,
-                                                 int (*s_doff)[kPathMaxR + 1]) {
+                                                 int (*s_doff)[kPathMaxR + 1], const int32_t* cu_in) {
     const int lane = threadIdx.x & 63;
     const int E = g.E, R = g.R, A = g.A;
     constexpr int PER = kPathMaxE / 64;
@@ -142,10 +142,10 @@ __device__ __forceinline__ void path_scan_totals(const PathGeom& g, const int* s
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int e = lane * per + i;
-        if (i < per && e < E) s_cu[e] = run;
+        if (i < per && e < E) s_cu[e] = cu_in ? gptr(cu_in)[e] : run;  // the given layout's, else formed
         run += pad[i];
     }
-    if (lane == 0) s_cu[E] = total;
+    if (lane == 0) s_cu[E] = cu_in ? gptr(cu_in)[E] : total;
     const int ng_r = lane < R ? s_tot[path_col_c1(g, lane)] : 0;
     const int nd_r = lane < R ? s_tot[path_col_c2(g, lane)] : 0;
     int tg, td;
@@ -164,7 +164,8 @@ __device__ __forceinline__ void path_small_outputs(const PathGeom& g, const Path
                                                    const int* s_cu, const int (*s_doff)[kPathMaxR + 1]) {
     const int tid = threadIdx.x;
     const int E = g.E, R = g.R;
-    for (int e = tid; e <= E; e += NT) gptr(o.cu_seqlens)[e] = s_cu[e];
+    if (o.cu_seqlens)
+        for (int e = tid; e <= E; e += NT) gptr(o.cu_seqlens)[e] = s_cu[e];
     for (int e = tid; e < E; e += NT) {
         const int c = s_tot[e];
         const int cu0 = s_cu[e];
@@ -339,7 +340,7 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
     __syncthreads();
     // ---- tokens (waves 0 .. kPlanW - 2): slot codes, is_token_in_rank, rank ballots; the last
     // wave meanwhile forms cu_seqlens and the dedup segment starts ---------------------------------
-    if (wv == kPlanW - 1) path_scan_totals(g, s_tot, s_cu, s_doff);
+    if (wv == kPlanW - 1) path_scan_totals(g, s_tot, s_cu, s_doff, o.cu_in);
     for (int base = wv * 64; wv < kPlanW - 1 && base < nt; base += (kPlanW - 1) * 64) {
         const int tk = base + lane;
         const bool live = tk < nt;
@@ -545,9 +546,10 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
         const uint32_t type = (code >> 10) & 3u;
         const int r = (int)((code >> 12) & 31u);
         const int h = (int)(code >> 17);
-        const int P = s_cu[e] + s_excl[e] + s_ecnt[wv][e] + erank[it];
         const int64_t gs = s0 + si;
-        gptr(o.e2p)[gs] = P;
+        // the slot's permuted row: given (mep_plan), else its stable position
+        const int P = o.p_in ? gptr(o.p_in)[gs] : s_cu[e] + s_excl[e] + s_ecnt[wv][e] + erank[it];
+        if (o.e2p) gptr(o.e2p)[gs] = P;
         if (o.p2e) gptr(o.p2e)[P] = (int32_t)gs;
         const int loff = P - s_cu[r * epn];
         const int raw = r * NvS + loff;
@@ -699,7 +701,18 @@ PathCall path_call(const LayoutCall& lc, const PlanCall& pc, void* ws) {
     c.g = path_geom(pc.g.N, pc.g.E, pc.g.K, pc.g.R, pc.g.S, pc.g.C, lc.A, pc.g.NvS);
     c.w = path_ws_views(ws, c.g);
     c.hdr = reinterpret_cast<WsHeader*>(ws);
-    c.o = PathOut{lc.out.tokens_per_expert, lc.out.cu_seqlens, lc.out.e2p, lc.out.p2e, lc.out.zero_fill, pc.o};
+    c.o = PathOut{lc.out.tokens_per_expert, lc.out.cu_seqlens, lc.out.e2p, lc.out.p2e, lc.out.zero_fill, pc.o,
+                  nullptr, nullptr};
+    c.ids = pc.ids;
+    return c;
+}
+
+PathCall path_call_plan(const PlanCall& pc, const int32_t* cu_seqlens, const int32_t* e2p, int A, void* ws) {
+    PathCall c;
+    c.g = path_geom(pc.g.N, pc.g.E, pc.g.K, pc.g.R, pc.g.S, pc.g.C, A, pc.g.NvS);
+    c.w = path_ws_views(ws, c.g);
+    c.hdr = reinterpret_cast<WsHeader*>(ws);
+    c.o = PathOut{nullptr, nullptr, nullptr, nullptr, nullptr, pc.o, cu_seqlens, e2p};
     c.ids = pc.ids;
     return c;
 }

@@ -940,6 +940,14 @@ extern "C" int mep_plan(const int32_t* topk_ids, const int32_t* cu_seqlens,
                                 num_channels, NvS, out, ws, ws_bytes, c);
     if (rc != MEP_OK) return rc;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (path_supported(N, E, K, R)) {
+        // the plan-tile path: the counting kernel over the ids, then the plan-tile kernel, which
+        // takes every slot's row and the group offsets from the given layout
+        const PathCall pc = path_call_plan(c, cu_seqlens, expanded_to_permuted, alignment, ws);
+        path_launch_count(pc, st);
+        path_launch_plan(pc, st, nullptr, nullptr);
+        return launch_status();
+    }
     plan_launch_count(c, st);
     plan_launch_write(c, st);
     return launch_status();

@@ -11,9 +11,10 @@
 //   E + 2R + r    slots to rank r beyond the first                 (duplicates, which MoonEP
 //                                                                   planning.py encodes as -dst-1)
 //
-// Geometry.  A shard of n tokens is cut into plan tiles of T tokens (T*K <= 2048 slots); a
-// counting workgroup owns `sub` consecutive plan tiles, which are consecutive tokens.  Counting
-// workgroups form groups of GW.
+// Geometry.  A shard of n tokens is cut into plan tiles of T tokens (T*K <= 4096 slots, and for
+// small batches fewer tokens, so that there are about 256 tiles); a counting workgroup owns
+// `sub` consecutive plan tiles, which are consecutive tokens.  Counting workgroups form groups
+// of GW.
 //
 // Epilogue of a counting workgroup, once its LDS rows are complete (it waits for no other
 // workgroup):

@@ -1,9 +1,12 @@
 // The fused layout + plan path over plan tiles (path.h): the counting kernel (for ids given by
 // the caller; the routing kernel does the same counting in its epilogue when it runs in the
 // fused call), and the plan-tile kernel, which writes every per-slot and per-token output of the
-// layout and the plan for one tile from the prefixes the counting epilogue left.
+// layout and the plan for one tile from the prefixes the counting epilogue left.  mep_plan runs
+// the same two kernels with its layout as an input: the plan-tile kernel then takes each slot's
+// row and the expert offsets from it and writes only the plan.
 //
-// Plan-tile kernel, one workgroup of 1024 threads per tile (at most 2048 slots):
+// Plan-tile kernel, one workgroup per tile (at most 4096 slots) of 1024 threads when every tile
+// has a compute unit, else of 512 (two tiles per unit):
 //   prologue   the tile's ids into LDS; the exclusive prefix of every column before the tile
 //              (a sum of the rows the counting epilogue left, 16-byte loads spread over every
 //              thread), cu_seqlens, the dedup segment starts;

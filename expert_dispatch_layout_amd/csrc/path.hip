@@ -729,7 +729,9 @@ void path_launch_plan(const PathCall& c, hipStream_t st, hipEvent_t start, hipEv
         launch_ext(kernel, dim3(c.g.ntiles), dim3(nt), 0, st, start, stop, 0, c.ids, c.g, c.w, c.o, c.hdr);
     };
     const bool wideE = c.g.E > 256, wideR = c.g.R > 8;
-    if (c.g.ntiles <= device_units()) {
+    // 1024 threads when every tile has a compute unit and enough slots to share out; otherwise
+    // 512 (two tiles per unit; fewer waves to clear and synchronise for a small tile)
+    if (c.g.ntiles <= device_units() && (int64_t)c.g.T * c.g.K > 512) {
         constexpr int NT = kPlanNTBig;
         if (!wideR) wideE ? launch(path_plan_kernel<9, 3, NT>, NT) : launch(path_plan_kernel<8, 3, NT>, NT);
         else wideE ? launch(path_plan_kernel<9, 5, NT>, NT) : launch(path_plan_kernel<8, 5, NT>, NT);

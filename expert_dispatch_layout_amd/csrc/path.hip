@@ -39,7 +39,7 @@ constexpr int kCountNT = 512;
 // (two tiles per compute unit at once, whose dependent chains then overlap).
 constexpr int kPlanNTBig = 1024;
 constexpr int kPlanNTSmall = 512;
-constexpr int kPlanRowNT = 512;  // threads that load the prefix rows (at most 7 row slices to sum)
+constexpr int kPlanRowNT = 512;  // threads that load the prefix rows
 enum : uint32_t { kSlotPlain = 0, kSlotHead = 1, kSlotDup = 2 };
 
 __device__ __forceinline__ uint32_t slot_code(int e, uint32_t type, int r, int h) {
@@ -212,6 +212,7 @@ template <int NBE, int NBR, int kPlanNT>
 __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __restrict__ ids, PathGeom g,
                                                             PathWs w, PathOut o, WsHeader* hdr) {
     constexpr int kPlanW = kPlanNT / 64;
+    constexpr int kPlanRowBatch = 8;  // prefix rows a loader thread has in flight at once
     constexpr int kPlanIters = kPathSlots / kPlanNT;  // 64-slot steps per wave, at most
     __shared__ __align__(16) uint32_t s_code[kPathSlots];
     __shared__ int s_ecnt[kPlanW][kPathMaxE];
@@ -243,20 +244,24 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
     const bool want_shx = o.p.chan || (shard_last && (o.p.ntpr || o.p.ntpe));
 
     // ---- prologue: every global load of the tile, issued together ----------------------------
-    {
-        const MEP_GLOBAL int32_t* gid = gptr(ids) + s0;
-        if (((s0 & 3) == 0) && ((((uintptr_t)ids) & 15u) == 0)) {
-            const int nq = ns >> 2;
-            for (int q = tid; q < nq; q += kPlanNT) {
-                const u32x4 v = reinterpret_cast<const MEP_GLOBAL u32x4*>(gid)[q];
+    // The tile's ids: 16-byte loads into registers, stored into LDS only once the prefix rows'
+    // loads below are in flight as well, so that the two round trips overlap (plain loads where
+    // the slots are not 16-byte aligned).
+    constexpr int kIdQ = kPathSlots / 4 / kPlanNT;  // id quads per thread, at most
+    const MEP_GLOBAL int32_t* gid = gptr(ids) + s0;
+    const int nq = ((s0 & 3) == 0) && ((((uintptr_t)ids) & 15u) == 0) ? ns >> 2 : 0;
+    u32x4 idv[kIdQ];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s_code[4 * q + i] = v[i];
-            }
-            for (int s = (nq << 2) + tid; s < ns; s += kPlanNT) s_code[s] = (uint32_t)gid[s];
-        } else {
-            for (int s = tid; s < ns; s += kPlanNT) s_code[s] = (uint32_t)gid[s];
+    for (int i = 0; i < kIdQ; ++i)
+        if (tid + i * kPlanNT < nq) idv[i] = reinterpret_cast<const MEP_GLOBAL u32x4*>(gid)[tid + i * kPlanNT];
+    auto store_ids = [&]() {
+#pragma unroll
+        for (int i = 0; i < kIdQ; ++i) {
+            const int q = tid + i * kPlanNT;
+            if (q < nq) *reinterpret_cast<u32x4*>(&s_code[4 * q]) = idv[i];
         }
-    }
+        for (int s = (nq << 2) + tid; s < ns; s += kPlanNT) s_code[s] = (uint32_t)gid[s];
+    };
     // prefixes before this tile (and before the shard's first tile) and the totals: sums of rows
     // the counting epilogue left -- the group sum rows of both parities (one holds this call's
     // sums, the other is zero), the total rows of the earlier workgroups of the tile's group, the
@@ -278,45 +283,69 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
         const int r_f = r_t + 1;                // first workgroup row of the shard start's group
         const int nf = (shx_all || shx_rank) ? (wgf - wgf0) + 1 : 0;
         const int nrows = r_f + nf;
-        // row slices: as many as the loader threads allow, but no more than eight rows per slice
-        // need (each slice is summed again through LDS)
-        const int nsl = min(kPlanRowNT / NQ, max(1, (nrows + 7) / 8));
+        const int r_l = nf > 0 ? nrows - 1 : nrows;  // the shard start's prefix row
+        const int d_w = wg0 - r_w, d_f = wgf0 - r_f;  // row -> workgroup, in the two groups
+        // row slices: as many as one batch of loads per thread needs (each slice is summed again
+        // through LDS), within the loader threads
+        const int nsl = min(kPlanRowNT / NQ, max(1, (nrows + kPlanRowBatch - 1) / kPlanRowBatch));
         const int q = tid % NQ, sl = tid / NQ;
         const bool need_f = shx_all || (shx_rank && 4 * q < E + R && 4 * q + 4 > E);
-        // every row as a word offset from the first group sum row (rows past the list, and the
-        // shard start's rows of columns that do not need them, read group row 0 and count nowhere)
+        // every row as a word offset from the first group sum row (rows past the list read group
+        // row 0; they, and the shard start's rows in columns that do not need them, count nowhere)
         const MEP_GLOBAL uint32_t* base = gptr(w.gsum);
         const int64_t ow = w.wrow - w.gsum, ot = w.tpre - w.gsum;
         u32x4 tot = {0u, 0u, 0u, 0u}, ex = tot, sx = tot;
-        if (sl < nsl) {
-            for (int r0 = sl; r0 < nrows; r0 += 8 * nsl) {
-                u32x4 v[8];
-                uint32_t use[8];  // bit 0: totals, bit 1: prefix of the tile, bit 2: of the shard start
+        u32x4 v[kPlanRowBatch];
+        uint32_t use[kPlanRowBatch];  // bit 0: totals, bit 1: prefix of the tile, bit 2: of the shard start
+        auto issue = [&](int r0) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int r = r0 + i * nsl;
-                    const bool in_g = r < r_w, par1 = r >= ng;
-                    const int gi = par1 ? r - ng : r;
-                    const bool in_w = r >= r_w && r < r_t, in_t = r == r_t;
-                    const bool in_wf = need_f && r >= r_f && r < nrows - 1, in_tf = need_f && r == nrows - 1;
-                    const int64_t off = in_g    ? (par1 ? (int64_t)kPathGsumWords : 0) + (int64_t)gi * NCs
-                                        : in_w  ? ow + (int64_t)(wg0 + (r - r_w)) * NCs
-                                        : in_t  ? ot + (int64_t)j * NCs
-                                        : in_wf ? ow + (int64_t)(wgf0 + (r - r_f)) * NCs
-                                        : in_tf ? ot + (int64_t)jf * NCs
-                                                : 0;
-                    use[i] = in_g ? 1u | (gi < grp ? 2u : 0u) | (gi < grpf ? 4u : 0u)
-                                  : (in_w || in_t) ? 2u : (in_wf || in_tf) ? 4u : 0u;
-                    v[i] = reinterpret_cast<const MEP_GLOBAL u32x4*>(base + off)[q];
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const u32x4 z = {0u, 0u, 0u, 0u};
-                    tot += (use[i] & 1u) ? v[i] : z;
-                    ex += (use[i] & 2u) ? v[i] : z;
-                    sx += (use[i] & 4u) ? v[i] : z;
-                }
+            for (int i = 0; i < kPlanRowBatch; ++i) {
+                // the row's place from comparisons with the segment starts (group sum rows of
+                // parity 0, of parity 1, total rows of the tile's group, the tile's prefix row,
+                // total rows of the shard start's group, the shard start's prefix row, past the
+                // list), one two-way select per statement: nested conditional expressions compile
+                // to divergent branches
+                const int r = r0 + i * nsl;
+                const bool c1 = r >= ng, c2 = r >= r_w, c3 = r >= r_t, c4 = r >= r_f, c5 = r >= r_l,
+                           c6 = r >= nrows;
+                const int gi = c1 ? r - ng : r;
+                const int i5 = c6 ? 0 : jf;
+                const int i4 = c5 ? i5 : r + d_f;
+                const int i3 = c4 ? i4 : j;
+                const int i2 = c3 ? i3 : r + d_w;
+                const int idx = c2 ? i2 : gi;
+                const int64_t b_g = c1 ? (int64_t)kPathGsumWords : 0;
+                const int64_t b_p = (c3 && !(c4 && !c5)) ? ot : ow;  // a prefix row, else a total row
+                const int64_t b_w = c6 ? 0 : b_p;
+                const int64_t rb = c2 ? b_w : b_g;
+                const uint32_t u_g = 1u | (gi < grp ? 2u : 0u) | (gi < grpf ? 4u : 0u);
+                const uint32_t u_f = (c6 || !need_f) ? 0u : 4u;
+                const uint32_t u_w = c4 ? u_f : 2u;
+                use[i] = c2 ? u_w : u_g;
+                v[i] = reinterpret_cast<const MEP_GLOBAL u32x4*>(base + rb + (uint32_t)(idx * NCs))[q];
             }
+        };
+        auto accumulate = [&]() {
+#pragma unroll
+            for (int i = 0; i < kPlanRowBatch; ++i) {
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                tot += (use[i] & 1u) ? v[i] : z;
+                ex += (use[i] & 2u) ? v[i] : z;
+                sx += (use[i] & 4u) ? v[i] : z;
+            }
+        };
+        // the ids are stored on both sides of the branch, after the loads on the loaders' side (a
+        // store after the join would wait for every load of the loaders)
+        if (sl < nsl) {
+            issue(sl);
+            store_ids();
+            accumulate();
+            for (int r0 = sl + kPlanRowBatch * nsl; r0 < nrows; r0 += kPlanRowBatch * nsl) {
+                issue(r0);
+                accumulate();
+            }
+        } else {
+            store_ids();
         }
         if (tid < kPlanRowNT) {
             s_pq[0][tid] = tot;

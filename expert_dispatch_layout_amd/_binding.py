@@ -336,7 +336,7 @@ class KernelTimer:
         return ms.value
 
     def __del__(self):
-        h = KernelTimer._hip
+        h = type(self)._hip  # not the module global, which interpreter shutdown may clear first
         if h is not None:
             for e in (self.start, self.stop):
                 if e:

@@ -13,7 +13,7 @@
 // Two kernels:
 //   plan    one workgroup per destination rank d.  Wave 0 runs the balancing loop (every
 //           workgroup gets the same moves; workgroup 0 stores z and the group totals); then
-//           the waves run the owners' quota loops, owner o on wave o mod 4, each appending its
+//           the waves run the owners' quota loops, owner o on wave o mod 8, each appending its
 //           (destination, expert, slots) allocations to an LDS list and leaving each expert's
 //           remainder with its owner; the owners' loops are short and run in every workgroup,
 //           which is cheaper than a second launch.  From the list the workgroup forms row d of
@@ -38,7 +38,7 @@ constexpr int kBalMaxRanks = 128;
 constexpr int kBalMaxExperts = 1024;
 constexpr int kBalMaxCopies = 64;
 constexpr int kBalMaxK = 32;
-constexpr int kBalBlock = 256;
+constexpr int kBalBlock = 512;  // 8 waves: owners' quota loops on 8 waves at once
 constexpr int kBalTokBlock = 256;
 
 struct BalArgs {
@@ -82,8 +82,6 @@ __device__ __forceinline__ long long wave_ext64(long long v) {
     return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
 }
 
-__device__ __forceinline__ long long wave_max64(long long v) { return wave_ext64<true>(v); }
-__device__ __forceinline__ long long wave_min64(long long v) { return wave_ext64<false>(v); }
 
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
@@ -98,17 +96,185 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Arg-extremum keys: the value in the high bits, the index tie-break in the low 11 bits.
-constexpr long long kIdxSpan = 2048;
-__device__ __forceinline__ long long key_max_low(long long v, int i) { return v * kIdxSpan + (kIdxSpan - 1 - i); }
-__device__ __forceinline__ long long key_min_low(long long v, int i) { return v * kIdxSpan + i; }
-__device__ __forceinline__ long long key_max_high(long long v, int i) { return v * kIdxSpan + i; }
-__device__ __forceinline__ long long key_value(long long k) {
-    // floor division: the index part is always in [0, kIdxSpan)
-    return k >= 0 ? k / kIdxSpan : -((-k + kIdxSpan - 1) / kIdxSpan);
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xf, false);
 }
-__device__ __forceinline__ int key_index_low(long long k) { return (int)(kIdxSpan - 1 - (k - key_value(k) * kIdxSpan)); }
-__device__ __forceinline__ int key_index(long long k) { return (int)(k - key_value(k) * kIdxSpan); }
+
+// Wave-wide 32-bit max / min: the lane moves of wave_ext64, one 32-bit operation each.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_ext32(uint32_t v) {
+    auto pick = [](uint32_t p, uint32_t q) { return MAX ? (p > q ? p : q) : (p < q ? p : q); };
+    v = pick(v, dpp32<0xB1, 0xf>(v));   // quad_perm 1,0,3,2
+    v = pick(v, dpp32<0x4E, 0xf>(v));   // quad_perm 2,3,0,1
+    v = pick(v, dpp32<0x141, 0xf>(v));  // row_half_mirror
+    v = pick(v, dpp32<0x140, 0xf>(v));  // row_mirror
+    v = pick(v, dpp32<0x142, 0xa>(v));  // row_bcast:15 into rows 1 and 3
+    v = pick(v, dpp32<0x143, 0xc>(v));  // row_bcast:31 into rows 2 and 3
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Arg-extremum keys: the value in the high bits and an index tie-break in the low bits, so that
+// one integer maximum (or minimum) over the wave gives both.  Wide keys (64-bit: the value times
+// 2048 plus an 11-bit index) take any value the plan forms; narrow keys (32-bit: the value plus
+// 2^21 in the high 22 bits, a 10-bit index below) take values in (-2^21, 2^21), and reduce with
+// one 32-bit operation per lane move instead of a 64-bit compare and two selects.  max_low:
+// largest value, ties to the lower index; min_low: smallest value, ties to the lower index;
+// max_high: largest value, ties to the higher index.
+template <bool N32>
+struct BalKeys;
+
+template <>
+struct BalKeys<false> {
+    using T = long long;
+    static constexpr long long kSpan = 2048;
+    static constexpr T kLow = LLONG_MIN, kHigh = LLONG_MAX;
+    __device__ static T max_low(long long v, int i) { return v * kSpan + (kSpan - 1 - i); }
+    __device__ static T min_low(long long v, int i) { return v * kSpan + i; }
+    __device__ static T max_high(long long v, int i) { return v * kSpan + i; }
+    // floor division: the index part is always in [0, kSpan)
+    __device__ static long long value(T k) { return k >= 0 ? k / kSpan : -((-k + kSpan - 1) / kSpan); }
+    __device__ static int index_low(T k) { return (int)(kSpan - 1 - (k - value(k) * kSpan)); }
+    __device__ static int index(T k) { return (int)(k - value(k) * kSpan); }
+    __device__ static T wave_max(T v) { return wave_ext64<true>(v); }
+    __device__ static T wave_min(T v) { return wave_ext64<false>(v); }
+};
+
+template <>
+struct BalKeys<true> {
+    using T = uint32_t;
+    static constexpr int kBits = 10;
+    static constexpr long long kOff = 1ll << 21;
+    static constexpr T kLow = 0u, kHigh = 0xFFFFFFFFu;
+    __device__ static T pack(long long v, int i) { return ((T)(v + kOff) << kBits) | (T)i; }
+    __device__ static T max_low(long long v, int i) { return pack(v, (1 << kBits) - 1 - i); }
+    __device__ static T min_low(long long v, int i) { return pack(v, i); }
+    __device__ static T max_high(long long v, int i) { return pack(v, i); }
+    __device__ static long long value(T k) { return (long long)(k >> kBits) - kOff; }
+    __device__ static int index_low(T k) { return (1 << kBits) - 1 - (int)(k & ((1u << kBits) - 1u)); }
+    __device__ static int index(T k) { return (int)(k & ((1u << kBits) - 1u)); }
+    __device__ static T wave_max(T v) { return wave_ext32<true>(v); }
+    __device__ static T wave_min(T v) { return wave_ext32<false>(v); }
+};
+constexpr long long kNarrowLimit = 1ll << 21;  // narrow keys: every value of magnitude below this
+
+// The balancing loop on one wave (lane holds ranks lane and lane + 64): while some rank has a
+// surplus and some a deficit, the largest surplus (lowest rank on ties) fills the largest deficit
+// (lowest rank on ties) completely; each move (from, to, slots) goes to `s_moves`.  Returns the
+// number of moves.
+template <bool N32>
+__device__ __forceinline__ int balance_moves(long long (&bal)[2], int R, int lane, int* s_moves) {
+    using Kt = BalKeys<N32>;
+    int nmoves = 0;
+    for (;;) {
+        typename Kt::T kmax = Kt::kLow, kmin = Kt::kHigh;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int r = lane + 64 * c;
+            if (r < R) {
+                const typename Kt::T k1 = Kt::max_low(bal[c], r), k2 = Kt::min_low(bal[c], r);
+                kmax = k1 > kmax ? k1 : kmax;
+                kmin = k2 < kmin ? k2 : kmin;
+            }
+        }
+        kmax = Kt::wave_max(kmax);
+        kmin = Kt::wave_min(kmin);
+        const long long surplus = Kt::value(kmax), deficit = Kt::value(kmin);
+        if (surplus <= 0 || deficit >= 0) break;
+        const int sr = Kt::index_low(kmax), dr = Kt::index(kmin);
+        const long long move = -deficit;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int r = lane + 64 * c;
+            if (r == sr) bal[c] -= move;
+            if (r == dr) bal[c] = 0;
+        }
+        if (lane == 0) {
+            s_moves[3 * nmoves] = sr;
+            s_moves[3 * nmoves + 1] = dr;
+            s_moves[3 * nmoves + 2] = (int)move;
+        }
+        ++nmoves;
+    }
+    return nmoves;
+}
+
+// Owner o's quota loop on one wave: while a destination's quota (the largest, lowest rank on
+// ties) and an expert's remainder (the largest, lowest expert on ties) are both left, the smaller
+// of the two moves; each allocation (destination, expert, slots) is appended to `s_ent`.
+template <bool N32, int kCh>
+__device__ __forceinline__ void owner_quotas(long long (&quota)[2], long long (&rem)[kCh], int o, int R, int epn,
+                                             int lane, int* s_nent, int (*s_ent)[3]) {
+    using Kt = BalKeys<N32>;
+    for (;;) {
+        typename Kt::T kq = Kt::kLow;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int r = lane + 64 * c;
+            if (r < R) {
+                const typename Kt::T k = Kt::max_low(quota[c], r);
+                kq = k > kq ? k : kq;
+            }
+        }
+        typename Kt::T kr = Kt::kLow;
+#pragma unroll
+        for (int c = 0; c < kCh; ++c) {
+            const int jj = lane + 64 * c;
+            if (jj < epn) {
+                const typename Kt::T k = Kt::max_low(rem[c], jj);
+                kr = k > kr ? k : kr;
+            }
+        }
+        kq = Kt::wave_max(kq);
+        kr = Kt::wave_max(kr);
+        const long long mq = Kt::value(kq), mr = Kt::value(kr);
+        if (mq <= 0 || mr <= 0) break;
+        const int tr = Kt::index_low(kq), sj = Kt::index_low(kr);
+        const long long take = mr < mq ? mr : mq;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+            if (lane + 64 * c == tr) quota[c] -= take;
+#pragma unroll
+        for (int c = 0; c < kCh; ++c)
+            if (lane + 64 * c == sj) rem[c] -= take;
+        if (lane == 0) {
+            const int at = atomicAdd(s_nent, 1);
+            s_ent[at][0] = tr;
+            s_ent[at][1] = o * epn + sj;
+            s_ent[at][2] = (int)take;
+        }
+    }
+}
+
+// Destination d's experts to copy, on one wave: B passes, each taking the largest remote count
+// (the higher expert on ties; -1 once none is left) and clearing it.
+template <bool N32, int kCh>
+__device__ __forceinline__ void copy_choice(long long (&remote)[kCh], const BalArgs& a, int d, int lane, int* s_slot,
+                                            unsigned char* s_picked) {
+    using Kt = BalKeys<N32>;
+    for (int b = 0; b < a.B; ++b) {
+        typename Kt::T k = Kt::kLow;
+#pragma unroll
+        for (int c = 0; c < kCh; ++c) {
+            const int e = lane + 64 * c;
+            if (e < a.E) {
+                const typename Kt::T kk = Kt::max_high(remote[c], e);
+                k = kk > k ? kk : k;
+            }
+        }
+        k = Kt::wave_max(k);
+        const int best = Kt::index(k);
+        const int chosen = Kt::value(k) > 0 ? best : -1;
+#pragma unroll
+        for (int c = 0; c < kCh; ++c)
+            if (lane + 64 * c == best) remote[c] = 0;
+        if (lane == 0) {
+            s_slot[b] = chosen;
+            a.experts_to_copy[d * a.B + b] = chosen;
+            if (chosen >= 0) s_picked[chosen] = 1;
+        }
+    }
+}
 
 // ---------------------------------------------------------------------------------------------
 // plan kernel (balancing, owners' quotas, destination groups)
@@ -134,6 +300,8 @@ __global__ __launch_bounds__(kBalBlock) void balance_plan_kernel(BalArgs a) {
     __shared__ unsigned char s_picked[kBalMaxExperts];
     __shared__ int s_slot[kBalMaxCopies];
     __shared__ int s_wave[kBalWaves];
+    __shared__ int s_wide;    // some slot count or rank balance needs wide keys
+    __shared__ int s_narrow;  // the keys the loops use (the same in every workgroup)
     const int d = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
@@ -153,7 +321,10 @@ __global__ __launch_bounds__(kBalBlock) void balance_plan_kernel(BalArgs a) {
         s_eoff[i] = -1;
         s_picked[i] = 0;
     }
-    if (tid == 0) s_nent = 0;
+    if (tid == 0) {
+        s_nent = 0;
+        s_wide = 0;
+    }
     if (d == 0)
         for (int i = tid; i < R * R; i += kBalBlock) a.z[i] = 0;
     lds_barrier();
@@ -163,6 +334,7 @@ __global__ __launch_bounds__(kBalBlock) void balance_plan_kernel(BalArgs a) {
         if (e < E) {
             s_tot[e] = tot[i];
             atomicAdd(&s_group[e / epn], tot[i]);
+            if (tot[i] < 0 || tot[i] >= kNarrowLimit) s_wide = 1;
         }
     }
     lds_barrier();
@@ -178,43 +350,24 @@ __global__ __launch_bounds__(kBalBlock) void balance_plan_kernel(BalArgs a) {
             if (r < R && d == 0) a.group_tokens[r] = (int32_t)s2;
             bal[c] = s2 - a.cap;
         }
-        int nmoves = 0;
-        for (;;) {
-            long long kmax = LLONG_MIN, kmin = LLONG_MAX;
+        // narrow keys when every balance is within their range (then so is every quota, and
+        // every remainder is a slot count, checked above)
+        bool wide = s_wide != 0;
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int r = lane + 64 * c;
-                if (r < R) {
-                    const long long k1 = key_max_low(bal[c], r), k2 = key_min_low(bal[c], r);
-                    kmax = k1 > kmax ? k1 : kmax;
-                    kmin = k2 < kmin ? k2 : kmin;
-                }
-            }
-            kmax = wave_max64(kmax);
-            kmin = wave_min64(kmin);
-            const long long surplus = key_value(kmax), deficit = key_value(kmin);
-            if (surplus <= 0 || deficit >= 0) break;
-            const int sr = key_index_low(kmax), dr = key_index(kmin);
-            const long long move = -deficit;
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int r = lane + 64 * c;
-                if (r == sr) bal[c] -= move;
-                if (r == dr) bal[c] = 0;
-            }
-            if (lane == 0) {
-                s_moves[3 * nmoves] = sr;
-                s_moves[3 * nmoves + 1] = dr;
-                s_moves[3 * nmoves + 2] = (int)move;
-            }
-            ++nmoves;
+        for (int c = 0; c < 2; ++c)
+            if (lane + 64 * c < R && (bal[c] <= -kNarrowLimit || bal[c] >= kNarrowLimit)) wide = true;
+        wide = __ballot(wide) != 0ull;
+        const int nmoves = wide ? balance_moves<false>(bal, R, lane, s_moves) : balance_moves<true>(bal, R, lane, s_moves);
+        if (lane == 0) {
+            s_narrow = wide ? 0 : 1;
+            s_nmoves = nmoves;
         }
-        if (lane == 0) s_nmoves = nmoves;
     }
     lds_barrier();
 
-    // ---- quota allocation of every owner's moves over its experts (owner o on wave o mod 4) ----
+    // ---- quota allocation of every owner's moves over its experts (owner o on wave o mod 8) ----
     const int nmoves = s_nmoves;
+    const bool narrow = s_narrow != 0;
     for (int o = wv; o < R; o += kBalWaves) {
         long long quota[2];
 #pragma unroll
@@ -232,46 +385,8 @@ __global__ __launch_bounds__(kBalBlock) void balance_plan_kernel(BalArgs a) {
             const int jj = lane + 64 * c;
             rem[c] = jj < epn ? s_tot[o * epn + jj] : 0;
         }
-        for (;;) {
-            long long kq = LLONG_MIN;
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int r = lane + 64 * c;
-                if (r < R) {
-                    const long long k = key_max_low(quota[c], r);
-                    kq = k > kq ? k : kq;
-                }
-            }
-            kq = wave_max64(kq);
-            const long long mq = key_value(kq);
-            if (mq <= 0) break;
-            long long kr = LLONG_MIN;
-#pragma unroll
-            for (int c = 0; c < kCh; ++c) {
-                const int jj = lane + 64 * c;
-                if (jj < epn) {
-                    const long long k = key_max_low(rem[c], jj);
-                    kr = k > kr ? k : kr;
-                }
-            }
-            kr = wave_max64(kr);
-            const long long mr = key_value(kr);
-            if (mr <= 0) break;
-            const int tr = key_index_low(kq), sj = key_index_low(kr);
-            const long long take = mr < mq ? mr : mq;
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-                if (lane + 64 * c == tr) quota[c] -= take;
-#pragma unroll
-            for (int c = 0; c < kCh; ++c)
-                if (lane + 64 * c == sj) rem[c] -= take;
-            if (lane == 0) {
-                const int at = atomicAdd(&s_nent, 1);
-                s_ent[at][0] = tr;
-                s_ent[at][1] = o * epn + sj;
-                s_ent[at][2] = (int)take;
-            }
-        }
+        if (narrow) owner_quotas<true, kCh>(quota, rem, o, R, epn, lane, &s_nent, s_ent);
+        else owner_quotas<false, kCh>(quota, rem, o, R, epn, lane, &s_nent, s_ent);
 #pragma unroll
         for (int c = 0; c < kCh; ++c) {
             const int jj = lane + 64 * c;
@@ -320,28 +435,8 @@ __global__ __launch_bounds__(kBalBlock) void balance_plan_kernel(BalArgs a) {
         }
         n = wave_sum(n);
         if (lane == 0) a.remote_stats[2 * d] = n;
-        for (int b = 0; b < B; ++b) {
-            long long k = LLONG_MIN;
-#pragma unroll
-            for (int c = 0; c < kCh; ++c) {
-                const int e = lane + 64 * c;
-                if (e < E) {
-                    const long long kk = key_max_high(remote[c], e);
-                    k = kk > k ? kk : k;
-                }
-            }
-            k = wave_max64(k);
-            const int best = key_index(k);
-            const int chosen = key_value(k) > 0 ? best : -1;
-#pragma unroll
-            for (int c = 0; c < kCh; ++c)
-                if (lane + 64 * c == best) remote[c] = 0;
-            if (lane == 0) {
-                s_slot[b] = chosen;
-                a.experts_to_copy[d * B + b] = chosen;
-                if (chosen >= 0) s_picked[chosen] = 1;
-            }
-        }
+        if (narrow) copy_choice<true, kCh>(remote, a, d, lane, s_slot, s_picked);
+        else copy_choice<false, kCh>(remote, a, d, lane, s_slot, s_picked);
     }
     lds_barrier();
     // E + B groups, a few consecutive per thread, scanned across the workgroup
@@ -395,7 +490,12 @@ __global__ __launch_bounds__(kBalBlock) void balance_plan_kernel(BalArgs a) {
 // ---------------------------------------------------------------------------------------------
 // A wave holds 64 / K whole tokens, one slot per lane (lanes past the last whole token idle), so
 // the dependent loads of the search run for every slot at once and a slot finds the ranks of
-// its token's earlier slots in the lanes just below it.
+// its token's earlier slots in the lanes just below it.  With at most kBalRowRanks ranks, a
+// multiple of 4, a slot reads its expert's whole cumulative row at once (16-byte loads) and
+// searches it in registers; otherwise a binary search (a dependent load per step).
+constexpr int kBalRowRanks = 16;
+
+template <bool ROW>
 __global__ __launch_bounds__(kBalTokBlock) void balance_dst_kernel(const int32_t* __restrict__ ids,
                                                                    const int32_t* __restrict__ cu_seqlens,
                                                                    const int32_t* __restrict__ e2p,
@@ -432,12 +532,34 @@ __global__ __launch_bounds__(kBalTokBlock) void balance_dst_kernel(const int32_t
         const int e = ids[i];
         const int q = e2p[i] - cu_seqlens[e];
         const int32_t* cum = alloc_cumsum + (int64_t)e * R;
-        int lo = 0, hi = R, pc = 0;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            const int ac = cum[mid];
-            if (ac > q) hi = mid;
-            else { lo = mid + 1; pc = ac; }
+        // lo = the first rank whose cumulative allocation exceeds q, pc = the one before it (0)
+        int lo = 0, pc = 0;
+        if constexpr (ROW) {
+            int cv[kBalRowRanks];
+#pragma unroll
+            for (int r4 = 0; r4 < kBalRowRanks; r4 += 4) {
+                int4 v = {0, 0, 0, 0};
+                if (r4 < R) v = *reinterpret_cast<const int4*>(cum + r4);
+                cv[r4] = v.x;
+                cv[r4 + 1] = v.y;
+                cv[r4 + 2] = v.z;
+                cv[r4 + 3] = v.w;
+            }
+            lo = R;
+#pragma unroll
+            for (int r = kBalRowRanks - 1; r >= 0; --r)
+                if (r < R && cv[r] > q) lo = r;
+#pragma unroll
+            for (int r = 0; r < kBalRowRanks; ++r)
+                if (r + 1 == lo) pc = cv[r];
+        } else {
+            int hi = R;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                const int ac = cum[mid];
+                if (ac > q) hi = mid;
+                else { lo = mid + 1; pc = ac; }
+            }
         }
         if (lo >= R) lo = R - 1;  // only for inputs that break the layout's invariants
         rank = lo;
@@ -520,8 +642,9 @@ extern "C" int mep_plan_balanced(const int32_t* topk_ids, const int32_t* tokens_
     else launch_ggl(balance_plan_kernel<16>, dim3(R), dim3(kBalBlock), 0, st, a);
     // at least one workgroup: workgroup 0 also counts the copies per owner
     const int64_t waves = N > 0 ? ceil_div64(N, 64 / K) : 1;
-    launch_ggl(balance_dst_kernel, dim3((unsigned)ceil_div64(waves, kBalTokBlock / 64)), dim3(kBalTokBlock), 0,
-               st, topk_ids, cu_seqlens, expanded_to_permuted, out->alloc_cumsum, out->expert_offsets,
+    auto dst_kernel = R <= kBalRowRanks && R % 4 == 0 ? balance_dst_kernel<true> : balance_dst_kernel<false>;
+    launch_ggl(dst_kernel, dim3((unsigned)ceil_div64(waves, kBalTokBlock / 64)), dim3(kBalTokBlock), 0, st,
+               topk_ids, cu_seqlens, expanded_to_permuted, out->alloc_cumsum, out->expert_offsets,
                num_copies > 0 ? out->experts_to_copy : nullptr, N, E, K, R, num_copies, NvS, out->dst,
                out->remote_stats);
     return launch_status();

@@ -67,6 +67,7 @@ CASES = [
     (0, 16, 2, 4, 2, 4, 1.0, 2.0),             # empty batch
     (256, 8, 2, 4, 2, 1, 0.0, 2.0),            # capacity 0: no rank is short
     (256, 8, 2, 4, 2, 1, 100.0, 2.0),          # capacity above every load: no moves
+    (256, 8, 2, 4, 2, 1, 20000.0, 2.0),        # balances beyond 2^21: the 64-bit keys
 ]
 
 
@@ -105,4 +106,17 @@ def test_balanced_dsv3_batch():
     print("balanced dsv3 batch", flush=True)
     ids = _skewed_ids(rng, N, E, K, 96.0)
     P = check_balanced(ids, E, R, 4, 128, N * K // R)
+    assert P.z.any() and (P.experts_to_copy >= 0).any()
+
+
+def test_balanced_wide_keys_with_moves():
+    """4.8 M one-slot tokens over two ranks of one expert each: the hot expert holds about 3.5 M
+    slots, beyond the 2^21 range of the 32-bit arg-extremum keys, so the balancing, quota and
+    copy loops run on 64-bit keys; one move and one copy."""
+    rng = np.random.default_rng(8)
+    N, E, K, R = 4_800_000, 2, 1, 2
+    print("balanced wide keys N=%d" % N, flush=True)
+    ids = _skewed_ids(rng, N, E, K, 1.0)
+    assert np.count_nonzero(ids == 0) >= 1 << 21
+    P = check_balanced(ids, E, R, 1, 1, N * K // R)
     assert P.z.any() and (P.experts_to_copy >= 0).any()

@@ -40,6 +40,7 @@ constexpr int kCountNT = 512;
 constexpr int kPlanNTBig = 1024;
 constexpr int kPlanNTSmall = 512;
 constexpr int kPlanRowNT = 512;  // threads that load the prefix rows
+static_assert(kPlanRowNT >= (kPathMaxNC + 3) / 4, "every column quad has a loader thread");
 enum : uint32_t { kSlotPlain = 0, kSlotHead = 1, kSlotDup = 2 };
 
 __device__ __forceinline__ uint32_t slot_code(int e, uint32_t type, int r, int h) {

@@ -171,9 +171,8 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 // experts [l*NPL, (l+1)*NPL); a key is the correctly rounded sigmoid plus the bias, ordered by
 // (key desc, expert asc) as one 64-bit word; group scores (binary32 sums of the top keys) and
 // ranks (score desc, group asc) as in the fast path but exact; then K rounds of a wave-wide
-// arg-max over the heads of the lanes' sorted keys.  Writes the K ids and weights.  Out of line,
-// so that its registers do not add to those of the kernel; the fields it needs are passed one by
-// one (a structure passed by value goes through scratch memory, a round trip per field).
+// arg-max over the heads of the lanes' sorted keys.  Writes the K ids and weights.  It runs after
+// the streaming loop, so inlined there its registers do not add to the loop's.
 template <int LPT, bool BF16, int MODE>
 __device__ __forceinline__ void exact_token_sig(const void* logits, const float* bias, int32_t* ids,
                                              float* weights, int K, int group_topn, int renormalize,

@@ -478,12 +478,18 @@ __global__ __launch_bounds__(kPlanNT) void path_plan_kernel(const int32_t* __res
         if (live) {
             if (o.p.itr) {
                 MEP_GLOBAL uint8_t* row = gptr(o.p.itr) + (t0 + tk) * R;
-                if ((R & 3) == 0) {
-                    for (int bb = 0; bb < R; bb += 4) {
-                        const uint32_t wd = ((m >> bb) & 1u) | (((m >> (bb + 1)) & 1u) << 8) |
-                                            (((m >> (bb + 2)) & 1u) << 16) | (((m >> (bb + 3)) & 1u) << 24);
-                        *reinterpret_cast<MEP_GLOBAL uint32_t*>(row + bb) = wd;
+                // four rank bits -> four bytes of 0 / 1 (the multiply places bit i at bit 8 i, with
+                // no carries between the shifted copies)
+                auto bytes4 = [](uint32_t b4) { return ((b4 & 15u) * 0x204081u) & 0x01010101u; };
+                if ((R & 15) == 0 && (((uintptr_t)o.p.itr) & 15u) == 0) {
+                    for (int bb = 0; bb < R; bb += 16) {
+                        const u32x4 v = {bytes4(m >> bb), bytes4(m >> (bb + 4)), bytes4(m >> (bb + 8)),
+                                         bytes4(m >> (bb + 12))};
+                        *reinterpret_cast<MEP_GLOBAL u32x4*>(row + bb) = v;
                     }
+                } else if ((R & 3) == 0) {
+                    for (int bb = 0; bb < R; bb += 4)
+                        *reinterpret_cast<MEP_GLOBAL uint32_t*>(row + bb) = bytes4(m >> bb);
                 } else {
                     for (int bb = 0; bb < R; ++bb) row[bb] = (uint8_t)((m >> bb) & 1u);
                 }

@@ -209,6 +209,41 @@ def test_fused_workspace_reuse_and_sharing():
         assert ws_error(ws) == 0
 
 
+def test_layout_plan_unaligned_buffers():
+    """mep_layout_plan with ids 4- but not 16-byte aligned (the plan-tile kernel then loads them
+    word by word) and is_token_in_rank 4- but not 16-byte aligned with R = 16 (its rows then go
+    out as words instead of 16-byte stores): every output as the oracle's."""
+    N, E, K, A, R, S, C = 3000, 64, 4, 16, 16, 4, 6
+    print("layout+plan unaligned N=%d E=%d K=%d R=%d" % (N, E, K, R), flush=True)
+    rng = np.random.default_rng(11)
+    ids_o = np.argsort(rng.random((N, E)), axis=1)[:, :K].astype(np.int32)
+    ids = torch.zeros(N * K + 1, dtype=torch.int32, device=DEV)[1:].view(N, K)
+    ids.copy_(torch.from_numpy(ids_o))
+    assert ids.data_ptr() % 16 == 4
+    L = B.alloc_layout(N, E, K, A, DEV)
+    P = B.alloc_plan(N, E, K, R, S, C, DEV)
+    P.is_token_in_rank = torch.full((N * R + 4,), 7, dtype=torch.uint8, device=DEV)[4:].view(N, R)
+    assert P.is_token_in_rank.data_ptr() % 16 == 4
+    ws = B.alloc_workspace(B.plan_workspace_size(N, E, K, R, S), DEV)
+    nvs = B.default_nvs(N, E, K, R, A)
+    B.mep_layout_plan(ids, E, A, L, R, S, C, nvs, P, ws)
+    torch.cuda.synchronize()
+    Lo = oracle.layout(ids_o, E, A)
+    T = int(Lo.cu_seqlens[E])
+    for name in ("tokens_per_expert", "cu_seqlens", "expanded_to_permuted", "zero_fill"):
+        assert np.array_equal(_np(getattr(L, name)), getattr(Lo, name)), name
+    assert np.array_equal(_np(L.permuted_to_expanded)[:T], Lo.permuted_to_expanded)
+    Po = oracle.plan(ids_o, Lo.cu_seqlens, Lo.expanded_to_permuted, E, R, S, C, nvs)
+    for name in ("is_token_in_rank", "num_tokens_per_rank", "num_tokens_per_expert",
+                 "rank_prefix_matrix", "channel_prefix_matrix", "recv_tokens", "recv_cu_seqlens",
+                 "recv_zero_fill", "dst", "dup_counts", "dup_offsets"):
+        assert np.array_equal(_np(getattr(P, name)), getattr(Po, name)), name
+    G, D = int(Po.dup_offsets[R, 0]), int(Po.dup_offsets[R, 1])
+    assert np.array_equal(_np(P.dup_groups)[:G], Po.dup_groups)
+    assert np.array_equal(_np(P.dup_loffs)[:D], Po.dup_loffs)
+    assert ws_error(ws) == 0
+
+
 def test_fused_run_twice_identical():
     wl = synth.WORKLOADS["dsv3"]
     inp = synth.make_inputs(wl, N=16384)

@@ -491,8 +491,9 @@ __global__ __launch_bounds__(kBalBlock) void balance_plan_kernel(BalArgs a) {
 // A wave holds 64 / K whole tokens, one slot per lane (lanes past the last whole token idle), so
 // the dependent loads of the search run for every slot at once and a slot finds the ranks of
 // its token's earlier slots in the lanes just below it.  With at most kBalRowRanks ranks, a
-// multiple of 4, a slot reads its expert's whole cumulative row at once (16-byte loads) and
-// searches it in registers; otherwise a binary search (a dependent load per step).
+// multiple of 4, and a 16-byte aligned table, a slot reads its expert's whole cumulative row at
+// once (16-byte loads) and searches it in registers; otherwise a binary search (a dependent load
+// per step).
 constexpr int kBalRowRanks = 16;
 
 template <bool ROW>
@@ -642,7 +643,10 @@ extern "C" int mep_plan_balanced(const int32_t* topk_ids, const int32_t* tokens_
     else launch_ggl(balance_plan_kernel<16>, dim3(R), dim3(kBalBlock), 0, st, a);
     // at least one workgroup: workgroup 0 also counts the copies per owner
     const int64_t waves = N > 0 ? ceil_div64(N, 64 / K) : 1;
-    auto dst_kernel = R <= kBalRowRanks && R % 4 == 0 ? balance_dst_kernel<true> : balance_dst_kernel<false>;
+    // the row search's 16-byte loads need 16-byte aligned rows: R a multiple of 4 and the table
+    // itself aligned (outputs are only required to be 4-byte aligned)
+    const bool row = R <= kBalRowRanks && R % 4 == 0 && aligned(out->alloc_cumsum, 16);
+    auto dst_kernel = row ? balance_dst_kernel<true> : balance_dst_kernel<false>;
     launch_ggl(dst_kernel, dim3((unsigned)ceil_div64(waves, kBalTokBlock / 64)), dim3(kBalTokBlock), 0, st,
                topk_ids, cu_seqlens, expanded_to_permuted, out->alloc_cumsum, out->expert_offsets,
                num_copies > 0 ? out->experts_to_copy : nullptr, N, E, K, R, num_copies, NvS, out->dst,

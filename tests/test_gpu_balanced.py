@@ -109,6 +109,30 @@ def test_balanced_dsv3_batch():
     assert P.z.any() and (P.experts_to_copy >= 0).any()
 
 
+def test_balanced_unaligned_cumsum():
+    """alloc_cumsum 4- but not 16-byte aligned: dst takes the binary search instead of the
+    16-byte row loads, with the same result."""
+    rng = np.random.default_rng(9)
+    N, E, K, R, nb, tp = 1000, 64, 8, 8, 4, 1
+    ids = _skewed_ids(rng, N, E, K, 8.0)
+    cap = N * K // R
+    NvS = B.balanced_nvs(N, E, K, R, nb, tp, cap)
+    L = oracle.layout(ids, E, 1)
+    want = oracle.plan_balanced(ids, L.tokens_per_expert, L.cu_seqlens, L.expanded_to_permuted,
+                                E, R, nb, tp, cap, NvS)
+    lay = SimpleNamespace(tokens_per_expert=torch.from_numpy(L.tokens_per_expert).to(DEV),
+                          cu_seqlens=torch.from_numpy(L.cu_seqlens).to(DEV),
+                          expanded_to_permuted=torch.from_numpy(L.expanded_to_permuted).to(DEV))
+    out = B.alloc_balanced(N, E, K, R, nb, DEV)
+    out.alloc_cumsum = torch.zeros(E * R + 1, dtype=torch.int32, device=DEV)[1:].view(E, R)
+    assert out.alloc_cumsum.data_ptr() % 16 == 4
+    B.mep_plan_balanced(torch.from_numpy(ids).to(DEV), lay, E, R, nb, tp, cap, NvS, out)
+    torch.cuda.synchronize()
+    for f in B.BALANCED_FIELDS:
+        assert np.array_equal(getattr(out, f).cpu().numpy(), getattr(want, f)), f
+    assert want.z.any()
+
+
 def test_balanced_wide_keys_with_moves():
     """4.8 M one-slot tokens over two ranks of one expert each: the hot expert holds about 3.5 M
     slots, beyond the 2^21 range of the 32-bit arg-extremum keys, so the balancing, quota and

@@ -706,6 +706,10 @@ PathGeom path_geom(int64_t N, int E, int K, int R, int S, int C, int A, int64_t 
 // zero by those kernels); the rows of this path follow them, overlapping only parts of the
 // workspace that every call of either kernel set rewrites before reading.
 constexpr size_t kPlanArriveBytes = 8192;
+// the plan-tile kernel reads the prefix rows as 16-byte quads: every row starts 16-byte aligned
+// (the workspace is 256-byte aligned and rows are NCs words, a multiple of 4)
+static_assert(sizeof(WsHeader) % 16 == 0 && kPathGsumWords * 4 % 16 == 0 && kPlanArriveBytes % 16 == 0,
+              "prefix rows 16-byte aligned");
 
 PathWsLayout path_ws_layout(const PathGeom& g) {
     PathWsLayout L;

@@ -68,6 +68,9 @@ CASES = [
     (256, 8, 2, 4, 2, 1, 0.0, 2.0),            # capacity 0: no rank is short
     (256, 8, 2, 4, 2, 1, 100.0, 2.0),          # capacity above every load: no moves
     (256, 8, 2, 4, 2, 1, 20000.0, 2.0),        # balances beyond 2^21: the 64-bit keys
+    (640, 96, 6, 16, 3, 2, 0.9, 12.0),         # R = 16: four 16-byte loads per allocation row
+    (600, 48, 4, 12, 2, 1, 1.0, 8.0),          # R = 12: three
+    (500, 36, 4, 6, 2, 1, 1.0, 6.0),           # R = 6: binary search
 ]
 
 
